@@ -1,0 +1,21 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    config.addinivalue_line("markers", "slow: large inputs (minutes of CPU)")
+
+
+@pytest.fixture(scope="session")
+def c_oracle():
+    from oracle import c_oracle
+
+    c_oracle.build(force=False)
+    return c_oracle
