@@ -1,0 +1,193 @@
+/*
+ * moe_decode.h -- C ABI of the MI355X (gfx950) decode-step MoE layer.
+ *
+ * One call runs one MoE layer of a decode (or speculative-verify) step for T
+ * tokens, from the router to the residual-add + RMSNorm boundary:
+ *
+ *   logits   = x . W_r^T                       (fp32 accumulation)
+ *   s        = sigmoid(logits)
+ *   ids      = top-k experts by s (+ bias), ties to the lower id
+ *   w        = R * s[ids] / sum s[ids]          (unbiased scores)
+ *   for each route (t, j), e = ids[t, j]:
+ *     g, u   = W13[e][0:I] . x_t, W13[e][I:2I] . x_t   (fp8 block-scaled)
+ *     a      = silu(min(g, L)) * clamp(u, -L, L)
+ *     y      = W2[e] . a
+ *   y_s      = the same expert MLP with the shared weights (weight 1)
+ *   h        = sum_j w[t, j] * y[t, j] + y_s[t] + residual[t]
+ *   residual_out = bf16(h);  out = bf16(h / sqrt(mean(h^2) + eps) * gamma)
+ *
+ * Where this comes from (vLLM API pages on the GLM-5.3-Flash specialized
+ * decode):
+ *   - page "vllm.models.glm5next.nvidia.specialized_decode.runtime.decode",
+ *     LayerStages._build_mega: the fused MoE stage is built only for sigmoid
+ *     scoring, one expert group and normalised top-k; its constructor takes
+ *     w13/w2 fp8 weights with their block scales, top_k, swiglu_limit,
+ *     routed_scaling_factor and the power-of-two (e8m0) scale flag; buffers
+ *     and the shared-expert side stream are made once at build time.
+ *   - same page, LayerStages._mega_moe: the shared expert runs on a side
+ *     stream forked from and joined back to the caller's stream; the routed
+ *     rows come back unfinalized with their expert weights and the shared
+ *     output beside them; the router bias is handed to the expert kernel.
+ *   - same page, LayerStages._router: router logits in fp32 from a bf16
+ *     router weight.
+ *   - page "vllm.models.glm5next.nvidia.specialized_decode.runtime.draft",
+ *     SpecializedDraft.reduced_norm / _build_ar_norm: the boundary after the
+ *     MoE finalizes the routed rows (it is built with top_k) and returns
+ *     norm(x + residual) together with the new residual.  On one GPU there is
+ *     no all-reduce to fuse into it.
+ *
+ * Conventions
+ *   - All tensors are row-major and contiguous, in device memory of the
+ *     plan's device, owned by the caller.  The library never frees them and
+ *     never writes an input.
+ *   - bf16 = 16-bit brain float bit patterns; fp8 = OCP e4m3fn codes;
+ *     e8m0 = one unsigned byte b per block meaning 2^(b-127) (255 invalid).
+ *   - Block scales cover 128x128 weight blocks and are multiplied in:
+ *     weight = code value * scale.
+ *   - Every entry point returns 0 on success or a moe_decode_status code; none
+ *     aborts.  moe_decode_strerror names a code.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_DECODE_OK = 0,
+  MOE_DECODE_ERR_INVALID_ARG = 1, /* null required pointer, T out of range, bad enum */
+  MOE_DECODE_ERR_UNSUPPORTED = 2, /* a size or device this library does not handle */
+  MOE_DECODE_ERR_HIP = 3,         /* a HIP runtime call failed */
+  MOE_DECODE_ERR_NO_MEMORY = 4    /* workspace allocation failed at plan time */
+} moe_decode_status;
+
+typedef enum { MOE_DECODE_SCALE_FP32 = 0, MOE_DECODE_SCALE_E8M0 = 1 } moe_decode_scale_fmt;
+
+/* Expert kernel family.  AUTO picks by token count; the others force one. */
+typedef enum {
+  MOE_DECODE_PATH_AUTO = 0,
+  MOE_DECODE_PATH_GEMV = 1,    /* fp8 dequant-FMA GEMV, one weight pass per touched expert */
+  MOE_DECODE_PATH_GROUPED = 2  /* fp8 MFMA over expert-grouped tokens */
+} moe_decode_path;
+
+/*
+ * Layer constants, fixed at plan time (the pages fix them in the stage
+ * constructors).  Limits: H, I and Is multiples of 128 with H <= 8192,
+ * I <= 8192 and Is <= 8192; 1 <= top_k <= 16; top_k <= E <= 1024;
+ * 1 <= max_tokens <= 256.  shared_intermediate = 0 means no shared expert.
+ */
+typedef struct {
+  int32_t hidden;              /* H */
+  int32_t num_experts;         /* E */
+  int32_t top_k;               /* k */
+  int32_t intermediate;        /* I, routed expert */
+  int32_t shared_intermediate; /* Is, shared expert (0 = none) */
+  int32_t max_tokens;          /* largest T a run may pass */
+  int32_t scale_fmt;           /* moe_decode_scale_fmt, for routed and shared weights */
+  int32_t path;                /* moe_decode_path */
+  float swiglu_limit;          /* L > 0 */
+  float routed_scaling_factor; /* R */
+  float rms_eps;               /* eps >= 0 */
+} moe_decode_desc;
+
+/*
+ * Per-call device pointers.  Shapes use T (the run's token count) and the
+ * plan's constants.  Scale tensors are float32 for MOE_DECODE_SCALE_FP32 and
+ * uint8 for MOE_DECODE_SCALE_E8M0.
+ */
+typedef struct {
+  const void* hidden;       /* [T, H] bf16: the MoE input x */
+  const void* residual;     /* [T, H] bf16 */
+  const void* router_w;     /* [E, H] bf16 */
+  const float* router_bias; /* [E] fp32 score-correction bias, or NULL */
+  const void* w13;          /* [E, 2I, H] fp8: rows [0, I) gate, [I, 2I) up */
+  const void* w13_scale;    /* [E, 2I/128, H/128] */
+  const void* w2;           /* [E, H, I] fp8 */
+  const void* w2_scale;     /* [E, H/128, I/128] */
+  const void* sw13;         /* [2Is, H] fp8 (ignored when Is = 0) */
+  const void* sw13_scale;   /* [2Is/128, H/128] */
+  const void* sw2;          /* [H, Is] fp8 */
+  const void* sw2_scale;    /* [H/128, Is/128] */
+  const void* gamma;        /* [H] bf16 RMSNorm weight */
+  void* out;                /* [T, H] bf16: RMSNorm(h) * gamma */
+  void* residual_out;       /* [T, H] bf16: h; may alias residual, nothing else */
+  int32_t* topk_ids;        /* [T, k] selected experts in rank order, or NULL */
+  float* topk_weights;      /* [T, k] their weights (R-scaled), or NULL */
+} moe_decode_args;
+
+typedef struct moe_decode_plan_s* moe_decode_plan_t;
+
+/*
+ * Checks a descriptor on the host without touching any device.
+ * Returns OK, INVALID_ARG (null, bad enum, non-positive size) or
+ * UNSUPPORTED (outside the limits above).
+ */
+int moe_decode_desc_check(const moe_decode_desc* d);
+
+/*
+ * Checks a run's arguments against a descriptor on the host (pointers are
+ * not dereferenced).  Returns OK or INVALID_ARG (T < 0, T > max_tokens, a
+ * required pointer NULL, out aliasing an input).
+ */
+int moe_decode_args_check(const moe_decode_desc* d, const moe_decode_args* a, int32_t T);
+
+/*
+ * Builds a plan on HIP device `device`: validates the descriptor, checks the
+ * device is gfx950, allocates the workspace for max_tokens, creates the side
+ * stream (default priority) and its events.  On success *out owns them until
+ * moe_decode_destroy; on failure *out is set to NULL and nothing is leaked.
+ */
+int moe_decode_plan(const moe_decode_desc* d, int device, moe_decode_plan_t* out);
+
+/*
+ * Runs the layer for T tokens, asynchronously on `stream` (a hipStream_t of
+ * the plan's device; NULL = the null stream).  No allocation and no host
+ * synchronisation, so the call may be captured into a HIP graph.  The shared
+ * expert runs on the plan's side stream, forked from `stream` at entry and
+ * joined back before the boundary.  T = 0 returns OK and launches nothing.
+ * On an error after the fork the side stream is joined back first.  Runs on
+ * one plan must not overlap (they share its workspace).
+ */
+int moe_decode_run(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, void* stream);
+
+/* Frees the plan's workspace, side stream and events.  NULL is a no-op. */
+int moe_decode_destroy(moe_decode_plan_t p);
+
+/* Static text naming a status code. */
+const char* moe_decode_strerror(int code);
+
+/*
+ * Token -> expert permutation of the plan's last run, copied on `stream`
+ * into caller device buffers (any may be NULL):
+ *   counts [E]      routes per expert
+ *   offsets [E+1]   exclusive prefix sum of counts
+ *   perm [T*k]      routes r = t*k + j sorted by expert, in r order within one
+ *   touched [E]     experts with count > 0 in ascending id; n_touched [1] of them
+ * T must be the last run's T.  This is the pages' expanded-index-to-permuted-
+ * index table (LayerStages._mega_moe) in inverse form.
+ */
+int moe_decode_last_routes(moe_decode_plan_t p, int32_t T, int32_t* counts, int32_t* offsets,
+                           int32_t* perm, int32_t* touched, int32_t* n_touched, void* stream);
+
+/*
+ * Measurement hook: when both are non-NULL, each later run records hipEvent_t
+ * `begin` on `stream` just before the routed-expert projection kernels and
+ * `end` just after them (the kernels that stream the routed weights).
+ * NULL, NULL switches it off.
+ */
+int moe_decode_set_expert_events(moe_decode_plan_t p, void* begin, void* end);
+
+/* Which expert path a run with T tokens takes (moe_decode_path value). */
+int moe_decode_path_for(moe_decode_plan_t p, int32_t T);
+
+/* Device bytes the plan holds for its workspace. */
+size_t moe_decode_workspace_bytes(moe_decode_plan_t p);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_DECODE_H */

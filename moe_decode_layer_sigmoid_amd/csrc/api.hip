@@ -1,0 +1,296 @@
+// C ABI of the MoE decode layer: validation, plan (workspace, side stream,
+// events), run (fork/join of the shared expert, kernel sequence), destroy.
+//
+// Follows the vLLM API page "vllm.models.glm5next.nvidia.specialized_decode.
+// runtime.decode": LayerStages._build_mega allocates the route-order buffer
+// and the shared-expert stream once, before any capture; LayerStages._mega_moe
+// forks the shared expert onto that stream (it waits on the caller's stream)
+// and joins it back (the caller's stream waits on it) after the routed
+// experts.  Page "vllm.models.deepseek_v41.nvidia.specialized_decode.runtime.
+// draft", DraftDecode.run: on an error the side stream is rejoined before the
+// error is reported, so a graph capture sees no unjoined work.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "../../include/moe_decode.h"
+#include "device_common.h"
+#include "launch.h"
+
+struct moe_decode_plan_s {
+  moe_decode_desc desc;
+  int device;
+  void* ws_base;
+  size_t ws_bytes;
+  moe::Workspace ws;
+  hipStream_t side;
+  hipEvent_t fork, join;
+  hipEvent_t user_begin, user_end;
+};
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int path_for(const moe_decode_desc& d, int32_t T) {
+  (void)T;
+  if (d.path == MOE_DECODE_PATH_GEMV || d.path == MOE_DECODE_PATH_GROUPED) return d.path;
+  return MOE_DECODE_PATH_GEMV;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+// Lays the workspace out from `base` (nullptr: only sizes it).
+size_t layout(const moe_decode_desc& d, char* base, moe::Workspace* ws) {
+  const size_t T = d.max_tokens, E = d.num_experts, k = d.top_k, H = d.hidden;
+  const size_t I = d.intermediate, Is = d.shared_intermediate;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  moe::Workspace w{};
+  w.logits = reinterpret_cast<float*>(take(T * E * 4));
+  w.ids = reinterpret_cast<int32_t*>(take(T * k * 4));
+  w.weights = reinterpret_cast<float*>(take(T * k * 4));
+  w.counts = reinterpret_cast<int32_t*>(take(E * 4));
+  w.offsets = reinterpret_cast<int32_t*>(take((E + 1) * 4));
+  w.touched = reinterpret_cast<int32_t*>(take(E * 4));
+  w.n_touched = reinterpret_cast<int32_t*>(take(4));
+  w.perm = reinterpret_cast<int32_t*>(take(T * k * 4));
+  w.inv = reinterpret_cast<int32_t*>(take(T * k * 4));
+  w.act = reinterpret_cast<float*>(take(T * k * I * 4));
+  w.act_s = reinterpret_cast<float*>(take(T * (Is ? Is : 1) * 4));
+  w.rows = reinterpret_cast<float*>(take(T * k * H * 4));
+  w.y_s = reinterpret_cast<float*>(take(T * H * 4));
+  w.counter = reinterpret_cast<uint32_t*>(take(64));
+  if (ws) *ws = w;
+  return off;
+}
+
+moe::LayerDims dims(const moe_decode_desc& d, int32_t T) {
+  moe::LayerDims x;
+  x.T = T;
+  x.H = d.hidden;
+  x.E = d.num_experts;
+  x.k = d.top_k;
+  x.I = d.intermediate;
+  x.Is = d.shared_intermediate;
+  x.e8m0 = d.scale_fmt == MOE_DECODE_SCALE_E8M0;
+  x.limit = d.swiglu_limit;
+  x.rsf = d.routed_scaling_factor;
+  x.eps = d.rms_eps;
+  return x;
+}
+
+}  // namespace
+
+static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t T,
+                         hipStream_t s);
+
+extern "C" {
+
+const char* moe_decode_strerror(int code) {
+  switch (code) {
+    case MOE_DECODE_OK: return "ok";
+    case MOE_DECODE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_DECODE_ERR_UNSUPPORTED: return "unsupported size or device";
+    case MOE_DECODE_ERR_HIP: return "HIP runtime error";
+    case MOE_DECODE_ERR_NO_MEMORY: return "device allocation failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_decode_desc_check(const moe_decode_desc* d) {
+  if (!d) return MOE_DECODE_ERR_INVALID_ARG;
+  if (d->hidden <= 0 || d->num_experts <= 0 || d->top_k <= 0 || d->intermediate <= 0 ||
+      d->shared_intermediate < 0 || d->max_tokens <= 0)
+    return MOE_DECODE_ERR_INVALID_ARG;
+  if (d->scale_fmt != MOE_DECODE_SCALE_FP32 && d->scale_fmt != MOE_DECODE_SCALE_E8M0)
+    return MOE_DECODE_ERR_INVALID_ARG;
+  if (d->path < MOE_DECODE_PATH_AUTO || d->path > MOE_DECODE_PATH_GROUPED)
+    return MOE_DECODE_ERR_INVALID_ARG;
+  if (!(d->swiglu_limit > 0.f) || !(d->rms_eps >= 0.f) ||
+      !(d->routed_scaling_factor == d->routed_scaling_factor))
+    return MOE_DECODE_ERR_INVALID_ARG;
+  if (d->hidden % moe::kBlock || d->intermediate % moe::kBlock ||
+      d->shared_intermediate % moe::kBlock)
+    return MOE_DECODE_ERR_UNSUPPORTED;
+  if (d->hidden > 8192 || d->intermediate > 8192 || d->shared_intermediate > 8192)
+    return MOE_DECODE_ERR_UNSUPPORTED;
+  if (d->top_k > moe::kMaxTopK || d->top_k > d->num_experts ||
+      d->num_experts > moe::kMaxExperts || d->max_tokens > moe::kMaxTokens)
+    return MOE_DECODE_ERR_UNSUPPORTED;
+  if (d->path == MOE_DECODE_PATH_GROUPED) return MOE_DECODE_ERR_UNSUPPORTED;
+  return MOE_DECODE_OK;
+}
+
+int moe_decode_args_check(const moe_decode_desc* d, const moe_decode_args* a, int32_t T) {
+  if (!d || !a) return MOE_DECODE_ERR_INVALID_ARG;
+  if (T < 0 || T > d->max_tokens) return MOE_DECODE_ERR_INVALID_ARG;
+  const void* req[] = {a->hidden, a->residual, a->router_w, a->w13, a->w13_scale, a->w2,
+                       a->w2_scale, a->gamma, a->out, a->residual_out};
+  for (const void* p : req)
+    if (!p) return MOE_DECODE_ERR_INVALID_ARG;
+  if (d->shared_intermediate > 0 && (!a->sw13 || !a->sw13_scale || !a->sw2 || !a->sw2_scale))
+    return MOE_DECODE_ERR_INVALID_ARG;
+  // 16-byte vector loads and stores need 16-byte aligned tensors.
+  const void* vec[] = {a->hidden, a->residual, a->router_w, a->w13, a->w2, a->gamma,
+                       a->out, a->residual_out, a->sw13, a->sw2};
+  for (const void* p : vec)
+    if (p && !aligned16(p)) return MOE_DECODE_ERR_INVALID_ARG;
+  // out is written while hidden/residual/gamma are still being read.
+  if (a->out == a->hidden || a->out == a->residual || a->out == a->residual_out ||
+      a->residual_out == a->hidden)
+    return MOE_DECODE_ERR_INVALID_ARG;
+  return MOE_DECODE_OK;
+}
+
+int moe_decode_plan(const moe_decode_desc* d, int device, moe_decode_plan_t* out) {
+  if (!out) return MOE_DECODE_ERR_INVALID_ARG;
+  *out = nullptr;
+  int rc = moe_decode_desc_check(d);
+  if (rc) return rc;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev)
+    return MOE_DECODE_ERR_INVALID_ARG;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return MOE_DECODE_ERR_HIP;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MOE_DECODE_ERR_UNSUPPORTED;
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess) return MOE_DECODE_ERR_HIP;
+  if (hipSetDevice(device) != hipSuccess) return MOE_DECODE_ERR_HIP;
+
+  auto* p = new (std::nothrow) moe_decode_plan_s();
+  if (!p) {
+    (void)hipSetDevice(prev);
+    return MOE_DECODE_ERR_NO_MEMORY;
+  }
+  p->desc = *d;
+  p->device = device;
+  p->ws_bytes = layout(*d, nullptr, nullptr);
+  rc = MOE_DECODE_OK;
+  if (hipMalloc(&p->ws_base, p->ws_bytes) != hipSuccess) {
+    p->ws_base = nullptr;
+    rc = MOE_DECODE_ERR_NO_MEMORY;
+  }
+  if (!rc) {
+    layout(*d, static_cast<char*>(p->ws_base), &p->ws);
+    if (hipMemset(p->ws_base, 0, p->ws_bytes) != hipSuccess ||
+        hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking) != hipSuccess)
+      rc = MOE_DECODE_ERR_HIP;
+  }
+  if (!rc && (hipEventCreateWithFlags(&p->fork, hipEventDisableTiming) != hipSuccess ||
+              hipEventCreateWithFlags(&p->join, hipEventDisableTiming) != hipSuccess))
+    rc = MOE_DECODE_ERR_HIP;
+  if (!rc && hipDeviceSynchronize() != hipSuccess) rc = MOE_DECODE_ERR_HIP;
+  (void)hipSetDevice(prev);
+  if (rc) {
+    moe_decode_destroy(p);
+    return rc;
+  }
+  *out = p;
+  return MOE_DECODE_OK;
+}
+
+int moe_decode_destroy(moe_decode_plan_t p) {
+  if (!p) return MOE_DECODE_OK;
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(p->device);
+  if (p->side) (void)hipStreamSynchronize(p->side);
+  if (p->fork) (void)hipEventDestroy(p->fork);
+  if (p->join) (void)hipEventDestroy(p->join);
+  if (p->side) (void)hipStreamDestroy(p->side);
+  if (p->ws_base) (void)hipFree(p->ws_base);
+  (void)hipSetDevice(prev);
+  delete p;
+  return MOE_DECODE_OK;
+}
+
+int moe_decode_run(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, void* stream) {
+  if (!p) return MOE_DECODE_ERR_INVALID_ARG;
+  int rc = moe_decode_args_check(&p->desc, a, T);
+  if (rc) return rc;
+  if (T == 0) return MOE_DECODE_OK;
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) return MOE_DECODE_ERR_HIP;
+  if (prev != p->device && hipSetDevice(p->device) != hipSuccess) return MOE_DECODE_ERR_HIP;
+  rc = run_on_device(p, a, T, static_cast<hipStream_t>(stream));
+  if (prev != p->device) (void)hipSetDevice(prev);
+  return rc;
+}
+
+static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t T,
+                         hipStream_t s) {
+  const moe::LayerDims d = dims(p->desc, T);
+  const bool has_shared = d.Is > 0;
+
+  if (hipEventRecord(p->fork, s) != hipSuccess) return MOE_DECODE_ERR_HIP;
+  if (hipStreamWaitEvent(p->side, p->fork, 0) != hipSuccess) return MOE_DECODE_ERR_HIP;
+
+  hipError_t err = hipSuccess;
+  auto step = [&](hipError_t e) {
+    if (err == hipSuccess && e != hipSuccess) err = e;
+  };
+  if (has_shared) {
+    step(moe::launch_gate_up_gemv(d, true, a->hidden, a->sw13, a->sw13_scale, p->ws, p->side));
+    if (err == hipSuccess) step(moe::launch_down_gemv(d, true, a->sw2, a->sw2_scale, p->ws, p->side));
+  }
+  if (err == hipSuccess)
+    step(moe::launch_router(d, a->hidden, a->router_w, a->router_bias, p->ws, a->topk_ids,
+                            a->topk_weights, s));
+  if (err == hipSuccess && p->user_begin) step(hipEventRecord(p->user_begin, s));
+  if (err == hipSuccess)
+    step(moe::launch_gate_up_gemv(d, false, a->hidden, a->w13, a->w13_scale, p->ws, s));
+  if (err == hipSuccess) step(moe::launch_down_gemv(d, false, a->w2, a->w2_scale, p->ws, s));
+  if (err == hipSuccess && p->user_end) step(hipEventRecord(p->user_end, s));
+
+  // Join the side stream on every path, then run the boundary.
+  hipError_t jerr = hipEventRecord(p->join, p->side);
+  if (jerr == hipSuccess) jerr = hipStreamWaitEvent(s, p->join, 0);
+  if (err == hipSuccess) err = jerr;
+  if (err == hipSuccess)
+    step(moe::launch_epilogue(d, a->residual, a->gamma, p->ws, a->out, a->residual_out, s));
+  return err == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;
+}
+
+int moe_decode_last_routes(moe_decode_plan_t p, int32_t T, int32_t* counts, int32_t* offsets,
+                           int32_t* perm, int32_t* touched, int32_t* n_touched, void* stream) {
+  if (!p || T < 0 || T > p->desc.max_tokens) return MOE_DECODE_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t E = p->desc.num_experts, R = static_cast<size_t>(T) * p->desc.top_k;
+  struct {
+    void* dst;
+    const void* src;
+    size_t n;
+  } cp[] = {{counts, p->ws.counts, E * 4},
+            {offsets, p->ws.offsets, (E + 1) * 4},
+            {perm, p->ws.perm, R * 4},
+            {touched, p->ws.touched, E * 4},
+            {n_touched, p->ws.n_touched, 4}};
+  for (auto& c : cp)
+    if (c.dst && c.n &&
+        hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return MOE_DECODE_ERR_HIP;
+  return MOE_DECODE_OK;
+}
+
+int moe_decode_set_expert_events(moe_decode_plan_t p, void* begin, void* end) {
+  if (!p || (!begin) != (!end)) return MOE_DECODE_ERR_INVALID_ARG;
+  p->user_begin = static_cast<hipEvent_t>(begin);
+  p->user_end = static_cast<hipEvent_t>(end);
+  return MOE_DECODE_OK;
+}
+
+int moe_decode_path_for(moe_decode_plan_t p, int32_t T) {
+  if (!p) return -MOE_DECODE_ERR_INVALID_ARG;
+  return path_for(p->desc, T);
+}
+
+size_t moe_decode_workspace_bytes(moe_decode_plan_t p) { return p ? p->ws_bytes : 0; }
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Host-side launchers of the MoE decode kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Device workspace of one plan, sized for max_tokens.
+struct Workspace {
+  float* logits;       // [maxT, E]
+  int32_t* ids;        // [maxT, k]
+  float* weights;      // [maxT, k]
+  int32_t* counts;     // [E]
+  int32_t* offsets;    // [E + 1]
+  int32_t* touched;    // [E]
+  int32_t* n_touched;  // [1]
+  int32_t* perm;       // [maxT * k]  permuted position -> route t*k+j
+  int32_t* inv;        // [maxT * k]  route -> permuted position
+  float* act;          // [maxT * k, I]   routed SwiGLU output, permuted order
+  float* act_s;        // [maxT, Is]      shared SwiGLU output
+  float* rows;         // [maxT * k, H]   routed down output, permuted order
+  float* y_s;          // [maxT, H]       shared expert output
+  uint32_t* counter;   // [1] last-block counter of the router (self-resetting)
+};
+
+struct LayerDims {
+  int T, H, E, k, I, Is;
+  bool e8m0;
+  float limit, rsf, eps;
+};
+
+// Router logits, sigmoid, top-k, weights and the route tables.
+hipError_t launch_router(const LayerDims& d, const void* hidden, const void* router_w,
+                         const float* bias, const Workspace& ws, int32_t* ids_out,
+                         float* weights_out, hipStream_t s);
+
+// gate_up + clamped SwiGLU (GEMV).  Routed: one grid row per touched-expert
+// slot; shared: all tokens through the shared weights.
+hipError_t launch_gate_up_gemv(const LayerDims& d, bool shared, const void* hidden,
+                               const void* w13, const void* w13_scale, const Workspace& ws,
+                               hipStream_t s);
+
+// down projection (GEMV) of the SwiGLU activations.
+hipError_t launch_down_gemv(const LayerDims& d, bool shared, const void* w2,
+                            const void* w2_scale, const Workspace& ws, hipStream_t s);
+
+// Weighted combine + shared + residual, RMSNorm * gamma, bf16 outputs.
+hipError_t launch_epilogue(const LayerDims& d, const void* residual, const void* gamma,
+                           const Workspace& ws, void* out, void* residual_out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,207 @@
+"""GPU parity: the HIP layer (through the C ABI) against the CPU oracle.
+
+Needs an MI355X; every test is marked `gpu`.  Sizes: the tiny layer and small
+random layers are compared in full; the 1- and 16-token decode layers are
+compared in full with the C oracle; the 64- and 128-token wide layers are
+compared on every token's expert ids and on sampled token rows of the
+outputs (the oracle computes those rows one by one).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_decode_layer_sigmoid_amd as md
+import oracle
+from synth import LayerShape, WORKLOADS, make_layer
+from layer_harness import (check_ids, check_layer, make_plan, run_layer, to_device,
+                           assert_close)
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    assert md.lib() is not None
+
+
+def _case(shape, c_oracle, rows=None, max_tokens=None, path=md.PATH_AUTO, with_bias=False,
+          alias=False, seed=0):
+    _log("case", shape, "rows", rows, "bias", with_bias, "alias", alias)
+    inp = make_layer(shape, seed=seed, with_bias=with_bias, bias_std=0.1)
+    dev = to_device(inp)
+    plan = make_plan(shape, max_tokens=max_tokens, path=path)
+    got = run_layer(plan, dev, shape.T, alias_residual=alias)
+    err = check_layer(inp, got, rows=rows, c_oracle=c_oracle)
+    _log("  errors", err)
+    plan.close()
+    return inp, got, err
+
+
+def test_tiny_layer(c_oracle):
+    _case(WORKLOADS["tiny_t1"], c_oracle)
+
+
+@pytest.mark.parametrize("name", ["decode_t1", "decode_t16"])
+def test_decode_layers_full(name, c_oracle):
+    inp, got, err = _case(WORKLOADS[name], c_oracle)
+    if name == "decode_t16":
+        d = len(np.unique(got["ids"]))
+        _log("  distinct experts", d)
+        assert 60 <= d <= 100
+
+
+@pytest.mark.parametrize("name", ["wide_t64_e8m0", "verify_t128"])
+def test_wide_layers_sampled(name, c_oracle):
+    sh = WORKLOADS[name]
+    rows = [0, 1, sh.T // 2, sh.T - 1]
+    _case(sh, c_oracle, rows=rows)
+
+
+SMALL = [
+    # T, H, E, k, I, Is, fmt
+    (1, 128, 4, 1, 128, 0, "fp32"),
+    (3, 256, 16, 4, 256, 128, "e8m0"),
+    (7, 384, 33, 5, 128, 256, "fp32"),
+    (20, 256, 64, 8, 384, 128, "fp32"),
+    (5, 1152, 70, 16, 256, 128, "e8m0"),
+    (2, 640, 8, 8, 128, 128, "fp32"),  # k == E: every expert taken
+    (64, 256, 128, 8, 128, 128, "e8m0"),
+    (130, 128, 200, 6, 128, 0, "fp32"),  # more than two 64-token mask words
+    (1, 8192, 16, 2, 128, 128, "fp32"),  # widest hidden
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[str(c) for c in SMALL])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_small_layers(case, with_bias, c_oracle):
+    T, H, E, k, I, Is, fmt = case
+    sh = LayerShape(T=T, H=H, E=E, k=k, I=I, Is=Is, scale_fmt=fmt, tag=300 + sum(case[:6]))
+    _case(sh, c_oracle, with_bias=with_bias)
+
+
+def test_route_tables_match_oracle(c_oracle):
+    sh = WORKLOADS["decode_t16"].replace(H=1024, I=256, Is=256, tag=301)
+    inp = make_layer(sh)
+    dev = to_device(inp)
+    plan = make_plan(sh)
+    got = run_layer(plan, dev, sh.T)
+    E, R = sh.E, sh.T * sh.k
+    cnt = torch.empty(E, dtype=torch.int32, device="cuda")
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(R, dtype=torch.int32, device="cuda")
+    tch = torch.empty(E, dtype=torch.int32, device="cuda")
+    nt = torch.empty(1, dtype=torch.int32, device="cuda")
+    plan.last_routes(sh.T, cnt, off, perm, tch, nt)
+    torch.cuda.synchronize()
+    counts, offsets, operm, _ = oracle.route_table(got["ids"], E)
+    assert np.array_equal(cnt.cpu().numpy(), counts)
+    assert np.array_equal(off.cpu().numpy(), offsets)
+    assert np.array_equal(perm.cpu().numpy(), operm)
+    touched = np.nonzero(counts)[0]
+    assert nt.item() == len(touched)
+    assert np.array_equal(tch.cpu().numpy()[: len(touched)], touched)
+    plan.close()
+
+
+def test_same_expert_for_every_token(c_oracle):
+    """All tokens pick the same experts: one expert carries T tokens (the
+    token loop runs several register passes)."""
+    sh = LayerShape(T=37, H=256, E=16, k=2, I=128, Is=128, tag=302)
+    inp = make_layer(sh)
+    # Every token carries token 0's vector x0; router rows 3 and 9 point along
+    # x0 (logits |x0| and |x0|/2), every other row is zero (logit 0).
+    from synth import f32_to_bf16_bits
+    inp.hidden = np.ascontiguousarray(np.tile(inp.hidden[:1], (37, 1)))
+    x0 = oracle.bf16_bits_to_f64(inp.hidden[0])
+    wr = np.zeros((16, 256), np.float32)
+    wr[3] = (x0 / np.linalg.norm(x0)).astype(np.float32)
+    wr[9] = 0.5 * wr[3]
+    inp.router_w = f32_to_bf16_bits(wr)
+    dev = to_device(inp)
+    plan = make_plan(sh)
+    got = run_layer(plan, dev, sh.T)
+    assert np.all(np.sort(got["ids"], 1) == [3, 9])
+    check_layer(inp, got, c_oracle=c_oracle)
+    plan.close()
+
+
+def test_residual_alias_and_determinism(c_oracle):
+    sh = WORKLOADS["decode_t16"].replace(H=2048, I=512, Is=512, tag=303)
+    inp = make_layer(sh)
+    dev = to_device(inp)
+    plan = make_plan(sh)
+    a = run_layer(plan, dev, sh.T)
+    b = run_layer(plan, dev, sh.T)
+    c = run_layer(plan, dev, sh.T, alias_residual=True)
+    for key in ("out", "residual_out", "ids", "weights"):
+        assert np.array_equal(a[key], b[key]), key
+        assert np.array_equal(a[key], c[key]), key
+    check_layer(inp, a, c_oracle=c_oracle)
+    plan.close()
+
+
+def test_smaller_T_than_plan_and_zero(c_oracle):
+    sh = LayerShape(T=9, H=512, E=32, k=4, I=256, Is=128, tag=304)
+    inp = make_layer(sh)
+    dev = to_device(inp)
+    plan = make_plan(sh, max_tokens=64)
+    got = run_layer(plan, dev, sh.T)
+    check_layer(inp, got, c_oracle=c_oracle)
+    # T = 0 launches nothing and succeeds
+    plan.run(0, hidden=dev["hidden"], residual=dev["residual"], router_w=dev["router_w"],
+             w13=dev["w13"], w13_scale=dev["w13_scale"], w2=dev["w2"], w2_scale=dev["w2_scale"],
+             sw13=dev["sw13"], sw13_scale=dev["sw13_scale"], sw2=dev["sw2"],
+             sw2_scale=dev["sw2_scale"], gamma=dev["gamma"],
+             out=torch.empty(1, 512, dtype=torch.int16, device="cuda"),
+             residual_out=torch.empty(1, 512, dtype=torch.int16, device="cuda"))
+    with pytest.raises(md.MoeDecodeError):
+        run_layer(plan, dev, 65)
+    plan.close()
+
+
+def test_graph_replay_matches_eager(c_oracle):
+    """One run captured into a HIP graph, replayed several times with eager
+    work in between; every replay equals the eager result bit for bit."""
+    sh = WORKLOADS["decode_t16"].replace(H=1024, I=512, Is=256, tag=305)
+    inp = make_layer(sh)
+    dev = to_device(inp)
+    plan = make_plan(sh)
+    eager = run_layer(plan, dev, sh.T, keep_device=True)
+    T, H, k = sh.T, sh.H, sh.k
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    res = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    args = plan.make_args(hidden=dev["hidden"], residual=dev["residual"],
+                          router_w=dev["router_w"], w13=dev["w13"], w13_scale=dev["w13_scale"],
+                          w2=dev["w2"], w2_scale=dev["w2_scale"], sw13=dev["sw13"],
+                          sw13_scale=dev["sw13_scale"], sw2=dev["sw2"],
+                          sw2_scale=dev["sw2_scale"], gamma=dev["gamma"], out=out,
+                          residual_out=res, topk_ids=ids, topk_weights=w)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        plan.run_args(args, T)  # warm up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            plan.run_args(args, T)
+    torch.cuda.synchronize()
+    for i in range(4):
+        out.zero_()
+        res.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager["dev"]["out"]), i
+        assert torch.equal(res, eager["dev"]["residual_out"]), i
+        assert torch.equal(ids, eager["dev"]["ids"]), i
+        # eager work between replays
+        run_layer(plan, dev, T)
+    plan.close()
