@@ -123,7 +123,9 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ router_w,
     const float* __restrict__ bias, int T, int H, int E, int k, float rsf, Workspace ws,
     int32_t* __restrict__ ids_out, float* __restrict__ w_out, uint32_t total_blocks) {
-  extern __shared__ unsigned char smem[];
+  // 16-byte aligned: the 64-bit token masks below need 8-byte aligned LDS
+  // addresses, and dynamic LDS starts right after the static variables.
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int s_last;
   __shared__ int s_tmp[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
