@@ -70,8 +70,15 @@ typedef enum { MOE_DECODE_SCALE_FP32 = 0, MOE_DECODE_SCALE_E8M0 = 1 } moe_decode
 /* Expert kernel family.  AUTO picks by token count; the others force one. */
 typedef enum {
   MOE_DECODE_PATH_AUTO = 0,
-  MOE_DECODE_PATH_GEMV = 1,    /* fp8 dequant-FMA GEMV, one weight pass per touched expert */
-  MOE_DECODE_PATH_GROUPED = 2  /* fp8 MFMA over expert-grouped tokens */
+  /* fp8 dequant-FMA GEMV, one weight pass per touched expert.  Up to 16
+   * tokens the whole step is one persistent kernel (router, shared expert,
+   * routed experts and boundary on one ordered work queue); above that the
+   * GEMV_SPLIT kernels run. */
+  MOE_DECODE_PATH_GEMV = 1,
+  MOE_DECODE_PATH_GROUPED = 2,   /* fp8 MFMA over expert-grouped tokens */
+  /* The GEMV kernels launched one after another (router, gate_up, down,
+   * boundary), the shared expert on the plan's side stream. */
+  MOE_DECODE_PATH_GEMV_SPLIT = 3
 } moe_decode_path;
 
 /*
@@ -146,9 +153,10 @@ int moe_decode_plan(const moe_decode_desc* d, int device, moe_decode_plan_t* out
 /*
  * Runs the layer for T tokens, asynchronously on `stream` (a hipStream_t of
  * the plan's device; NULL = the null stream).  No allocation and no host
- * synchronisation, so the call may be captured into a HIP graph.  The shared
- * expert runs on the plan's side stream, forked from `stream` at entry and
- * joined back before the boundary.  T = 0 returns OK and launches nothing.
+ * synchronisation, so the call may be captured into a HIP graph.  On the
+ * split GEMV path the shared expert runs on the plan's side stream, forked
+ * from `stream` at entry and joined back before the boundary; the fused path
+ * queues it inside its single kernel.  T = 0 returns OK and launches nothing.
  * On an error after the fork the side stream is joined back first.  Runs on
  * one plan must not overlap (they share its workspace).
  */
@@ -181,8 +189,18 @@ int moe_decode_last_routes(moe_decode_plan_t p, int32_t T, int32_t* counts, int3
  */
 int moe_decode_set_expert_events(moe_decode_plan_t p, void* begin, void* end);
 
-/* Which expert path a run with T tokens takes (moe_decode_path value). */
+/* Which kernels a run with T tokens takes: MOE_DECODE_PATH_GEMV (the fused
+ * persistent kernel), MOE_DECODE_PATH_GEMV_SPLIT or MOE_DECODE_PATH_GROUPED;
+ * negative status on a bad argument. */
 int moe_decode_path_for(moe_decode_plan_t p, int32_t T);
+
+/*
+ * Health check of the fused kernel's bounded waits: synchronises the plan's
+ * device, returns in *gave_up whether any wait since the last check ran out
+ * of its spin budget (which would mean a result is not trustworthy) and
+ * clears the flag.  Not capturable; for tests and monitoring.
+ */
+int moe_decode_check_waits(moe_decode_plan_t p, int32_t* gave_up);
 
 /* Device bytes the plan holds for its workspace. */
 size_t moe_decode_workspace_bytes(moe_decode_plan_t p);

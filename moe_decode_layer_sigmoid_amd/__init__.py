@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     PATH_AUTO,
     PATH_GEMV,
     PATH_GROUPED,
+    PATH_GEMV_SPLIT,
     SCALE_E8M0,
     SCALE_FP32,
     args_check,

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_decode.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_NO_MEMORY = range(5)
 SCALE_FP32, SCALE_E8M0 = 0, 1
-PATH_AUTO, PATH_GEMV, PATH_GROUPED = 0, 1, 2
+PATH_AUTO, PATH_GEMV, PATH_GROUPED, PATH_GEMV_SPLIT = 0, 1, 2, 3
 
 
 class MoeDecodeError(RuntimeError):
@@ -72,10 +72,11 @@ def lib():
         L.moe_decode_last_routes.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp]
         L.moe_decode_set_expert_events.argtypes = [vp, vp, vp]
         L.moe_decode_path_for.argtypes = [vp, i32]
+        L.moe_decode_check_waits.argtypes = [vp, ctypes.POINTER(i32)]
         L.moe_decode_workspace_bytes.argtypes = [vp]
         L.moe_decode_workspace_bytes.restype = ctypes.c_size_t
         for f in ("desc_check", "args_check", "plan", "run", "destroy", "last_routes",
-                  "set_expert_events", "path_for"):
+                  "set_expert_events", "path_for", "check_waits"):
             getattr(L, "moe_decode_" + f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -84,7 +85,7 @@ def lib():
 EXPORTED = ["moe_decode_desc_check", "moe_decode_args_check", "moe_decode_plan",
             "moe_decode_run", "moe_decode_destroy", "moe_decode_strerror",
             "moe_decode_last_routes", "moe_decode_set_expert_events", "moe_decode_path_for",
-            "moe_decode_workspace_bytes"]
+            "moe_decode_check_waits", "moe_decode_workspace_bytes"]
 
 
 def strerror(code: int) -> str:
@@ -180,6 +181,15 @@ class Plan:
 
     def path_for(self, T: int) -> int:
         return lib().moe_decode_path_for(self._h, T)
+
+    def check_waits(self) -> bool:
+        """True when a bounded wait of the fused kernel gave up since the
+        last check (synchronises the device; clears the flag)."""
+        flag = ctypes.c_int32(0)
+        rc = lib().moe_decode_check_waits(self._h, ctypes.byref(flag))
+        if rc:
+            raise MoeDecodeError(rc, "moe_decode_check_waits")
+        return bool(flag.value)
 
     def workspace_bytes(self) -> int:
         return lib().moe_decode_workspace_bytes(self._h)

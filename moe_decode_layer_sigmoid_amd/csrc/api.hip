@@ -28,16 +28,18 @@ struct moe_decode_plan_s {
   hipStream_t side;
   hipEvent_t fork, join;
   hipEvent_t user_begin, user_end;
+  uint32_t fused_grid;  // workgroups of the fused kernel (0: fused path unavailable)
 };
 
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int path_for(const moe_decode_desc& d, int32_t T) {
-  (void)T;
-  if (d.path == MOE_DECODE_PATH_GEMV || d.path == MOE_DECODE_PATH_GROUPED) return d.path;
-  return MOE_DECODE_PATH_GEMV;
+int path_for(const moe_decode_plan_s& p, int32_t T) {
+  const int want = p.desc.path;
+  if (want == MOE_DECODE_PATH_GEMV_SPLIT || want == MOE_DECODE_PATH_GROUPED) return want;
+  if (T <= moe::kFusedMaxTokens && p.fused_grid > 0) return MOE_DECODE_PATH_GEMV;
+  return MOE_DECODE_PATH_GEMV_SPLIT;
 }
 
 size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
@@ -67,6 +69,7 @@ size_t layout(const moe_decode_desc& d, char* base, moe::Workspace* ws) {
   w.rows = reinterpret_cast<float*>(take(T * k * H * 4));
   w.y_s = reinterpret_cast<float*>(take(T * H * 4));
   w.counter = reinterpret_cast<uint32_t*>(take(64));
+  w.sync = reinterpret_cast<uint32_t*>(take((moe::kSyncGuDone + E) * 4));
   if (ws) *ws = w;
   return off;
 }
@@ -111,7 +114,7 @@ int moe_decode_desc_check(const moe_decode_desc* d) {
     return MOE_DECODE_ERR_INVALID_ARG;
   if (d->scale_fmt != MOE_DECODE_SCALE_FP32 && d->scale_fmt != MOE_DECODE_SCALE_E8M0)
     return MOE_DECODE_ERR_INVALID_ARG;
-  if (d->path < MOE_DECODE_PATH_AUTO || d->path > MOE_DECODE_PATH_GROUPED)
+  if (d->path < MOE_DECODE_PATH_AUTO || d->path > MOE_DECODE_PATH_GEMV_SPLIT)
     return MOE_DECODE_ERR_INVALID_ARG;
   if (!(d->swiglu_limit > 0.f) || !(d->rms_eps >= 0.f) ||
       !(d->routed_scaling_factor == d->routed_scaling_factor))
@@ -186,6 +189,11 @@ int moe_decode_plan(const moe_decode_desc* d, int device, moe_decode_plan_t* out
   if (!rc && (hipEventCreateWithFlags(&p->fork, hipEventDisableTiming) != hipSuccess ||
               hipEventCreateWithFlags(&p->join, hipEventDisableTiming) != hipSuccess))
     rc = MOE_DECODE_ERR_HIP;
+  if (!rc) {
+    const int per_cu = moe::fused_blocks_per_cu(moe::fused_nj(d->hidden, d->intermediate,
+                                                                d->shared_intermediate));
+    p->fused_grid = static_cast<uint32_t>(per_cu > 0 ? per_cu * prop.multiProcessorCount : 0);
+  }
   if (!rc && hipDeviceSynchronize() != hipSuccess) rc = MOE_DECODE_ERR_HIP;
   (void)hipSetDevice(prev);
   if (rc) {
@@ -224,8 +232,38 @@ int moe_decode_run(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, voi
   return rc;
 }
 
+static int run_fused(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, hipStream_t s) {
+  moe::FusedArgs f{};
+  moe::fused_items(dims(p->desc, T), &f);
+  f.hidden = static_cast<const uint16_t*>(a->hidden);
+  f.residual = static_cast<const uint16_t*>(a->residual);
+  f.router_w = static_cast<const uint16_t*>(a->router_w);
+  f.bias = a->router_bias;
+  f.w13 = static_cast<const uint8_t*>(a->w13);
+  f.w13_scale = a->w13_scale;
+  f.w2 = static_cast<const uint8_t*>(a->w2);
+  f.w2_scale = a->w2_scale;
+  f.sw13 = static_cast<const uint8_t*>(a->sw13);
+  f.sw13_scale = a->sw13_scale;
+  f.sw2 = static_cast<const uint8_t*>(a->sw2);
+  f.sw2_scale = a->sw2_scale;
+  f.gamma = static_cast<const uint16_t*>(a->gamma);
+  f.out = static_cast<uint16_t*>(a->out);
+  f.residual_out = static_cast<uint16_t*>(a->residual_out);
+  f.ids_out = a->topk_ids;
+  f.w_out = a->topk_weights;
+  f.grid = p->fused_grid < static_cast<uint32_t>(f.total) ? p->fused_grid
+                                                          : static_cast<uint32_t>(f.total);
+  hipError_t err = hipSuccess;
+  if (p->user_begin) err = hipEventRecord(p->user_begin, s);
+  if (err == hipSuccess) err = moe::launch_decode_fused(f, p->ws, s);
+  if (err == hipSuccess && p->user_end) err = hipEventRecord(p->user_end, s);
+  return err == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;
+}
+
 static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t T,
                          hipStream_t s) {
+  if (path_for(*p, T) == MOE_DECODE_PATH_GEMV) return run_fused(p, a, T, s);
   const moe::LayerDims d = dims(p->desc, T);
   const bool has_shared = d.Is > 0;
 
@@ -287,8 +325,25 @@ int moe_decode_set_expert_events(moe_decode_plan_t p, void* begin, void* end) {
 }
 
 int moe_decode_path_for(moe_decode_plan_t p, int32_t T) {
-  if (!p) return -MOE_DECODE_ERR_INVALID_ARG;
-  return path_for(p->desc, T);
+  if (!p || T < 0 || T > p->desc.max_tokens) return -MOE_DECODE_ERR_INVALID_ARG;
+  return path_for(*p, T);
+}
+
+int moe_decode_check_waits(moe_decode_plan_t p, int32_t* gave_up) {
+  if (!p || !gave_up) return MOE_DECODE_ERR_INVALID_ARG;
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(p->device) != hipSuccess)
+    return MOE_DECODE_ERR_HIP;
+  uint32_t flag = 0;
+  int rc = MOE_DECODE_OK;
+  if (hipDeviceSynchronize() != hipSuccess ||
+      hipMemcpy(&flag, p->ws.sync + moe::kSyncError, 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemset(p->ws.sync + moe::kSyncError, 0, 4) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess)
+    rc = MOE_DECODE_ERR_HIP;
+  (void)hipSetDevice(prev);
+  *gave_up = flag != 0;
+  return rc;
 }
 
 size_t moe_decode_workspace_bytes(moe_decode_plan_t p) { return p ? p->ws_bytes : 0; }

@@ -1,0 +1,310 @@
+// The whole layer step for 1..16 tokens as one persistent kernel on gfx950.
+//
+// The pages run the decode-step MoE as one fused "mega MoE" kernel per layer
+// (vLLM API page "vllm.models.glm5next.nvidia.specialized_decode.runtime.
+// decode", LayerStages._build_mega logs the MoE layers it runs as one
+// kernel), with the shared expert overlapping the router and the routed
+// experts (LayerStages._mega_moe) and the boundary finalizing the routed rows
+// (page "...runtime.draft", SpecializedDraft.reduced_norm).  Here one launch
+// does all of it: the shared expert's work is queued ahead of the routed
+// experts, so its weight stream overlaps the router and the top-k instead of
+// running on a second stream.
+//
+// Work queue.  Every workgroup takes tickets from one atomic counter, in
+// order, and runs the item a ticket names:
+//   router items     logits of 4 experts (one per wave) for all tokens; the
+//                    last router item to finish selects the top-k of every
+//                    token, builds the route tables and raises route_ready
+//   shared gate_up   8 SwiGLU rows of the shared expert
+//   shared down      16 output rows of the shared expert   (after all shared gate_up)
+//   routed gate_up   8 SwiGLU rows of one touched-expert slot (after route_ready)
+//   routed down      16 output rows of one slot             (after that slot's gate_up)
+//   boundary         one token: combine + shared + residual + RMSNorm (after all down)
+// An item only waits for items with smaller tickets, which running
+// workgroups already hold, so the queue cannot deadlock however many
+// workgroups are resident.  Every wait is bounded (it raises an error word
+// and gives up rather than hang).  The next ticket is fetched while the
+// current item runs.  The last workgroup to leave zeroes the counters for
+// the next launch (also under HIP-graph replay).
+//
+// Publication across workgroups (and XCDs): producers fence at agent scope
+// (release) before bumping a counter; a consumer's spinning thread fences at
+// agent scope (acquire) once the counter is reached, before a workgroup
+// barrier.
+#include "device_common.h"
+#include "gemv_tiles.h"
+#include "launch.h"
+#include "routing_device.h"
+
+namespace moe {
+namespace fused {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr size_t kRouteSmem = 16 * 16 * 4 + kMaxExperts * 8 + kMaxExperts * 4 + 16;
+
+__device__ __forceinline__ void signal_add(uint32_t* c) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void wait_geq(const uint32_t* c, uint32_t target, uint32_t* err) {
+  if (threadIdx.x == 0) {
+    uint32_t n = 0;
+    while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++n == kSpinLimit) {
+        __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+template <int NJ>
+hipError_t launch_nj(const FusedArgs& a, const Workspace& ws, hipStream_t s);
+template <int NJ>
+int occupancy_nj();
+
+#ifdef MOE_FUSED_NJ
+// This object holds the kernel for one chunk count (the build compiles this
+// file once per value, in parallel).
+template <int NJ>
+__global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Workspace ws) {
+  __shared__ __attribute__((aligned(16))) unsigned char s_route[kRouteSmem];
+  __shared__ uint32_t s_ticket;
+  __shared__ int s_flag;
+  __shared__ float s_part[kWaves];
+  uint32_t* sync = ws.sync;
+  uint32_t* err = sync + kSyncError;
+  const int wave = threadIdx.x >> 6;
+  const int H = a.H, I = a.I, Is = a.Is, k = a.k, T = a.T, E = a.E;
+  const bool e8m0 = a.e8m0 != 0;
+
+  if (threadIdx.x == 0)
+    s_ticket = __hip_atomic_fetch_add(sync + kSyncTicket, 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  uint32_t t = s_ticket;
+  bool routed_ready = false;
+  int n_touched = 0;
+  while (t < static_cast<uint32_t>(a.total)) {
+    uint32_t nxt = 0;
+    if (threadIdx.x == 0)
+      nxt = __hip_atomic_fetch_add(sync + kSyncTicket, 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    const int it = static_cast<int>(t);
+    // Decode the item into one of four kinds; the shared and the routed
+    // projections share one call site each (one copy of each tile's code).
+    enum { kSkip, kRouter, kGateUp, kDown, kBoundary } kind = kSkip;
+    const uint8_t* W = nullptr;
+    const void* S = nullptr;
+    size_t sbase = 0;
+    int rows_i = 0, r0 = 0, n = 0, base = 0;
+    const int32_t* perm = nullptr;
+    uint32_t* done = nullptr;
+    if (it < a.o_sgu) {
+      kind = kRouter;
+    } else if (it < a.o_sdn) {
+      // shared gate_up: SwiGLU rows 8*s + 2*wave, +1
+      kind = kGateUp;
+      W = a.sw13;
+      S = a.sw13_scale;
+      rows_i = Is;
+      r0 = (it - a.o_sgu) * 2 * kWaves + 2 * wave;
+      n = T;
+      done = sync + kSyncSguDone;
+    } else if (it < a.o_rgu) {
+      // shared down: rows 16*j + 4*wave .. +3, after all shared gate_up
+      wait_geq(sync + kSyncSguDone, static_cast<uint32_t>(a.n_sgu), err);
+      kind = kDown;
+      W = a.sw2;
+      S = a.sw2_scale;
+      rows_i = Is;
+      r0 = (it - a.o_sdn) * 4 * kWaves + 4 * wave;
+      n = T;
+      done = sync + kSyncSdnDone;
+    } else {
+      if (!routed_ready) {
+        wait_geq(sync + kSyncRouteReady, 1u, err);
+        routed_ready = true;
+        n_touched = *ws.n_touched;
+      }
+      if (it < a.o_epi) {
+        const bool gu = it < a.o_rdn;
+        const int u = gu ? it - a.o_rgu : it - a.o_rdn;
+        const int per = gu ? a.gu_per : a.dn_per;
+        const int d = u / per, tile = u % per;
+        if (d < n_touched) {
+          const int e = ws.touched[d];
+          n = ws.counts[e];
+          base = ws.offsets[e];
+          perm = ws.perm;
+          rows_i = I;
+          if (gu) {
+            kind = kGateUp;
+            W = a.w13 + static_cast<size_t>(e) * 2 * I * H;
+            S = a.w13_scale;
+            sbase = static_cast<size_t>(e) * (2 * I / kBlock) * (H / kBlock);
+            r0 = tile * 2 * kWaves + 2 * wave;
+            done = sync + kSyncGuDone + d;
+          } else {
+            wait_geq(sync + kSyncGuDone + d, static_cast<uint32_t>(a.gu_per), err);
+            kind = kDown;
+            W = a.w2 + static_cast<size_t>(e) * H * I;
+            S = a.w2_scale;
+            sbase = static_cast<size_t>(e) * (H / kBlock) * (I / kBlock);
+            r0 = tile * 4 * kWaves + 4 * wave;
+            done = sync + kSyncRdnDone;
+          }
+        }
+      } else {
+        wait_geq(sync + kSyncRdnDone, static_cast<uint32_t>(n_touched * a.dn_per), err);
+        if (Is) wait_geq(sync + kSyncSdnDone, static_cast<uint32_t>(a.n_sdn), err);
+        kind = kBoundary;
+      }
+    }
+
+    if (kind == kRouter) {
+      // logits of experts 4*it + wave; the last router item selects and routes
+      const int e = it * kWaves + wave;
+      if (e < E)
+        router_wave<2 * NJ>(a.hidden, a.router_w + static_cast<size_t>(e) * H, H, T, E, e,
+                            ws.logits);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(sync + kSyncRouterDone, 1u,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_flag = prev == static_cast<uint32_t>(a.n_router) - 1;
+        if (s_flag) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      }
+      __syncthreads();
+      if (s_flag) {
+        select_and_route(T, E, k, a.rsf, ws.logits, a.bias, ws, a.ids_out, a.w_out, s_route);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        if (threadIdx.x == 0)
+          __hip_atomic_store(sync + kSyncRouteReady, 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else if (kind == kGateUp) {
+      float* dst = perm ? ws.act : ws.act_s;
+      gate_up_wave<NJ, 1>(a.hidden, W, S, sbase, e8m0, H, rows_i, r0, n, perm, base, k, dst,
+                       a.limit);
+      signal_add(done);
+    } else if (kind == kDown) {
+      down_wave<NJ, 1>(W, S, sbase, e8m0, H, rows_i, r0, n, base, perm ? ws.act : ws.act_s,
+                    perm ? ws.rows : ws.y_s);
+      signal_add(done);
+    } else if (kind == kBoundary) {
+      epilogue_token(it - a.o_epi, a.residual, a.gamma, H, k, Is > 0, a.eps, ws, a.out,
+                     a.residual_out, s_part);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) s_ticket = nxt;
+    __syncthreads();
+    t = s_ticket;
+  }
+
+  // The last workgroup out zeroes the counters for the next launch.
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(sync + kSyncExit, 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    s_flag = prev == a.grid - 1;
+  }
+  __syncthreads();
+  if (s_flag) {
+    for (int i = threadIdx.x; i < kSyncGuDone + a.dmax; i += kThreads)
+      if (i != kSyncError) __hip_atomic_store(sync + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <int NJ>
+hipError_t launch_nj(const FusedArgs& a, const Workspace& ws, hipStream_t s) {
+  hipLaunchKernelGGL(decode_fused_kernel<NJ>, dim3(a.grid), dim3(kThreads), 0, s, a, ws);
+  return hipGetLastError();
+}
+
+template <int NJ>
+int occupancy_nj() {
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_fused_kernel<NJ>, kThreads, 0) !=
+      hipSuccess)
+    return 0;
+  return blocks;
+}
+
+template hipError_t launch_nj<MOE_FUSED_NJ>(const FusedArgs&, const Workspace&, hipStream_t);
+template int occupancy_nj<MOE_FUSED_NJ>();
+#endif  // MOE_FUSED_NJ
+
+}  // namespace fused
+
+#ifndef MOE_FUSED_NJ
+using fused::kWaves;
+using fused::launch_nj;
+using fused::occupancy_nj;
+
+int fused_nj(int H, int I, int Is) {
+  int nj = (H + 1023) / 1024;
+  nj = nj > (I + 1023) / 1024 ? nj : (I + 1023) / 1024;
+  nj = nj > (Is + 1023) / 1024 ? nj : (Is + 1023) / 1024;
+  return nj;
+}
+
+int fused_blocks_per_cu(int nj) {
+  switch (nj) {
+#define X(N) \
+  case N:    \
+    return occupancy_nj<N>();
+    X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8)
+#undef X
+    default:
+      return 0;
+  }
+}
+
+void fused_items(const LayerDims& d, FusedArgs* a) {
+  a->T = d.T;
+  a->H = d.H;
+  a->E = d.E;
+  a->k = d.k;
+  a->I = d.I;
+  a->Is = d.Is;
+  a->e8m0 = d.e8m0 ? 1 : 0;
+  a->limit = d.limit;
+  a->rsf = d.rsf;
+  a->eps = d.eps;
+  a->n_router = (d.E + kWaves - 1) / kWaves;
+  a->n_sgu = d.Is ? d.Is / (2 * kWaves) : 0;
+  a->n_sdn = d.Is ? d.H / (4 * kWaves) : 0;
+  a->gu_per = d.I / (2 * kWaves);
+  a->dn_per = d.H / (4 * kWaves);
+  a->dmax = d.T * d.k < d.E ? d.T * d.k : d.E;
+  a->o_sgu = a->n_router;
+  a->o_sdn = a->o_sgu + a->n_sgu;
+  a->o_rgu = a->o_sdn + a->n_sdn;
+  a->o_rdn = a->o_rgu + a->dmax * a->gu_per;
+  a->o_epi = a->o_rdn + a->dmax * a->dn_per;
+  a->total = a->o_epi + d.T;
+}
+
+hipError_t launch_decode_fused(const FusedArgs& a, const Workspace& ws, hipStream_t s) {
+  switch (fused_nj(a.H, a.I, a.Is)) {
+#define X(N) \
+  case N:    \
+    return launch_nj<N>(a, ws, s);
+    X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8)
+#undef X
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+#endif  // !MOE_FUSED_NJ
+
+}  // namespace moe

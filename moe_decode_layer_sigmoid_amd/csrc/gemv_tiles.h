@@ -1,0 +1,371 @@
+// One-wave GEMV tiles of the fp8 expert projections, the router logits and
+// the per-token boundary, shared by the separate kernels and the fused
+// persistent decode kernel.
+//
+// Follows the vLLM API page "vllm.models.glm5next.nvidia.specialized_decode.
+// runtime.decode" (LayerStages._build_mega: fp8 w13/w2 with block scales,
+// swiglu_limit; LayerStages._router: bf16 router weight, fp32 logits) and
+// the page "...runtime.draft" (SpecializedDraft.reduced_norm: the boundary
+// returns norm(x + residual) and the new residual).
+//
+// Layout of a wave's work: lanes split a weight row into 16-byte chunks
+// (chunk c = lane + 64 j), so every load instruction of the wave reads 1 KiB
+// of one row contiguously; all of a wave's weight loads are issued before the
+// first one is used.  Weights are read with non-temporal loads: they are
+// streamed once per step and should not displace the activations in L2.
+#pragma once
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace moe {
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streamed (read-once) 16-byte load.
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// 16 fp8 weights (one 16-byte chunk) dotted with 16 floats.
+__device__ __forceinline__ float dot16_fp8(const uint4& w, const float* x) {
+  float wf[16];
+  fp8x4_to_f32(w.x, wf);
+  fp8x4_to_f32(w.y, wf + 4);
+  fp8x4_to_f32(w.z, wf + 8);
+  fp8x4_to_f32(w.w, wf + 12);
+  float p = 0.f;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) p = fmaf(wf[m], x[m], p);
+  return p;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Four e4m3fn codes -> two dwords of bf16 pairs (exact: an e4m3 value has at
+// most 4 significant bits, so the top half of its float is the value).
+__device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t* lo, uint32_t* hi) {
+  const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+  const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+  *lo = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
+  *hi = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Keeps the compiler from hoisting work on `v` out of a loop (the weights
+// stay raw fp8 in registers; each token pass converts them again instead of
+// holding 4x as many converted registers).
+__device__ __forceinline__ void opaque(uint4& v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
+
+// gate_up + clamped SwiGLU of one wave: SwiGLU outputs i0, i0+1 (i0 even)
+// from gate rows i0, i0+1 and up rows I+i0, I+i0+1 of one expert, for its n
+// tokens.  Token q is row perm[base+q] / k of hidden (perm == nullptr: row q).
+// Writes act[(base + q) * I + i0 + {0, 1}].  Products are exact (bf16 x
+// e4m3 in the bf16 dot2 unit), sums in fp32.
+// NJ = 16-byte chunks per lane per row = ceil(H / 1024); TB = tokens per
+// register pass over the loaded weights.
+template <int NJ, int TB>
+__device__ __forceinline__ void gate_up_wave(const uint16_t* __restrict__ hidden,
+                                             const uint8_t* __restrict__ W,
+                                             const void* __restrict__ scale, size_t sbase,
+                                             bool e8m0, int H, int I, int i0, int n,
+                                             const int32_t* perm, int base, int k,
+                                             float* __restrict__ act, float limit) {
+  const int lane = threadIdx.x & 63;
+  const int kb_n = H / kBlock;
+  const int nchunk = H / 16;
+  const int rows[4] = {i0, i0 + 1, I + i0, I + i0 + 1};
+  uint4 wv[4][NJ];
+  float sc[2][NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int c = lane + 64 * j;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      wv[r][j] = c < nchunk ? ld_stream16(W + static_cast<size_t>(rows[r]) * H + 16 * c)
+                            : make_uint4(0, 0, 0, 0);
+    const int kb = min(c, nchunk - 1) / 8;
+    sc[0][j] = load_scale(scale, e8m0, sbase + static_cast<size_t>(i0 / kBlock) * kb_n + kb);
+    sc[1][j] = load_scale(scale, e8m0, sbase + static_cast<size_t>((I + i0) / kBlock) * kb_n + kb);
+  }
+  for (int q0 = 0; q0 < n; q0 += TB) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) opaque(wv[r][j]);
+    int tok[TB];
+#pragma unroll
+    for (int qq = 0; qq < TB; ++qq) {
+      const int q = q0 + qq;
+      tok[qq] = q < n ? (perm ? perm[base + q] / k : q) : -1;
+    }
+    float acc[4][TB];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int qq = 0; qq < TB; ++qq) acc[r][qq] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int c = lane + 64 * j;
+      if (c >= nchunk) continue;
+      uint32_t xs[TB][8];
+#pragma unroll
+      for (int qq = 0; qq < TB; ++qq) {
+        if (tok[qq] < 0) continue;
+        const uint4* xp =
+            reinterpret_cast<const uint4*>(hidden + static_cast<size_t>(tok[qq]) * H + 16 * c);
+        const uint4 a = xp[0], b = xp[1];
+        xs[qq][0] = a.x; xs[qq][1] = a.y; xs[qq][2] = a.z; xs[qq][3] = a.w;
+        xs[qq][4] = b.x; xs[qq][5] = b.y; xs[qq][6] = b.z; xs[qq][7] = b.w;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint32_t wb[8];
+        fp8x4_to_bf16x4(wv[r][j].x, &wb[0], &wb[1]);
+        fp8x4_to_bf16x4(wv[r][j].y, &wb[2], &wb[3]);
+        fp8x4_to_bf16x4(wv[r][j].z, &wb[4], &wb[5]);
+        fp8x4_to_bf16x4(wv[r][j].w, &wb[6], &wb[7]);
+#pragma unroll
+        for (int qq = 0; qq < TB; ++qq) {
+          if (tok[qq] < 0) continue;
+          float p = 0.f;
+#pragma unroll
+          for (int m = 0; m < 8; ++m) p = dot2_bf16(wb[m], xs[qq][m], p);
+          acc[r][qq] = fmaf(sc[r >> 1][j], p, acc[r][qq]);
+        }
+      }
+    }
+#pragma unroll
+    for (int qq = 0; qq < TB; ++qq) {
+      if (tok[qq] < 0) continue;
+      const float g0 = wave_sum(acc[0][qq]), g1 = wave_sum(acc[1][qq]);
+      const float u0 = wave_sum(acc[2][qq]), u1 = wave_sum(acc[3][qq]);
+      if (lane == 0) {
+        float* o = act + static_cast<size_t>(base + q0 + qq) * I + i0;
+        o[0] = clamped_swiglu(g0, u0, limit);
+        o[1] = clamped_swiglu(g1, u1, limit);
+      }
+    }
+  }
+}
+
+// down projection of one wave: output rows h0 .. h0+3 (h0 % 4 == 0) of one
+// expert for its n SwiGLU rows act[(base + q) * I], written to
+// out[(base + q) * H + h0 .. +3].  fp32 products and sums (the SwiGLU
+// activations stay fp32).  NJ = ceil(I / 1024); TB = tokens per pass.
+template <int NJ, int TB>
+__device__ __forceinline__ void down_wave(const uint8_t* __restrict__ W,
+                                          const void* __restrict__ scale, size_t sbase,
+                                          bool e8m0, int H, int I, int h0, int n, int base,
+                                          const float* act, float* out) {
+  const int lane = threadIdx.x & 63;
+  const int ib_n = I / kBlock;
+  const int nchunk = I / 16;
+  uint4 wv[4][NJ];
+  float sc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int c = lane + 64 * j;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      wv[r][j] = c < nchunk ? ld_stream16(W + static_cast<size_t>(h0 + r) * I + 16 * c)
+                            : make_uint4(0, 0, 0, 0);
+    sc[j] = load_scale(scale, e8m0,
+                       sbase + static_cast<size_t>(h0 / kBlock) * ib_n + min(c, nchunk - 1) / 8);
+  }
+  for (int q0 = 0; q0 < n; q0 += TB) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) opaque(wv[r][j]);
+    const int nq = min(TB, n - q0);
+    float acc[4][TB];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int qq = 0; qq < TB; ++qq) acc[r][qq] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int c = lane + 64 * j;
+      if (c >= nchunk) continue;
+#pragma unroll
+      for (int qq = 0; qq < TB; ++qq) {
+        if (qq >= nq) continue;
+        const float4* ap = reinterpret_cast<const float4*>(
+            act + static_cast<size_t>(base + q0 + qq) * I + 16 * c);
+        float af[16];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float4 v = ap[m];
+          af[4 * m] = v.x;
+          af[4 * m + 1] = v.y;
+          af[4 * m + 2] = v.z;
+          af[4 * m + 3] = v.w;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r][qq] = fmaf(sc[j], dot16_fp8(wv[r][j], af), acc[r][qq]);
+      }
+    }
+#pragma unroll
+    for (int qq = 0; qq < TB; ++qq) {
+      if (qq >= nq) continue;
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = wave_sum(acc[r][qq]);
+      if (lane == 0) {
+        float4* o = reinterpret_cast<float4*>(out + static_cast<size_t>(base + q0 + qq) * H + h0);
+        *o = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+}
+
+constexpr int kRouterTokB = 4;  // tokens per register pass of a router wave
+
+// Router logits of one expert row for tokens [0, T):
+// logits[t * E + e] = sum_h hidden[t, h] * router_w[e, h] in fp32.
+// The row stays in registers; tokens go in passes of kRouterTokB.
+// NJ2 = 16-byte chunks per lane = ceil(H / 512).
+template <int NJ2>
+__device__ __forceinline__ void router_wave(const uint16_t* __restrict__ hidden,
+                                            const uint16_t* __restrict__ row, int H, int T,
+                                            int E, int e, float* logits) {
+  const int lane = threadIdx.x & 63;
+  const int nchunk = H / 8;
+  uint4 wv[NJ2];
+#pragma unroll
+  for (int j = 0; j < NJ2; ++j) {
+    const int c = lane + 64 * j;
+    wv[j] = c < nchunk ? ld_stream16(row + 8 * c) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll 1
+  for (int t0 = 0; t0 < T; t0 += kRouterTokB) {
+    float acc[kRouterTokB];
+#pragma unroll
+    for (int q = 0; q < kRouterTokB; ++q) acc[q] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ2; ++j) {
+      const int c = lane + 64 * j;
+      if (c >= nchunk) continue;
+      const uint32_t w[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
+#pragma unroll
+      for (int q = 0; q < kRouterTokB; ++q) {
+        if (t0 + q >= T) continue;
+        const uint4 xv =
+            *reinterpret_cast<const uint4*>(hidden + static_cast<size_t>(t0 + q) * H + 8 * c);
+        const uint32_t x[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          acc[q] = fmaf(bf16_lo(w[m]), bf16_lo(x[m]), acc[q]);
+          acc[q] = fmaf(bf16_hi(w[m]), bf16_hi(x[m]), acc[q]);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kRouterTokB; ++q) {
+      if (t0 + q >= T) continue;
+      const float v = wave_sum(acc[q]);
+      if (lane == 0) logits[static_cast<size_t>(t0 + q) * E + e] = v;
+    }
+  }
+}
+
+constexpr int kEpiPass = 4;  // H <= 8192 = 4 passes x 256 threads x 8
+
+// The boundary for token t, by one 256-thread workgroup:
+// h = sum_j w[t, j] * rows[inv[t, j]] + y_s[t] + residual[t] (fixed order),
+// residual_out = bf16(h), out = bf16(h / sqrt(mean(h^2) + eps) * gamma).
+// s_part: 4 floats of LDS.
+__device__ __forceinline__ void epilogue_token(int t, const uint16_t* residual,
+                                               const uint16_t* __restrict__ gamma, int H, int k,
+                                               bool has_shared, float eps, const Workspace& ws,
+                                               uint16_t* out, uint16_t* residual_out,
+                                               float* s_part) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int pos[kMaxTopK];
+  float wj[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    pos[j] = j < k ? ws.inv[t * k + j] : 0;
+    wj[j] = j < k ? ws.weights[t * k + j] : 0.f;
+  }
+  float hv[kEpiPass][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int p = 0; p < kEpiPass; ++p) {
+    const int c0 = 8 * (threadIdx.x + 256 * p);
+    if (c0 >= H) continue;
+    float acc[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) acc[m] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j >= k) continue;
+      const float4* row =
+          reinterpret_cast<const float4*>(ws.rows + static_cast<size_t>(pos[j]) * H + c0);
+      const float4 a = row[0], b = row[1];
+      const float w = wj[j];
+      acc[0] = fmaf(w, a.x, acc[0]);
+      acc[1] = fmaf(w, a.y, acc[1]);
+      acc[2] = fmaf(w, a.z, acc[2]);
+      acc[3] = fmaf(w, a.w, acc[3]);
+      acc[4] = fmaf(w, b.x, acc[4]);
+      acc[5] = fmaf(w, b.y, acc[5]);
+      acc[6] = fmaf(w, b.z, acc[6]);
+      acc[7] = fmaf(w, b.w, acc[7]);
+    }
+    if (has_shared) {
+      const float4* ys = reinterpret_cast<const float4*>(ws.y_s + static_cast<size_t>(t) * H + c0);
+      const float4 a = ys[0], b = ys[1];
+      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    }
+    const uint4 rv = *reinterpret_cast<const uint4*>(residual + static_cast<size_t>(t) * H + c0);
+    const uint32_t u[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      acc[2 * m] += bf16_lo(u[m]);
+      acc[2 * m + 1] += bf16_hi(u[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      hv[p][m] = acc[m];
+      ss = fmaf(acc[m], acc[m], ss);
+    }
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) s_part[wave] = ss;
+  __syncthreads();
+  const float tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+  __syncthreads();
+  const float inv_rms = 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
+#pragma unroll
+  for (int p = 0; p < kEpiPass; ++p) {
+    const int c0 = 8 * (threadIdx.x + 256 * p);
+    if (c0 >= H) continue;
+    const uint4 gv = *reinterpret_cast<const uint4*>(gamma + c0);
+    const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
+    uint32_t o[4], r[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float h0 = hv[p][2 * m], h1 = hv[p][2 * m + 1];
+      o[m] = f32_to_bf16(h0 * inv_rms * bf16_lo(g[m])) |
+             (f32_to_bf16(h1 * inv_rms * bf16_hi(g[m])) << 16);
+      r[m] = f32_to_bf16(h0) | (f32_to_bf16(h1) << 16);
+    }
+    *reinterpret_cast<uint4*>(out + static_cast<size_t>(t) * H + c0) =
+        make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(residual_out + static_cast<size_t>(t) * H + c0) =
+        make_uint4(r[0], r[1], r[2], r[3]);
+  }
+}
+
+}  // namespace moe

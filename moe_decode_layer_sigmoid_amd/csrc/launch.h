@@ -22,6 +22,49 @@ struct Workspace {
   float* rows;         // [maxT * k, H]   routed down output, permuted order
   float* y_s;          // [maxT, H]       shared expert output
   uint32_t* counter;   // [1] last-block counter of the router (self-resetting)
+  uint32_t* sync;      // [kSyncGuDone + E] counters of the fused kernel (self-resetting)
+};
+
+// Words of Workspace::sync.
+enum : int {
+  kSyncTicket = 0,
+  kSyncRouterDone = 1,
+  kSyncRouteReady = 2,
+  kSyncSguDone = 3,
+  kSyncSdnDone = 4,
+  kSyncRdnDone = 5,
+  kSyncExit = 6,
+  kSyncError = 7,  // sticky: set when a bounded wait gave up
+  kSyncGuDone = 16  // one counter per touched-expert slot
+};
+
+constexpr int kFusedMaxTokens = 16;
+
+// Arguments of the fused persistent kernel (see decode_fused.hip).
+struct FusedArgs {
+  const uint16_t* hidden;
+  const uint16_t* residual;
+  const uint16_t* router_w;
+  const float* bias;
+  const uint8_t* w13;
+  const void* w13_scale;
+  const uint8_t* w2;
+  const void* w2_scale;
+  const uint8_t* sw13;
+  const void* sw13_scale;
+  const uint8_t* sw2;
+  const void* sw2_scale;
+  const uint16_t* gamma;
+  uint16_t* out;
+  uint16_t* residual_out;
+  int32_t* ids_out;
+  float* w_out;
+  int T, H, E, k, I, Is, e8m0;
+  float limit, rsf, eps;
+  // work-queue layout: item offsets and counts
+  int n_router, n_sgu, n_sdn, gu_per, dn_per, dmax;
+  int o_sgu, o_sdn, o_rgu, o_rdn, o_epi, total;
+  uint32_t grid;
 };
 
 struct LayerDims {
@@ -44,6 +87,12 @@ hipError_t launch_gate_up_gemv(const LayerDims& d, bool shared, const void* hidd
 // down projection (GEMV) of the SwiGLU activations.
 hipError_t launch_down_gemv(const LayerDims& d, bool shared, const void* w2,
                             const void* w2_scale, const Workspace& ws, hipStream_t s);
+
+// Fused persistent kernel of the whole step (T <= kFusedMaxTokens).
+int fused_nj(int H, int I, int Is);
+int fused_blocks_per_cu(int nj);
+void fused_items(const LayerDims& d, FusedArgs* a);
+hipError_t launch_decode_fused(const FusedArgs& a, const Workspace& ws, hipStream_t s);
 
 // Weighted combine + shared + residual, RMSNorm * gamma, bf16 outputs.
 hipError_t launch_epilogue(const LayerDims& d, const void* residual, const void* gamma,

@@ -1,0 +1,205 @@
+// Device routines of the routing step: top-k selection of one token and the
+// token -> expert route tables, for one 256-thread workgroup.
+//
+// Follows the vLLM API page "vllm.models.glm5next.nvidia.specialized_decode.
+// runtime.decode": LayerStages._build_mega (sigmoid scoring with one group,
+// normalised top-k weights times routed_scaling_factor) and
+// LayerStages._mega_moe (the score-correction bias goes with the logits; the
+// boundary receives the route order with the unfinalized rows).
+#pragma once
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int kRouteThreads = 256;
+
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive scan of v over the 256 threads (4 waves); returns the prefix and
+// writes the total to *total.  s_tmp holds 4 ints.
+__device__ inline int block_exclusive_scan(int v, int* s_tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) s_tmp[wave] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int x = s_tmp[w];
+    if (w < wave) base += x;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
+}
+
+// Top-k of one token in one wave.  Keys are sigmoid(logit) (+ bias); the
+// largest key wins, equal keys go to the lower expert id (a packed
+// (key, ~id) wave maximum, k rounds).  Lane j < k ends with the j-th pick and
+// its weight R * s_j / sum of the k picked scores.
+__device__ inline void select_token(const float* logits, const float* bias, int E, int k,
+                                    float rsf, int* pick_id, float* pick_w) {
+  const int lane = threadIdx.x & 63;
+  float key[16], sc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) {
+      const float s = sigmoidf_(logits[e]);
+      sc[i] = s;
+      key[i] = bias ? s + bias[e] : s;
+    } else {
+      sc[i] = 0.f;
+      key[i] = 0.f;
+    }
+  }
+  uint32_t taken = 0;
+  float ssum = 0.f, my_s = 0.f;
+  int my_id = -1;
+  for (int j = 0; j < k; ++j) {
+    uint32_t bk = 0, bid = 0;
+    float bs = 0.f;
+    bool have = false;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = lane + 64 * i;
+      const bool ok = e < E && !((taken >> i) & 1u);
+      const uint32_t kb = ordered_bits(key[i]);
+      if (ok && (!have || kb > bk)) {
+        have = true;
+        bk = kb;
+        bid = static_cast<uint32_t>(e);
+        bs = sc[i];
+      }
+    }
+    uint32_t hi = have ? bk : 0u;
+    uint32_t lo = have ? (0xffffffffu - bid) : 0u;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const uint32_t h2 = __shfl_xor(hi, off, 64), l2 = __shfl_xor(lo, off, 64);
+      if (h2 > hi || (h2 == hi && l2 > lo)) {
+        hi = h2;
+        lo = l2;
+      }
+    }
+    const int win = static_cast<int>(0xffffffffu - lo);
+    const float wsc = __shfl(bs, win & 63, 64);
+    if (lane == (win & 63)) taken |= 1u << (win >> 6);
+    ssum += wsc;
+    if (lane == j) {
+      my_id = win;
+      my_s = wsc;
+    }
+  }
+  if (lane < k) {
+    *pick_id = my_id;
+    *pick_w = rsf * my_s / ssum;
+  }
+}
+
+// LDS bytes select_and_route needs (16-byte aligned base).
+__host__ __device__ inline size_t route_smem_bytes(int T, int E, int k) {
+  const size_t R = static_cast<size_t>(T) * k, MW = (T + 63) / 64;
+  return ((R * 4 + 7) & ~static_cast<size_t>(7)) + static_cast<size_t>(E) * MW * 8 +
+         static_cast<size_t>(E) * 4 + 16;
+}
+
+// Top-k of every token, then the route tables, by one 256-thread workgroup.
+// logits [T, E] must be visible to the workgroup.  Writes ws.ids/weights
+// (and the optional outputs), ws.counts/offsets/touched/n_touched/perm/inv.
+// smem: route_smem_bytes(T, E, k) bytes, 8-byte aligned.
+__device__ inline void select_and_route(int T, int E, int k, float rsf, const float* logits,
+                                        const float* bias, const Workspace& ws,
+                                        int32_t* ids_out, float* w_out, unsigned char* smem) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int R = T * k;
+  const int MW = (T + 63) / 64;
+  int* s_ids = reinterpret_cast<int*>(smem);  // [T*k]
+  unsigned long long* s_mask = reinterpret_cast<unsigned long long*>(
+      smem + ((static_cast<size_t>(R) * 4 + 7) & ~static_cast<size_t>(7)));  // [E*MW]
+  int* s_off = reinterpret_cast<int*>(s_mask + static_cast<size_t>(E) * MW);  // [E]
+  int* s_tmp = s_off + E;                                                      // [4]
+
+  for (int t = wave; t < T; t += 4) {
+    int id = 0;
+    float w = 0.f;
+    select_token(logits + static_cast<size_t>(t) * E, bias, E, k, rsf, &id, &w);
+    if (lane < k) {
+      const int r = t * k + lane;
+      s_ids[r] = id;
+      ws.ids[r] = id;
+      ws.weights[r] = w;
+      if (ids_out) ids_out[r] = id;
+      if (w_out) w_out[r] = w;
+    }
+  }
+  for (int i = threadIdx.x; i < E * MW; i += kRouteThreads) s_mask[i] = 0ull;
+  __syncthreads();
+
+  // Token bitmask of every expert.
+  for (int r = threadIdx.x; r < R; r += kRouteThreads) {
+    const int e = s_ids[r], t = r / k;
+    atomicOr(&s_mask[static_cast<size_t>(e) * MW + (t >> 6)], 1ull << (t & 63));
+  }
+  __syncthreads();
+  // Counts and touched flags, packed so that one scan gives both prefixes:
+  // bits [11, 32) count routes (<= 4096), bits [0, 11) touched experts
+  // (<= 1024).  Thread i owns experts 4i .. 4i+3 (E <= 1024).
+  {
+    int packed[4], local = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = 4 * threadIdx.x + m;
+      int cnt = 0;
+      if (e < E)
+        for (int w = 0; w < MW; ++w) cnt += __popcll(s_mask[static_cast<size_t>(e) * MW + w]);
+      packed[m] = (cnt << 11) | (cnt > 0 ? 1 : 0);
+      local += packed[m];
+    }
+    int total = 0;
+    int run = block_exclusive_scan(local, s_tmp, &total);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = 4 * threadIdx.x + m;
+      if (e < E) {
+        const int cnt = packed[m] >> 11;
+        const int off = run >> 11, tidx = run & 0x7ff;
+        s_off[e] = off;
+        ws.counts[e] = cnt;
+        ws.offsets[e] = off;
+        if (cnt > 0) ws.touched[tidx] = e;
+      }
+      run += packed[m];
+    }
+    if (threadIdx.x == 0) {
+      ws.offsets[E] = total >> 11;
+      *ws.n_touched = total & 0x7ff;
+    }
+  }
+  __syncthreads();
+  // Stable position of every route: its expert's offset plus the number of
+  // earlier tokens routed to the same expert.
+  for (int r = threadIdx.x; r < R; r += kRouteThreads) {
+    const int e = s_ids[r], t = r / k;
+    const unsigned long long* m = s_mask + static_cast<size_t>(e) * MW;
+    int rank = 0;
+    for (int w = 0; w < (t >> 6); ++w) rank += __popcll(m[w]);
+    rank += __popcll(m[t >> 6] & ((1ull << (t & 63)) - 1ull));
+    const int pos = s_off[e] + rank;
+    ws.perm[pos] = r;
+    ws.inv[r] = pos;
+  }
+}
+
+}  // namespace moe

@@ -49,8 +49,9 @@ def test_tiny_layer(c_oracle):
 
 
 @pytest.mark.parametrize("name", ["decode_t1", "decode_t16"])
-def test_decode_layers_full(name, c_oracle):
-    inp, got, err = _case(WORKLOADS[name], c_oracle)
+@pytest.mark.parametrize("path", [md.PATH_AUTO, md.PATH_GEMV_SPLIT], ids=["auto", "split"])
+def test_decode_layers_full(name, path, c_oracle):
+    inp, got, err = _case(WORKLOADS[name], c_oracle, path=path)
     if name == "decode_t16":
         d = len(np.unique(got["ids"]))
         _log("  distinct experts", d)
@@ -80,10 +81,31 @@ SMALL = [
 
 @pytest.mark.parametrize("case", SMALL, ids=[str(c) for c in SMALL])
 @pytest.mark.parametrize("with_bias", [False, True])
-def test_small_layers(case, with_bias, c_oracle):
+@pytest.mark.parametrize("path", [md.PATH_AUTO, md.PATH_GEMV_SPLIT], ids=["auto", "split"])
+def test_small_layers(case, with_bias, path, c_oracle):
     T, H, E, k, I, Is, fmt = case
     sh = LayerShape(T=T, H=H, E=E, k=k, I=I, Is=Is, scale_fmt=fmt, tag=300 + sum(case[:6]))
-    _case(sh, c_oracle, with_bias=with_bias)
+    _case(sh, c_oracle, with_bias=with_bias, path=path)
+
+
+@pytest.mark.parametrize("T", [1, 3, 16])
+def test_fused_and_split_paths_agree(T, c_oracle):
+    """The fused persistent kernel and the separate kernels compute the same
+    layer (same ids, outputs within the oracle tolerance of each other)."""
+    sh = WORKLOADS["decode_t16"].replace(T=T, H=2048, I=768, Is=512, tag=310 + T)
+    inp = make_layer(sh)
+    dev = to_device(inp)
+    fused = make_plan(sh, path=md.PATH_AUTO)
+    split = make_plan(sh, path=md.PATH_GEMV_SPLIT)
+    assert fused.path_for(T) == md.PATH_GEMV and split.path_for(T) == md.PATH_GEMV_SPLIT
+    a = run_layer(fused, dev, T)
+    b = run_layer(split, dev, T)
+    assert np.array_equal(a["ids"], b["ids"])
+    assert_close(a["out"], b["out"], "fused vs split out")
+    check_layer(inp, a, c_oracle=c_oracle)
+    check_layer(inp, b, c_oracle=c_oracle)
+    fused.close()
+    split.close()
 
 
 def test_route_tables_match_oracle(c_oracle):
