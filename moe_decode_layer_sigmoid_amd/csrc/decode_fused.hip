@@ -27,10 +27,13 @@
 // current item runs.  The last workgroup to leave zeroes the counters for
 // the next launch (also under HIP-graph replay).
 //
-// Publication across workgroups (and XCDs): producers fence at agent scope
-// (release) before bumping a counter; a consumer's spinning thread fences at
-// agent scope (acquire) once the counter is reached, before a workgroup
-// barrier.
+// Hand-off across workgroups (and XCDs): everything one item leaves for
+// another (logits, route tables, SwiGLU rows, down rows) is written with
+// agent-scope atomic stores, which write through to the device coherence
+// point; the producer waits for its stores to complete before it bumps a
+// counter, and consumers read that data with agent-scope atomic loads after
+// the counter is reached.  No L2 write-back or invalidate is needed, so the
+// thousands of hand-offs of one step cost no cache-wide operation.
 #include "device_common.h"
 #include "gemv_tiles.h"
 #include "launch.h"
@@ -44,12 +47,17 @@ constexpr int kWaves = kThreads / kWave;
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr size_t kRouteSmem = 16 * 16 * 4 + kMaxExperts * 8 + kMaxExperts * 4 + 16;
 
+// Publishes this workgroup's coherent stores and bumps counter c: every lane
+// waits for its stores to reach the coherence point, then one lane adds 1.
 __device__ __forceinline__ void signal_add(uint32_t* c) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  wait_memory();
   __syncthreads();
   if (threadIdx.x == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Waits until counter c reaches target (bounded: raises *err and gives up
+// after kSpinLimit polls).  Data behind the counter is then read with
+// coherent loads.
 __device__ __forceinline__ void wait_geq(const uint32_t* c, uint32_t target, uint32_t* err) {
   if (threadIdx.x == 0) {
     uint32_t n = 0;
@@ -60,7 +68,6 @@ __device__ __forceinline__ void wait_geq(const uint32_t* c, uint32_t target, uin
         break;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
 }
@@ -132,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
       if (!routed_ready) {
         wait_geq(sync + kSyncRouteReady, 1u, err);
         routed_ready = true;
-        n_touched = *ws.n_touched;
+        n_touched = ld_i32<true>(ws.n_touched);
       }
       if (it < a.o_epi) {
         const bool gu = it < a.o_rdn;
@@ -140,9 +147,9 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
         const int per = gu ? a.gu_per : a.dn_per;
         const int d = u / per, tile = u % per;
         if (d < n_touched) {
-          const int e = ws.touched[d];
-          n = ws.counts[e];
-          base = ws.offsets[e];
+          const int e = ld_i32<true>(ws.touched + d);
+          n = ld_i32<true>(ws.counts + e);
+          base = ld_i32<true>(ws.offsets + e);
           perm = ws.perm;
           rows_i = I;
           if (gu) {
@@ -173,20 +180,20 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
       // logits of experts 4*it + wave; the last router item selects and routes
       const int e = it * kWaves + wave;
       if (e < E)
-        router_wave<2 * NJ>(a.hidden, a.router_w + static_cast<size_t>(e) * H, H, T, E, e,
-                            ws.logits);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        router_wave<2 * NJ, true>(a.hidden, a.router_w + static_cast<size_t>(e) * H, H, T, E, e,
+                                  ws.logits);
+      wait_memory();
       __syncthreads();
       if (threadIdx.x == 0) {
         const uint32_t prev = __hip_atomic_fetch_add(sync + kSyncRouterDone, 1u,
                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_flag = prev == static_cast<uint32_t>(a.n_router) - 1;
-        if (s_flag) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       }
       __syncthreads();
       if (s_flag) {
-        select_and_route(T, E, k, a.rsf, ws.logits, a.bias, ws, a.ids_out, a.w_out, s_route);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        select_and_route<true>(T, E, k, a.rsf, ws.logits, a.bias, ws, a.ids_out, a.w_out,
+                               s_route);
+        wait_memory();
         __syncthreads();
         if (threadIdx.x == 0)
           __hip_atomic_store(sync + kSyncRouteReady, 1u, __ATOMIC_RELAXED,
@@ -194,15 +201,15 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
       }
     } else if (kind == kGateUp) {
       float* dst = perm ? ws.act : ws.act_s;
-      gate_up_wave<NJ, 1>(a.hidden, W, S, sbase, e8m0, H, rows_i, r0, n, perm, base, k, dst,
+      gate_up_wave<NJ, 1, true>(a.hidden, W, S, sbase, e8m0, H, rows_i, r0, n, perm, base, k, dst,
                        a.limit);
       signal_add(done);
     } else if (kind == kDown) {
-      down_wave<NJ, 1>(W, S, sbase, e8m0, H, rows_i, r0, n, base, perm ? ws.act : ws.act_s,
+      down_wave<NJ, 1, true>(W, S, sbase, e8m0, H, rows_i, r0, n, base, perm ? ws.act : ws.act_s,
                     perm ? ws.rows : ws.y_s);
       signal_add(done);
     } else if (kind == kBoundary) {
-      epilogue_token(it - a.o_epi, a.residual, a.gamma, H, k, Is > 0, a.eps, ws, a.out,
+      epilogue_token<true>(it - a.o_epi, a.residual, a.gamma, H, k, Is > 0, a.eps, ws, a.out,
                      a.residual_out, s_part);
     }
     __syncthreads();
@@ -213,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
 
   // The last workgroup out zeroes the counters for the next launch.
   if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(sync + kSyncExit, 1u, __ATOMIC_ACQ_REL,
+    const uint32_t prev = __hip_atomic_fetch_add(sync + kSyncExit, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     s_flag = prev == a.grid - 1;
   }

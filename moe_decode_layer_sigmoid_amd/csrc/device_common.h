@@ -55,6 +55,66 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Loads and stores of data that workgroups of one launch hand to each other.
+// With C = true they are agent-scope relaxed atomics: the stores write
+// through to the device coherence point and the loads read from it, so no
+// cache flush or invalidate is needed around the hand-off (see
+// wait_memory()).  With C = false they are plain accesses (a kernel
+// boundary orders them).
+template <bool C>
+__device__ __forceinline__ float ld_f32(const float* p) {
+  if (C) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *p;
+}
+template <bool C>
+__device__ __forceinline__ int ld_i32(const int* p) {
+  if (C) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *p;
+}
+template <bool C>
+__device__ __forceinline__ void st_f32(float* p, float v) {
+  if (C) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool C>
+__device__ __forceinline__ void st_i32(int* p, int v) {
+  if (C) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+// 16-byte versions (two 8-byte atomics when C; p must be 16-byte aligned).
+template <bool C>
+__device__ __forceinline__ float4 ld_f32x4(const float* p) {
+  if (C) {
+    const auto* q = reinterpret_cast<const unsigned long long*>(p);
+    const unsigned long long a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float4(__uint_as_float(static_cast<uint32_t>(a)),
+                       __uint_as_float(static_cast<uint32_t>(a >> 32)),
+                       __uint_as_float(static_cast<uint32_t>(b)),
+                       __uint_as_float(static_cast<uint32_t>(b >> 32)));
+  }
+  return *reinterpret_cast<const float4*>(p);
+}
+template <bool C>
+__device__ __forceinline__ void st_f32x4(float* p, float4 v) {
+  if (C) {
+    auto* q = reinterpret_cast<unsigned long long*>(p);
+    const unsigned long long a = (static_cast<unsigned long long>(__float_as_uint(v.y)) << 32) |
+                                 __float_as_uint(v.x);
+    const unsigned long long b = (static_cast<unsigned long long>(__float_as_uint(v.w)) << 32) |
+                                 __float_as_uint(v.z);
+    __hip_atomic_store(q, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    *reinterpret_cast<float4*>(p) = v;
+  }
+}
+
+// Every lane waits until its earlier memory operations have completed (for
+// the coherent stores above: reached the device coherence point).  Also a
+// compiler barrier.
+__device__ __forceinline__ void wait_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
 // silu(min(g, L)) * clamp(u, -L, L)

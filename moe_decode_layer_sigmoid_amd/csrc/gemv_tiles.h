@@ -72,7 +72,7 @@ __device__ __forceinline__ void opaque(uint4& v) {
 // e4m3 in the bf16 dot2 unit), sums in fp32.
 // NJ = 16-byte chunks per lane per row = ceil(H / 1024); TB = tokens per
 // register pass over the loaded weights.
-template <int NJ, int TB>
+template <int NJ, int TB, bool C = false>
 __device__ __forceinline__ void gate_up_wave(const uint16_t* __restrict__ hidden,
                                              const uint8_t* __restrict__ W,
                                              const void* __restrict__ scale, size_t sbase,
@@ -97,15 +97,11 @@ __device__ __forceinline__ void gate_up_wave(const uint16_t* __restrict__ hidden
     sc[1][j] = load_scale(scale, e8m0, sbase + static_cast<size_t>((I + i0) / kBlock) * kb_n + kb);
   }
   for (int q0 = 0; q0 < n; q0 += TB) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) opaque(wv[r][j]);
     int tok[TB];
 #pragma unroll
     for (int qq = 0; qq < TB; ++qq) {
       const int q = q0 + qq;
-      tok[qq] = q < n ? (perm ? perm[base + q] / k : q) : -1;
+      tok[qq] = q < n ? (perm ? ld_i32<C>(perm + base + q) / k : q) : -1;
     }
     float acc[4][TB];
 #pragma unroll
@@ -150,9 +146,16 @@ __device__ __forceinline__ void gate_up_wave(const uint16_t* __restrict__ hidden
       const float u0 = wave_sum(acc[2][qq]), u1 = wave_sum(acc[3][qq]);
       if (lane == 0) {
         float* o = act + static_cast<size_t>(base + q0 + qq) * I + i0;
-        o[0] = clamped_swiglu(g0, u0, limit);
-        o[1] = clamped_swiglu(g1, u1, limit);
+        st_f32<C>(o, clamped_swiglu(g0, u0, limit));
+        st_f32<C>(o + 1, clamped_swiglu(g1, u1, limit));
       }
+    }
+    if (q0 + TB < n) {
+      // another pass follows: keep the raw weights, convert them again
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) opaque(wv[r][j]);
     }
   }
 }
@@ -161,7 +164,7 @@ __device__ __forceinline__ void gate_up_wave(const uint16_t* __restrict__ hidden
 // expert for its n SwiGLU rows act[(base + q) * I], written to
 // out[(base + q) * H + h0 .. +3].  fp32 products and sums (the SwiGLU
 // activations stay fp32).  NJ = ceil(I / 1024); TB = tokens per pass.
-template <int NJ, int TB>
+template <int NJ, int TB, bool C = false>
 __device__ __forceinline__ void down_wave(const uint8_t* __restrict__ W,
                                           const void* __restrict__ scale, size_t sbase,
                                           bool e8m0, int H, int I, int h0, int n, int base,
@@ -182,10 +185,6 @@ __device__ __forceinline__ void down_wave(const uint8_t* __restrict__ W,
                        sbase + static_cast<size_t>(h0 / kBlock) * ib_n + min(c, nchunk - 1) / 8);
   }
   for (int q0 = 0; q0 < n; q0 += TB) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) opaque(wv[r][j]);
     const int nq = min(TB, n - q0);
     float acc[4][TB];
 #pragma unroll
@@ -199,12 +198,11 @@ __device__ __forceinline__ void down_wave(const uint8_t* __restrict__ W,
 #pragma unroll
       for (int qq = 0; qq < TB; ++qq) {
         if (qq >= nq) continue;
-        const float4* ap = reinterpret_cast<const float4*>(
-            act + static_cast<size_t>(base + q0 + qq) * I + 16 * c);
+        const float* ap = act + static_cast<size_t>(base + q0 + qq) * I + 16 * c;
         float af[16];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const float4 v = ap[m];
+          const float4 v = ld_f32x4<C>(ap + 4 * m);
           af[4 * m] = v.x;
           af[4 * m + 1] = v.y;
           af[4 * m + 2] = v.z;
@@ -220,10 +218,15 @@ __device__ __forceinline__ void down_wave(const uint8_t* __restrict__ W,
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = wave_sum(acc[r][qq]);
-      if (lane == 0) {
-        float4* o = reinterpret_cast<float4*>(out + static_cast<size_t>(base + q0 + qq) * H + h0);
-        *o = make_float4(v[0], v[1], v[2], v[3]);
-      }
+      if (lane == 0)
+        st_f32x4<C>(out + static_cast<size_t>(base + q0 + qq) * H + h0,
+                    make_float4(v[0], v[1], v[2], v[3]));
+    }
+    if (q0 + TB < n) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) opaque(wv[r][j]);
     }
   }
 }
@@ -234,7 +237,7 @@ constexpr int kRouterTokB = 4;  // tokens per register pass of a router wave
 // logits[t * E + e] = sum_h hidden[t, h] * router_w[e, h] in fp32.
 // The row stays in registers; tokens go in passes of kRouterTokB.
 // NJ2 = 16-byte chunks per lane = ceil(H / 512).
-template <int NJ2>
+template <int NJ2, bool C = false>
 __device__ __forceinline__ void router_wave(const uint16_t* __restrict__ hidden,
                                             const uint16_t* __restrict__ row, int H, int T,
                                             int E, int e, float* logits) {
@@ -273,7 +276,7 @@ __device__ __forceinline__ void router_wave(const uint16_t* __restrict__ hidden,
     for (int q = 0; q < kRouterTokB; ++q) {
       if (t0 + q >= T) continue;
       const float v = wave_sum(acc[q]);
-      if (lane == 0) logits[static_cast<size_t>(t0 + q) * E + e] = v;
+      if (lane == 0) st_f32<C>(logits + static_cast<size_t>(t0 + q) * E + e, v);
     }
   }
 }
@@ -284,6 +287,7 @@ constexpr int kEpiPass = 4;  // H <= 8192 = 4 passes x 256 threads x 8
 // h = sum_j w[t, j] * rows[inv[t, j]] + y_s[t] + residual[t] (fixed order),
 // residual_out = bf16(h), out = bf16(h / sqrt(mean(h^2) + eps) * gamma).
 // s_part: 4 floats of LDS.
+template <bool C = false>
 __device__ __forceinline__ void epilogue_token(int t, const uint16_t* residual,
                                                const uint16_t* __restrict__ gamma, int H, int k,
                                                bool has_shared, float eps, const Workspace& ws,
@@ -294,8 +298,8 @@ __device__ __forceinline__ void epilogue_token(int t, const uint16_t* residual,
   float wj[kMaxTopK];
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
-    pos[j] = j < k ? ws.inv[t * k + j] : 0;
-    wj[j] = j < k ? ws.weights[t * k + j] : 0.f;
+    pos[j] = j < k ? ld_i32<C>(ws.inv + t * k + j) : 0;
+    wj[j] = j < k ? ld_f32<C>(ws.weights + t * k + j) : 0.f;
   }
   float hv[kEpiPass][8];
   float ss = 0.f;
@@ -309,9 +313,8 @@ __device__ __forceinline__ void epilogue_token(int t, const uint16_t* residual,
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
       if (j >= k) continue;
-      const float4* row =
-          reinterpret_cast<const float4*>(ws.rows + static_cast<size_t>(pos[j]) * H + c0);
-      const float4 a = row[0], b = row[1];
+      const float* row = ws.rows + static_cast<size_t>(pos[j]) * H + c0;
+      const float4 a = ld_f32x4<C>(row), b = ld_f32x4<C>(row + 4);
       const float w = wj[j];
       acc[0] = fmaf(w, a.x, acc[0]);
       acc[1] = fmaf(w, a.y, acc[1]);
@@ -323,8 +326,8 @@ __device__ __forceinline__ void epilogue_token(int t, const uint16_t* residual,
       acc[7] = fmaf(w, b.w, acc[7]);
     }
     if (has_shared) {
-      const float4* ys = reinterpret_cast<const float4*>(ws.y_s + static_cast<size_t>(t) * H + c0);
-      const float4 a = ys[0], b = ys[1];
+      const float* ys = ws.y_s + static_cast<size_t>(t) * H + c0;
+      const float4 a = ld_f32x4<C>(ys), b = ld_f32x4<C>(ys + 4);
       acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
       acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
     }

@@ -48,6 +48,7 @@ __device__ inline int block_exclusive_scan(int v, int* s_tmp, int* total) {
 // largest key wins, equal keys go to the lower expert id (a packed
 // (key, ~id) wave maximum, k rounds).  Lane j < k ends with the j-th pick and
 // its weight R * s_j / sum of the k picked scores.
+template <bool C>
 __device__ inline void select_token(const float* logits, const float* bias, int E, int k,
                                     float rsf, int* pick_id, float* pick_w) {
   const int lane = threadIdx.x & 63;
@@ -56,7 +57,7 @@ __device__ inline void select_token(const float* logits, const float* bias, int 
   for (int i = 0; i < 16; ++i) {
     const int e = lane + 64 * i;
     if (e < E) {
-      const float s = sigmoidf_(logits[e]);
+      const float s = sigmoidf_(ld_f32<C>(logits + e));
       sc[i] = s;
       key[i] = bias ? s + bias[e] : s;
     } else {
@@ -119,6 +120,7 @@ __host__ __device__ inline size_t route_smem_bytes(int T, int E, int k) {
 // logits [T, E] must be visible to the workgroup.  Writes ws.ids/weights
 // (and the optional outputs), ws.counts/offsets/touched/n_touched/perm/inv.
 // smem: route_smem_bytes(T, E, k) bytes, 8-byte aligned.
+template <bool C = false>
 __device__ inline void select_and_route(int T, int E, int k, float rsf, const float* logits,
                                         const float* bias, const Workspace& ws,
                                         int32_t* ids_out, float* w_out, unsigned char* smem) {
@@ -134,12 +136,12 @@ __device__ inline void select_and_route(int T, int E, int k, float rsf, const fl
   for (int t = wave; t < T; t += 4) {
     int id = 0;
     float w = 0.f;
-    select_token(logits + static_cast<size_t>(t) * E, bias, E, k, rsf, &id, &w);
+    select_token<C>(logits + static_cast<size_t>(t) * E, bias, E, k, rsf, &id, &w);
     if (lane < k) {
       const int r = t * k + lane;
       s_ids[r] = id;
-      ws.ids[r] = id;
-      ws.weights[r] = w;
+      st_i32<C>(ws.ids + r, id);
+      st_f32<C>(ws.weights + r, w);
       if (ids_out) ids_out[r] = id;
       if (w_out) w_out[r] = w;
     }
@@ -176,15 +178,15 @@ __device__ inline void select_and_route(int T, int E, int k, float rsf, const fl
         const int cnt = packed[m] >> 11;
         const int off = run >> 11, tidx = run & 0x7ff;
         s_off[e] = off;
-        ws.counts[e] = cnt;
-        ws.offsets[e] = off;
-        if (cnt > 0) ws.touched[tidx] = e;
+        st_i32<C>(ws.counts + e, cnt);
+        st_i32<C>(ws.offsets + e, off);
+        if (cnt > 0) st_i32<C>(ws.touched + tidx, e);
       }
       run += packed[m];
     }
     if (threadIdx.x == 0) {
-      ws.offsets[E] = total >> 11;
-      *ws.n_touched = total & 0x7ff;
+      st_i32<C>(ws.offsets + E, total >> 11);
+      st_i32<C>(ws.n_touched, total & 0x7ff);
     }
   }
   __syncthreads();
@@ -197,8 +199,8 @@ __device__ inline void select_and_route(int T, int E, int k, float rsf, const fl
     for (int w = 0; w < (t >> 6); ++w) rank += __popcll(m[w]);
     rank += __popcll(m[t >> 6] & ((1ull << (t & 63)) - 1ull));
     const int pos = s_off[e] + rank;
-    ws.perm[pos] = r;
-    ws.inv[r] = pos;
+    st_i32<C>(ws.perm + pos, r);
+    st_i32<C>(ws.inv + r, pos);
   }
 }
 
