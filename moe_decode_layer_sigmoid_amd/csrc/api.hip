@@ -15,7 +15,7 @@
 #include <cstring>
 #include <new>
 
-#include "../../include/moe_decode.h"
+#include "moe_decode.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -69,7 +69,7 @@ size_t layout(const moe_decode_desc& d, char* base, moe::Workspace* ws) {
   w.rows = reinterpret_cast<float*>(take(T * k * H * 4));
   w.y_s = reinterpret_cast<float*>(take(T * H * 4));
   w.counter = reinterpret_cast<uint32_t*>(take(64));
-  w.sync = reinterpret_cast<uint32_t*>(take((moe::kSyncGuDone + E) * 4));
+  w.sync = reinterpret_cast<uint32_t*>(take(moe::sync_words(static_cast<int>(E)) * 4));
   if (ws) *ws = w;
   return off;
 }
@@ -252,8 +252,7 @@ static int run_fused(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, h
   f.residual_out = static_cast<uint16_t*>(a->residual_out);
   f.ids_out = a->topk_ids;
   f.w_out = a->topk_weights;
-  f.grid = p->fused_grid < static_cast<uint32_t>(f.total) ? p->fused_grid
-                                                          : static_cast<uint32_t>(f.total);
+  f.grid = p->fused_grid;
   hipError_t err = hipSuccess;
   if (p->user_begin) err = hipEventRecord(p->user_begin, s);
   if (err == hipSuccess) err = moe::launch_decode_fused(f, p->ws, s);
@@ -337,8 +336,9 @@ int moe_decode_check_waits(moe_decode_plan_t p, int32_t* gave_up) {
   uint32_t flag = 0;
   int rc = MOE_DECODE_OK;
   if (hipDeviceSynchronize() != hipSuccess ||
-      hipMemcpy(&flag, p->ws.sync + moe::kSyncError, 4, hipMemcpyDeviceToHost) != hipSuccess ||
-      hipMemset(p->ws.sync + moe::kSyncError, 0, 4) != hipSuccess ||
+      hipMemcpy(&flag, p->ws.sync + moe::kSyncError * moe::kSyncStride, 4,
+                hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemset(p->ws.sync + moe::kSyncError * moe::kSyncStride, 0, 4) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess)
     rc = MOE_DECODE_ERR_HIP;
   (void)hipSetDevice(prev);

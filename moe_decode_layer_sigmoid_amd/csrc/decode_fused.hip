@@ -10,22 +10,24 @@
 // experts, so its weight stream overlaps the router and the top-k instead of
 // running on a second stream.
 //
-// Work queue.  Every workgroup takes tickets from one atomic counter, in
-// order, and runs the item a ticket names:
+// Work items, in order:
 //   router items     logits of 4 experts (one per wave) for all tokens; the
 //                    last router item to finish selects the top-k of every
 //                    token, builds the route tables and raises route_ready
 //   shared gate_up   8 SwiGLU rows of the shared expert
 //   shared down      16 output rows of the shared expert   (after all shared gate_up)
-//   routed gate_up   8 SwiGLU rows of one touched-expert slot (after route_ready)
-//   routed down      16 output rows of one slot             (after that slot's gate_up)
+//   routed gate_up   8 SwiGLU rows of one touched expert    (after route_ready)
+//   routed down      16 output rows of one touched expert   (after its gate_up)
 //   boundary         one token: combine + shared + residual + RMSNorm (after all down)
-// An item only waits for items with smaller tickets, which running
-// workgroups already hold, so the queue cannot deadlock however many
-// workgroups are resident.  Every wait is bounded (it raises an error word
-// and gives up rather than hang).  The next ticket is fetched while the
-// current item runs.  The last workgroup to leave zeroes the counters for
-// the next launch (also under HIP-graph replay).
+// The routed items are counted from the touched experts only, so their
+// number is known once route_ready is up.  Workgroup w runs items w, w + G,
+// w + 2G, ... (G = grid size) in increasing order, and an item waits only
+// for items with smaller numbers, so when all G workgroups are resident at
+// once (the grid is sized to the device's occupancy for this kernel) every
+// wait ends.  Waits are bounded anyway: a wait that runs out of its spin
+// budget raises a sticky error word (moe_decode_check_waits) and gives up
+// instead of hanging.  Counters live on separate 128-byte lines; the last
+// workgroup out (two-level exit count) zeroes them for the next launch.
 //
 // Hand-off across workgroups (and XCDs): everything one item leaves for
 // another (logits, route tables, SwiGLU rows, down rows) is written with
@@ -83,31 +85,30 @@ int occupancy_nj();
 template <int NJ>
 __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Workspace ws) {
   __shared__ __attribute__((aligned(16))) unsigned char s_route[kRouteSmem];
-  __shared__ uint32_t s_ticket;
   __shared__ int s_flag;
   __shared__ float s_part[kWaves];
   uint32_t* sync = ws.sync;
-  uint32_t* err = sync + kSyncError;
+  auto ctr = [sync](int i) { return sync + static_cast<size_t>(i) * kSyncStride; };
+  uint32_t* err = ctr(kSyncError);
   const int wave = threadIdx.x >> 6;
   const int H = a.H, I = a.I, Is = a.Is, k = a.k, T = a.T, E = a.E;
   const bool e8m0 = a.e8m0 != 0;
 
-  if (threadIdx.x == 0)
-    s_ticket = __hip_atomic_fetch_add(sync + kSyncTicket, 1u, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  uint32_t t = s_ticket;
   bool routed_ready = false;
-  int n_touched = 0;
-  while (t < static_cast<uint32_t>(a.total)) {
-    uint32_t nxt = 0;
-    if (threadIdx.x == 0)
-      nxt = __hip_atomic_fetch_add(sync + kSyncTicket, 1u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-    const int it = static_cast<int>(t);
+  int n_touched = 0, total = a.o_rgu;
+  for (int it = blockIdx.x;; it += gridDim.x) {
+    if (it >= a.o_rgu && !routed_ready) {
+      // The routed items exist once the router has counted the touched experts.
+      wait_geq(ctr(kSyncRouteReady), 1u, err);
+      routed_ready = true;
+      n_touched = ld_i32<true>(ws.n_touched);
+      total = a.o_rgu + n_touched * (a.gu_per + a.dn_per) + T;
+    }
+    if (it >= total) break;
+
     // Decode the item into one of four kinds; the shared and the routed
     // projections share one call site each (one copy of each tile's code).
-    enum { kSkip, kRouter, kGateUp, kDown, kBoundary } kind = kSkip;
+    enum { kRouter, kGateUp, kDown, kBoundary } kind;
     const uint8_t* W = nullptr;
     const void* S = nullptr;
     size_t sbase = 0;
@@ -124,55 +125,65 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
       rows_i = Is;
       r0 = (it - a.o_sgu) * 2 * kWaves + 2 * wave;
       n = T;
-      done = sync + kSyncSguDone;
+      done = ctr(kSyncSguDone);
     } else if (it < a.o_rgu) {
       // shared down: rows 16*j + 4*wave .. +3, after all shared gate_up
-      wait_geq(sync + kSyncSguDone, static_cast<uint32_t>(a.n_sgu), err);
+      wait_geq(ctr(kSyncSguDone), static_cast<uint32_t>(a.n_sgu), err);
       kind = kDown;
       W = a.sw2;
       S = a.sw2_scale;
       rows_i = Is;
       r0 = (it - a.o_sdn) * 4 * kWaves + 4 * wave;
       n = T;
-      done = sync + kSyncSdnDone;
+      done = ctr(kSyncSdnDone);
     } else {
-      if (!routed_ready) {
-        wait_geq(sync + kSyncRouteReady, 1u, err);
-        routed_ready = true;
-        n_touched = ld_i32<true>(ws.n_touched);
-      }
-      if (it < a.o_epi) {
-        const bool gu = it < a.o_rdn;
-        const int u = gu ? it - a.o_rgu : it - a.o_rdn;
+      const int u = it - a.o_rgu;
+      const int n_gu = n_touched * a.gu_per, n_dn = n_touched * a.dn_per;
+      if (u < n_gu + n_dn) {
+        const bool gu = u < n_gu;
+        const int v = gu ? u : u - n_gu;
         const int per = gu ? a.gu_per : a.dn_per;
-        const int d = u / per, tile = u % per;
-        if (d < n_touched) {
-          const int e = ld_i32<true>(ws.touched + d);
-          n = ld_i32<true>(ws.counts + e);
-          base = ld_i32<true>(ws.offsets + e);
-          perm = ws.perm;
-          rows_i = I;
-          if (gu) {
-            kind = kGateUp;
-            W = a.w13 + static_cast<size_t>(e) * 2 * I * H;
-            S = a.w13_scale;
-            sbase = static_cast<size_t>(e) * (2 * I / kBlock) * (H / kBlock);
-            r0 = tile * 2 * kWaves + 2 * wave;
-            done = sync + kSyncGuDone + d;
-          } else {
-            wait_geq(sync + kSyncGuDone + d, static_cast<uint32_t>(a.gu_per), err);
-            kind = kDown;
-            W = a.w2 + static_cast<size_t>(e) * H * I;
-            S = a.w2_scale;
-            sbase = static_cast<size_t>(e) * (H / kBlock) * (I / kBlock);
-            r0 = tile * 4 * kWaves + 4 * wave;
-            done = sync + kSyncRdnDone;
-          }
+        const int d = v / per, tile = v % per;
+        const int e = ld_i32<true>(ws.touched + d);
+        n = ld_i32<true>(ws.counts + e);
+        base = ld_i32<true>(ws.offsets + e);
+        perm = ws.perm;
+        rows_i = I;
+        if (gu) {
+          kind = kGateUp;
+          W = a.w13 + static_cast<size_t>(e) * 2 * I * H;
+          S = a.w13_scale;
+          sbase = static_cast<size_t>(e) * (2 * I / kBlock) * (H / kBlock);
+          r0 = tile * 2 * kWaves + 2 * wave;
+          done = ctr(sync_gu(d));
+        } else {
+          wait_geq(ctr(sync_gu(d)), static_cast<uint32_t>(a.gu_per), err);
+          kind = kDown;
+          W = a.w2 + static_cast<size_t>(e) * H * I;
+          S = a.w2_scale;
+          sbase = static_cast<size_t>(e) * (H / kBlock) * (I / kBlock);
+          r0 = tile * 4 * kWaves + 4 * wave;
+          done = ctr(sync_dn(d));
         }
       } else {
-        wait_geq(sync + kSyncRdnDone, static_cast<uint32_t>(n_touched * a.dn_per), err);
-        if (Is) wait_geq(sync + kSyncSdnDone, static_cast<uint32_t>(a.n_sdn), err);
+        // boundary: after every down row of every touched slot and of the shared expert
+        if (threadIdx.x == 0) {
+          for (int d = 0; d < n_touched; ++d) {
+            uint32_t spins = 0;
+            while (__hip_atomic_load(ctr(sync_dn(d)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                   static_cast<uint32_t>(a.dn_per)) {
+              __builtin_amdgcn_s_sleep(1);
+              if (++spins == kSpinLimit) {
+                __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+              }
+            }
+          }
+        }
+        __syncthreads();
+        if (Is) wait_geq(ctr(kSyncSdnDone), static_cast<uint32_t>(a.n_sdn), err);
         kind = kBoundary;
+        r0 = u - n_gu - n_dn;  // the token
       }
     }
 
@@ -185,8 +196,8 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
       wait_memory();
       __syncthreads();
       if (threadIdx.x == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(sync + kSyncRouterDone, 1u,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t prev = __hip_atomic_fetch_add(ctr(kSyncRouterDone), 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
         s_flag = prev == static_cast<uint32_t>(a.n_router) - 1;
       }
       __syncthreads();
@@ -196,38 +207,44 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
         wait_memory();
         __syncthreads();
         if (threadIdx.x == 0)
-          __hip_atomic_store(sync + kSyncRouteReady, 1u, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(ctr(kSyncRouteReady), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     } else if (kind == kGateUp) {
-      float* dst = perm ? ws.act : ws.act_s;
-      gate_up_wave<NJ, 1, true>(a.hidden, W, S, sbase, e8m0, H, rows_i, r0, n, perm, base, k, dst,
-                       a.limit);
+      gate_up_wave<NJ, 1, true>(a.hidden, W, S, sbase, e8m0, H, rows_i, r0, n, perm, base, k,
+                                perm ? ws.act : ws.act_s, a.limit);
       signal_add(done);
     } else if (kind == kDown) {
       down_wave<NJ, 1, true>(W, S, sbase, e8m0, H, rows_i, r0, n, base, perm ? ws.act : ws.act_s,
-                    perm ? ws.rows : ws.y_s);
+                             perm ? ws.rows : ws.y_s);
       signal_add(done);
-    } else if (kind == kBoundary) {
-      epilogue_token<true>(it - a.o_epi, a.residual, a.gamma, H, k, Is > 0, a.eps, ws, a.out,
-                     a.residual_out, s_part);
+    } else {
+      epilogue_token<true>(r0, a.residual, a.gamma, H, k, Is > 0, a.eps, ws, a.out,
+                           a.residual_out, s_part);
     }
     __syncthreads();
-    if (threadIdx.x == 0) s_ticket = nxt;
-    __syncthreads();
-    t = s_ticket;
   }
 
-  // The last workgroup out zeroes the counters for the next launch.
+  // Two-level exit count; the last workgroup out zeroes every counter for the
+  // next launch (HIP-graph replays included).  The error word stays set.
   if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(sync + kSyncExit, 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    s_flag = prev == a.grid - 1;
+    const uint32_t lines = kSyncExitLines;
+    const uint32_t line = blockIdx.x % lines;
+    const uint32_t share = a.grid / lines + (line < a.grid % lines ? 1u : 0u);
+    const uint32_t prev = __hip_atomic_fetch_add(ctr(kSyncExit0 + static_cast<int>(line)), 1u,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int last = 0;
+    if (prev == share - 1) {
+      const uint32_t top = __hip_atomic_fetch_add(ctr(kSyncExitTop), 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+      last = top == (a.grid < lines ? a.grid : lines) - 1;
+    }
+    s_flag = last;
   }
   __syncthreads();
   if (s_flag) {
-    for (int i = threadIdx.x; i < kSyncGuDone + a.dmax; i += kThreads)
-      if (i != kSyncError) __hip_atomic_store(sync + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = threadIdx.x; i < kSyncSlot0 + 2 * a.dmax; i += kThreads)
+      if (i != kSyncError)
+        __hip_atomic_store(ctr(i), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -296,9 +313,6 @@ void fused_items(const LayerDims& d, FusedArgs* a) {
   a->o_sgu = a->n_router;
   a->o_sdn = a->o_sgu + a->n_sgu;
   a->o_rgu = a->o_sdn + a->n_sdn;
-  a->o_rdn = a->o_rgu + a->dmax * a->gu_per;
-  a->o_epi = a->o_rdn + a->dmax * a->dn_per;
-  a->total = a->o_epi + d.T;
 }
 
 hipError_t launch_decode_fused(const FusedArgs& a, const Workspace& ws, hipStream_t s) {

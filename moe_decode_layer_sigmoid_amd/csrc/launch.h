@@ -22,21 +22,28 @@ struct Workspace {
   float* rows;         // [maxT * k, H]   routed down output, permuted order
   float* y_s;          // [maxT, H]       shared expert output
   uint32_t* counter;   // [1] last-block counter of the router (self-resetting)
-  uint32_t* sync;      // [kSyncGuDone + E] counters of the fused kernel (self-resetting)
+  uint32_t* sync;      // [sync_words(E)] counters of the fused kernel (self-resetting)
 };
 
-// Words of Workspace::sync.
+// Counters of the fused kernel in Workspace::sync, one 128-byte line each
+// (atomics to one line serialise; separate lines proceed in parallel).
+constexpr int kSyncStride = 32;  // uint32 words per counter line
 enum : int {
-  kSyncTicket = 0,
-  kSyncRouterDone = 1,
-  kSyncRouteReady = 2,
-  kSyncSguDone = 3,
-  kSyncSdnDone = 4,
-  kSyncRdnDone = 5,
-  kSyncExit = 6,
-  kSyncError = 7,  // sticky: set when a bounded wait gave up
-  kSyncGuDone = 16  // one counter per touched-expert slot
+  kSyncRouterDone = 0,
+  kSyncRouteReady = 1,
+  kSyncSguDone = 2,
+  kSyncSdnDone = 3,
+  kSyncError = 4,     // sticky: set when a bounded wait gave up
+  kSyncExit0 = 5,     // kSyncExitLines first-level exit counters
+  kSyncExitLines = 8,
+  kSyncExitTop = kSyncExit0 + kSyncExitLines,
+  kSyncSlot0 = kSyncExitTop + 1  // then per touched-expert slot d: gate_up done, down done
 };
+__host__ __device__ constexpr int sync_gu(int d) { return kSyncSlot0 + 2 * d; }
+__host__ __device__ constexpr int sync_dn(int d) { return kSyncSlot0 + 2 * d + 1; }
+__host__ __device__ constexpr size_t sync_words(int E) {
+  return static_cast<size_t>(kSyncSlot0 + 2 * E) * kSyncStride;
+}
 
 constexpr int kFusedMaxTokens = 16;
 
@@ -63,7 +70,7 @@ struct FusedArgs {
   float limit, rsf, eps;
   // work-queue layout: item offsets and counts
   int n_router, n_sgu, n_sdn, gu_per, dn_per, dmax;
-  int o_sgu, o_sdn, o_rgu, o_rdn, o_epi, total;
+  int o_sgu, o_sdn, o_rgu;  // routed items follow o_rgu once the touched count is known
   uint32_t grid;
 };
 
