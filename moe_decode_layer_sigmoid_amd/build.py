@@ -16,8 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_decode.so")
 SOURCES = ["api.hip", "router.hip", "experts_gemv.hip", "epilogue.hip", "decode_fused.hip"]
-# decode_fused.hip is also compiled once per register chunk count (the
-# template argument of its kernel), each into its own object.
+# decode_fused.hip is also compiled once per register chunk count and scale
+# format (the template arguments of its kernel), each into its own object.
 FUSED_NJ = range(1, 9)
 ARCH = "gfx950"
 
@@ -56,9 +56,11 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         jobs.append((obj, [hipcc(), *FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj]))
     for nj in FUSED_NJ:
-        obj = os.path.join(objdir, "decode_fused_nj%d.o" % nj)
-        jobs.append((obj, [hipcc(), *FLAGS, *inc, "-DMOE_FUSED_NJ=%d" % nj, "-c",
-                           os.path.join(CSRC, "decode_fused.hip"), "-o", obj]))
+        for e8 in (0, 1):
+            obj = os.path.join(objdir, "decode_fused_nj%d_e%d.o" % (nj, e8))
+            jobs.append((obj, [hipcc(), *FLAGS, *inc, "-DMOE_FUSED_NJ=%d" % nj,
+                               "-DMOE_FUSED_E8=%d" % e8, "-c",
+                               os.path.join(CSRC, "decode_fused.hip"), "-o", obj]))
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", "0")) or os.cpu_count() or 1))
     with ThreadPoolExecutor(workers) as ex:
         results = list(ex.map(lambda j: _run(j[1]), jobs))

@@ -70,6 +70,7 @@ size_t layout(const moe_decode_desc& d, char* base, moe::Workspace* ws) {
   w.y_s = reinterpret_cast<float*>(take(T * H * 4));
   w.counter = reinterpret_cast<uint32_t*>(take(64));
   w.sync = reinterpret_cast<uint32_t*>(take(moe::sync_words(static_cast<int>(E)) * 4));
+  w.zero_bias = reinterpret_cast<float*>(take(E * 4));
   if (ws) *ws = w;
   return off;
 }
@@ -190,8 +191,9 @@ int moe_decode_plan(const moe_decode_desc* d, int device, moe_decode_plan_t* out
               hipEventCreateWithFlags(&p->join, hipEventDisableTiming) != hipSuccess))
     rc = MOE_DECODE_ERR_HIP;
   if (!rc) {
-    const int per_cu = moe::fused_blocks_per_cu(moe::fused_nj(d->hidden, d->intermediate,
-                                                                d->shared_intermediate));
+    const int per_cu = moe::fused_blocks_per_cu(
+        moe::fused_nj(d->hidden, d->intermediate, d->shared_intermediate),
+        d->scale_fmt == MOE_DECODE_SCALE_E8M0);
     p->fused_grid = static_cast<uint32_t>(per_cu > 0 ? per_cu * prop.multiProcessorCount : 0);
   }
   if (!rc && hipDeviceSynchronize() != hipSuccess) rc = MOE_DECODE_ERR_HIP;
@@ -238,7 +240,7 @@ static int run_fused(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, h
   f.hidden = static_cast<const uint16_t*>(a->hidden);
   f.residual = static_cast<const uint16_t*>(a->residual);
   f.router_w = static_cast<const uint16_t*>(a->router_w);
-  f.bias = a->router_bias;
+  f.bias = a->router_bias ? a->router_bias : p->ws.zero_bias;
   f.w13 = static_cast<const uint8_t*>(a->w13);
   f.w13_scale = a->w13_scale;
   f.w2 = static_cast<const uint8_t*>(a->w2);
@@ -278,7 +280,8 @@ static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t 
     if (err == hipSuccess) step(moe::launch_down_gemv(d, true, a->sw2, a->sw2_scale, p->ws, p->side));
   }
   if (err == hipSuccess)
-    step(moe::launch_router(d, a->hidden, a->router_w, a->router_bias, p->ws, a->topk_ids,
+    step(moe::launch_router(d, a->hidden, a->router_w,
+                            a->router_bias ? a->router_bias : p->ws.zero_bias, p->ws, a->topk_ids,
                             a->topk_weights, s));
   if (err == hipSuccess && p->user_begin) step(hipEventRecord(p->user_begin, s));
   if (err == hipSuccess)

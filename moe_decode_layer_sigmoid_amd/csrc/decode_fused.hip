@@ -74,15 +74,15 @@ __device__ __forceinline__ void wait_geq(const uint32_t* c, uint32_t target, uin
   __syncthreads();
 }
 
-template <int NJ>
+template <int NJ, bool E8>
 hipError_t launch_nj(const FusedArgs& a, const Workspace& ws, hipStream_t s);
-template <int NJ>
+template <int NJ, bool E8>
 int occupancy_nj();
 
 #ifdef MOE_FUSED_NJ
 // This object holds the kernel for one chunk count (the build compiles this
 // file once per value, in parallel).
-template <int NJ>
+template <int NJ, bool E8>
 __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Workspace ws) {
   __shared__ __attribute__((aligned(16))) unsigned char s_route[kRouteSmem];
   __shared__ int s_flag;
@@ -92,7 +92,6 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
   uint32_t* err = ctr(kSyncError);
   const int wave = threadIdx.x >> 6;
   const int H = a.H, I = a.I, Is = a.Is, k = a.k, T = a.T, E = a.E;
-  const bool e8m0 = a.e8m0 != 0;
 
   bool routed_ready = false;
   int n_touched = 0, total = a.o_rgu;
@@ -210,12 +209,12 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
           __hip_atomic_store(ctr(kSyncRouteReady), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     } else if (kind == kGateUp) {
-      gate_up_wave<NJ, 1, true>(a.hidden, W, S, sbase, e8m0, H, rows_i, r0, n, perm, base, k,
-                                perm ? ws.act : ws.act_s, a.limit);
+      gate_up_wave<NJ, 1, true, E8>(a.hidden, W, S, sbase, H, rows_i, r0, n, perm, base, k,
+                                    perm ? ws.act : ws.act_s, a.limit);
       signal_add(done);
     } else if (kind == kDown) {
-      down_wave<NJ, 1, true>(W, S, sbase, e8m0, H, rows_i, r0, n, base, perm ? ws.act : ws.act_s,
-                             perm ? ws.rows : ws.y_s);
+      down_wave<NJ, 1, true, E8>(W, S, sbase, H, rows_i, r0, n, base, perm ? ws.act : ws.act_s,
+                                 perm ? ws.rows : ws.y_s);
       signal_add(done);
     } else {
       epilogue_token<true>(r0, a.residual, a.gamma, H, k, Is > 0, a.eps, ws, a.out,
@@ -248,23 +247,24 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
   }
 }
 
-template <int NJ>
+template <int NJ, bool E8>
 hipError_t launch_nj(const FusedArgs& a, const Workspace& ws, hipStream_t s) {
-  hipLaunchKernelGGL(decode_fused_kernel<NJ>, dim3(a.grid), dim3(kThreads), 0, s, a, ws);
+  hipLaunchKernelGGL((decode_fused_kernel<NJ, E8>), dim3(a.grid), dim3(kThreads), 0, s, a, ws);
   return hipGetLastError();
 }
 
-template <int NJ>
+template <int NJ, bool E8>
 int occupancy_nj() {
   int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_fused_kernel<NJ>, kThreads, 0) !=
-      hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_fused_kernel<NJ, E8>, kThreads,
+                                                   0) != hipSuccess)
     return 0;
   return blocks;
 }
 
-template hipError_t launch_nj<MOE_FUSED_NJ>(const FusedArgs&, const Workspace&, hipStream_t);
-template int occupancy_nj<MOE_FUSED_NJ>();
+template hipError_t launch_nj<MOE_FUSED_NJ, (MOE_FUSED_E8 != 0)>(const FusedArgs&,
+                                                                  const Workspace&, hipStream_t);
+template int occupancy_nj<MOE_FUSED_NJ, (MOE_FUSED_E8 != 0)>();
 #endif  // MOE_FUSED_NJ
 
 }  // namespace fused
@@ -281,11 +281,13 @@ int fused_nj(int H, int I, int Is) {
   return nj;
 }
 
-int fused_blocks_per_cu(int nj) {
-  switch (nj) {
-#define X(N) \
-  case N:    \
-    return occupancy_nj<N>();
+int fused_blocks_per_cu(int nj, bool e8m0) {
+  switch (nj * 2 + (e8m0 ? 1 : 0)) {
+#define X(N)                           \
+  case 2 * N:                          \
+    return occupancy_nj<N, false>();   \
+  case 2 * N + 1:                      \
+    return occupancy_nj<N, true>();
     X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8)
 #undef X
     default:
@@ -316,10 +318,12 @@ void fused_items(const LayerDims& d, FusedArgs* a) {
 }
 
 hipError_t launch_decode_fused(const FusedArgs& a, const Workspace& ws, hipStream_t s) {
-  switch (fused_nj(a.H, a.I, a.Is)) {
-#define X(N) \
-  case N:    \
-    return launch_nj<N>(a, ws, s);
+  switch (fused_nj(a.H, a.I, a.Is) * 2 + (a.e8m0 ? 1 : 0)) {
+#define X(N)                          \
+  case 2 * N:                         \
+    return launch_nj<N, false>(a, ws, s); \
+  case 2 * N + 1:                     \
+    return launch_nj<N, true>(a, ws, s);
     X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8)
 #undef X
     default:

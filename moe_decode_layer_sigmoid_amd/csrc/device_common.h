@@ -43,9 +43,12 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
   return b == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(b << 23);
 }
 
-// Block scale number `idx` of a scale tensor (fp32 or e8m0 bytes).
-__device__ __forceinline__ float load_scale(const void* s, bool e8m0, size_t idx) {
-  if (e8m0) return e8m0_to_f32(static_cast<const uint8_t*>(s)[idx]);
+// Block scale number `idx` of a scale tensor: fp32, or e8m0 bytes (E8).  A
+// compile-time format keeps the load free of branches (a branch around a
+// load makes the compiler wait for it at the join, serialising the loads).
+template <bool E8>
+__device__ __forceinline__ float load_scale(const void* s, size_t idx) {
+  if (E8) return e8m0_to_f32(static_cast<const uint8_t*>(s)[idx]);
   return static_cast<const float*>(s)[idx];
 }
 

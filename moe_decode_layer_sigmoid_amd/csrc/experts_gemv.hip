@@ -45,11 +45,11 @@ __device__ __forceinline__ bool slot_info(bool shared, int T, const Workspace& w
   return true;
 }
 
-template <int NJ>
+template <int NJ, bool E8>
 __global__ __launch_bounds__(kThreads) void gate_up_kernel(
     const uint16_t* __restrict__ hidden, const uint8_t* __restrict__ w13,
-    const void* __restrict__ scale, int e8m0, int H, int I, int k, int T, int shared,
-    Workspace ws, float limit) {
+    const void* __restrict__ scale, int H, int I, int k, int T, int shared, Workspace ws,
+    float limit) {
   const int wave = threadIdx.x >> 6;
   const int i0 = (blockIdx.x * kWaves + wave) * 2;
   SlotInfo si;
@@ -57,22 +57,23 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(
   const size_t rows_per_e = static_cast<size_t>(2) * I;
   const uint8_t* W = w13 + static_cast<size_t>(si.e) * rows_per_e * H;
   const size_t sbase = static_cast<size_t>(si.e) * (rows_per_e / kBlock) * (H / kBlock);
-  gate_up_wave<NJ, 4>(hidden, W, scale, sbase, e8m0, H, I, i0, si.n, shared ? nullptr : ws.perm,
-                   si.base, k, shared ? ws.act_s : ws.act, limit);
+  gate_up_wave<NJ, 1, false, E8>(hidden, W, scale, sbase, H, I, i0, si.n,
+                                  shared ? nullptr : ws.perm, si.base, k,
+                                  shared ? ws.act_s : ws.act, limit);
 }
 
-template <int NJ>
+template <int NJ, bool E8>
 __global__ __launch_bounds__(kThreads) void down_kernel(
-    const uint8_t* __restrict__ w2, const void* __restrict__ scale, int e8m0, int H, int I,
-    int T, int shared, Workspace ws) {
+    const uint8_t* __restrict__ w2, const void* __restrict__ scale, int H, int I, int T,
+    int shared, Workspace ws) {
   const int wave = threadIdx.x >> 6;
   const int h0 = (blockIdx.x * kWaves + wave) * 4;
   SlotInfo si;
   if (!slot_info(shared, T, ws, &si) || h0 >= H) return;
   const uint8_t* W = w2 + static_cast<size_t>(si.e) * H * I;
   const size_t sbase = static_cast<size_t>(si.e) * (H / kBlock) * (I / kBlock);
-  down_wave<NJ, 4>(W, scale, sbase, e8m0, H, I, h0, si.n, si.base, shared ? ws.act_s : ws.act,
-                shared ? ws.y_s : ws.rows);
+  down_wave<NJ, 1, false, E8>(W, scale, sbase, H, I, h0, si.n, si.base,
+                              shared ? ws.act_s : ws.act, shared ? ws.y_s : ws.rows);
 }
 
 }  // namespace
@@ -88,12 +89,16 @@ hipError_t launch_gate_up_gemv(const LayerDims& d, bool shared, const void* hidd
   dim3 grid(I / (2 * kWaves), slots);
   const auto* x = static_cast<const uint16_t*>(hidden);
   const auto* w = static_cast<const uint8_t*>(w13);
-  switch (nj) {
-#define X(N)                                                                                  \
-  case N:                                                                                     \
-    hipLaunchKernelGGL(gate_up_kernel<N>, grid, dim3(kThreads), 0, s, x, w, w13_scale,        \
-                       static_cast<int>(d.e8m0), d.H, I, d.k, d.T, static_cast<int>(shared), ws, \
-                       d.limit);                                                              \
+  const int sh = static_cast<int>(shared);
+  switch (nj * 2 + (d.e8m0 ? 1 : 0)) {
+#define X(N)                                                                                    \
+  case 2 * N:                                                                                   \
+    hipLaunchKernelGGL((gate_up_kernel<N, false>), grid, dim3(kThreads), 0, s, x, w, w13_scale, \
+                       d.H, I, d.k, d.T, sh, ws, d.limit);                                      \
+    break;                                                                                      \
+  case 2 * N + 1:                                                                               \
+    hipLaunchKernelGGL((gate_up_kernel<N, true>), grid, dim3(kThreads), 0, s, x, w, w13_scale,  \
+                       d.H, I, d.k, d.T, sh, ws, d.limit);                                      \
     break;
     MOE_NJ_CASES(X)
 #undef X
@@ -110,11 +115,16 @@ hipError_t launch_down_gemv(const LayerDims& d, bool shared, const void* w2,
   const int slots = shared ? 1 : (d.T * d.k < d.E ? d.T * d.k : d.E);
   dim3 grid(d.H / (4 * kWaves), slots);
   const auto* w = static_cast<const uint8_t*>(w2);
-  switch (nj) {
+  const int sh = static_cast<int>(shared);
+  switch (nj * 2 + (d.e8m0 ? 1 : 0)) {
 #define X(N)                                                                                  \
-  case N:                                                                                     \
-    hipLaunchKernelGGL(down_kernel<N>, grid, dim3(kThreads), 0, s, w, w2_scale,               \
-                       static_cast<int>(d.e8m0), d.H, I, d.T, static_cast<int>(shared), ws); \
+  case 2 * N:                                                                                 \
+    hipLaunchKernelGGL((down_kernel<N, false>), grid, dim3(kThreads), 0, s, w, w2_scale, d.H,  \
+                       I, d.T, sh, ws);                                                       \
+    break;                                                                                    \
+  case 2 * N + 1:                                                                             \
+    hipLaunchKernelGGL((down_kernel<N, true>), grid, dim3(kThreads), 0, s, w, w2_scale, d.H,   \
+                       I, d.T, sh, ws);                                                       \
     break;
     MOE_NJ_CASES(X)
 #undef X

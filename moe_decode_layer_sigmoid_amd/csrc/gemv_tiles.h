@@ -65,20 +65,26 @@ __device__ __forceinline__ void opaque(uint4& v) {
 }
 
 
+// All loads below are branch-free: out-of-range chunks and tokens read a
+// clamped, valid address and are masked afterwards.  A load under a branch
+// makes the compiler wait for it where the branches join, which serialises
+// the loads of a wave; these tiles issue every weight load of the wave
+// before the first one is used.
+
 // gate_up + clamped SwiGLU of one wave: SwiGLU outputs i0, i0+1 (i0 even)
 // from gate rows i0, i0+1 and up rows I+i0, I+i0+1 of one expert, for its n
-// tokens.  Token q is row perm[base+q] / k of hidden (perm == nullptr: row q).
-// Writes act[(base + q) * I + i0 + {0, 1}].  Products are exact (bf16 x
-// e4m3 in the bf16 dot2 unit), sums in fp32.
+// tokens (n >= 1).  Token q is row perm[base+q] / k of hidden (perm ==
+// nullptr: row q).  Writes act[(base + q) * I + i0 + {0, 1}].  Products are
+// exact (bf16 x e4m3 in the bf16 dot2 unit), sums in fp32.
 // NJ = 16-byte chunks per lane per row = ceil(H / 1024); TB = tokens per
-// register pass over the loaded weights.
-template <int NJ, int TB, bool C = false>
+// register pass over the loaded weights; C = coherent hand-off of perm/act;
+// E8 = e8m0 scales.
+template <int NJ, int TB, bool C, bool E8>
 __device__ __forceinline__ void gate_up_wave(const uint16_t* __restrict__ hidden,
                                              const uint8_t* __restrict__ W,
-                                             const void* __restrict__ scale, size_t sbase,
-                                             bool e8m0, int H, int I, int i0, int n,
-                                             const int32_t* perm, int base, int k,
-                                             float* __restrict__ act, float limit) {
+                                             const void* __restrict__ scale, size_t sbase, int H,
+                                             int I, int i0, int n, const int32_t* perm, int base,
+                                             int k, float* __restrict__ act, float limit) {
   const int lane = threadIdx.x & 63;
   const int kb_n = H / kBlock;
   const int nchunk = H / 16;
@@ -88,20 +94,24 @@ __device__ __forceinline__ void gate_up_wave(const uint16_t* __restrict__ hidden
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int c = lane + 64 * j;
+    const int cc = c < nchunk ? c : nchunk - 1;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      wv[r][j] = c < nchunk ? ld_stream16(W + static_cast<size_t>(rows[r]) * H + 16 * c)
-                            : make_uint4(0, 0, 0, 0);
-    const int kb = min(c, nchunk - 1) / 8;
-    sc[0][j] = load_scale(scale, e8m0, sbase + static_cast<size_t>(i0 / kBlock) * kb_n + kb);
-    sc[1][j] = load_scale(scale, e8m0, sbase + static_cast<size_t>((I + i0) / kBlock) * kb_n + kb);
+      wv[r][j] = ld_stream16(W + static_cast<size_t>(rows[r]) * H + 16 * cc);
+    const int kb = cc / 8;
+    const float s0 = load_scale<E8>(scale, sbase + static_cast<size_t>(i0 / kBlock) * kb_n + kb);
+    const float s1 =
+        load_scale<E8>(scale, sbase + static_cast<size_t>((I + i0) / kBlock) * kb_n + kb);
+    // a chunk past the row end contributes nothing
+    sc[0][j] = c < nchunk ? s0 : 0.f;
+    sc[1][j] = c < nchunk ? s1 : 0.f;
   }
   for (int q0 = 0; q0 < n; q0 += TB) {
     int tok[TB];
 #pragma unroll
     for (int qq = 0; qq < TB; ++qq) {
-      const int q = q0 + qq;
-      tok[qq] = q < n ? (perm ? ld_i32<C>(perm + base + q) / k : q) : -1;
+      const int q = q0 + qq < n ? q0 + qq : n - 1;
+      tok[qq] = perm ? ld_i32<C>(perm + base + q) / k : q;
     }
     float acc[4][TB];
 #pragma unroll
@@ -111,13 +121,12 @@ __device__ __forceinline__ void gate_up_wave(const uint16_t* __restrict__ hidden
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int c = lane + 64 * j;
-      if (c >= nchunk) continue;
+      const int cc = c < nchunk ? c : nchunk - 1;
       uint32_t xs[TB][8];
 #pragma unroll
       for (int qq = 0; qq < TB; ++qq) {
-        if (tok[qq] < 0) continue;
         const uint4* xp =
-            reinterpret_cast<const uint4*>(hidden + static_cast<size_t>(tok[qq]) * H + 16 * c);
+            reinterpret_cast<const uint4*>(hidden + static_cast<size_t>(tok[qq]) * H + 16 * cc);
         const uint4 a = xp[0], b = xp[1];
         xs[qq][0] = a.x; xs[qq][1] = a.y; xs[qq][2] = a.z; xs[qq][3] = a.w;
         xs[qq][4] = b.x; xs[qq][5] = b.y; xs[qq][6] = b.z; xs[qq][7] = b.w;
@@ -131,7 +140,6 @@ __device__ __forceinline__ void gate_up_wave(const uint16_t* __restrict__ hidden
         fp8x4_to_bf16x4(wv[r][j].w, &wb[6], &wb[7]);
 #pragma unroll
         for (int qq = 0; qq < TB; ++qq) {
-          if (tok[qq] < 0) continue;
           float p = 0.f;
 #pragma unroll
           for (int m = 0; m < 8; ++m) p = dot2_bf16(wb[m], xs[qq][m], p);
@@ -141,7 +149,7 @@ __device__ __forceinline__ void gate_up_wave(const uint16_t* __restrict__ hidden
     }
 #pragma unroll
     for (int qq = 0; qq < TB; ++qq) {
-      if (tok[qq] < 0) continue;
+      if (q0 + qq >= n) continue;  // uniform: no loads below
       const float g0 = wave_sum(acc[0][qq]), g1 = wave_sum(acc[1][qq]);
       const float u0 = wave_sum(acc[2][qq]), u1 = wave_sum(acc[3][qq]);
       if (lane == 0) {
@@ -161,14 +169,14 @@ __device__ __forceinline__ void gate_up_wave(const uint16_t* __restrict__ hidden
 }
 
 // down projection of one wave: output rows h0 .. h0+3 (h0 % 4 == 0) of one
-// expert for its n SwiGLU rows act[(base + q) * I], written to
+// expert for its n >= 1 SwiGLU rows act[(base + q) * I], written to
 // out[(base + q) * H + h0 .. +3].  fp32 products and sums (the SwiGLU
-// activations stay fp32).  NJ = ceil(I / 1024); TB = tokens per pass.
-template <int NJ, int TB, bool C = false>
+// activations stay fp32).  NJ = ceil(I / 1024); TB, C, E8 as above.
+template <int NJ, int TB, bool C, bool E8>
 __device__ __forceinline__ void down_wave(const uint8_t* __restrict__ W,
-                                          const void* __restrict__ scale, size_t sbase,
-                                          bool e8m0, int H, int I, int h0, int n, int base,
-                                          const float* act, float* out) {
+                                          const void* __restrict__ scale, size_t sbase, int H,
+                                          int I, int h0, int n, int base, const float* act,
+                                          float* out) {
   const int lane = threadIdx.x & 63;
   const int ib_n = I / kBlock;
   const int nchunk = I / 16;
@@ -177,15 +185,14 @@ __device__ __forceinline__ void down_wave(const uint8_t* __restrict__ W,
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int c = lane + 64 * j;
+    const int cc = c < nchunk ? c : nchunk - 1;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      wv[r][j] = c < nchunk ? ld_stream16(W + static_cast<size_t>(h0 + r) * I + 16 * c)
-                            : make_uint4(0, 0, 0, 0);
-    sc[j] = load_scale(scale, e8m0,
-                       sbase + static_cast<size_t>(h0 / kBlock) * ib_n + min(c, nchunk - 1) / 8);
+      wv[r][j] = ld_stream16(W + static_cast<size_t>(h0 + r) * I + 16 * cc);
+    const float s0 = load_scale<E8>(scale, sbase + static_cast<size_t>(h0 / kBlock) * ib_n + cc / 8);
+    sc[j] = c < nchunk ? s0 : 0.f;
   }
   for (int q0 = 0; q0 < n; q0 += TB) {
-    const int nq = min(TB, n - q0);
     float acc[4][TB];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -194,11 +201,11 @@ __device__ __forceinline__ void down_wave(const uint8_t* __restrict__ W,
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int c = lane + 64 * j;
-      if (c >= nchunk) continue;
+      const int cc = c < nchunk ? c : nchunk - 1;
 #pragma unroll
       for (int qq = 0; qq < TB; ++qq) {
-        if (qq >= nq) continue;
-        const float* ap = act + static_cast<size_t>(base + q0 + qq) * I + 16 * c;
+        const int q = q0 + qq < n ? q0 + qq : n - 1;
+        const float* ap = act + static_cast<size_t>(base + q) * I + 16 * cc;
         float af[16];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -214,7 +221,7 @@ __device__ __forceinline__ void down_wave(const uint8_t* __restrict__ W,
     }
 #pragma unroll
     for (int qq = 0; qq < TB; ++qq) {
-      if (qq >= nq) continue;
+      if (q0 + qq >= n) continue;
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = wave_sum(acc[r][qq]);
@@ -231,9 +238,9 @@ __device__ __forceinline__ void down_wave(const uint8_t* __restrict__ W,
   }
 }
 
-constexpr int kRouterTokB = 4;  // tokens per register pass of a router wave
+constexpr int kRouterTokB = 2;  // tokens per register pass of a router wave
 
-// Router logits of one expert row for tokens [0, T):
+// Router logits of one expert row for tokens [0, T) (T >= 1):
 // logits[t * E + e] = sum_h hidden[t, h] * router_w[e, h] in fp32.
 // The row stays in registers; tokens go in passes of kRouterTokB.
 // NJ2 = 16-byte chunks per lane = ceil(H / 512).
@@ -247,7 +254,8 @@ __device__ __forceinline__ void router_wave(const uint16_t* __restrict__ hidden,
 #pragma unroll
   for (int j = 0; j < NJ2; ++j) {
     const int c = lane + 64 * j;
-    wv[j] = c < nchunk ? ld_stream16(row + 8 * c) : make_uint4(0, 0, 0, 0);
+    const uint4 v = ld_stream16(row + 8 * (c < nchunk ? c : nchunk - 1));
+    wv[j] = c < nchunk ? v : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll 1
   for (int t0 = 0; t0 < T; t0 += kRouterTokB) {
@@ -257,19 +265,15 @@ __device__ __forceinline__ void router_wave(const uint16_t* __restrict__ hidden,
 #pragma unroll
     for (int j = 0; j < NJ2; ++j) {
       const int c = lane + 64 * j;
-      if (c >= nchunk) continue;
+      const int cc = c < nchunk ? c : nchunk - 1;
       const uint32_t w[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
 #pragma unroll
       for (int q = 0; q < kRouterTokB; ++q) {
-        if (t0 + q >= T) continue;
-        const uint4 xv =
-            *reinterpret_cast<const uint4*>(hidden + static_cast<size_t>(t0 + q) * H + 8 * c);
+        const int t = t0 + q < T ? t0 + q : T - 1;
+        const uint4 xv = *reinterpret_cast<const uint4*>(hidden + static_cast<size_t>(t) * H + 8 * cc);
         const uint32_t x[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          acc[q] = fmaf(bf16_lo(w[m]), bf16_lo(x[m]), acc[q]);
-          acc[q] = fmaf(bf16_hi(w[m]), bf16_hi(x[m]), acc[q]);
-        }
+        for (int m = 0; m < 4; ++m) acc[q] = dot2_bf16(w[m], x[m], acc[q]);
       }
     }
 #pragma unroll
@@ -298,40 +302,51 @@ __device__ __forceinline__ void epilogue_token(int t, const uint16_t* residual,
   float wj[kMaxTopK];
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) {
-    pos[j] = j < k ? ld_i32<C>(ws.inv + t * k + j) : 0;
-    wj[j] = j < k ? ld_f32<C>(ws.weights + t * k + j) : 0.f;
+    const int jj = j < k ? j : k - 1;
+    pos[j] = ld_i32<C>(ws.inv + t * k + jj);
+    const float w = ld_f32<C>(ws.weights + t * k + jj);
+    wj[j] = j < k ? w : 0.f;
   }
   float hv[kEpiPass][8];
   float ss = 0.f;
 #pragma unroll
   for (int p = 0; p < kEpiPass; ++p) {
     const int c0 = 8 * (threadIdx.x + 256 * p);
-    if (c0 >= H) continue;
+    if (c0 >= H) continue;  // uniform per pass up to the last partial pass
     float acc[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) acc[m] = 0.f;
+    // routes in groups of four: the group's eight loads go out together
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      if (j >= k) continue;
-      const float* row = ws.rows + static_cast<size_t>(pos[j]) * H + c0;
-      const float4 a = ld_f32x4<C>(row), b = ld_f32x4<C>(row + 4);
-      const float w = wj[j];
-      acc[0] = fmaf(w, a.x, acc[0]);
-      acc[1] = fmaf(w, a.y, acc[1]);
-      acc[2] = fmaf(w, a.z, acc[2]);
-      acc[3] = fmaf(w, a.w, acc[3]);
-      acc[4] = fmaf(w, b.x, acc[4]);
-      acc[5] = fmaf(w, b.y, acc[5]);
-      acc[6] = fmaf(w, b.z, acc[6]);
-      acc[7] = fmaf(w, b.w, acc[7]);
+    for (int j0 = 0; j0 < kMaxTopK; j0 += 4) {
+      if (j0 >= k) break;
+      float4 ra[4], rb[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float* row = ws.rows + static_cast<size_t>(pos[j0 + q]) * H + c0;
+        ra[q] = ld_f32x4<C>(row);
+        rb[q] = ld_f32x4<C>(row + 4);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float w = wj[j0 + q];
+        acc[0] = fmaf(w, ra[q].x, acc[0]);
+        acc[1] = fmaf(w, ra[q].y, acc[1]);
+        acc[2] = fmaf(w, ra[q].z, acc[2]);
+        acc[3] = fmaf(w, ra[q].w, acc[3]);
+        acc[4] = fmaf(w, rb[q].x, acc[4]);
+        acc[5] = fmaf(w, rb[q].y, acc[5]);
+        acc[6] = fmaf(w, rb[q].z, acc[6]);
+        acc[7] = fmaf(w, rb[q].w, acc[7]);
+      }
     }
-    if (has_shared) {
-      const float* ys = ws.y_s + static_cast<size_t>(t) * H + c0;
-      const float4 a = ld_f32x4<C>(ys), b = ld_f32x4<C>(ys + 4);
-      acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-      acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
-    }
+    const float* ys = ws.y_s + static_cast<size_t>(t) * H + c0;
+    const float4 ya = ld_f32x4<C>(ys), yb = ld_f32x4<C>(ys + 4);
     const uint4 rv = *reinterpret_cast<const uint4*>(residual + static_cast<size_t>(t) * H + c0);
+    if (has_shared) {
+      acc[0] += ya.x; acc[1] += ya.y; acc[2] += ya.z; acc[3] += ya.w;
+      acc[4] += yb.x; acc[5] += yb.y; acc[6] += yb.z; acc[7] += yb.w;
+    }
     const uint32_t u[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {

@@ -23,6 +23,7 @@ struct Workspace {
   float* y_s;          // [maxT, H]       shared expert output
   uint32_t* counter;   // [1] last-block counter of the router (self-resetting)
   uint32_t* sync;      // [sync_words(E)] counters of the fused kernel (self-resetting)
+  float* zero_bias;    // [E] zeros: the router bias when the caller passes none
 };
 
 // Counters of the fused kernel in Workspace::sync, one 128-byte line each
@@ -97,7 +98,7 @@ hipError_t launch_down_gemv(const LayerDims& d, bool shared, const void* w2,
 
 // Fused persistent kernel of the whole step (T <= kFusedMaxTokens).
 int fused_nj(int H, int I, int Is);
-int fused_blocks_per_cu(int nj);
+int fused_blocks_per_cu(int nj, bool e8m0);
 void fused_items(const LayerDims& d, FusedArgs* a);
 hipError_t launch_decode_fused(const FusedArgs& a, const Workspace& ws, hipStream_t s);
 

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
   __threadfence();
 
   // ---- phase 2: top-k of every token and the route tables
-  select_and_route(T, E, k, rsf, ws.logits, bias, ws, ids_out, w_out, smem);
+  select_and_route<false>(T, E, k, rsf, ws.logits, bias, ws, ids_out, w_out, smem);
   if (threadIdx.x == 0)
     __hip_atomic_store(ws.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

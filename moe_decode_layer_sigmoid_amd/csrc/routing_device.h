@@ -44,7 +44,8 @@ __device__ inline int block_exclusive_scan(int v, int* s_tmp, int* total) {
   return base + inc - v;
 }
 
-// Top-k of one token in one wave.  Keys are sigmoid(logit) (+ bias); the
+// Top-k of one token in one wave.  Keys are sigmoid(logit) + bias (bias is
+// never null: a zero vector stands in for no bias); the
 // largest key wins, equal keys go to the lower expert id (a packed
 // (key, ~id) wave maximum, k rounds).  Lane j < k ends with the j-th pick and
 // its weight R * s_j / sum of the k picked scores.
@@ -53,17 +54,14 @@ __device__ inline void select_token(const float* logits, const float* bias, int 
                                     float rsf, int* pick_id, float* pick_w) {
   const int lane = threadIdx.x & 63;
   float key[16], sc[16];
+  // Branch-free loads (clamped index; slots past E are never picked).
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int e = lane + 64 * i;
-    if (e < E) {
-      const float s = sigmoidf_(ld_f32<C>(logits + e));
-      sc[i] = s;
-      key[i] = bias ? s + bias[e] : s;
-    } else {
-      sc[i] = 0.f;
-      key[i] = 0.f;
-    }
+    const int ee = e < E ? e : E - 1;
+    const float s = sigmoidf_(ld_f32<C>(logits + ee));
+    sc[i] = s;
+    key[i] = s + bias[ee];
   }
   uint32_t taken = 0;
   float ssum = 0.f, my_s = 0.f;
