@@ -21,10 +21,11 @@
 //   boundary         one token: combine + shared + residual + RMSNorm (after all down)
 // The routed items are counted from the touched experts only, so their
 // number is known once route_ready is up.  Workgroup w runs items w, w + G,
-// w + 2G, ... (G = grid size) in increasing order, and an item waits only
-// for items with smaller numbers, so when all G workgroups are resident at
-// once (the grid is sized to the device's occupancy for this kernel) every
-// wait ends.  Waits are bounded anyway: a wait that runs out of its spin
+// w + 2G, ... (G = grid size) in increasing order, one loop per kind of
+// item so that each kind's registers are allocated on their own; an item
+// waits only for items with
+// smaller numbers, so when all G workgroups are resident at once (the grid
+// is sized to the device's occupancy for this kernel) every wait ends.  Waits are bounded anyway: a wait that runs out of its spin
 // budget raises a sticky error word (moe_decode_check_waits) and gives up
 // instead of hanging.  Counters live on separate 128-byte lines; the last
 // workgroup out (two-level exit count) zeroes them for the next launch.
@@ -48,6 +49,8 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr size_t kRouteSmem = 16 * 16 * 4 + kMaxExperts * 8 + kMaxExperts * 4 + 16;
+constexpr int kMaxRoutes = kFusedMaxTokens * kMaxTopK;  // most touched-expert slots
+static_assert(3 * kMaxRoutes * 4 <= kRouteSmem, "slot table must fit the routing scratch");
 
 // Publishes this workgroup's coherent stores and bumps counter c: every lane
 // waits for its stores to reach the coherence point, then one lane adds 1.
@@ -84,6 +87,8 @@ int occupancy_nj();
 // file once per value, in parallel).
 template <int NJ, bool E8>
 __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Workspace ws) {
+  // Routing scratch of the routing workgroup; afterwards every workgroup
+  // keeps the touched-expert table (expert, token count, first position) here.
   __shared__ __attribute__((aligned(16))) unsigned char s_route[kRouteSmem];
   __shared__ int s_flag;
   __shared__ float s_part[kWaves];
@@ -92,134 +97,122 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
   uint32_t* err = ctr(kSyncError);
   const int wave = threadIdx.x >> 6;
   const int H = a.H, I = a.I, Is = a.Is, k = a.k, T = a.T, E = a.E;
+  const int G = static_cast<int>(gridDim.x);
+  int it = blockIdx.x;
 
-  bool routed_ready = false;
-  int n_touched = 0, total = a.o_rgu;
-  for (int it = blockIdx.x;; it += gridDim.x) {
-    if (it >= a.o_rgu && !routed_ready) {
-      // The routed items exist once the router has counted the touched experts.
-      wait_geq(ctr(kSyncRouteReady), 1u, err);
-      routed_ready = true;
-      n_touched = ld_i32<true>(ws.n_touched);
-      total = a.o_rgu + n_touched * (a.gu_per + a.dn_per) + T;
+  // Each kind of item has a loop of its own (a workgroup's items still run in
+  // increasing order); one loop per kind keeps the register allocation of
+  // each kind separate.
+
+  // ---- router items: logits of experts 4*it + wave; the last one to finish
+  // selects the top-k of every token and builds the route tables
+  for (; it < a.o_sgu; it += G) {
+    const int e = it * kWaves + wave;
+    if (e < E)
+      router_wave<2 * NJ, true>(a.hidden, a.router_w + static_cast<size_t>(e) * H, H, T, E, e,
+                                ws.logits);
+    wait_memory();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(ctr(kSyncRouterDone), 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      s_flag = prev == static_cast<uint32_t>(a.n_router) - 1;
     }
-    if (it >= total) break;
-
-    // Decode the item into one of four kinds; the shared and the routed
-    // projections share one call site each (one copy of each tile's code).
-    enum { kRouter, kGateUp, kDown, kBoundary } kind;
-    const uint8_t* W = nullptr;
-    const void* S = nullptr;
-    size_t sbase = 0;
-    int rows_i = 0, r0 = 0, n = 0, base = 0;
-    const int32_t* perm = nullptr;
-    uint32_t* done = nullptr;
-    if (it < a.o_sgu) {
-      kind = kRouter;
-    } else if (it < a.o_sdn) {
-      // shared gate_up: SwiGLU rows 8*s + 2*wave, +1
-      kind = kGateUp;
-      W = a.sw13;
-      S = a.sw13_scale;
-      rows_i = Is;
-      r0 = (it - a.o_sgu) * 2 * kWaves + 2 * wave;
-      n = T;
-      done = ctr(kSyncSguDone);
-    } else if (it < a.o_rgu) {
-      // shared down: rows 16*j + 4*wave .. +3, after all shared gate_up
-      wait_geq(ctr(kSyncSguDone), static_cast<uint32_t>(a.n_sgu), err);
-      kind = kDown;
-      W = a.sw2;
-      S = a.sw2_scale;
-      rows_i = Is;
-      r0 = (it - a.o_sdn) * 4 * kWaves + 4 * wave;
-      n = T;
-      done = ctr(kSyncSdnDone);
-    } else {
-      const int u = it - a.o_rgu;
-      const int n_gu = n_touched * a.gu_per, n_dn = n_touched * a.dn_per;
-      if (u < n_gu + n_dn) {
-        const bool gu = u < n_gu;
-        const int v = gu ? u : u - n_gu;
-        const int per = gu ? a.gu_per : a.dn_per;
-        const int d = v / per, tile = v % per;
-        const int e = ld_i32<true>(ws.touched + d);
-        n = ld_i32<true>(ws.counts + e);
-        base = ld_i32<true>(ws.offsets + e);
-        perm = ws.perm;
-        rows_i = I;
-        if (gu) {
-          kind = kGateUp;
-          W = a.w13 + static_cast<size_t>(e) * 2 * I * H;
-          S = a.w13_scale;
-          sbase = static_cast<size_t>(e) * (2 * I / kBlock) * (H / kBlock);
-          r0 = tile * 2 * kWaves + 2 * wave;
-          done = ctr(sync_gu(d));
-        } else {
-          wait_geq(ctr(sync_gu(d)), static_cast<uint32_t>(a.gu_per), err);
-          kind = kDown;
-          W = a.w2 + static_cast<size_t>(e) * H * I;
-          S = a.w2_scale;
-          sbase = static_cast<size_t>(e) * (H / kBlock) * (I / kBlock);
-          r0 = tile * 4 * kWaves + 4 * wave;
-          done = ctr(sync_dn(d));
-        }
-      } else {
-        // boundary: after every down row of every touched slot and of the shared expert
-        if (threadIdx.x == 0) {
-          for (int d = 0; d < n_touched; ++d) {
-            uint32_t spins = 0;
-            while (__hip_atomic_load(ctr(sync_dn(d)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-                   static_cast<uint32_t>(a.dn_per)) {
-              __builtin_amdgcn_s_sleep(1);
-              if (++spins == kSpinLimit) {
-                __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-              }
-            }
-          }
-        }
-        __syncthreads();
-        if (Is) wait_geq(ctr(kSyncSdnDone), static_cast<uint32_t>(a.n_sdn), err);
-        kind = kBoundary;
-        r0 = u - n_gu - n_dn;  // the token
-      }
-    }
-
-    if (kind == kRouter) {
-      // logits of experts 4*it + wave; the last router item selects and routes
-      const int e = it * kWaves + wave;
-      if (e < E)
-        router_wave<2 * NJ, true>(a.hidden, a.router_w + static_cast<size_t>(e) * H, H, T, E, e,
-                                  ws.logits);
+    __syncthreads();
+    if (s_flag) {
+      select_and_route<true>(T, E, k, a.rsf, ws.logits, a.bias, ws, a.ids_out, a.w_out, s_route);
       wait_memory();
       __syncthreads();
-      if (threadIdx.x == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(ctr(kSyncRouterDone), 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        s_flag = prev == static_cast<uint32_t>(a.n_router) - 1;
-      }
-      __syncthreads();
-      if (s_flag) {
-        select_and_route<true>(T, E, k, a.rsf, ws.logits, a.bias, ws, a.ids_out, a.w_out,
-                               s_route);
-        wait_memory();
-        __syncthreads();
-        if (threadIdx.x == 0)
-          __hip_atomic_store(ctr(kSyncRouteReady), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    } else if (kind == kGateUp) {
-      gate_up_wave<NJ, 1, true, E8>(a.hidden, W, S, sbase, H, rows_i, r0, n, perm, base, k,
-                                    perm ? ws.act : ws.act_s, a.limit);
-      signal_add(done);
-    } else if (kind == kDown) {
-      down_wave<NJ, 1, true, E8>(W, S, sbase, H, rows_i, r0, n, base, perm ? ws.act : ws.act_s,
-                                 perm ? ws.rows : ws.y_s);
-      signal_add(done);
-    } else {
-      epilogue_token<true>(r0, a.residual, a.gamma, H, k, Is > 0, a.eps, ws, a.out,
-                           a.residual_out, s_part);
+      if (threadIdx.x == 0)
+        __hip_atomic_store(ctr(kSyncRouteReady), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    __syncthreads();
+  }
+
+  // ---- shared gate_up: SwiGLU rows 8*s + 2*wave, +1
+  for (; it < a.o_sdn; it += G) {
+    const int i0 = (it - a.o_sgu) * 2 * kWaves + 2 * wave;
+    gate_up_wave<NJ, 1, true, E8>(a.hidden, a.sw13, a.sw13_scale, 0, H, Is, i0, T, nullptr, 0, k,
+                                  ws.act_s, a.limit);
+    signal_add(ctr(kSyncSguDone));
+    __syncthreads();
+  }
+
+  // ---- shared down: rows 16*j + 4*wave .. +3, after all shared gate_up
+  for (; it < a.o_rgu; it += G) {
+    wait_geq(ctr(kSyncSguDone), static_cast<uint32_t>(a.n_sgu), err);
+    const int h0 = (it - a.o_sdn) * 4 * kWaves + 4 * wave;
+    down_wave<NJ, 1, true, E8>(a.sw2, a.sw2_scale, 0, H, Is, h0, T, 0, ws.act_s, ws.y_s);
+    signal_add(ctr(kSyncSdnDone));
+    __syncthreads();
+  }
+
+  // ---- the routed items exist once the router has counted the touched experts
+  wait_geq(ctr(kSyncRouteReady), 1u, err);
+  const int n_touched = ld_i32<true>(ws.n_touched);
+  int* s_e = reinterpret_cast<int*>(s_route);
+  int* s_n = s_e + kMaxRoutes;
+  int* s_b = s_n + kMaxRoutes;
+  for (int d = threadIdx.x; d < n_touched; d += kThreads) {
+    const int e = ld_i32<true>(ws.touched + d);
+    s_e[d] = e;
+    s_n[d] = ld_i32<true>(ws.counts + e);
+    s_b[d] = ld_i32<true>(ws.offsets + e);
+  }
+  __syncthreads();
+  const int o_rdn = a.o_rgu + n_touched * a.gu_per;
+  const int o_epi = o_rdn + n_touched * a.dn_per;
+
+  // ---- routed gate_up
+  for (; it < o_rdn; it += G) {
+    const int u = it - a.o_rgu;
+    const int d = u / a.gu_per, tile = u % a.gu_per;
+    const int e = s_e[d];
+    const int i0 = tile * 2 * kWaves + 2 * wave;
+    gate_up_wave<NJ, 1, true, E8>(a.hidden, a.w13 + static_cast<size_t>(e) * 2 * I * H,
+                                  a.w13_scale,
+                                  static_cast<size_t>(e) * (2 * I / kBlock) * (H / kBlock), H, I,
+                                  i0, s_n[d], ws.perm, s_b[d], k, ws.act, a.limit);
+    signal_add(ctr(sync_gu(d)));
+    __syncthreads();
+  }
+
+  // ---- routed down, after its expert's gate_up
+  for (; it < o_epi; it += G) {
+    const int v = it - o_rdn;
+    const int d = v / a.dn_per, tile = v % a.dn_per;
+    wait_geq(ctr(sync_gu(d)), static_cast<uint32_t>(a.gu_per), err);
+    const int e = s_e[d];
+    const int h0 = tile * 4 * kWaves + 4 * wave;
+    down_wave<NJ, 1, true, E8>(a.w2 + static_cast<size_t>(e) * H * I, a.w2_scale,
+                               static_cast<size_t>(e) * (H / kBlock) * (I / kBlock), H, I, h0,
+                               s_n[d], s_b[d], ws.act, ws.rows);
+    signal_add(ctr(sync_dn(d)));
+    __syncthreads();
+  }
+
+  // ---- phase C: the boundary, one token per item, after every down row
+  const int total = o_epi + T;
+  if (it < total) {
+    if (threadIdx.x == 0) {
+      for (int d = 0; d < n_touched; ++d) {
+        uint32_t spins = 0;
+        while (__hip_atomic_load(ctr(sync_dn(d)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+               static_cast<uint32_t>(a.dn_per)) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins == kSpinLimit) {
+            __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (Is) wait_geq(ctr(kSyncSdnDone), static_cast<uint32_t>(a.n_sdn), err);
+  }
+  for (; it < total; it += G) {
+    epilogue_token<true>(it - o_epi, a.residual, a.gamma, H, k, Is > 0, a.eps, ws, a.out,
+                         a.residual_out, s_part);
     __syncthreads();
   }
 
