@@ -13,30 +13,33 @@
 // Work items, in order:
 //   router items     logits of 4 experts (one per wave) for all tokens; the
 //                    last router item to finish selects the top-k of every
-//                    token, builds the route tables and raises route_ready
+//                    token, builds the route tables and raises the route flag
 //   shared gate_up   8 SwiGLU rows of the shared expert
 //   shared down      16 output rows of the shared expert   (after all shared gate_up)
-//   routed gate_up   8 SwiGLU rows of one touched expert    (after route_ready)
+//   routed gate_up   8 SwiGLU rows of one touched expert    (after the route flag)
 //   routed down      16 output rows of one touched expert   (after its gate_up)
 //   boundary         one token: combine + shared + residual + RMSNorm (after all down)
 // The routed items are counted from the touched experts only, so their
-// number is known once route_ready is up.  Workgroup w runs items w, w + G,
-// w + 2G, ... (G = grid size) in increasing order, one loop per kind of
-// item so that each kind's registers are allocated on their own; an item
-// waits only for items with
-// smaller numbers, so when all G workgroups are resident at once (the grid
-// is sized to the device's occupancy for this kernel) every wait ends.  Waits are bounded anyway: a wait that runs out of its spin
-// budget raises a sticky error word (moe_decode_check_waits) and gives up
-// instead of hanging.  Counters live on separate 128-byte lines; the last
-// workgroup out (two-level exit count) zeroes them for the next launch.
+// number is known once the route flag is up.  Workgroup w runs items w,
+// w + G, w + 2G, ... (G = grid size) in increasing order, one loop per kind
+// of item so that each kind's registers are allocated on their own.  An item
+// waits only for items with smaller numbers, so when all G workgroups are
+// resident at once (the grid is sized to the device's occupancy for this
+// kernel) every wait ends.  Waits are bounded anyway: a wait that runs out of
+// its spin budget raises a sticky error word (moe_decode_check_waits) and
+// gives up instead of hanging.  The last workgroup out (two-level exit
+// count) zeroes the counters and flags for the next launch.
 //
 // Hand-off across workgroups (and XCDs): everything one item leaves for
 // another (logits, route tables, SwiGLU rows, down rows) is written with
 // agent-scope atomic stores, which write through to the device coherence
-// point; the producer waits for its stores to complete before it bumps a
-// counter, and consumers read that data with agent-scope atomic loads after
-// the counter is reached.  No L2 write-back or invalidate is needed, so the
-// thousands of hand-offs of one step cost no cache-wide operation.
+// point; the producer waits for its stores to complete before it bumps its
+// counter, and consumers read that data with agent-scope atomic loads once
+// the flag is up.  No L2 write-back or invalidate is needed.  Counters are
+// only bumped by producers; the producer that completes a counter sets a
+// flag replicated over several 128-byte lines, and each waiting workgroup
+// polls its own replica, so a flip reaches hundreds of waiters without all
+// of them hammering one line.
 #include "device_common.h"
 #include "gemv_tiles.h"
 #include "launch.h"
@@ -52,24 +55,45 @@ constexpr size_t kRouteSmem = 16 * 16 * 4 + kMaxExperts * 8 + kMaxExperts * 4 + 
 constexpr int kMaxRoutes = kFusedMaxTokens * kMaxTopK;  // most touched-expert slots
 static_assert(3 * kMaxRoutes * 4 <= kRouteSmem, "slot table must fit the routing scratch");
 
-// Publishes this workgroup's coherent stores and bumps counter c: every lane
-// waits for its stores to reach the coherence point, then one lane adds 1.
-__device__ __forceinline__ void signal_add(uint32_t* c) {
-  wait_memory();
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+struct Sync {
+  uint32_t* base;
+  __device__ uint32_t* line(int i) const { return base + static_cast<size_t>(i) * kSyncStride; }
+};
+
+// Sets flag f (all kFlagRep replicas).  Called by one thread.
+__device__ __forceinline__ void raise_flag(const Sync& sy, int f) {
+#pragma unroll
+  for (int r = 0; r < kFlagRep; ++r)
+    __hip_atomic_store(sy.line(f + r), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Waits until counter c reaches target (bounded: raises *err and gives up
-// after kSpinLimit polls).  Data behind the counter is then read with
-// coherent loads.
-__device__ __forceinline__ void wait_geq(const uint32_t* c, uint32_t target, uint32_t* err) {
+// Publishes this workgroup's coherent stores, then bumps counter `cnt`; the
+// bump that reaches `target` raises flag `f` (f < 0: no flag).  Returns, to
+// every thread, whether this bump completed the counter.
+__device__ __forceinline__ bool signal(const Sync& sy, int cnt, uint32_t target, int f, int* s_flag) {
+  wait_memory();
+  __syncthreads();
   if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(sy.line(cnt), 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev + 1 == target;
+    if (last && f >= 0) raise_flag(sy, f);
+    *s_flag = last;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// Waits until flag f is up, polling this workgroup's replica (bounded: sets
+// the error word and gives up after kSpinLimit polls).
+__device__ __forceinline__ void wait_flag(const Sync& sy, int f) {
+  if (threadIdx.x == 0) {
+    const uint32_t* p = sy.line(f + static_cast<int>(blockIdx.x % kFlagRep));
     uint32_t n = 0;
-    while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(1);
+    while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+      __builtin_amdgcn_s_sleep(2);
       if (++n == kSpinLimit) {
-        __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(sy.line(kSyncError), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
     }
@@ -83,8 +107,8 @@ template <int NJ, bool E8>
 int occupancy_nj();
 
 #ifdef MOE_FUSED_NJ
-// This object holds the kernel for one chunk count (the build compiles this
-// file once per value, in parallel).
+// This object holds the kernel for one chunk count and scale format (the
+// build compiles this file once per pair, in parallel).
 template <int NJ, bool E8>
 __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Workspace ws) {
   // Routing scratch of the routing workgroup; afterwards every workgroup
@@ -92,9 +116,7 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
   __shared__ __attribute__((aligned(16))) unsigned char s_route[kRouteSmem];
   __shared__ int s_flag;
   __shared__ float s_part[kWaves];
-  uint32_t* sync = ws.sync;
-  auto ctr = [sync](int i) { return sync + static_cast<size_t>(i) * kSyncStride; };
-  uint32_t* err = ctr(kSyncError);
+  const Sync sy{ws.sync};
   const int wave = threadIdx.x >> 6;
   const int H = a.H, I = a.I, Is = a.Is, k = a.k, T = a.T, E = a.E;
   const int G = static_cast<int>(gridDim.x);
@@ -111,20 +133,11 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
     if (e < E)
       router_wave<2 * NJ, true>(a.hidden, a.router_w + static_cast<size_t>(e) * H, H, T, E, e,
                                 ws.logits);
-    wait_memory();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const uint32_t prev = __hip_atomic_fetch_add(ctr(kSyncRouterDone), 1u, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-      s_flag = prev == static_cast<uint32_t>(a.n_router) - 1;
-    }
-    __syncthreads();
-    if (s_flag) {
+    if (signal(sy, kSyncRouterCnt, static_cast<uint32_t>(a.n_router), -1, &s_flag)) {
       select_and_route<true>(T, E, k, a.rsf, ws.logits, a.bias, ws, a.ids_out, a.w_out, s_route);
       wait_memory();
       __syncthreads();
-      if (threadIdx.x == 0)
-        __hip_atomic_store(ctr(kSyncRouteReady), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0) raise_flag(sy, sync_flag(kFlagRoute));
     }
     __syncthreads();
   }
@@ -134,21 +147,19 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
     const int i0 = (it - a.o_sgu) * 2 * kWaves + 2 * wave;
     gate_up_wave<NJ, 1, true, E8>(a.hidden, a.sw13, a.sw13_scale, 0, H, Is, i0, T, nullptr, 0, k,
                                   ws.act_s, a.limit);
-    signal_add(ctr(kSyncSguDone));
-    __syncthreads();
+    signal(sy, kSyncSguCnt, static_cast<uint32_t>(a.n_sgu), sync_flag(kFlagSgu), &s_flag);
   }
 
   // ---- shared down: rows 16*j + 4*wave .. +3, after all shared gate_up
   for (; it < a.o_rgu; it += G) {
-    wait_geq(ctr(kSyncSguDone), static_cast<uint32_t>(a.n_sgu), err);
+    wait_flag(sy, sync_flag(kFlagSgu));
     const int h0 = (it - a.o_sdn) * 4 * kWaves + 4 * wave;
-    down_wave<NJ, 1, true, E8>(a.sw2, a.sw2_scale, 0, H, Is, h0, T, 0, ws.act_s, ws.y_s);
-    signal_add(ctr(kSyncSdnDone));
-    __syncthreads();
+    down_wave<NJ, 1, true, E8>(a.sw2, a.sw2_scale, 0, H, Is, h0, T, 0, nullptr, ws.act_s, ws.y_s);
+    signal(sy, kSyncSdnCnt, static_cast<uint32_t>(a.n_sdn), sync_flag(kFlagSdn), &s_flag);
   }
 
   // ---- the routed items exist once the router has counted the touched experts
-  wait_geq(ctr(kSyncRouteReady), 1u, err);
+  wait_flag(sy, sync_flag(kFlagRoute));
   const int n_touched = ld_i32<true>(ws.n_touched);
   int* s_e = reinterpret_cast<int*>(s_route);
   int* s_n = s_e + kMaxRoutes;
@@ -173,42 +184,35 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
                                   a.w13_scale,
                                   static_cast<size_t>(e) * (2 * I / kBlock) * (H / kBlock), H, I,
                                   i0, s_n[d], ws.perm, s_b[d], k, ws.act, a.limit);
-    signal_add(ctr(sync_gu(d)));
-    __syncthreads();
+    signal(sy, sync_gu_cnt(d), static_cast<uint32_t>(a.gu_per), sync_gu_flag(d), &s_flag);
   }
 
-  // ---- routed down, after its expert's gate_up
+  // ---- routed down, after its expert's gate_up; rows land at their route
+  // index t*k + j, where the boundary reads them
   for (; it < o_epi; it += G) {
     const int v = it - o_rdn;
     const int d = v / a.dn_per, tile = v % a.dn_per;
-    wait_geq(ctr(sync_gu(d)), static_cast<uint32_t>(a.gu_per), err);
+    wait_flag(sy, sync_gu_flag(d));
     const int e = s_e[d];
     const int h0 = tile * 4 * kWaves + 4 * wave;
     down_wave<NJ, 1, true, E8>(a.w2 + static_cast<size_t>(e) * H * I, a.w2_scale,
                                static_cast<size_t>(e) * (H / kBlock) * (I / kBlock), H, I, h0,
-                               s_n[d], s_b[d], ws.act, ws.rows);
-    signal_add(ctr(sync_dn(d)));
+                               s_n[d], s_b[d], ws.perm, ws.act, ws.rows);
+    if (signal(sy, sync_dn_cnt(d), static_cast<uint32_t>(a.dn_per), -1, &s_flag) &&
+        threadIdx.x == 0) {
+      // this expert is complete; the last expert to complete raises the flag
+      const uint32_t prev = __hip_atomic_fetch_add(sy.line(kSyncDnSlots), 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      if (prev + 1 == static_cast<uint32_t>(n_touched)) raise_flag(sy, sync_flag(kFlagDnAll));
+    }
     __syncthreads();
   }
 
-  // ---- phase C: the boundary, one token per item, after every down row
+  // ---- the boundary, one token per item, after every down row
   const int total = o_epi + T;
   if (it < total) {
-    if (threadIdx.x == 0) {
-      for (int d = 0; d < n_touched; ++d) {
-        uint32_t spins = 0;
-        while (__hip_atomic_load(ctr(sync_dn(d)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-               static_cast<uint32_t>(a.dn_per)) {
-          __builtin_amdgcn_s_sleep(1);
-          if (++spins == kSpinLimit) {
-            __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-        }
-      }
-    }
-    __syncthreads();
-    if (Is) wait_geq(ctr(kSyncSdnDone), static_cast<uint32_t>(a.n_sdn), err);
+    wait_flag(sy, sync_flag(kFlagDnAll));
+    if (Is) wait_flag(sy, sync_flag(kFlagSdn));
   }
   for (; it < total; it += G) {
     epilogue_token<true>(it - o_epi, a.residual, a.gamma, H, k, Is > 0, a.eps, ws, a.out,
@@ -216,17 +220,17 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
     __syncthreads();
   }
 
-  // Two-level exit count; the last workgroup out zeroes every counter for the
-  // next launch (HIP-graph replays included).  The error word stays set.
+  // Two-level exit count; the last workgroup out zeroes every counter and flag
+  // for the next launch (HIP-graph replays included).  The error word stays.
   if (threadIdx.x == 0) {
     const uint32_t lines = kSyncExitLines;
     const uint32_t line = blockIdx.x % lines;
     const uint32_t share = a.grid / lines + (line < a.grid % lines ? 1u : 0u);
-    const uint32_t prev = __hip_atomic_fetch_add(ctr(kSyncExit0 + static_cast<int>(line)), 1u,
+    const uint32_t prev = __hip_atomic_fetch_add(sy.line(kSyncExit0 + static_cast<int>(line)), 1u,
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int last = 0;
     if (prev == share - 1) {
-      const uint32_t top = __hip_atomic_fetch_add(ctr(kSyncExitTop), 1u, __ATOMIC_RELAXED,
+      const uint32_t top = __hip_atomic_fetch_add(sy.line(kSyncExitTop), 1u, __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT);
       last = top == (a.grid < lines ? a.grid : lines) - 1;
     }
@@ -234,9 +238,9 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
   }
   __syncthreads();
   if (s_flag) {
-    for (int i = threadIdx.x; i < kSyncSlot0 + 2 * a.dmax; i += kThreads)
+    for (int i = threadIdx.x; i < sync_lines(a.dmax); i += kThreads)
       if (i != kSyncError)
-        __hip_atomic_store(ctr(i), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(sy.line(i), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -73,7 +73,8 @@ __global__ __launch_bounds__(kThreads) void down_kernel(
   const uint8_t* W = w2 + static_cast<size_t>(si.e) * H * I;
   const size_t sbase = static_cast<size_t>(si.e) * (H / kBlock) * (I / kBlock);
   down_wave<NJ, 1, false, E8>(W, scale, sbase, H, I, h0, si.n, si.base,
-                              shared ? ws.act_s : ws.act, shared ? ws.y_s : ws.rows);
+                              shared ? nullptr : ws.perm, shared ? ws.act_s : ws.act,
+                              shared ? ws.y_s : ws.rows);
 }
 
 }  // namespace

@@ -170,12 +170,14 @@ __device__ __forceinline__ void gate_up_wave(const uint16_t* __restrict__ hidden
 
 // down projection of one wave: output rows h0 .. h0+3 (h0 % 4 == 0) of one
 // expert for its n >= 1 SwiGLU rows act[(base + q) * I], written to
-// out[(base + q) * H + h0 .. +3].  fp32 products and sums (the SwiGLU
-// activations stay fp32).  NJ = ceil(I / 1024); TB, C, E8 as above.
+// out[o * H + h0 .. +3] with o = out_route[base + q] (the route index t*k+j),
+// or o = base + q when out_route is null.  fp32 products and sums (the
+// SwiGLU activations stay fp32).  NJ = ceil(I / 1024); TB, C, E8 as above.
 template <int NJ, int TB, bool C, bool E8>
 __device__ __forceinline__ void down_wave(const uint8_t* __restrict__ W,
                                           const void* __restrict__ scale, size_t sbase, int H,
-                                          int I, int h0, int n, int base, const float* act,
+                                          int I, int h0, int n, int base,
+                                          const int32_t* out_route, const float* act,
                                           float* out) {
   const int lane = threadIdx.x & 63;
   const int ib_n = I / kBlock;
@@ -225,9 +227,10 @@ __device__ __forceinline__ void down_wave(const uint8_t* __restrict__ W,
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = wave_sum(acc[r][qq]);
-      if (lane == 0)
-        st_f32x4<C>(out + static_cast<size_t>(base + q0 + qq) * H + h0,
-                    make_float4(v[0], v[1], v[2], v[3]));
+      if (lane == 0) {
+        const int o = out_route ? ld_i32<C>(out_route + base + q0 + qq) : base + q0 + qq;
+        st_f32x4<C>(out + static_cast<size_t>(o) * H + h0, make_float4(v[0], v[1], v[2], v[3]));
+      }
     }
     if (q0 + TB < n) {
 #pragma unroll
@@ -291,6 +294,13 @@ constexpr int kEpiPass = 4;  // H <= 8192 = 4 passes x 256 threads x 8
 // h = sum_j w[t, j] * rows[inv[t, j]] + y_s[t] + residual[t] (fixed order),
 // residual_out = bf16(h), out = bf16(h / sqrt(mean(h^2) + eps) * gamma).
 // s_part: 4 floats of LDS.
+constexpr int kEpiGroup = 8;  // routes whose rows one round of loads fetches
+
+// The boundary for token t, by one 256-thread workgroup:
+// h = sum_j w[t, j] * rows[t*k + j] + y_s[t] + residual[t] (fixed order),
+// residual_out = bf16(h), out = bf16(h / sqrt(mean(h^2) + eps) * gamma).
+// Every load of a group of routes is issued before any is used.
+// s_part: 4 floats of LDS.
 template <bool C = false>
 __device__ __forceinline__ void epilogue_token(int t, const uint16_t* residual,
                                                const uint16_t* __restrict__ gamma, int H, int k,
@@ -298,46 +308,38 @@ __device__ __forceinline__ void epilogue_token(int t, const uint16_t* residual,
                                                uint16_t* out, uint16_t* residual_out,
                                                float* s_part) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int pos[kMaxTopK];
-  float wj[kMaxTopK];
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    const int jj = j < k ? j : k - 1;
-    pos[j] = ld_i32<C>(ws.inv + t * k + jj);
-    const float w = ld_f32<C>(ws.weights + t * k + jj);
-    wj[j] = j < k ? w : 0.f;
-  }
+  const float* rows_t = ws.rows + static_cast<size_t>(t) * k * H;
   float hv[kEpiPass][8];
   float ss = 0.f;
 #pragma unroll
   for (int p = 0; p < kEpiPass; ++p) {
     const int c0 = 8 * (threadIdx.x + 256 * p);
-    if (c0 >= H) continue;  // uniform per pass up to the last partial pass
+    if (c0 >= H) continue;  // uniform up to the last partial pass
     float acc[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) acc[m] = 0.f;
-    // routes in groups of four: the group's eight loads go out together
+    for (int j0 = 0; j0 < k; j0 += kEpiGroup) {
+      float wj[kEpiGroup];
+      float4 ra[kEpiGroup], rb[kEpiGroup];
 #pragma unroll
-    for (int j0 = 0; j0 < kMaxTopK; j0 += 4) {
-      if (j0 >= k) break;
-      float4 ra[4], rb[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float* row = ws.rows + static_cast<size_t>(pos[j0 + q]) * H + c0;
+      for (int q = 0; q < kEpiGroup; ++q) {
+        const int j = j0 + q < k ? j0 + q : k - 1;  // clamped: no branch around the loads
+        const float w = ld_f32<C>(ws.weights + t * k + j);
+        wj[q] = j0 + q < k ? w : 0.f;
+        const float* row = rows_t + static_cast<size_t>(j) * H + c0;
         ra[q] = ld_f32x4<C>(row);
         rb[q] = ld_f32x4<C>(row + 4);
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float w = wj[j0 + q];
-        acc[0] = fmaf(w, ra[q].x, acc[0]);
-        acc[1] = fmaf(w, ra[q].y, acc[1]);
-        acc[2] = fmaf(w, ra[q].z, acc[2]);
-        acc[3] = fmaf(w, ra[q].w, acc[3]);
-        acc[4] = fmaf(w, rb[q].x, acc[4]);
-        acc[5] = fmaf(w, rb[q].y, acc[5]);
-        acc[6] = fmaf(w, rb[q].z, acc[6]);
-        acc[7] = fmaf(w, rb[q].w, acc[7]);
+      for (int q = 0; q < kEpiGroup; ++q) {
+        acc[0] = fmaf(wj[q], ra[q].x, acc[0]);
+        acc[1] = fmaf(wj[q], ra[q].y, acc[1]);
+        acc[2] = fmaf(wj[q], ra[q].z, acc[2]);
+        acc[3] = fmaf(wj[q], ra[q].w, acc[3]);
+        acc[4] = fmaf(wj[q], rb[q].x, acc[4]);
+        acc[5] = fmaf(wj[q], rb[q].y, acc[5]);
+        acc[6] = fmaf(wj[q], rb[q].z, acc[6]);
+        acc[7] = fmaf(wj[q], rb[q].w, acc[7]);
       }
     }
     const float* ys = ws.y_s + static_cast<size_t>(t) * H + c0;

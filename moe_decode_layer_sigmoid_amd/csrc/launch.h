@@ -19,31 +19,45 @@ struct Workspace {
   int32_t* inv;        // [maxT * k]  route -> permuted position
   float* act;          // [maxT * k, I]   routed SwiGLU output, permuted order
   float* act_s;        // [maxT, Is]      shared SwiGLU output
-  float* rows;         // [maxT * k, H]   routed down output, permuted order
+  float* rows;         // [maxT * k, H]   routed down output, at route index t*k+j
   float* y_s;          // [maxT, H]       shared expert output
   uint32_t* counter;   // [1] last-block counter of the router (self-resetting)
   uint32_t* sync;      // [sync_words(E)] counters of the fused kernel (self-resetting)
   float* zero_bias;    // [E] zeros: the router bias when the caller passes none
 };
 
-// Counters of the fused kernel in Workspace::sync, one 128-byte line each
-// (atomics to one line serialise; separate lines proceed in parallel).
-constexpr int kSyncStride = 32;  // uint32 words per counter line
+// Counters and flags of the fused kernel in Workspace::sync, one 128-byte
+// line each: atomics and polls on one line serialise, separate lines proceed
+// in parallel.  Producers bump a counter (only producers touch it); the one
+// that completes it sets a flag replicated over kFlagRep lines, and waiting
+// workgroups poll the replica of their own (so no line is polled by many).
+constexpr int kSyncStride = 32;  // uint32 words per line
+constexpr int kFlagRep = 8;      // replicas of every flag
 enum : int {
-  kSyncRouterDone = 0,
-  kSyncRouteReady = 1,
-  kSyncSguDone = 2,
-  kSyncSdnDone = 3,
-  kSyncError = 4,     // sticky: set when a bounded wait gave up
-  kSyncExit0 = 5,     // kSyncExitLines first-level exit counters
+  kSyncRouterCnt = 0,   // router items done
+  kSyncSguCnt = 1,      // shared gate_up tiles done
+  kSyncSdnCnt = 2,      // shared down tiles done
+  kSyncDnSlots = 3,     // touched experts whose down tiles are all done
+  kSyncError = 4,       // sticky: set when a bounded wait gave up
+  kSyncExit0 = 5,       // kSyncExitLines first-level exit counters
   kSyncExitLines = 8,
   kSyncExitTop = kSyncExit0 + kSyncExitLines,
-  kSyncSlot0 = kSyncExitTop + 1  // then per touched-expert slot d: gate_up done, down done
+  kSyncFlags = 16,      // global flags, kFlagRep lines each:
+  kFlagRoute = 0,       //   route tables ready
+  kFlagSgu = 1,         //   shared gate_up done
+  kFlagSdn = 2,         //   shared down done
+  kFlagDnAll = 3,       //   every touched expert's down done
+  kNumFlags = 4,
+  kSyncSlot0 = kSyncFlags + kNumFlags * kFlagRep,  // per touched-expert slot:
+  kSlotLines = 2 + kFlagRep                        //   gate_up count, down count, gate_up flag
 };
-__host__ __device__ constexpr int sync_gu(int d) { return kSyncSlot0 + 2 * d; }
-__host__ __device__ constexpr int sync_dn(int d) { return kSyncSlot0 + 2 * d + 1; }
+__host__ __device__ constexpr int sync_flag(int f) { return kSyncFlags + f * kFlagRep; }
+__host__ __device__ constexpr int sync_gu_cnt(int d) { return kSyncSlot0 + d * kSlotLines; }
+__host__ __device__ constexpr int sync_dn_cnt(int d) { return kSyncSlot0 + d * kSlotLines + 1; }
+__host__ __device__ constexpr int sync_gu_flag(int d) { return kSyncSlot0 + d * kSlotLines + 2; }
+__host__ __device__ constexpr int sync_lines(int slots) { return kSyncSlot0 + slots * kSlotLines; }
 __host__ __device__ constexpr size_t sync_words(int E) {
-  return static_cast<size_t>(kSyncSlot0 + 2 * E) * kSyncStride;
+  return static_cast<size_t>(sync_lines(E)) * kSyncStride;
 }
 
 constexpr int kFusedMaxTokens = 16;

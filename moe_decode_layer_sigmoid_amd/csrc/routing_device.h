@@ -44,10 +44,36 @@ __device__ inline int block_exclusive_scan(int v, int* s_tmp, int* total) {
   return base + inc - v;
 }
 
+// One step of the DPP wave maximum of (hi, lo) pairs: lanes take the
+// neighbour's pair named by the DPP control when it is larger.
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ void dpp_max_step(uint32_t& hi, uint32_t& lo) {
+  const uint32_t h2 = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, BANK_MASK, false);
+  const uint32_t l2 = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, BANK_MASK, false);
+  const bool take = h2 > hi || (h2 == hi && l2 > lo);
+  hi = take ? h2 : hi;
+  lo = take ? l2 : lo;
+}
+
+// Maximum of the (hi, lo) pairs of the 64 lanes, lexicographic, in every
+// lane: shifts within rows of 16 lanes, then row broadcasts 15 and 31 carry
+// the rows' maxima up to lane 63, which is read back to all lanes.
+__device__ __forceinline__ void wave_max_pair(uint32_t& hi, uint32_t& lo) {
+  dpp_max_step<0x111, 0xf, 0xf>(hi, lo);  // row_shr:1
+  dpp_max_step<0x112, 0xf, 0xf>(hi, lo);  // row_shr:2
+  dpp_max_step<0x113, 0xf, 0xf>(hi, lo);  // row_shr:3
+  dpp_max_step<0x114, 0xf, 0xe>(hi, lo);  // row_shr:4
+  dpp_max_step<0x118, 0xf, 0xc>(hi, lo);  // row_shr:8
+  dpp_max_step<0x142, 0xa, 0xf>(hi, lo);  // row_bcast:15
+  dpp_max_step<0x143, 0xc, 0xf>(hi, lo);  // row_bcast:31
+  hi = __builtin_amdgcn_readlane(hi, 63);
+  lo = __builtin_amdgcn_readlane(lo, 63);
+}
+
 // Top-k of one token in one wave.  Keys are sigmoid(logit) + bias (bias is
 // never null: a zero vector stands in for no bias); the
 // largest key wins, equal keys go to the lower expert id (a packed
-// (key, ~id) wave maximum, k rounds).  Lane j < k ends with the j-th pick and
+// (key, ~id) DPP wave maximum, k rounds).  Lane j < k ends with the j-th pick and
 // its weight R * s_j / sum of the k picked scores.
 template <bool C>
 __device__ inline void select_token(const float* logits, const float* bias, int E, int k,
@@ -84,14 +110,7 @@ __device__ inline void select_token(const float* logits, const float* bias, int 
     }
     uint32_t hi = have ? bk : 0u;
     uint32_t lo = have ? (0xffffffffu - bid) : 0u;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const uint32_t h2 = __shfl_xor(hi, off, 64), l2 = __shfl_xor(lo, off, 64);
-      if (h2 > hi || (h2 == hi && l2 > lo)) {
-        hi = h2;
-        lo = l2;
-      }
-    }
+    wave_max_pair(hi, lo);
     const int win = static_cast<int>(0xffffffffu - lo);
     const float wsc = __shfl(bs, win & 63, 64);
     if (lane == (win & 63)) taken |= 1u << (win >> 6);
