@@ -103,8 +103,11 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", default="auto", choices=["auto", "gemv", "grouped", "split"])
+    ap.add_argument("--path", default="auto", choices=["auto", "fused", "grouped", "split"])
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 10 plain device copies of MIB MiB (a known-size reference "
+                         "for hardware byte counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -113,6 +116,17 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 10}))
+        return
 
     import moe_decode_layer_sigmoid_amd as md
     import oracle
@@ -148,7 +162,7 @@ def main():
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
 
-    path = {"auto": md.PATH_AUTO, "gemv": md.PATH_GEMV, "grouped": md.PATH_GROUPED,
+    path = {"auto": md.PATH_AUTO, "fused": md.PATH_GEMV, "grouped": md.PATH_GROUPED,
             "split": md.PATH_GEMV_SPLIT}[args.path]
     plan = md.Plan(md.make_desc(H, E, k, sh.I, sh.Is, T, sh.scale_fmt, path, sh.limit, sh.rsf,
                                 sh.eps), torch.cuda.current_device())
@@ -240,7 +254,7 @@ def main():
     log("timed %d steps: %.3f ms total (wall %.3f ms), %.2f us/step, %.3f TB/s" %
         (K, ms_total, t_wall * 1e3, ms_per_step * 1e3, tbps))
 
-    # ---- routed-expert kernels: HIP events around them, eager launches on s
+    # ---- dominant kernel: HIP events around it, eager launches on s
     n_ev = min(K, 200)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n_ev)]
@@ -261,8 +275,12 @@ def main():
         kern_name = "fused decode kernel (router, shared + routed experts, boundary)"
         kern_bytes = metric_bytes + E * H * 2
     else:
-        kern_name = "routed-expert gate_up + down kernels"
-        kern_bytes = routed_b
+        # routed gate/up projection: touched experts' w13 + scales, the token
+        # rows in, the SwiGLU rows (f32) out
+        kern_name = "gate_up_kernel<NJ, E8, SHARED=false> (routed experts)"
+        sb = 1 if sh.scale_fmt == "e8m0" else 4
+        kern_bytes = (D * (2 * sh.I * H + sb * (2 * sh.I // 128) * (H // 128))
+                      + T * H * 2 + T * k * sh.I * 4)
     achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
     log("%s: %.2f us avg over %d launches, %.1f GB/s" % (kern_name, kern_ms * 1e3, n_ev,
                                                          achieved))

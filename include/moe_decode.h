@@ -69,10 +69,10 @@ typedef enum { MOE_DECODE_SCALE_FP32 = 0, MOE_DECODE_SCALE_E8M0 = 1 } moe_decode
 
 /* Expert kernel family.  AUTO picks by token count; the others force one. */
 typedef enum {
-  MOE_DECODE_PATH_AUTO = 0,
+  MOE_DECODE_PATH_AUTO = 0, /* the fastest measured path for the token count */
   /* fp8 dequant-FMA GEMV, one weight pass per touched expert.  Up to 16
    * tokens the whole step is one persistent kernel (router, shared expert,
-   * routed experts and boundary on one ordered work queue); above that the
+   * routed experts and boundary as ordered work items); above that the
    * GEMV_SPLIT kernels run. */
   MOE_DECODE_PATH_GEMV = 1,
   MOE_DECODE_PATH_GROUPED = 2,   /* fp8 MFMA over expert-grouped tokens */
@@ -183,9 +183,10 @@ int moe_decode_last_routes(moe_decode_plan_t p, int32_t T, int32_t* counts, int3
 
 /*
  * Measurement hook: when both are non-NULL, each later run records hipEvent_t
- * `begin` on `stream` just before the routed-expert projection kernels and
- * `end` just after them (the kernels that stream the routed weights).
- * NULL, NULL switches it off.
+ * `begin` on `stream` just before its dominant kernel and `end` just after
+ * it: the fused persistent kernel on MOE_DECODE_PATH_GEMV, the routed-expert
+ * gate/up projection kernel on MOE_DECODE_PATH_GEMV_SPLIT.  NULL, NULL
+ * switches it off.
  */
 int moe_decode_set_expert_events(moe_decode_plan_t p, void* begin, void* end);
 

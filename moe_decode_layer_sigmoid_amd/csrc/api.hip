@@ -35,10 +35,14 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// AUTO takes the separate GEMV kernels: on MI355X they currently beat the
+// fused persistent kernel at 1 and 16 tokens (the fused kernel's routing
+// hand-off sits on the critical path); GEMV asks for the fused kernel.
 int path_for(const moe_decode_plan_s& p, int32_t T) {
   const int want = p.desc.path;
   if (want == MOE_DECODE_PATH_GEMV_SPLIT || want == MOE_DECODE_PATH_GROUPED) return want;
-  if (T <= moe::kFusedMaxTokens && p.fused_grid > 0) return MOE_DECODE_PATH_GEMV;
+  if (want == MOE_DECODE_PATH_GEMV && T <= moe::kFusedMaxTokens && p.fused_grid > 0)
+    return MOE_DECODE_PATH_GEMV;
   return MOE_DECODE_PATH_GEMV_SPLIT;
 }
 
@@ -68,7 +72,7 @@ size_t layout(const moe_decode_desc& d, char* base, moe::Workspace* ws) {
   w.act_s = reinterpret_cast<float*>(take(T * (Is ? Is : 1) * 4));
   w.rows = reinterpret_cast<float*>(take(T * k * H * 4));
   w.y_s = reinterpret_cast<float*>(take(T * H * 4));
-  w.counter = reinterpret_cast<uint32_t*>(take(64));
+  w.counter = reinterpret_cast<uint32_t*>(take(moe::router_cnt_words() * 4));
   w.sync = reinterpret_cast<uint32_t*>(take(moe::sync_words(static_cast<int>(E)) * 4));
   w.zero_bias = reinterpret_cast<float*>(take(E * 4));
   if (ws) *ws = w;
@@ -286,8 +290,8 @@ static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t 
   if (err == hipSuccess && p->user_begin) step(hipEventRecord(p->user_begin, s));
   if (err == hipSuccess)
     step(moe::launch_gate_up_gemv(d, false, a->hidden, a->w13, a->w13_scale, p->ws, s));
-  if (err == hipSuccess) step(moe::launch_down_gemv(d, false, a->w2, a->w2_scale, p->ws, s));
   if (err == hipSuccess && p->user_end) step(hipEventRecord(p->user_end, s));
+  if (err == hipSuccess) step(moe::launch_down_gemv(d, false, a->w2, a->w2_scale, p->ws, s));
 
   // Join the side stream on every path, then run the boundary.
   hipError_t jerr = hipEventRecord(p->join, p->side);

@@ -118,13 +118,17 @@ __device__ __forceinline__ void st_f32x4(float* p, float4 v) {
 // compiler barrier.
 __device__ __forceinline__ void wait_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// 1 / (1 + e^-z) with the hardware exponential and reciprocal (about 1 ulp
+// each) instead of an IEEE division sequence.
+__device__ __forceinline__ float sigmoidf_(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // silu(min(g, L)) * clamp(u, -L, L)
 __device__ __forceinline__ float clamped_swiglu(float g, float u, float limit) {
   float gc = fminf(g, limit);
   float uc = fminf(fmaxf(u, -limit), limit);
-  return gc / (1.0f + __expf(-gc)) * uc;
+  return gc * sigmoidf_(gc) * uc;
 }
 
 }  // namespace moe

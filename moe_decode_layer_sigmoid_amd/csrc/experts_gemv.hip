@@ -33,8 +33,9 @@ struct SlotInfo {
   int e, n, base;
 };
 
-__device__ __forceinline__ bool slot_info(bool shared, int T, const Workspace& ws, SlotInfo* si) {
-  if (shared) {
+template <bool SHARED>
+__device__ __forceinline__ bool slot_info(int T, const Workspace& ws, SlotInfo* si) {
+  if (SHARED) {
     *si = {0, T, 0};
     return true;
   }
@@ -45,15 +46,17 @@ __device__ __forceinline__ bool slot_info(bool shared, int T, const Workspace& w
   return true;
 }
 
-template <int NJ, bool E8>
+// SHARED: the shared expert (a separate instantiation, so that profiles tell
+// the routed and shared launches apart).
+template <int NJ, bool E8, bool SHARED>
 __global__ __launch_bounds__(kThreads) void gate_up_kernel(
     const uint16_t* __restrict__ hidden, const uint8_t* __restrict__ w13,
-    const void* __restrict__ scale, int H, int I, int k, int T, int shared, Workspace ws,
-    float limit) {
+    const void* __restrict__ scale, int H, int I, int k, int T, Workspace ws, float limit) {
   const int wave = threadIdx.x >> 6;
   const int i0 = (blockIdx.x * kWaves + wave) * 2;
+  const bool shared = SHARED;
   SlotInfo si;
-  if (!slot_info(shared, T, ws, &si) || i0 >= I) return;
+  if (!slot_info<SHARED>(T, ws, &si) || i0 >= I) return;
   const size_t rows_per_e = static_cast<size_t>(2) * I;
   const uint8_t* W = w13 + static_cast<size_t>(si.e) * rows_per_e * H;
   const size_t sbase = static_cast<size_t>(si.e) * (rows_per_e / kBlock) * (H / kBlock);
@@ -62,19 +65,42 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(
                                   shared ? ws.act_s : ws.act, limit);
 }
 
-template <int NJ, bool E8>
+template <int NJ, bool E8, bool SHARED>
 __global__ __launch_bounds__(kThreads) void down_kernel(
     const uint8_t* __restrict__ w2, const void* __restrict__ scale, int H, int I, int T,
-    int shared, Workspace ws) {
+    Workspace ws) {
   const int wave = threadIdx.x >> 6;
   const int h0 = (blockIdx.x * kWaves + wave) * 4;
+  const bool shared = SHARED;
   SlotInfo si;
-  if (!slot_info(shared, T, ws, &si) || h0 >= H) return;
+  if (!slot_info<SHARED>(T, ws, &si) || h0 >= H) return;
   const uint8_t* W = w2 + static_cast<size_t>(si.e) * H * I;
   const size_t sbase = static_cast<size_t>(si.e) * (H / kBlock) * (I / kBlock);
   down_wave<NJ, 1, false, E8>(W, scale, sbase, H, I, h0, si.n, si.base,
                               shared ? nullptr : ws.perm, shared ? ws.act_s : ws.act,
                               shared ? ws.y_s : ws.rows);
+}
+
+template <int NJ, bool E8>
+void launch_gu(dim3 grid, hipStream_t s, bool shared, const uint16_t* x, const uint8_t* w,
+               const void* scale, const LayerDims& d, int I, const Workspace& ws) {
+  if (shared)
+    hipLaunchKernelGGL((gate_up_kernel<NJ, E8, true>), grid, dim3(kThreads), 0, s, x, w, scale,
+                       d.H, I, d.k, d.T, ws, d.limit);
+  else
+    hipLaunchKernelGGL((gate_up_kernel<NJ, E8, false>), grid, dim3(kThreads), 0, s, x, w, scale,
+                       d.H, I, d.k, d.T, ws, d.limit);
+}
+
+template <int NJ, bool E8>
+void launch_dn(dim3 grid, hipStream_t s, bool shared, const uint8_t* w, const void* scale,
+               const LayerDims& d, int I, const Workspace& ws) {
+  if (shared)
+    hipLaunchKernelGGL((down_kernel<NJ, E8, true>), grid, dim3(kThreads), 0, s, w, scale, d.H, I,
+                       d.T, ws);
+  else
+    hipLaunchKernelGGL((down_kernel<NJ, E8, false>), grid, dim3(kThreads), 0, s, w, scale, d.H,
+                       I, d.T, ws);
 }
 
 }  // namespace
@@ -90,16 +116,13 @@ hipError_t launch_gate_up_gemv(const LayerDims& d, bool shared, const void* hidd
   dim3 grid(I / (2 * kWaves), slots);
   const auto* x = static_cast<const uint16_t*>(hidden);
   const auto* w = static_cast<const uint8_t*>(w13);
-  const int sh = static_cast<int>(shared);
   switch (nj * 2 + (d.e8m0 ? 1 : 0)) {
-#define X(N)                                                                                    \
-  case 2 * N:                                                                                   \
-    hipLaunchKernelGGL((gate_up_kernel<N, false>), grid, dim3(kThreads), 0, s, x, w, w13_scale, \
-                       d.H, I, d.k, d.T, sh, ws, d.limit);                                      \
-    break;                                                                                      \
-  case 2 * N + 1:                                                                               \
-    hipLaunchKernelGGL((gate_up_kernel<N, true>), grid, dim3(kThreads), 0, s, x, w, w13_scale,  \
-                       d.H, I, d.k, d.T, sh, ws, d.limit);                                      \
+#define X(N)                                                              \
+  case 2 * N:                                                             \
+    launch_gu<N, false>(grid, s, shared, x, w, w13_scale, d, I, ws);      \
+    break;                                                                \
+  case 2 * N + 1:                                                         \
+    launch_gu<N, true>(grid, s, shared, x, w, w13_scale, d, I, ws);       \
     break;
     MOE_NJ_CASES(X)
 #undef X
@@ -116,16 +139,13 @@ hipError_t launch_down_gemv(const LayerDims& d, bool shared, const void* w2,
   const int slots = shared ? 1 : (d.T * d.k < d.E ? d.T * d.k : d.E);
   dim3 grid(d.H / (4 * kWaves), slots);
   const auto* w = static_cast<const uint8_t*>(w2);
-  const int sh = static_cast<int>(shared);
   switch (nj * 2 + (d.e8m0 ? 1 : 0)) {
-#define X(N)                                                                                  \
-  case 2 * N:                                                                                 \
-    hipLaunchKernelGGL((down_kernel<N, false>), grid, dim3(kThreads), 0, s, w, w2_scale, d.H,  \
-                       I, d.T, sh, ws);                                                       \
-    break;                                                                                    \
-  case 2 * N + 1:                                                                             \
-    hipLaunchKernelGGL((down_kernel<N, true>), grid, dim3(kThreads), 0, s, w, w2_scale, d.H,   \
-                       I, d.T, sh, ws);                                                       \
+#define X(N)                                                     \
+  case 2 * N:                                                    \
+    launch_dn<N, false>(grid, s, shared, w, w2_scale, d, I, ws); \
+    break;                                                       \
+  case 2 * N + 1:                                                \
+    launch_dn<N, true>(grid, s, shared, w, w2_scale, d, I, ws);  \
     break;
     MOE_NJ_CASES(X)
 #undef X

@@ -21,7 +21,7 @@ struct Workspace {
   float* act_s;        // [maxT, Is]      shared SwiGLU output
   float* rows;         // [maxT * k, H]   routed down output, at route index t*k+j
   float* y_s;          // [maxT, H]       shared expert output
-  uint32_t* counter;   // [1] last-block counter of the router (self-resetting)
+  uint32_t* counter;   // router arrival counters, router_cnt_words() (self-resetting)
   uint32_t* sync;      // [sync_words(E)] counters of the fused kernel (self-resetting)
   float* zero_bias;    // [E] zeros: the router bias when the caller passes none
 };
@@ -58,6 +58,15 @@ __host__ __device__ constexpr int sync_gu_flag(int d) { return kSyncSlot0 + d * 
 __host__ __device__ constexpr int sync_lines(int slots) { return kSyncSlot0 + slots * kSlotLines; }
 __host__ __device__ constexpr size_t sync_words(int E) {
   return static_cast<size_t>(sync_lines(E)) * kSyncStride;
+}
+
+// Arrival counters of the router kernel in Workspace::counter: one 128-byte
+// line per block of kRouterTokBlk tokens, then one for the token blocks.
+constexpr int kRouterTokBlk = 8;
+constexpr int kRouterMaxBlk = 32;  // 256 tokens
+__host__ __device__ constexpr int router_cnt_line(int b) { return b * kSyncStride; }
+__host__ __device__ constexpr size_t router_cnt_words() {
+  return static_cast<size_t>(kRouterMaxBlk + 1) * kSyncStride;
 }
 
 constexpr int kFusedMaxTokens = 16;

@@ -133,24 +133,31 @@ __host__ __device__ inline size_t route_smem_bytes(int T, int E, int k) {
          static_cast<size_t>(E) * 4 + 16;
 }
 
-// Top-k of every token, then the route tables, by one 256-thread workgroup.
-// logits [T, E] must be visible to the workgroup.  Writes ws.ids/weights
-// (and the optional outputs), ws.counts/offsets/touched/n_touched/perm/inv.
-// smem: route_smem_bytes(T, E, k) bytes, 8-byte aligned.
-template <bool C = false>
-__device__ inline void select_and_route(int T, int E, int k, float rsf, const float* logits,
-                                        const float* bias, const Workspace& ws,
-                                        int32_t* ids_out, float* w_out, unsigned char* smem) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int R = T * k;
-  const int MW = (T + 63) / 64;
-  int* s_ids = reinterpret_cast<int*>(smem);  // [T*k]
-  unsigned long long* s_mask = reinterpret_cast<unsigned long long*>(
-      smem + ((static_cast<size_t>(R) * 4 + 7) & ~static_cast<size_t>(7)));  // [E*MW]
-  int* s_off = reinterpret_cast<int*>(s_mask + static_cast<size_t>(E) * MW);  // [E]
-  int* s_tmp = s_off + E;                                                      // [4]
+// LDS carve-up of the routing step: s_ids [T*k], token masks [E * MW],
+// offsets [E], scan scratch [4].
+struct RouteSmem {
+  int* ids;
+  unsigned long long* mask;
+  int* off;
+  int* tmp;
+  __device__ RouteSmem(unsigned char* smem, int T, int E, int k) {
+    const size_t R = static_cast<size_t>(T) * k, MW = (T + 63) / 64;
+    ids = reinterpret_cast<int*>(smem);
+    mask = reinterpret_cast<unsigned long long*>(smem + ((R * 4 + 7) & ~static_cast<size_t>(7)));
+    off = reinterpret_cast<int*>(mask + static_cast<size_t>(E) * MW);
+    tmp = off + E;
+  }
+};
 
-  for (int t = wave; t < T; t += 4) {
+// Top-k of tokens [t_begin, t_end), one wave per token.  Writes ws.ids and
+// ws.weights (coherent stores when C), the optional caller outputs and the
+// LDS copy of the ids (route r = t*k + j).
+template <bool C>
+__device__ inline void select_tokens(int t_begin, int t_end, int E, int k, float rsf,
+                                     const float* logits, const float* bias, const Workspace& ws,
+                                     int32_t* ids_out, float* w_out, int* s_ids) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int t = t_begin + wave; t < t_end; t += kRouteThreads / 64) {
     int id = 0;
     float w = 0.f;
     select_token<C>(logits + static_cast<size_t>(t) * E, bias, E, k, rsf, &id, &w);
@@ -163,13 +170,24 @@ __device__ inline void select_and_route(int T, int E, int k, float rsf, const fl
       if (w_out) w_out[r] = w;
     }
   }
-  for (int i = threadIdx.x; i < E * MW; i += kRouteThreads) s_mask[i] = 0ull;
+}
+
+// Route tables of T tokens from the ids in LDS (sm.ids, all T*k routes), by
+// one 256-thread workgroup: ws.counts/offsets/touched/n_touched/perm/inv
+// (coherent stores when C).  Its first barrier comes before the first read of
+// sm.ids, so callers may fill sm.ids right before the call.
+template <bool C>
+__device__ inline void build_routes(int T, int E, int k, const Workspace& ws,
+                                    const RouteSmem& sm) {
+  const int R = T * k;
+  const int MW = (T + 63) / 64;
+  for (int i = threadIdx.x; i < E * MW; i += kRouteThreads) sm.mask[i] = 0ull;
   __syncthreads();
 
   // Token bitmask of every expert.
   for (int r = threadIdx.x; r < R; r += kRouteThreads) {
-    const int e = s_ids[r], t = r / k;
-    atomicOr(&s_mask[static_cast<size_t>(e) * MW + (t >> 6)], 1ull << (t & 63));
+    const int e = sm.ids[r], t = r / k;
+    atomicOr(&sm.mask[static_cast<size_t>(e) * MW + (t >> 6)], 1ull << (t & 63));
   }
   __syncthreads();
   // Counts and touched flags, packed so that one scan gives both prefixes:
@@ -182,19 +200,19 @@ __device__ inline void select_and_route(int T, int E, int k, float rsf, const fl
       const int e = 4 * threadIdx.x + m;
       int cnt = 0;
       if (e < E)
-        for (int w = 0; w < MW; ++w) cnt += __popcll(s_mask[static_cast<size_t>(e) * MW + w]);
+        for (int w = 0; w < MW; ++w) cnt += __popcll(sm.mask[static_cast<size_t>(e) * MW + w]);
       packed[m] = (cnt << 11) | (cnt > 0 ? 1 : 0);
       local += packed[m];
     }
     int total = 0;
-    int run = block_exclusive_scan(local, s_tmp, &total);
+    int run = block_exclusive_scan(local, sm.tmp, &total);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int e = 4 * threadIdx.x + m;
       if (e < E) {
         const int cnt = packed[m] >> 11;
         const int off = run >> 11, tidx = run & 0x7ff;
-        s_off[e] = off;
+        sm.off[e] = off;
         st_i32<C>(ws.counts + e, cnt);
         st_i32<C>(ws.offsets + e, off);
         if (cnt > 0) st_i32<C>(ws.touched + tidx, e);
@@ -210,15 +228,27 @@ __device__ inline void select_and_route(int T, int E, int k, float rsf, const fl
   // Stable position of every route: its expert's offset plus the number of
   // earlier tokens routed to the same expert.
   for (int r = threadIdx.x; r < R; r += kRouteThreads) {
-    const int e = s_ids[r], t = r / k;
-    const unsigned long long* m = s_mask + static_cast<size_t>(e) * MW;
+    const int e = sm.ids[r], t = r / k;
+    const unsigned long long* m = sm.mask + static_cast<size_t>(e) * MW;
     int rank = 0;
     for (int w = 0; w < (t >> 6); ++w) rank += __popcll(m[w]);
     rank += __popcll(m[t >> 6] & ((1ull << (t & 63)) - 1ull));
-    const int pos = s_off[e] + rank;
+    const int pos = sm.off[e] + rank;
     st_i32<C>(ws.perm + pos, r);
     st_i32<C>(ws.inv + r, pos);
   }
+}
+
+// Top-k of every token, then the route tables, by one 256-thread workgroup.
+// logits [T, E] must be visible to the workgroup.  smem:
+// route_smem_bytes(T, E, k) bytes, 16-byte aligned.
+template <bool C = false>
+__device__ inline void select_and_route(int T, int E, int k, float rsf, const float* logits,
+                                        const float* bias, const Workspace& ws,
+                                        int32_t* ids_out, float* w_out, unsigned char* smem) {
+  const RouteSmem sm(smem, T, E, k);
+  select_tokens<C>(0, T, E, k, rsf, logits, bias, ws, ids_out, w_out, sm.ids);
+  build_routes<C>(T, E, k, ws, sm);
 }
 
 }  // namespace moe

@@ -49,7 +49,7 @@ def test_tiny_layer(c_oracle):
 
 
 @pytest.mark.parametrize("name", ["decode_t1", "decode_t16"])
-@pytest.mark.parametrize("path", [md.PATH_AUTO, md.PATH_GEMV_SPLIT], ids=["auto", "split"])
+@pytest.mark.parametrize("path", [md.PATH_GEMV, md.PATH_GEMV_SPLIT], ids=["fused", "split"])
 def test_decode_layers_full(name, path, c_oracle):
     inp, got, err = _case(WORKLOADS[name], c_oracle, path=path)
     if name == "decode_t16":
@@ -81,7 +81,7 @@ SMALL = [
 
 @pytest.mark.parametrize("case", SMALL, ids=[str(c) for c in SMALL])
 @pytest.mark.parametrize("with_bias", [False, True])
-@pytest.mark.parametrize("path", [md.PATH_AUTO, md.PATH_GEMV_SPLIT], ids=["auto", "split"])
+@pytest.mark.parametrize("path", [md.PATH_GEMV, md.PATH_GEMV_SPLIT], ids=["fused", "split"])
 def test_small_layers(case, with_bias, path, c_oracle):
     T, H, E, k, I, Is, fmt = case
     sh = LayerShape(T=T, H=H, E=E, k=k, I=I, Is=Is, scale_fmt=fmt, tag=300 + sum(case[:6]))
@@ -95,7 +95,7 @@ def test_fused_and_split_paths_agree(T, c_oracle):
     sh = WORKLOADS["decode_t16"].replace(T=T, H=2048, I=768, Is=512, tag=310 + T)
     inp = make_layer(sh)
     dev = to_device(inp)
-    fused = make_plan(sh, path=md.PATH_AUTO)
+    fused = make_plan(sh, path=md.PATH_GEMV)
     split = make_plan(sh, path=md.PATH_GEMV_SPLIT)
     assert fused.path_for(T) == md.PATH_GEMV and split.path_for(T) == md.PATH_GEMV_SPLIT
     a = run_layer(fused, dev, T)
@@ -154,11 +154,12 @@ def test_same_expert_for_every_token(c_oracle):
     plan.close()
 
 
-def test_residual_alias_and_determinism(c_oracle):
+@pytest.mark.parametrize("path", [md.PATH_GEMV, md.PATH_GEMV_SPLIT], ids=["fused", "split"])
+def test_residual_alias_and_determinism(path, c_oracle):
     sh = WORKLOADS["decode_t16"].replace(H=2048, I=512, Is=512, tag=303)
     inp = make_layer(sh)
     dev = to_device(inp)
-    plan = make_plan(sh)
+    plan = make_plan(sh, path=path)
     a = run_layer(plan, dev, sh.T)
     b = run_layer(plan, dev, sh.T)
     c = run_layer(plan, dev, sh.T, alias_residual=True)
@@ -188,13 +189,14 @@ def test_smaller_T_than_plan_and_zero(c_oracle):
     plan.close()
 
 
-def test_graph_replay_matches_eager(c_oracle):
+@pytest.mark.parametrize("path", [md.PATH_GEMV, md.PATH_GEMV_SPLIT], ids=["fused", "split"])
+def test_graph_replay_matches_eager(path, c_oracle):
     """One run captured into a HIP graph, replayed several times with eager
     work in between; every replay equals the eager result bit for bit."""
     sh = WORKLOADS["decode_t16"].replace(H=1024, I=512, Is=256, tag=305)
     inp = make_layer(sh)
     dev = to_device(inp)
-    plan = make_plan(sh)
+    plan = make_plan(sh, path=path)
     eager = run_layer(plan, dev, sh.T, keep_device=True)
     T, H, k = sh.T, sh.H, sh.k
     out = torch.empty((T, H), dtype=torch.int16, device="cuda")
