@@ -276,8 +276,11 @@ def main():
         kern_bytes = metric_bytes + E * H * 2
     else:
         # routed gate/up projection: touched experts' w13 + scales, the token
-        # rows in, the SwiGLU rows (f32) out
-        kern_name = "gate_up_kernel<NJ, E8, SHARED=false> (routed experts)"
+        # rows in, the SwiGLU rows out (f32, or hi + lo bf16 planes)
+        if path_taken == md.PATH_GROUPED:
+            kern_name = "gate_up_mfma_kernel<U, E8, SHARED=false> (routed experts)"
+        else:
+            kern_name = "gate_up_kernel<NJ, E8, SHARED=false> (routed experts)"
         sb = 1 if sh.scale_fmt == "e8m0" else 4
         kern_bytes = (D * (2 * sh.I * H + sb * (2 * sh.I // 128) * (H // 128))
                       + T * H * 2 + T * k * sh.I * 4)

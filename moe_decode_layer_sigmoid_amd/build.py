@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_decode.so")
-SOURCES = ["api.hip", "router.hip", "experts_gemv.hip", "epilogue.hip", "decode_fused.hip"]
+SOURCES = ["api.hip", "router.hip", "experts_gemv.hip", "experts_mfma.hip", "epilogue.hip",
+           "decode_fused.hip"]
 # decode_fused.hip is also compiled once per register chunk count and scale
 # format (the template arguments of its kernel), each into its own object.
 FUSED_NJ = range(1, 9)

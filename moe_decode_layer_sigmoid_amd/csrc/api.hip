@@ -43,6 +43,7 @@ int path_for(const moe_decode_plan_s& p, int32_t T) {
   if (want == MOE_DECODE_PATH_GEMV_SPLIT || want == MOE_DECODE_PATH_GROUPED) return want;
   if (want == MOE_DECODE_PATH_GEMV && T <= moe::kFusedMaxTokens && p.fused_grid > 0)
     return MOE_DECODE_PATH_GEMV;
+  if (want == MOE_DECODE_PATH_AUTO && T >= moe::kGroupedMinTokens) return MOE_DECODE_PATH_GROUPED;
   return MOE_DECODE_PATH_GEMV_SPLIT;
 }
 
@@ -132,7 +133,6 @@ int moe_decode_desc_check(const moe_decode_desc* d) {
   if (d->top_k > moe::kMaxTopK || d->top_k > d->num_experts ||
       d->num_experts > moe::kMaxExperts || d->max_tokens > moe::kMaxTokens)
     return MOE_DECODE_ERR_UNSUPPORTED;
-  if (d->path == MOE_DECODE_PATH_GROUPED) return MOE_DECODE_ERR_UNSUPPORTED;
   return MOE_DECODE_OK;
 }
 
@@ -268,7 +268,11 @@ static int run_fused(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, h
 
 static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t T,
                          hipStream_t s) {
-  if (path_for(*p, T) == MOE_DECODE_PATH_GEMV) return run_fused(p, a, T, s);
+  const int path = path_for(*p, T);
+  if (path == MOE_DECODE_PATH_GEMV) return run_fused(p, a, T, s);
+  const bool mfma = path == MOE_DECODE_PATH_GROUPED;
+  const auto gate_up = mfma ? moe::launch_gate_up_mfma : moe::launch_gate_up_gemv;
+  const auto down = mfma ? moe::launch_down_mfma : moe::launch_down_gemv;
   const moe::LayerDims d = dims(p->desc, T);
   const bool has_shared = d.Is > 0;
 
@@ -280,18 +284,17 @@ static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t 
     if (err == hipSuccess && e != hipSuccess) err = e;
   };
   if (has_shared) {
-    step(moe::launch_gate_up_gemv(d, true, a->hidden, a->sw13, a->sw13_scale, p->ws, p->side));
-    if (err == hipSuccess) step(moe::launch_down_gemv(d, true, a->sw2, a->sw2_scale, p->ws, p->side));
+    step(gate_up(d, true, a->hidden, a->sw13, a->sw13_scale, p->ws, p->side));
+    if (err == hipSuccess) step(down(d, true, a->sw2, a->sw2_scale, p->ws, p->side));
   }
   if (err == hipSuccess)
     step(moe::launch_router(d, a->hidden, a->router_w,
                             a->router_bias ? a->router_bias : p->ws.zero_bias, p->ws, a->topk_ids,
                             a->topk_weights, s));
   if (err == hipSuccess && p->user_begin) step(hipEventRecord(p->user_begin, s));
-  if (err == hipSuccess)
-    step(moe::launch_gate_up_gemv(d, false, a->hidden, a->w13, a->w13_scale, p->ws, s));
+  if (err == hipSuccess) step(gate_up(d, false, a->hidden, a->w13, a->w13_scale, p->ws, s));
   if (err == hipSuccess && p->user_end) step(hipEventRecord(p->user_end, s));
-  if (err == hipSuccess) step(moe::launch_down_gemv(d, false, a->w2, a->w2_scale, p->ws, s));
+  if (err == hipSuccess) step(down(d, false, a->w2, a->w2_scale, p->ws, s));
 
   // Join the side stream on every path, then run the boundary.
   hipError_t jerr = hipEventRecord(p->join, p->side);

@@ -1,0 +1,410 @@
+// fp8 expert projections on the gfx950 matrix cores (the many-token regime).
+//
+// Follows the vLLM API page "vllm.models.glm5next.nvidia.specialized_decode.
+// runtime.decode": LayerStages._build_mega builds the routed experts from
+// w13 / w2 fp8 weights with 128x128 block scales (w13_weight_scale_inv,
+// w2_weight_scale_inv; power-of-two e8m0 scales when that flag is set) and
+// swiglu_limit, and picks a grouped kernel for larger token counts; the
+// shared expert (SharedExpert) takes the same weight pair and limit.
+//
+// Each touched expert's weights are streamed from HBM once for all of its
+// tokens.  A wave owns 32 weight rows (gate_up: 16 gate rows and the 16
+// matching up rows; down: 32 consecutive output rows) and walks the
+// contraction dimension in 128-wide scale blocks.  The weights go from HBM
+// straight to the wave's own LDS area (global_load_lds_dwordx4): eight
+// consecutive lanes read the eight 16-byte pieces of one 128-byte block of
+// a row, so every load instruction fetches whole 128-byte lines (the
+// MFMA fragment order, four lanes per row, would fetch half lines and
+// reach noticeably less of the HBM bandwidth).  The pieces land XOR-
+// swizzled by row, so that the fragment reads from LDS spread over the
+// banks.  Each lane then reads 32 fp8 bytes of its fragment row, converts
+// them exactly to bf16, and v_mfma_f32_16x16x32_bf16 multiplies them with
+// the bf16 activations of up to 16 tokens (one MFMA row per token; rows past
+// the expert's token count repeat its last token and are never stored).
+// Products are exact and the four MFMAs of a block sum in fp32; the block's
+// partial is then scaled by the weight block scale and added to the fp32
+// result, as the dequantise-then-multiply definition has it.
+//
+// The gate_up output (clamped SwiGLU) is stored as two bf16 planes,
+// hi = bf16(a) and lo = bf16(a - hi), so that the down projection's
+// activations keep 16 significant bits: down runs one MFMA on each plane.
+//
+// Lane layout of v_mfma_f32_16x16x32_bf16 (lane l, group g = l / 16,
+// c = l % 16): A[c][8g + i] and B[8g + i][c] for i < 8; D[4g + i][c] for
+// i < 4.  A lane's 32 bytes of a 128-wide block feed the four MFMAs of the
+// block 8 bytes at a time (MFMA m takes contraction indices 32g + 8m + i),
+// and its activation loads follow the same order, so A and B agree.
+#include "device_common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kStageBlock = 4096;  // LDS bytes of one 128-wide block of a wave's 32 rows
+constexpr unsigned kCpolNT = 2;    // non-temporal: weights are read once per step
+
+// Issues the loads of one 128-wide block (byte offset kofs of every row) of
+// the wave's 32 rows into `stage` (kStageBlock bytes): load instruction i
+// covers rows 8i .. 8i+7, whose start pointers lane l finds in row[i] (its
+// row 8i + l / 8).  Lane l fetches piece (l % 8) ^ (l / 8) of its row and
+// lands at stage + 1024 i + 16 l, so row r's piece p sits at slot
+// p ^ (r % 8) of its 128 bytes.
+__device__ __forceinline__ void stage_block(const uint8_t* const row[4], int kofs,
+                                            unsigned char* stage) {
+  const int lane = threadIdx.x & 63;
+  const int piece = (lane & 7) ^ (lane >> 3);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_global_load_lds(row[i] + kofs + 16 * piece,
+                                     (lds_void_t*)(stage + 1024 * i), 16, 0,
+                                     kCpolNT);
+}
+
+// Piece p (16 bytes) of fragment row c of subtile s (rows 16 s + c) of a
+// staged block.
+__device__ __forceinline__ uint4 staged_piece(const unsigned char* stage, int s, int c, int p) {
+  const int r8 = c & 7;
+  return *reinterpret_cast<const uint4*>(stage + 1024 * (2 * s + (c >> 3)) + 128 * r8 +
+                                         16 * (p ^ r8));
+}
+
+// Eight e4m3fn codes (two dwords, byte 0 first) -> eight bf16 (exact).
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  const bf16x4_t ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const bf16x4_t cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// dwords 2m, 2m+1 of a lane's 32 raw bytes (lo: bytes 0-15, hi: 16-31)
+__device__ __forceinline__ bf16x8_t weight_frag(const uint4& lo, const uint4& hi, int m) {
+  const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  return fp8x8_to_bf16x8(w[2 * m], w[2 * m + 1]);
+}
+
+__device__ __forceinline__ f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float f) { return static_cast<uint16_t>(f32_to_bf16(f)); }
+
+// Per-slot expert, token count, permuted base position and this
+// workgroup's token range [p_begin, p_end) (uniform).  Routed: grid row y is
+// the touched-expert slot and the workgroup takes all of its tokens, in
+// passes of 16 * GR.  Shared: grid row y is one pass of 16 * GR tokens.
+struct Slot {
+  int e, n, base, p_begin, p_end;
+};
+
+template <bool SHARED, int GR>
+__device__ __forceinline__ bool slot_of(int T, const Workspace& ws, Slot* s) {
+  if (SHARED) {
+    const int p = blockIdx.y * 16 * GR;
+    *s = {0, T, 0, p, min(T, p + 16 * GR)};
+    return p < T;
+  }
+  const int d = blockIdx.y;
+  if (d >= *ws.n_touched) return false;
+  const int e = ws.touched[d];
+  const int n = ws.counts[e];
+  *s = {e, n, ws.offsets[e], 0, n};
+  return true;
+}
+
+// gate_up + clamped SwiGLU.  Wave: SwiGLU outputs [i0, i0 + 16) of one
+// expert for all its tokens; writes the hi / lo bf16 planes of
+// act[(base + q) * I + i].  U = scale blocks per round of loads; GR =
+// 16-token groups per pass over the weights.
+template <int U, int GR, bool E8, bool SHARED>
+__global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
+    const uint16_t* __restrict__ hidden, const uint8_t* __restrict__ w13,
+    const void* __restrict__ scale, int H, int I, int k, int T, Workspace ws, float limit) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const int i0 = (blockIdx.x * kWaves + wave) * 16;
+  Slot sl;
+  if (!slot_of<SHARED, GR>(T, ws, &sl) || i0 >= I) return;
+  unsigned char* stage = smem + wave * U * kStageBlock;
+  const int KB = H / kBlock;
+  const uint8_t* W = w13 + static_cast<size_t>(sl.e) * 2 * I * H;
+  // load rows: instructions 0, 1 = gate rows i0 .. i0+15, 2, 3 = up rows
+  const uint8_t* lrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    lrow[i] = W + static_cast<size_t>((i < 2 ? i0 : I + i0 - 16) + 8 * i + (lane >> 3)) * H;
+  const size_t sb = static_cast<size_t>(sl.e) * (2 * I / kBlock) * KB;
+  const size_t sg0 = sb + static_cast<size_t>(i0 / kBlock) * KB;
+  const size_t su0 = sb + static_cast<size_t>((I + i0) / kBlock) * KB;
+  uint16_t* act_hi = reinterpret_cast<uint16_t*>(SHARED ? ws.act_s : ws.act);
+  const size_t plane = static_cast<size_t>(SHARED ? T : T * k) * I;
+  uint16_t* act_lo = act_hi + plane;
+
+  for (int p0 = sl.p_begin; p0 < sl.p_end; p0 += 16 * GR) {
+    const int G = min(GR, (sl.p_end - p0 + 15) / 16);
+    const uint16_t* xrow[GR];
+#pragma unroll
+    for (int gr = 0; gr < GR; ++gr) {
+      const int q = min(p0 + gr * 16 + c, sl.p_end - 1);
+      const int t = SHARED ? q : ws.perm[sl.base + q] / k;
+      xrow[gr] = hidden + static_cast<size_t>(t) * H + 32 * g;
+    }
+    f32x4_t fg[GR], fu[GR];
+#pragma unroll
+    for (int gr = 0; gr < GR; ++gr) {
+      fg[gr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      fu[gr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int kb0 = 0; kb0 < KB; kb0 += U) {
+      float sg[U], su[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int kb = min(kb0 + j, KB - 1);  // a block past the end gets scale 0
+        stage_block(lrow, kb * kBlock, stage + j * kStageBlock);
+        const float a = load_scale<E8>(scale, sg0 + kb);
+        const float b = load_scale<E8>(scale, su0 + kb);
+        sg[j] = kb0 + j < KB ? a : 0.f;
+        su[j] = kb0 + j < KB ? b : 0.f;
+      }
+      // every load of the round is issued before the first wait
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int gr = 0; gr < GR; ++gr) {
+        if (gr >= G) break;
+        uint4 xa[U][4];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          const int kb = min(kb0 + j, KB - 1);
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            xa[j][m] = *reinterpret_cast<const uint4*>(xrow[gr] + kb * kBlock + 8 * m);
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          const unsigned char* st = stage + j * kStageBlock;
+          const uint4 g0 = staged_piece(st, 0, c, 2 * g), g1 = staged_piece(st, 0, c, 2 * g + 1);
+          const uint4 u0 = staged_piece(st, 1, c, 2 * g), u1 = staged_piece(st, 1, c, 2 * g + 1);
+          f32x4_t pg = {0.f, 0.f, 0.f, 0.f}, pu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const bf16x8_t a = as_bf16x8(xa[j][m]);
+            pg = mfma(a, weight_frag(g0, g1, m), pg);
+            pu = mfma(a, weight_frag(u0, u1, m), pu);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            fg[gr][i] = fmaf(sg[j], pg[i], fg[gr][i]);
+            fu[gr][i] = fmaf(su[j], pu[i], fu[gr][i]);
+          }
+        }
+      }
+      // the next round's loads overwrite the stage: its reads must be done
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    }
+    // lane holds tokens p0 + 16 gr + 4 g + i of SwiGLU output i0 + c
+#pragma unroll
+    for (int gr = 0; gr < GR; ++gr) {
+      if (gr >= G) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = p0 + gr * 16 + 4 * g + i;
+        if (q < sl.p_end) {
+          const float a = clamped_swiglu(fg[gr][i], fu[gr][i], limit);
+          const uint16_t hi = bf16_bits(a);
+          const uint16_t lo = bf16_bits(a - bf16_to_f32(hi));
+          const size_t o = static_cast<size_t>(sl.base + q) * I + i0 + c;
+          act_hi[o] = hi;
+          act_lo[o] = lo;
+        }
+      }
+    }
+  }
+}
+
+// down projection.  Wave: output rows [h0, h0 + 32) of one expert for all
+// its tokens, from the hi / lo activation planes; row q goes to
+// out[perm[base + q] * H] (routed: the route index t*k + j) or out[q * H]
+// (shared).
+template <int U, int GR, bool E8, bool SHARED>
+__global__ __launch_bounds__(kThreads) void down_mfma_kernel(
+    const uint8_t* __restrict__ w2, const void* __restrict__ scale, int H, int I, int k, int T,
+    Workspace ws) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const int h0 = (blockIdx.x * kWaves + wave) * 32;
+  Slot sl;
+  if (!slot_of<SHARED, GR>(T, ws, &sl) || h0 >= H) return;
+  unsigned char* stage = smem + wave * U * kStageBlock;
+  const int KB = I / kBlock;
+  const uint8_t* W = w2 + static_cast<size_t>(sl.e) * H * I;
+  const uint8_t* lrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lrow[i] = W + static_cast<size_t>(h0 + 8 * i + (lane >> 3)) * I;
+  const size_t s0 = static_cast<size_t>(sl.e) * (H / kBlock) * KB +
+                    static_cast<size_t>(h0 / kBlock) * KB;
+  const uint16_t* act_hi = reinterpret_cast<const uint16_t*>(SHARED ? ws.act_s : ws.act);
+  const size_t plane = static_cast<size_t>(SHARED ? T : T * k) * I;
+  const uint16_t* act_lo = act_hi + plane;
+  float* out = SHARED ? ws.y_s : ws.rows;
+
+  for (int p0 = sl.p_begin; p0 < sl.p_end; p0 += 16 * GR) {
+    const int G = min(GR, (sl.p_end - p0 + 15) / 16);
+    size_t arow[GR];
+#pragma unroll
+    for (int gr = 0; gr < GR; ++gr) {
+      const int q = min(p0 + gr * 16 + c, sl.p_end - 1);
+      arow[gr] = static_cast<size_t>(sl.base + q) * I + 32 * g;
+    }
+    f32x4_t f0[GR], f1[GR];
+#pragma unroll
+    for (int gr = 0; gr < GR; ++gr) {
+      f0[gr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      f1[gr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int kb0 = 0; kb0 < KB; kb0 += U) {
+      float sc[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int kb = min(kb0 + j, KB - 1);
+        stage_block(lrow, kb * kBlock, stage + j * kStageBlock);
+        const float s = load_scale<E8>(scale, s0 + kb);
+        sc[j] = kb0 + j < KB ? s : 0.f;
+      }
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int gr = 0; gr < GR; ++gr) {
+        if (gr >= G) break;
+        uint4 ah[U][4], al[U][4];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          const int kb = min(kb0 + j, KB - 1);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            ah[j][m] = *reinterpret_cast<const uint4*>(act_hi + arow[gr] + kb * kBlock + 8 * m);
+            al[j][m] = *reinterpret_cast<const uint4*>(act_lo + arow[gr] + kb * kBlock + 8 * m);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          const unsigned char* st = stage + j * kStageBlock;
+          const uint4 a0 = staged_piece(st, 0, c, 2 * g), a1 = staged_piece(st, 0, c, 2 * g + 1);
+          const uint4 b0 = staged_piece(st, 1, c, 2 * g), b1 = staged_piece(st, 1, c, 2 * g + 1);
+          f32x4_t p = {0.f, 0.f, 0.f, 0.f}, q = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const bf16x8_t wa = weight_frag(a0, a1, m);
+            const bf16x8_t wb = weight_frag(b0, b1, m);
+            p = mfma(as_bf16x8(ah[j][m]), wa, p);
+            p = mfma(as_bf16x8(al[j][m]), wa, p);
+            q = mfma(as_bf16x8(ah[j][m]), wb, q);
+            q = mfma(as_bf16x8(al[j][m]), wb, q);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f0[gr][i] = fmaf(sc[j], p[i], f0[gr][i]);
+            f1[gr][i] = fmaf(sc[j], q[i], f1[gr][i]);
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): stage reads done
+    }
+#pragma unroll
+    for (int gr = 0; gr < GR; ++gr) {
+      if (gr >= G) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = p0 + gr * 16 + 4 * g + i;
+        if (q < sl.p_end) {
+          const int o = SHARED ? q : ws.perm[sl.base + q];
+          float* row = out + static_cast<size_t>(o) * H + h0 + c;
+          row[0] = f0[gr][i];
+          row[16] = f1[gr][i];
+        }
+      }
+    }
+  }
+}
+
+// Routed: U scale blocks per round of loads, one 16-token group per pass
+// (an expert rarely has more than 16 of a step's tokens).  Shared: the same
+// tile shape, one grid row per 16 tokens, so that the passes run in parallel.
+constexpr int kU = 2;
+constexpr int kGR = 1;
+constexpr size_t kLds = static_cast<size_t>(kWaves) * kU * kStageBlock;
+
+template <bool E8>
+void launch_gu(dim3 grid, hipStream_t s, bool shared, const uint16_t* x, const uint8_t* w,
+               const void* scale, const LayerDims& d, int I, const Workspace& ws) {
+  if (shared)
+    hipLaunchKernelGGL((gate_up_mfma_kernel<kU, kGR, E8, true>), grid, dim3(kThreads), kLds, s, x,
+                       w, scale, d.H, I, d.k, d.T, ws, d.limit);
+  else
+    hipLaunchKernelGGL((gate_up_mfma_kernel<kU, kGR, E8, false>), grid, dim3(kThreads), kLds, s, x,
+                       w, scale, d.H, I, d.k, d.T, ws, d.limit);
+}
+
+template <bool E8>
+void launch_dn(dim3 grid, hipStream_t s, bool shared, const uint8_t* w, const void* scale,
+               const LayerDims& d, int I, const Workspace& ws) {
+  if (shared)
+    hipLaunchKernelGGL((down_mfma_kernel<kU, kGR, E8, true>), grid, dim3(kThreads), kLds, s, w,
+                       scale, d.H, I, d.k, d.T, ws);
+  else
+    hipLaunchKernelGGL((down_mfma_kernel<kU, kGR, E8, false>), grid, dim3(kThreads), kLds, s, w,
+                       scale, d.H, I, d.k, d.T, ws);
+}
+
+int grid_rows(const LayerDims& d, bool shared) {
+  if (shared) return (d.T + 16 * kGR - 1) / (16 * kGR);
+  return d.T * d.k < d.E ? d.T * d.k : d.E;
+}
+
+}  // namespace
+
+hipError_t launch_gate_up_mfma(const LayerDims& d, bool shared, const void* hidden,
+                               const void* w13, const void* w13_scale, const Workspace& ws,
+                               hipStream_t s) {
+  const int I = shared ? d.Is : d.I;
+  dim3 grid((I / 16 + kWaves - 1) / kWaves, grid_rows(d, shared));
+  const auto* x = static_cast<const uint16_t*>(hidden);
+  const auto* w = static_cast<const uint8_t*>(w13);
+  if (d.e8m0)
+    launch_gu<true>(grid, s, shared, x, w, w13_scale, d, I, ws);
+  else
+    launch_gu<false>(grid, s, shared, x, w, w13_scale, d, I, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_mfma(const LayerDims& d, bool shared, const void* w2,
+                            const void* w2_scale, const Workspace& ws, hipStream_t s) {
+  const int I = shared ? d.Is : d.I;
+  dim3 grid((d.H / 32 + kWaves - 1) / kWaves, grid_rows(d, shared));
+  const auto* w = static_cast<const uint8_t*>(w2);
+  if (d.e8m0)
+    launch_dn<true>(grid, s, shared, w, w2_scale, d, I, ws);
+  else
+    launch_dn<false>(grid, s, shared, w, w2_scale, d, I, ws);
+  return hipGetLastError();
+}
+
+}  // namespace moe

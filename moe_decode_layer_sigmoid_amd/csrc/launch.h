@@ -70,6 +70,8 @@ __host__ __device__ constexpr size_t router_cnt_words() {
 }
 
 constexpr int kFusedMaxTokens = 16;
+// AUTO takes the MFMA projections from this many tokens on.
+constexpr int kGroupedMinTokens = 32;
 
 // Arguments of the fused persistent kernel (see decode_fused.hip).
 struct FusedArgs {
@@ -117,6 +119,14 @@ hipError_t launch_gate_up_gemv(const LayerDims& d, bool shared, const void* hidd
 
 // down projection (GEMV) of the SwiGLU activations.
 hipError_t launch_down_gemv(const LayerDims& d, bool shared, const void* w2,
+                            const void* w2_scale, const Workspace& ws, hipStream_t s);
+
+// The same two projections on the matrix cores (bf16 MFMA on exactly
+// converted fp8 weights; SwiGLU activations as hi + lo bf16 planes).
+hipError_t launch_gate_up_mfma(const LayerDims& d, bool shared, const void* hidden,
+                               const void* w13, const void* w13_scale, const Workspace& ws,
+                               hipStream_t s);
+hipError_t launch_down_mfma(const LayerDims& d, bool shared, const void* w2,
                             const void* w2_scale, const Workspace& ws, hipStream_t s);
 
 // Fused persistent kernel of the whole step (T <= kFusedMaxTokens).

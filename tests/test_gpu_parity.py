@@ -49,7 +49,8 @@ def test_tiny_layer(c_oracle):
 
 
 @pytest.mark.parametrize("name", ["decode_t1", "decode_t16"])
-@pytest.mark.parametrize("path", [md.PATH_GEMV, md.PATH_GEMV_SPLIT], ids=["fused", "split"])
+@pytest.mark.parametrize("path", [md.PATH_GEMV, md.PATH_GEMV_SPLIT, md.PATH_GROUPED],
+                         ids=["fused", "split", "grouped"])
 def test_decode_layers_full(name, path, c_oracle):
     inp, got, err = _case(WORKLOADS[name], c_oracle, path=path)
     if name == "decode_t16":
@@ -59,10 +60,11 @@ def test_decode_layers_full(name, path, c_oracle):
 
 
 @pytest.mark.parametrize("name", ["wide_t64_e8m0", "verify_t128"])
-def test_wide_layers_sampled(name, c_oracle):
+@pytest.mark.parametrize("path", [md.PATH_AUTO, md.PATH_GEMV_SPLIT], ids=["auto", "split"])
+def test_wide_layers_sampled(name, path, c_oracle):
     sh = WORKLOADS[name]
     rows = [0, 1, sh.T // 2, sh.T - 1]
-    _case(sh, c_oracle, rows=rows)
+    _case(sh, c_oracle, rows=rows, path=path)
 
 
 SMALL = [
@@ -81,31 +83,34 @@ SMALL = [
 
 @pytest.mark.parametrize("case", SMALL, ids=[str(c) for c in SMALL])
 @pytest.mark.parametrize("with_bias", [False, True])
-@pytest.mark.parametrize("path", [md.PATH_GEMV, md.PATH_GEMV_SPLIT], ids=["fused", "split"])
+@pytest.mark.parametrize("path", [md.PATH_GEMV, md.PATH_GEMV_SPLIT, md.PATH_GROUPED],
+                         ids=["fused", "split", "grouped"])
 def test_small_layers(case, with_bias, path, c_oracle):
     T, H, E, k, I, Is, fmt = case
     sh = LayerShape(T=T, H=H, E=E, k=k, I=I, Is=Is, scale_fmt=fmt, tag=300 + sum(case[:6]))
     _case(sh, c_oracle, with_bias=with_bias, path=path)
 
 
-@pytest.mark.parametrize("T", [1, 3, 16])
-def test_fused_and_split_paths_agree(T, c_oracle):
-    """The fused persistent kernel and the separate kernels compute the same
-    layer (same ids, outputs within the oracle tolerance of each other)."""
+@pytest.mark.parametrize("T", [1, 3, 16, 40])
+def test_paths_agree(T, c_oracle):
+    """The fused persistent kernel, the separate GEMV kernels and the MFMA
+    kernels compute the same layer (same ids, outputs within the oracle
+    tolerance of each other)."""
     sh = WORKLOADS["decode_t16"].replace(T=T, H=2048, I=768, Is=512, tag=310 + T)
     inp = make_layer(sh)
     dev = to_device(inp)
-    fused = make_plan(sh, path=md.PATH_GEMV)
-    split = make_plan(sh, path=md.PATH_GEMV_SPLIT)
-    assert fused.path_for(T) == md.PATH_GEMV and split.path_for(T) == md.PATH_GEMV_SPLIT
-    a = run_layer(fused, dev, T)
-    b = run_layer(split, dev, T)
-    assert np.array_equal(a["ids"], b["ids"])
-    assert_close(a["out"], b["out"], "fused vs split out")
-    check_layer(inp, a, c_oracle=c_oracle)
-    check_layer(inp, b, c_oracle=c_oracle)
-    fused.close()
-    split.close()
+    paths = [md.PATH_GEMV_SPLIT, md.PATH_GROUPED] + ([md.PATH_GEMV] if T <= 16 else [])
+    res = []
+    for path in paths:
+        plan = make_plan(sh, path=path)
+        assert plan.path_for(T) == path
+        res.append(run_layer(plan, dev, T))
+        plan.close()
+    for r in res[1:]:
+        assert np.array_equal(res[0]["ids"], r["ids"])
+        assert_close(r["out"], res[0]["out"], "paths agree: out")
+    for r in res:
+        check_layer(inp, r, c_oracle=c_oracle)
 
 
 def test_route_tables_match_oracle(c_oracle):
@@ -132,29 +137,33 @@ def test_route_tables_match_oracle(c_oracle):
     plan.close()
 
 
-def test_same_expert_for_every_token(c_oracle):
+@pytest.mark.parametrize("T", [37, 150])
+@pytest.mark.parametrize("path", [md.PATH_GEMV_SPLIT, md.PATH_GROUPED], ids=["split", "grouped"])
+def test_same_expert_for_every_token(T, path, c_oracle):
     """All tokens pick the same experts: one expert carries T tokens (the
-    token loop runs several register passes)."""
-    sh = LayerShape(T=37, H=256, E=16, k=2, I=128, Is=128, tag=302)
+    GEMV token loop runs several register passes; the MFMA kernels run
+    several 16-token groups and, past 64 tokens, several weight passes)."""
+    sh = LayerShape(T=T, H=256, E=16, k=2, I=128, Is=128, tag=302)
     inp = make_layer(sh)
     # Every token carries token 0's vector x0; router rows 3 and 9 point along
     # x0 (logits |x0| and |x0|/2), every other row is zero (logit 0).
     from synth import f32_to_bf16_bits
-    inp.hidden = np.ascontiguousarray(np.tile(inp.hidden[:1], (37, 1)))
+    inp.hidden = np.ascontiguousarray(np.tile(inp.hidden[:1], (T, 1)))
     x0 = oracle.bf16_bits_to_f64(inp.hidden[0])
     wr = np.zeros((16, 256), np.float32)
     wr[3] = (x0 / np.linalg.norm(x0)).astype(np.float32)
     wr[9] = 0.5 * wr[3]
     inp.router_w = f32_to_bf16_bits(wr)
     dev = to_device(inp)
-    plan = make_plan(sh)
+    plan = make_plan(sh, path=path)
     got = run_layer(plan, dev, sh.T)
     assert np.all(np.sort(got["ids"], 1) == [3, 9])
     check_layer(inp, got, c_oracle=c_oracle)
     plan.close()
 
 
-@pytest.mark.parametrize("path", [md.PATH_GEMV, md.PATH_GEMV_SPLIT], ids=["fused", "split"])
+@pytest.mark.parametrize("path", [md.PATH_GEMV, md.PATH_GEMV_SPLIT, md.PATH_GROUPED],
+                         ids=["fused", "split", "grouped"])
 def test_residual_alias_and_determinism(path, c_oracle):
     sh = WORKLOADS["decode_t16"].replace(H=2048, I=512, Is=512, tag=303)
     inp = make_layer(sh)
@@ -189,7 +198,8 @@ def test_smaller_T_than_plan_and_zero(c_oracle):
     plan.close()
 
 
-@pytest.mark.parametrize("path", [md.PATH_GEMV, md.PATH_GEMV_SPLIT], ids=["fused", "split"])
+@pytest.mark.parametrize("path", [md.PATH_GEMV, md.PATH_GEMV_SPLIT, md.PATH_GROUPED],
+                         ids=["fused", "split", "grouped"])
 def test_graph_replay_matches_eager(path, c_oracle):
     """One run captured into a HIP graph, replayed several times with eager
     work in between; every replay equals the eager result bit for bit."""
