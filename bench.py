@@ -85,6 +85,83 @@ def cpu_baseline(inp, sh, metric_bytes, seconds):
     }
 
 
+def sources_digest():
+    """sha256 over the HIP sources and the C header: a traffic figure taken
+    with hardware counters holds only for the kernels it was taken on."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "moe_decode_layer_sigmoid_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)
+                   if f.endswith((".hip", ".h")))
+    files.append(os.path.join(ROOT, "include", "moe_decode.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+TRAFFIC_TAG = "traffic-record:"
+
+
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from a counter summary
+    under profiles/, if one was taken on the current sources."""
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
+        return None
+    digest = sources_digest()
+    for f in sorted(os.listdir(pdir)):
+        if not f.endswith(".md"):
+            continue
+        with open(os.path.join(pdir, f)) as fh:
+            for line in fh:
+                line = line.strip().strip("`")
+                if not line.startswith(TRAFFIC_TAG):
+                    continue
+                rec = json.loads(line[len(TRAFFIC_TAG):])
+                if (rec.get("workload") == workload and rec.get("kernel") == kernel
+                        and rec.get("sources_sha256") == digest):
+                    return rec
+    return None
+
+
+def _counter_mean(run_dir, kernel):
+    import csv
+    import glob
+
+    vals = []
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if kernel in r["Kernel_Name"]:
+                    vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit("no dispatch of %r in %s" % (kernel, run_dir))
+    return sum(vals) / len(vals), len(vals)
+
+
+def counters_summary(args):
+    """Prints the traffic record of one kernel from four rocprofv3 --pmc runs:
+    FETCH_SIZE and WRITE_SIZE of the workload, and of the copy calibration."""
+    fetch, nf = _counter_mean(args.pmc_fetch, args.kernel)
+    write, nw = _counter_mean(args.pmc_write, args.kernel)
+    copy_kernel = "copyBuffer"
+    cf, _ = _counter_mean(args.copy_fetch, copy_kernel)
+    cw, _ = _counter_mean(args.copy_write, copy_kernel)
+    copy_bytes = args.copy_calibration << 20
+    fs = copy_bytes / (cf * 1024.0)
+    ws = copy_bytes / (cw * 1024.0)
+    rec = {"workload": args.workload, "kernel": args.kernel,
+           "fetch_kib": round(fetch, 1), "write_kib": round(write, 1),
+           "dispatches": [nf, nw], "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
+           "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+           "bytes": int(round(fetch * 1024 * fs + write * 1024 * ws)),
+           "sources_sha256": sources_digest()}
+    print(TRAFFIC_TAG + json.dumps(rec))
+
+
 def sh_name(sh):
     from synth import WORKLOADS
 
@@ -100,6 +177,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="decode_t1")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="override the workload's token count (a sweep point, not a headline)")
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -108,7 +187,20 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 10 plain device copies of MIB MiB (a known-size reference "
                          "for hardware byte counters) and exit")
+    ap.add_argument("--counters-summary", action="store_true",
+                    help="print the traffic record of --kernel from rocprofv3 --pmc output "
+                         "directories (--pmc-fetch, --pmc-write, --copy-fetch, --copy-write; "
+                         "--copy-calibration gives the copy size) and exit; needs no GPU")
+    ap.add_argument("--kernel", default="")
+    ap.add_argument("--pmc-fetch", default="")
+    ap.add_argument("--pmc-write", default="")
+    ap.add_argument("--copy-fetch", default="")
+    ap.add_argument("--copy-write", default="")
     args = ap.parse_args()
+
+    if args.counters_summary:
+        counters_summary(args)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this layer build runs on a single MI355X "
@@ -137,6 +229,8 @@ def main():
         sys.exit(2)
     md.lib()  # fails loudly when the HIP library is missing
     sh = WORKLOADS[args.workload]
+    if args.tokens:
+        sh = sh.replace(T=args.tokens)
     T, H, E, k = sh.T, sh.H, sh.E, sh.k
     log("workload", args.workload, sh)
 
@@ -263,30 +357,46 @@ def main():
             b.record(s)
             e.record(s)
         torch.cuda.synchronize()
+        # The launches queue up behind a GPU-side spin, so that they run back
+        # to back and host submission time never falls inside a bracket.
+        torch.cuda._sleep(int(2.5e8))
         for i, (b, e) in enumerate(evs):
             plan.set_expert_events(b, e)
             plan.run_args(arg_sets[i % copies], T)
         plan.set_expert_events(None, None)
+        queued_ahead = not s.query()
     torch.cuda.synchronize()
     kern_ms = float(np.mean([b.elapsed_time(e) for b, e in evs]))
+    if not queued_ahead:
+        log("note: the GPU caught up with the host during the bracketed launches")
     path_taken = plan.path_for(T)
+    e8 = "true" if sh.scale_fmt == "e8m0" else "false"
     if path_taken == md.PATH_GEMV:
         # one persistent kernel runs the whole step: its bytes are the step's
-        kern_name = "fused decode kernel (router, shared + routed experts, boundary)"
+        kern_name = "decode_fused_kernel (router, shared + routed experts, boundary)"
+        kern_id = "decode_fused_kernel<"
         kern_bytes = metric_bytes + E * H * 2
     else:
         # routed gate/up projection: touched experts' w13 + scales, the token
         # rows in, the SwiGLU rows out (f32, or hi + lo bf16 planes)
         if path_taken == md.PATH_GROUPED:
-            kern_name = "gate_up_mfma_kernel<U, E8, SHARED=false> (routed experts)"
+            kern_name = "gate_up_mfma_kernel<U, GR, E8, SHARED=false> (routed experts)"
+            kern_id = "gate_up_mfma_kernel<2, 1, %s, false>" % e8
         else:
             kern_name = "gate_up_kernel<NJ, E8, SHARED=false> (routed experts)"
+            kern_id = "gate_up_kernel<%d, %s, false>" % ((H + 1023) // 1024, e8)
         sb = 1 if sh.scale_fmt == "e8m0" else 4
         kern_bytes = (D * (2 * sh.I * H + sb * (2 * sh.I // 128) * (H // 128))
                       + T * H * 2 + T * k * sh.I * 4)
     achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
     log("%s: %.2f us avg over %d launches, %.1f GB/s" % (kern_name, kern_ms * 1e3, n_ev,
                                                          achieved))
+
+    trec = recorded_traffic(args.workload if not args.tokens else "%s@T%d" % (args.workload, T),
+                            kern_id)
+    traffic = trec["bytes"] if trec else None
+    log("traffic record: %s" % ("bytes %d (%.3f x algorithmic)" % (traffic, traffic / kern_bytes)
+                                if trec else "none for the current sources"))
 
     rec = {
         "metric": METRIC,
@@ -304,7 +414,7 @@ def main():
         "dtype": "fp8e4m3 weights x bf16 activations, f32 accumulate",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(K)) fp8 block-quantised weights)",
         "config": {
-            "workload": args.workload, "tokens": T, "hidden": H, "experts": E, "top_k": k,
+            "workload": args.workload + ("" if not args.tokens else "@T%d" % T), "tokens": T, "hidden": H, "experts": E, "top_k": k,
             "intermediate": sh.I, "shared_intermediate": sh.Is, "scale_fmt": sh.scale_fmt,
             "distinct_experts": D, "metric_bytes_per_step": metric_bytes,
             "router_bytes": E * H * 2, "weight_copies": copies,
@@ -318,8 +428,9 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "bytes_per_launch": kern_bytes,
+            "kernel_id": kern_id,
             "avg_launch_us": round(kern_ms * 1e3, 3),
         },
         "check": {"ids_match": bool(ids_ok), "row0_rel_l2": rel0},

@@ -69,13 +69,20 @@ typedef enum { MOE_DECODE_SCALE_FP32 = 0, MOE_DECODE_SCALE_E8M0 = 1 } moe_decode
 
 /* Expert kernel family.  AUTO picks by token count; the others force one. */
 typedef enum {
-  MOE_DECODE_PATH_AUTO = 0, /* the fastest measured path for the token count */
+  /* The faster path for the token count as measured on MI355X: GEMV_SPLIT
+   * below 8 tokens, GROUPED from 8 tokens on. */
+  MOE_DECODE_PATH_AUTO = 0,
   /* fp8 dequant-FMA GEMV, one weight pass per touched expert.  Up to 16
    * tokens the whole step is one persistent kernel (router, shared expert,
    * routed experts and boundary as ordered work items); above that the
    * GEMV_SPLIT kernels run. */
   MOE_DECODE_PATH_GEMV = 1,
-  MOE_DECODE_PATH_GROUPED = 2,   /* fp8 MFMA over expert-grouped tokens */
+  /* Tokens grouped by expert on the matrix cores: exactly converted fp8
+   * weights (staged through LDS) times bf16 activations in
+   * v_mfma_f32_16x16x32_bf16, fp32 accumulation per 128-wide scale block;
+   * the SwiGLU output goes to the down projection as hi + lo bf16 parts.
+   * Same kernel sequence and streams as GEMV_SPLIT. */
+  MOE_DECODE_PATH_GROUPED = 2,
   /* The GEMV kernels launched one after another (router, gate_up, down,
    * boundary), the shared expert on the plan's side stream. */
   MOE_DECODE_PATH_GEMV_SPLIT = 3
@@ -185,8 +192,8 @@ int moe_decode_last_routes(moe_decode_plan_t p, int32_t T, int32_t* counts, int3
  * Measurement hook: when both are non-NULL, each later run records hipEvent_t
  * `begin` on `stream` just before its dominant kernel and `end` just after
  * it: the fused persistent kernel on MOE_DECODE_PATH_GEMV, the routed-expert
- * gate/up projection kernel on MOE_DECODE_PATH_GEMV_SPLIT.  NULL, NULL
- * switches it off.
+ * gate/up projection kernel on MOE_DECODE_PATH_GEMV_SPLIT and
+ * MOE_DECODE_PATH_GROUPED.  NULL, NULL switches it off.
  */
 int moe_decode_set_expert_events(moe_decode_plan_t p, void* begin, void* end);
 

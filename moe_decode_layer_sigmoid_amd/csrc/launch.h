@@ -70,8 +70,9 @@ __host__ __device__ constexpr size_t router_cnt_words() {
 }
 
 constexpr int kFusedMaxTokens = 16;
-// AUTO takes the MFMA projections from this many tokens on.
-constexpr int kGroupedMinTokens = 32;
+// AUTO takes the MFMA projections from this many tokens on (at 8 to 12
+// tokens the two paths measure the same on MI355X; from 16 on MFMA wins).
+constexpr int kGroupedMinTokens = 8;
 
 // Arguments of the fused persistent kernel (see decode_fused.hip).
 struct FusedArgs {
