@@ -379,15 +379,15 @@ def main():
     else:
         # routed gate/up projection: touched experts' w13 + scales, the token
         # rows in, the SwiGLU rows out (f32, or hi + lo bf16 planes)
+        sb = 1 if sh.scale_fmt == "e8m0" else 4
+        kern_bytes = (D * (2 * sh.I * H + sb * (2 * sh.I // 128) * (H // 128))
+                      + T * H * 2 + T * k * sh.I * 4)
         if path_taken == md.PATH_GROUPED:
             kern_name = "gate_up_mfma_kernel<U, GR, E8, SHARED=false> (routed experts)"
             kern_id = "gate_up_mfma_kernel<2, 1, %s, false>" % e8
         else:
-            kern_name = "gate_up_kernel<NJ, E8, SHARED=false> (routed experts)"
-            kern_id = "gate_up_kernel<%d, %s, false>" % ((H + 1023) // 1024, e8)
-        sb = 1 if sh.scale_fmt == "e8m0" else 4
-        kern_bytes = (D * (2 * sh.I * H + sb * (2 * sh.I // 128) * (H // 128))
-                      + T * H * 2 + T * k * sh.I * 4)
+            kern_name = "gate_up_kernel<NJ, E8> (routed experts)"
+            kern_id = "gate_up_kernel<%d, %s>" % ((H + 1023) // 1024, e8)
     achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
     log("%s: %.2f us avg over %d launches, %.1f GB/s" % (kern_name, kern_ms * 1e3, n_ev,
                                                          achieved))

@@ -270,31 +270,49 @@ static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t 
                          hipStream_t s) {
   const int path = path_for(*p, T);
   if (path == MOE_DECODE_PATH_GEMV) return run_fused(p, a, T, s);
-  const bool mfma = path == MOE_DECODE_PATH_GROUPED;
-  const auto gate_up = mfma ? moe::launch_gate_up_mfma : moe::launch_gate_up_gemv;
-  const auto down = mfma ? moe::launch_down_mfma : moe::launch_down_gemv;
   const moe::LayerDims d = dims(p->desc, T);
   const bool has_shared = d.Is > 0;
-
-  if (hipEventRecord(p->fork, s) != hipSuccess) return MOE_DECODE_ERR_HIP;
-  if (hipStreamWaitEvent(p->side, p->fork, 0) != hipSuccess) return MOE_DECODE_ERR_HIP;
-
+  const void* bias = a->router_bias ? a->router_bias : p->ws.zero_bias;
   hipError_t err = hipSuccess;
   auto step = [&](hipError_t e) {
     if (err == hipSuccess && e != hipSuccess) err = e;
   };
-  if (has_shared) {
-    step(gate_up(d, true, a->hidden, a->sw13, a->sw13_scale, p->ws, p->side));
-    if (err == hipSuccess) step(down(d, true, a->sw2, a->sw2_scale, p->ws, p->side));
+
+  if (path == MOE_DECODE_PATH_GEMV_SPLIT) {
+    // router (with the shared expert's gate_up beside it), the routed
+    // gate_up, then the shared and routed down projections in one launch
+    step(moe::launch_router(d, a->hidden, a->router_w, static_cast<const float*>(bias), p->ws,
+                            a->topk_ids, a->topk_weights, has_shared ? a->sw13 : nullptr,
+                            a->sw13_scale, s));
+    if (err == hipSuccess && p->user_begin) step(hipEventRecord(p->user_begin, s));
+    if (err == hipSuccess)
+      step(moe::launch_gate_up_gemv(d, a->hidden, a->w13, a->w13_scale, p->ws, s));
+    if (err == hipSuccess && p->user_end) step(hipEventRecord(p->user_end, s));
+    if (err == hipSuccess)
+      step(moe::launch_down_gemv(d, a->w2, a->w2_scale, a->sw2, a->sw2_scale, p->ws, s));
+    if (err == hipSuccess)
+      step(moe::launch_epilogue(d, a->residual, a->gamma, p->ws, a->out, a->residual_out, s));
+    return err == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;
   }
-  if (err == hipSuccess)
-    step(moe::launch_router(d, a->hidden, a->router_w,
-                            a->router_bias ? a->router_bias : p->ws.zero_bias, p->ws, a->topk_ids,
-                            a->topk_weights, s));
+
+  // GROUPED: the shared expert on the side stream, forked once the router is
+  // queued (it then streams beside the routed experts, not beside the
+  // latency-bound router) and joined before the boundary.
+  step(moe::launch_router(d, a->hidden, a->router_w, static_cast<const float*>(bias), p->ws,
+                          a->topk_ids, a->topk_weights, nullptr, nullptr, s));
+  if (err != hipSuccess) return MOE_DECODE_ERR_HIP;
+  if (hipEventRecord(p->fork, s) != hipSuccess) return MOE_DECODE_ERR_HIP;
+  if (hipStreamWaitEvent(p->side, p->fork, 0) != hipSuccess) return MOE_DECODE_ERR_HIP;
+  if (has_shared) {
+    step(moe::launch_gate_up_mfma(d, true, a->hidden, a->sw13, a->sw13_scale, p->ws, p->side));
+    if (err == hipSuccess)
+      step(moe::launch_down_mfma(d, true, a->sw2, a->sw2_scale, p->ws, p->side));
+  }
   if (err == hipSuccess && p->user_begin) step(hipEventRecord(p->user_begin, s));
-  if (err == hipSuccess) step(gate_up(d, false, a->hidden, a->w13, a->w13_scale, p->ws, s));
+  if (err == hipSuccess)
+    step(moe::launch_gate_up_mfma(d, false, a->hidden, a->w13, a->w13_scale, p->ws, s));
   if (err == hipSuccess && p->user_end) step(hipEventRecord(p->user_end, s));
-  if (err == hipSuccess) step(down(d, false, a->w2, a->w2_scale, p->ws, s));
+  if (err == hipSuccess) step(moe::launch_down_mfma(d, false, a->w2, a->w2_scale, p->ws, s));
 
   // Join the side stream on every path, then run the boundary.
   hipError_t jerr = hipEventRecord(p->join, p->side);

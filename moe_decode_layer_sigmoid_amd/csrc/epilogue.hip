@@ -10,25 +10,100 @@
 // rows and is added with weight 1.  With one GPU there is no all-reduce in it.
 //
 // One workgroup per token; each thread owns 8 consecutive hidden elements
-// per pass and keeps its sums in registers between the two halves (sum of
-// squares, then scaling), so h is read once.  Sums run in a fixed order
-// (routes j = 0..k-1, shared, residual; waves 0..3), so results are
-// bitwise reproducible.
+// and keeps its sums in registers between the two halves (sum of squares,
+// then scaling), so h is read once.  Sums run in a fixed order, so results
+// are bitwise reproducible.
 #include "device_common.h"
-#include "gemv_tiles.h"
 #include "launch.h"
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;  // 8 columns per thread: H <= 8192 in one pass
+constexpr int kCols = 8;
+constexpr int kGroup = 8;        // routes whose rows one round of loads fetches
 
+// One workgroup per token.  Every load (top-k weights, the first kGroup
+// routed rows, the shared row, the residual and gamma) is issued before the
+// first is used, and addresses are clamped instead of branched around, so
+// the common case (k <= 8) costs one memory round trip before the sum of
+// squares.  Sums run in a fixed order: routes j = 0..k-1, shared, residual;
+// waves 0..15 for the sum of squares.
 __global__ __launch_bounds__(kThreads) void epilogue_kernel(
     const uint16_t* residual, const uint16_t* __restrict__ gamma, int H, int k, int has_shared,
     float eps, Workspace ws, uint16_t* out, uint16_t* residual_out) {
   __shared__ float s_part[kThreads / kWave];
-  epilogue_token(blockIdx.x, residual, gamma, H, k, has_shared != 0, eps, ws, out, residual_out,
-                 s_part);
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = kCols * threadIdx.x;
+  const bool live = c < H;
+  const int c0 = live ? c : H - kCols;  // clamped: loads stay in the row
+  const float* rows_t = ws.rows + static_cast<size_t>(t) * k * H + c0;
+  const float* ys = ws.y_s + static_cast<size_t>(t) * H + c0;
+  const uint4 rv = *reinterpret_cast<const uint4*>(residual + static_cast<size_t>(t) * H + c0);
+  const uint4 gv = *reinterpret_cast<const uint4*>(gamma + c0);
+  const float4 ya = *reinterpret_cast<const float4*>(ys);
+  const float4 yb = *reinterpret_cast<const float4*>(ys + 4);
+  float acc[kCols];
+#pragma unroll
+  for (int m = 0; m < kCols; ++m) acc[m] = 0.f;
+  for (int j0 = 0; j0 < k; j0 += kGroup) {
+    float wj[kGroup];
+    float4 ra[kGroup], rb[kGroup];
+#pragma unroll
+    for (int q = 0; q < kGroup; ++q) {
+      const int j = j0 + q < k ? j0 + q : k - 1;
+      const float w = ws.weights[t * k + j];
+      wj[q] = j0 + q < k ? w : 0.f;
+      ra[q] = *reinterpret_cast<const float4*>(rows_t + static_cast<size_t>(j) * H);
+      rb[q] = *reinterpret_cast<const float4*>(rows_t + static_cast<size_t>(j) * H + 4);
+    }
+#pragma unroll
+    for (int q = 0; q < kGroup; ++q) {
+      acc[0] = fmaf(wj[q], ra[q].x, acc[0]);
+      acc[1] = fmaf(wj[q], ra[q].y, acc[1]);
+      acc[2] = fmaf(wj[q], ra[q].z, acc[2]);
+      acc[3] = fmaf(wj[q], ra[q].w, acc[3]);
+      acc[4] = fmaf(wj[q], rb[q].x, acc[4]);
+      acc[5] = fmaf(wj[q], rb[q].y, acc[5]);
+      acc[6] = fmaf(wj[q], rb[q].z, acc[6]);
+      acc[7] = fmaf(wj[q], rb[q].w, acc[7]);
+    }
+  }
+  if (has_shared) {
+    acc[0] += ya.x; acc[1] += ya.y; acc[2] += ya.z; acc[3] += ya.w;
+    acc[4] += yb.x; acc[5] += yb.y; acc[6] += yb.z; acc[7] += yb.w;
+  }
+  const uint32_t u[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    acc[2 * m] += bf16_lo(u[m]);
+    acc[2 * m + 1] += bf16_hi(u[m]);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int m = 0; m < kCols; ++m) ss = fmaf(acc[m], acc[m], ss);
+  ss = wave_sum(live ? ss : 0.f);
+  if (lane == 0) s_part[wave] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kThreads / kWave; ++w) tot += s_part[w];
+  const float inv_rms = 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
+  if (!live) return;
+  const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
+  uint32_t o[4], r[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float h0 = acc[2 * m], h1 = acc[2 * m + 1];
+    o[m] = f32_to_bf16(h0 * inv_rms * bf16_lo(g[m])) |
+           (f32_to_bf16(h1 * inv_rms * bf16_hi(g[m])) << 16);
+    r[m] = f32_to_bf16(h0) | (f32_to_bf16(h1) << 16);
+  }
+  *reinterpret_cast<uint4*>(out + static_cast<size_t>(t) * H + c) =
+      make_uint4(o[0], o[1], o[2], o[3]);
+  *reinterpret_cast<uint4*>(residual_out + static_cast<size_t>(t) * H + c) =
+      make_uint4(r[0], r[1], r[2], r[3]);
 }
 
 }  // namespace

@@ -15,9 +15,10 @@
 // wave reduction finishes every row.  gate_up fuses the clamped SwiGLU into
 // its epilogue; down writes one fp32 row per route.
 //
-// Grid: x = row tiles of one expert, y = touched-expert slot (routed; slots
-// past the step's touched count exit at once, so the grid size depends only
-// on T and the launch can be captured) or a single row for the shared expert.
+// Grid: x = row tiles of one expert, y = slot.  gate_up: the touched
+// experts (the shared expert's gate_up runs in the router launch).  down:
+// the shared expert first (one more expert with all T tokens and weight 1),
+// then the touched experts.  No second stream is needed on this path.
 #include "device_common.h"
 #include "gemv_tiles.h"
 #include "launch.h"
@@ -28,101 +29,88 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 
-// Per-slot expert, token count and permuted base position.
-struct SlotInfo {
+// One slot of the grid's y dimension: row 0 is the shared expert (when
+// there is one), the next rows the touched experts in ascending id (rows
+// past the step's touched count exit at once, so the grid size depends only
+// on T and the launch can be captured).
+struct Slot {
+  bool shared;
   int e, n, base;
 };
 
-template <bool SHARED>
-__device__ __forceinline__ bool slot_info(int T, const Workspace& ws, SlotInfo* si) {
-  if (SHARED) {
-    *si = {0, T, 0};
+__device__ __forceinline__ bool slot_of(int T, int Is, const Workspace& ws, Slot* s) {
+  const int y = static_cast<int>(blockIdx.y);
+  if (Is > 0 && y == 0) {
+    *s = {true, 0, T, 0};
     return true;
   }
-  const int d = blockIdx.y;
+  const int d = Is > 0 ? y - 1 : y;
   if (d >= *ws.n_touched) return false;
   const int e = ws.touched[d];
-  *si = {e, ws.counts[e], ws.offsets[e]};
+  *s = {false, e, ws.counts[e], ws.offsets[e]};
   return true;
 }
 
-// SHARED: the shared expert (a separate instantiation, so that profiles tell
-// the routed and shared launches apart).
-template <int NJ, bool E8, bool SHARED>
+// gate_up + clamped SwiGLU of the touched experts: a wave owns SwiGLU
+// outputs i0, i0 + 1 of its slot's expert (grid row = touched slot).
+template <int NJ, bool E8>
 __global__ __launch_bounds__(kThreads) void gate_up_kernel(
     const uint16_t* __restrict__ hidden, const uint8_t* __restrict__ w13,
     const void* __restrict__ scale, int H, int I, int k, int T, Workspace ws, float limit) {
   const int wave = threadIdx.x >> 6;
   const int i0 = (blockIdx.x * kWaves + wave) * 2;
-  const bool shared = SHARED;
-  SlotInfo si;
-  if (!slot_info<SHARED>(T, ws, &si) || i0 >= I) return;
+  Slot sl;
+  if (!slot_of(T, 0, ws, &sl) || i0 >= I) return;
   const size_t rows_per_e = static_cast<size_t>(2) * I;
-  const uint8_t* W = w13 + static_cast<size_t>(si.e) * rows_per_e * H;
-  const size_t sbase = static_cast<size_t>(si.e) * (rows_per_e / kBlock) * (H / kBlock);
-  gate_up_wave<NJ, 1, false, E8>(hidden, W, scale, sbase, H, I, i0, si.n,
-                                  shared ? nullptr : ws.perm, si.base, k,
-                                  shared ? ws.act_s : ws.act, limit);
+  const uint8_t* W = w13 + static_cast<size_t>(sl.e) * rows_per_e * H;
+  const size_t sbase = static_cast<size_t>(sl.e) * (rows_per_e / kBlock) * (H / kBlock);
+  gate_up_wave<NJ, 1, false, E8>(hidden, W, scale, sbase, H, I, i0, sl.n, ws.perm, sl.base, k,
+                                  ws.act, limit);
 }
 
-template <int NJ, bool E8, bool SHARED>
+// down projection of the routed experts and the shared expert in one
+// launch: a wave owns output rows h0 .. h0 + 3 of its slot's expert.
+// Routed rows land at their route index (t*k + j), shared rows at t.
+template <int NJ, bool E8>
 __global__ __launch_bounds__(kThreads) void down_kernel(
-    const uint8_t* __restrict__ w2, const void* __restrict__ scale, int H, int I, int T,
-    Workspace ws) {
+    const uint8_t* __restrict__ w2, const void* __restrict__ scale,
+    const uint8_t* __restrict__ sw2, const void* __restrict__ sscale, int H, int I, int Is,
+    int T, Workspace ws) {
   const int wave = threadIdx.x >> 6;
   const int h0 = (blockIdx.x * kWaves + wave) * 4;
-  const bool shared = SHARED;
-  SlotInfo si;
-  if (!slot_info<SHARED>(T, ws, &si) || h0 >= H) return;
-  const uint8_t* W = w2 + static_cast<size_t>(si.e) * H * I;
-  const size_t sbase = static_cast<size_t>(si.e) * (H / kBlock) * (I / kBlock);
-  down_wave<NJ, 1, false, E8>(W, scale, sbase, H, I, h0, si.n, si.base,
-                              shared ? nullptr : ws.perm, shared ? ws.act_s : ws.act,
-                              shared ? ws.y_s : ws.rows);
-}
-
-template <int NJ, bool E8>
-void launch_gu(dim3 grid, hipStream_t s, bool shared, const uint16_t* x, const uint8_t* w,
-               const void* scale, const LayerDims& d, int I, const Workspace& ws) {
-  if (shared)
-    hipLaunchKernelGGL((gate_up_kernel<NJ, E8, true>), grid, dim3(kThreads), 0, s, x, w, scale,
-                       d.H, I, d.k, d.T, ws, d.limit);
-  else
-    hipLaunchKernelGGL((gate_up_kernel<NJ, E8, false>), grid, dim3(kThreads), 0, s, x, w, scale,
-                       d.H, I, d.k, d.T, ws, d.limit);
-}
-
-template <int NJ, bool E8>
-void launch_dn(dim3 grid, hipStream_t s, bool shared, const uint8_t* w, const void* scale,
-               const LayerDims& d, int I, const Workspace& ws) {
-  if (shared)
-    hipLaunchKernelGGL((down_kernel<NJ, E8, true>), grid, dim3(kThreads), 0, s, w, scale, d.H, I,
-                       d.T, ws);
-  else
-    hipLaunchKernelGGL((down_kernel<NJ, E8, false>), grid, dim3(kThreads), 0, s, w, scale, d.H,
-                       I, d.T, ws);
+  Slot sl;
+  if (!slot_of(T, Is, ws, &sl) || h0 >= H) return;
+  const int II = sl.shared ? Is : I;
+  const uint8_t* W = sl.shared ? sw2 : w2 + static_cast<size_t>(sl.e) * H * II;
+  const size_t sbase = static_cast<size_t>(sl.e) * (H / kBlock) * (II / kBlock);
+  down_wave<NJ, 1, false, E8>(W, sl.shared ? sscale : scale, sbase, H, II, h0, sl.n, sl.base,
+                              sl.shared ? nullptr : ws.perm, sl.shared ? ws.act_s : ws.act,
+                              sl.shared ? ws.y_s : ws.rows);
 }
 
 }  // namespace
 
 #define MOE_NJ_CASES(X) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8)
 
-hipError_t launch_gate_up_gemv(const LayerDims& d, bool shared, const void* hidden,
-                               const void* w13, const void* w13_scale, const Workspace& ws,
-                               hipStream_t s) {
-  const int I = shared ? d.Is : d.I;
+static int slot_rows(const LayerDims& d) {
+  return (d.T * d.k < d.E ? d.T * d.k : d.E) + (d.Is > 0 ? 1 : 0);
+}
+
+hipError_t launch_gate_up_gemv(const LayerDims& d, const void* hidden, const void* w13,
+                               const void* w13_scale, const Workspace& ws, hipStream_t s) {
   const int nj = (d.H + 1023) / 1024;
-  const int slots = shared ? 1 : (d.T * d.k < d.E ? d.T * d.k : d.E);
-  dim3 grid(I / (2 * kWaves), slots);
+  dim3 grid(d.I / (2 * kWaves), d.T * d.k < d.E ? d.T * d.k : d.E);
   const auto* x = static_cast<const uint16_t*>(hidden);
   const auto* w = static_cast<const uint8_t*>(w13);
   switch (nj * 2 + (d.e8m0 ? 1 : 0)) {
-#define X(N)                                                              \
-  case 2 * N:                                                             \
-    launch_gu<N, false>(grid, s, shared, x, w, w13_scale, d, I, ws);      \
-    break;                                                                \
-  case 2 * N + 1:                                                         \
-    launch_gu<N, true>(grid, s, shared, x, w, w13_scale, d, I, ws);       \
+#define X(N)                                                                                  \
+  case 2 * N:                                                                                 \
+    hipLaunchKernelGGL((gate_up_kernel<N, false>), grid, dim3(kThreads), 0, s, x, w, w13_scale, \
+                       d.H, d.I, d.k, d.T, ws, d.limit);                                      \
+    break;                                                                                    \
+  case 2 * N + 1:                                                                             \
+    hipLaunchKernelGGL((gate_up_kernel<N, true>), grid, dim3(kThreads), 0, s, x, w, w13_scale,  \
+                       d.H, d.I, d.k, d.T, ws, d.limit);                                      \
     break;
     MOE_NJ_CASES(X)
 #undef X
@@ -132,20 +120,23 @@ hipError_t launch_gate_up_gemv(const LayerDims& d, bool shared, const void* hidd
   return hipGetLastError();
 }
 
-hipError_t launch_down_gemv(const LayerDims& d, bool shared, const void* w2,
-                            const void* w2_scale, const Workspace& ws, hipStream_t s) {
-  const int I = shared ? d.Is : d.I;
-  const int nj = (I + 1023) / 1024;
-  const int slots = shared ? 1 : (d.T * d.k < d.E ? d.T * d.k : d.E);
-  dim3 grid(d.H / (4 * kWaves), slots);
+hipError_t launch_down_gemv(const LayerDims& d, const void* w2, const void* w2_scale,
+                            const void* sw2, const void* sw2_scale, const Workspace& ws,
+                            hipStream_t s) {
+  const int Imax = d.I > d.Is ? d.I : d.Is;
+  const int nj = (Imax + 1023) / 1024;  // chunks past a row's end are masked
+  dim3 grid(d.H / (4 * kWaves), slot_rows(d));
   const auto* w = static_cast<const uint8_t*>(w2);
+  const auto* sw = static_cast<const uint8_t*>(sw2);
   switch (nj * 2 + (d.e8m0 ? 1 : 0)) {
-#define X(N)                                                     \
-  case 2 * N:                                                    \
-    launch_dn<N, false>(grid, s, shared, w, w2_scale, d, I, ws); \
-    break;                                                       \
-  case 2 * N + 1:                                                \
-    launch_dn<N, true>(grid, s, shared, w, w2_scale, d, I, ws);  \
+#define X(N)                                                                                   \
+  case 2 * N:                                                                                  \
+    hipLaunchKernelGGL((down_kernel<N, false>), grid, dim3(kThreads), 0, s, w, w2_scale, sw,    \
+                       sw2_scale, d.H, d.I, d.Is, d.T, ws);                                    \
+    break;                                                                                     \
+  case 2 * N + 1:                                                                              \
+    hipLaunchKernelGGL((down_kernel<N, true>), grid, dim3(kThreads), 0, s, w, w2_scale, sw,     \
+                       sw2_scale, d.H, d.I, d.Is, d.T, ws);                                    \
     break;
     MOE_NJ_CASES(X)
 #undef X

@@ -62,8 +62,8 @@ __host__ __device__ constexpr size_t sync_words(int E) {
 
 // Arrival counters of the router kernel in Workspace::counter: one 128-byte
 // line per block of kRouterTokBlk tokens, then one for the token blocks.
-constexpr int kRouterTokBlk = 8;
-constexpr int kRouterMaxBlk = 32;  // 256 tokens
+constexpr int kRouterTokBlk = 4;   // one token per wave when ranking
+constexpr int kRouterMaxBlk = 64;  // 256 tokens
 __host__ __device__ constexpr int router_cnt_line(int b) { return b * kSyncStride; }
 __host__ __device__ constexpr size_t router_cnt_words() {
   return static_cast<size_t>(kRouterMaxBlk + 1) * kSyncStride;
@@ -107,20 +107,22 @@ struct LayerDims {
   float limit, rsf, eps;
 };
 
-// Router logits, sigmoid, top-k, weights and the route tables.
+// Router logits, sigmoid, top-k, weights and the route tables; with sw13
+// non-null also the shared expert's gate_up + SwiGLU (into ws.act_s).
 hipError_t launch_router(const LayerDims& d, const void* hidden, const void* router_w,
                          const float* bias, const Workspace& ws, int32_t* ids_out,
-                         float* weights_out, hipStream_t s);
+                         float* weights_out, const void* sw13, const void* sw13_scale,
+                         hipStream_t s);
 
-// gate_up + clamped SwiGLU (GEMV).  Routed: one grid row per touched-expert
-// slot; shared: all tokens through the shared weights.
-hipError_t launch_gate_up_gemv(const LayerDims& d, bool shared, const void* hidden,
-                               const void* w13, const void* w13_scale, const Workspace& ws,
-                               hipStream_t s);
+// gate_up + clamped SwiGLU (GEMV) of the touched experts (one grid row
+// each; the shared expert's runs in the router launch).
+hipError_t launch_gate_up_gemv(const LayerDims& d, const void* hidden, const void* w13,
+                               const void* w13_scale, const Workspace& ws, hipStream_t s);
 
-// down projection (GEMV) of the SwiGLU activations.
-hipError_t launch_down_gemv(const LayerDims& d, bool shared, const void* w2,
-                            const void* w2_scale, const Workspace& ws, hipStream_t s);
+// down projection (GEMV) of the same slots.
+hipError_t launch_down_gemv(const LayerDims& d, const void* w2, const void* w2_scale,
+                            const void* sw2, const void* sw2_scale, const Workspace& ws,
+                            hipStream_t s);
 
 // The same two projections on the matrix cores (bf16 MFMA on exactly
 // converted fp8 weights; SwiGLU activations as hi + lo bf16 planes).

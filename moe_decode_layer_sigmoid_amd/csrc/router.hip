@@ -8,8 +8,10 @@
 // routed_scaling_factor) and LayerStages._mega_moe (the route order table
 // handed to the boundary with the unfinalized rows).
 //
-// Grid: x = blocks of 4 experts (one expert row per wave), y = blocks of
-// kTokB tokens.  Phase 1: every wave loads its whole bf16 router row at once
+// Grid: x = blocks of 4 experts (one expert row per wave), then, when asked,
+// the shared expert's gate_up tiles (8 SwiGLU rows each, grid row 0 only: it
+// depends on no routing, so its weights stream while the router waits on
+// its memory round trips); y = blocks of kRouterTokBlk tokens.  Phase 1: every wave loads its whole bf16 router row at once
 // (one memory round trip), then dots it with the block's token rows.
 // Phase 2: the last workgroup of each token block (an arrival counter per
 // block) ranks that block's tokens, one wave per token.  Phase 3: the last
@@ -27,11 +29,14 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <int NJ2>
+// NJ2 = 16-byte chunks per lane of a bf16 router row (ceil(H / 512)); E8 =
+// e8m0 scales of the shared expert's weights.
+template <int NJ2, bool E8>
 __global__ __launch_bounds__(kThreads) void router_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ router_w,
     const float* __restrict__ bias, int T, int H, int E, int k, float rsf, Workspace ws,
-    int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out, int n_router,
+    const uint8_t* __restrict__ sw13, const void* __restrict__ sscale, int Is, float limit) {
   // 16-byte aligned: the 64-bit token masks need 8-byte aligned LDS
   // addresses, and dynamic LDS starts right after the static variables.
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -39,6 +44,18 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
   const int wave = threadIdx.x >> 6;
   const int t0 = blockIdx.y * kRouterTokBlk;
   const int nt = min(kRouterTokBlk, T - t0);
+
+  // ---- columns past the router's: the shared expert's gate_up + SwiGLU,
+  // which needs no routing and so streams in the router's shadow
+  if (static_cast<int>(blockIdx.x) >= n_router) {
+    if (blockIdx.y != 0) return;
+    constexpr int NJ = (NJ2 + 1) / 2;  // 16-byte fp8 chunks per lane = ceil(H / 1024)
+    const int i0 = ((static_cast<int>(blockIdx.x) - n_router) * 4 + wave) * 2;
+    if (i0 < Is)
+      gate_up_wave<NJ, 1, false, E8>(hidden, sw13, sscale, 0, H, Is, i0, T, nullptr, 0, k,
+                                      ws.act_s, limit);
+    return;
+  }
 
   // ---- phase 1: logits of this wave's expert for the block's tokens
   const int e = blockIdx.x * 4 + wave;
@@ -51,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
   uint32_t* cnt = ws.counter + router_cnt_line(blockIdx.y);
   if (threadIdx.x == 0)
     s_last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             gridDim.x - 1;
+             static_cast<uint32_t>(n_router) - 1;
   __syncthreads();
   if (!s_last) return;
 
@@ -80,17 +97,28 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
 
 hipError_t launch_router(const LayerDims& d, const void* hidden, const void* router_w,
                          const float* bias, const Workspace& ws, int32_t* ids_out,
-                         float* weights_out, hipStream_t s) {
+                         float* weights_out, const void* sw13, const void* sw13_scale,
+                         hipStream_t s) {
   if (d.T > kRouterMaxBlk * kRouterTokBlk) return hipErrorInvalidValue;
-  dim3 grid((d.E + 3) / 4, (d.T + kRouterTokBlk - 1) / kRouterTokBlk);
+  const int n_router = (d.E + 3) / 4;
+  const int n_shared = sw13 && d.Is > 0 ? d.Is / 8 : 0;  // 8 SwiGLU rows per workgroup
+  dim3 grid(n_router + n_shared, (d.T + kRouterTokBlk - 1) / kRouterTokBlk);
   const size_t smem = route_smem_bytes(d.T, d.E, d.k);
   const auto* x = static_cast<const uint16_t*>(hidden);
   const auto* w = static_cast<const uint16_t*>(router_w);
-  switch ((d.H + 511) / 512) {
-#define X(N)                                                                                  \
-  case N:                                                                                     \
-    hipLaunchKernelGGL((router_kernel<N>), grid, dim3(kThreads), smem, s, x, w, bias, d.T,    \
-                       d.H, d.E, d.k, d.rsf, ws, ids_out, weights_out);                       \
+  const auto* sw = static_cast<const uint8_t*>(sw13);
+  const int Is = n_shared ? d.Is : 0;
+  switch (((d.H + 511) / 512) * 2 + (d.e8m0 ? 1 : 0)) {
+#define X(N)                                                                                   \
+  case 2 * N:                                                                                  \
+    hipLaunchKernelGGL((router_kernel<N, false>), grid, dim3(kThreads), smem, s, x, w, bias,    \
+                       d.T, d.H, d.E, d.k, d.rsf, ws, ids_out, weights_out, n_router, sw,      \
+                       sw13_scale, Is, d.limit);                                               \
+    break;                                                                                     \
+  case 2 * N + 1:                                                                              \
+    hipLaunchKernelGGL((router_kernel<N, true>), grid, dim3(kThreads), smem, s, x, w, bias,     \
+                       d.T, d.H, d.E, d.k, d.rsf, ws, ids_out, weights_out, n_router, sw,      \
+                       sw13_scale, Is, d.limit);                                               \
     break;
     X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
 #undef X

@@ -44,13 +44,16 @@ __device__ inline int block_exclusive_scan(int v, int* s_tmp, int* total) {
   return base + inc - v;
 }
 
-// One step of the DPP wave maximum of (hi, lo) pairs: lanes take the
-// neighbour's pair named by the DPP control when it is larger.
+// One step of the DPP wave maximum of 64-bit values held as (hi, lo)
+// dwords: lanes take the neighbour's value named by the DPP control when it
+// is larger (one 64-bit compare).
 template <int CTRL, int ROW_MASK, int BANK_MASK>
 __device__ __forceinline__ void dpp_max_step(uint32_t& hi, uint32_t& lo) {
   const uint32_t h2 = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, BANK_MASK, false);
   const uint32_t l2 = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, BANK_MASK, false);
-  const bool take = h2 > hi || (h2 == hi && l2 > lo);
+  const unsigned long long a = (static_cast<unsigned long long>(hi) << 32) | lo;
+  const unsigned long long b = (static_cast<unsigned long long>(h2) << 32) | l2;
+  const bool take = b > a;
   hi = take ? h2 : hi;
   lo = take ? l2 : lo;
 }
@@ -71,49 +74,60 @@ __device__ __forceinline__ void wave_max_pair(uint32_t& hi, uint32_t& lo) {
 }
 
 // Top-k of one token in one wave.  Keys are sigmoid(logit) + bias (bias is
-// never null: a zero vector stands in for no bias); the
-// largest key wins, equal keys go to the lower expert id (a packed
-// (key, ~id) DPP wave maximum, k rounds).  Lane j < k ends with the j-th pick and
-// its weight R * s_j / sum of the k picked scores.
+// never null: a zero vector stands in for no bias); the largest key wins,
+// equal keys go to the lower expert id.  Lane l holds experts l + 64 i
+// (slot i < ceil(E / 64)) as order-preserving key bits, 0 marking a slot
+// that is taken or past E (a real key never maps to 0).  Each of the k
+// rounds takes every lane's best slot (strict >, so the lower slot, i.e. the
+// lower id, wins a tie), then a DPP wave maximum of (key, ~id).  (A radix
+// select over the key bits measures slower on gfx950: its 32 dependent
+// ballot/count steps cost more than k short DPP chains.)  Lane j < k ends
+// with the j-th pick and its weight R * s_j / sum of the k picked scores.
 template <bool C>
 __device__ inline void select_token(const float* logits, const float* bias, int E, int k,
                                     float rsf, int* pick_id, float* pick_w) {
   const int lane = threadIdx.x & 63;
-  float key[16], sc[16];
-  // Branch-free loads (clamped index; slots past E are never picked).
+  const int ns = (E + 63) >> 6;
+  float sc[16];
+  uint32_t kb[16];
+  // Branch-free loads (clamped index).
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int e = lane + 64 * i;
     const int ee = e < E ? e : E - 1;
     const float s = sigmoidf_(ld_f32<C>(logits + ee));
     sc[i] = s;
-    key[i] = s + bias[ee];
+    kb[i] = e < E ? ordered_bits(s + bias[ee]) : 0u;
   }
-  uint32_t taken = 0;
   float ssum = 0.f, my_s = 0.f;
   int my_id = -1;
   for (int j = 0; j < k; ++j) {
-    uint32_t bk = 0, bid = 0;
-    float bs = 0.f;
-    bool have = false;
+    uint32_t bk = kb[0];
+    int bi = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = lane + 64 * i;
-      const bool ok = e < E && !((taken >> i) & 1u);
-      const uint32_t kb = ordered_bits(key[i]);
-      if (ok && (!have || kb > bk)) {
-        have = true;
-        bk = kb;
-        bid = static_cast<uint32_t>(e);
-        bs = sc[i];
-      }
+    for (int i = 1; i < 16; ++i) {
+      if (i >= ns) break;  // uniform
+      const bool take = kb[i] > bk;
+      bk = take ? kb[i] : bk;
+      bi = take ? i : bi;
     }
-    uint32_t hi = have ? bk : 0u;
-    uint32_t lo = have ? (0xffffffffu - bid) : 0u;
+    uint32_t hi = bk;
+    uint32_t lo = bk ? 0xffffffffu - static_cast<uint32_t>(lane + 64 * bi) : 0u;
     wave_max_pair(hi, lo);
     const int win = static_cast<int>(0xffffffffu - lo);
-    const float wsc = __shfl(bs, win & 63, 64);
-    if (lane == (win & 63)) taken |= 1u << (win >> 6);
+    const int wslot = win >> 6, wlane = win & 63;  // uniform
+    float v = sc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      if (i >= ns) break;
+      v = i == wslot ? sc[i] : v;
+    }
+    const float wsc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), wlane));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i >= ns) break;
+      kb[i] = (i == wslot && lane == wlane) ? 0u : kb[i];
+    }
     ssum += wsc;
     if (lane == j) {
       my_id = win;
