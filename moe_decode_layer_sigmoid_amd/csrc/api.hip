@@ -76,6 +76,7 @@ size_t layout(const moe_decode_desc& d, char* base, moe::Workspace* ws) {
   w.counter = reinterpret_cast<uint32_t*>(take(moe::router_cnt_words() * 4));
   w.sync = reinterpret_cast<uint32_t*>(take(moe::sync_words(static_cast<int>(E)) * 4));
   w.zero_bias = reinterpret_cast<float*>(take(E * 4));
+  w.slot_tab = reinterpret_cast<int32_t*>(take(E * moe::kSlotInts * 4));
   if (ws) *ws = w;
   return off;
 }

@@ -122,11 +122,11 @@ __device__ __forceinline__ bool slot_of(int T, const Workspace& ws, Slot* s) {
     *s = {0, T, 0, p, min(T, p + 16 * GR)};
     return p < T;
   }
-  const int d = blockIdx.y;
-  if (d >= *ws.n_touched) return false;
-  const int e = ws.touched[d];
-  const int n = ws.counts[e];
-  *s = {e, n, ws.offsets[e], 0, n};
+  // the router's slot record: expert (-1: none this step), count, base
+  const int4 rec = *reinterpret_cast<const int4*>(ws.slot_tab +
+                                                 static_cast<size_t>(blockIdx.y) * kSlotInts);
+  if (rec.x < 0) return false;
+  *s = {rec.x, rec.y, rec.z, 0, rec.y};
   return true;
 }
 

@@ -24,7 +24,15 @@ struct Workspace {
   uint32_t* counter;   // router arrival counters, router_cnt_words() (self-resetting)
   uint32_t* sync;      // [sync_words(E)] counters of the fused kernel (self-resetting)
   float* zero_bias;    // [E] zeros: the router bias when the caller passes none
+  int32_t* slot_tab;   // [E][kSlotInts] touched slot d: expert (-1: no expert), route
+                       // count, first permuted position, -, first kSlotRoutes routes
 };
+
+// Per-slot record the router leaves for the expert kernels, so that a
+// workgroup finds its expert and its first routes with one load instead of a
+// chain of dependent ones.
+constexpr int kSlotInts = 16;
+constexpr int kSlotRoutes = 12;
 
 // Counters and flags of the fused kernel in Workspace::sync, one 128-byte
 // line each: atomics and polls on one line serialise, separate lines proceed

@@ -144,22 +144,24 @@ __device__ inline void select_token(const float* logits, const float* bias, int 
 __host__ __device__ inline size_t route_smem_bytes(int T, int E, int k) {
   const size_t R = static_cast<size_t>(T) * k, MW = (T + 63) / 64;
   return ((R * 4 + 7) & ~static_cast<size_t>(7)) + static_cast<size_t>(E) * MW * 8 +
-         static_cast<size_t>(E) * 4 + 16;
+         static_cast<size_t>(E) * 8 + 16;
 }
 
 // LDS carve-up of the routing step: s_ids [T*k], token masks [E * MW],
-// offsets [E], scan scratch [4].
+// offsets [E], touched slot of each expert [E], scan scratch [4].
 struct RouteSmem {
   int* ids;
   unsigned long long* mask;
   int* off;
+  int* slot;
   int* tmp;
   __device__ RouteSmem(unsigned char* smem, int T, int E, int k) {
     const size_t R = static_cast<size_t>(T) * k, MW = (T + 63) / 64;
     ids = reinterpret_cast<int*>(smem);
     mask = reinterpret_cast<unsigned long long*>(smem + ((R * 4 + 7) & ~static_cast<size_t>(7)));
     off = reinterpret_cast<int*>(mask + static_cast<size_t>(E) * MW);
-    tmp = off + E;
+    slot = off + E;
+    tmp = slot + E;
   }
 };
 
@@ -187,8 +189,9 @@ __device__ inline void select_tokens(int t_begin, int t_end, int E, int k, float
 }
 
 // Route tables of T tokens from the ids in LDS (sm.ids, all T*k routes), by
-// one 256-thread workgroup: ws.counts/offsets/touched/n_touched/perm/inv
-// (coherent stores when C).  Its first barrier comes before the first read of
+// one 256-thread workgroup: ws.counts/offsets/touched/n_touched/perm/inv and
+// the slot records ws.slot_tab (expert -1 for slots past the touched count,
+// up to min(T*k, E)) (coherent stores when C).  Its first barrier comes before the first read of
 // sm.ids, so callers may fill sm.ids right before the call.
 template <bool C>
 __device__ inline void build_routes(int T, int E, int k, const Workspace& ws,
@@ -227,9 +230,16 @@ __device__ inline void build_routes(int T, int E, int k, const Workspace& ws,
         const int cnt = packed[m] >> 11;
         const int off = run >> 11, tidx = run & 0x7ff;
         sm.off[e] = off;
+        sm.slot[e] = tidx;
         st_i32<C>(ws.counts + e, cnt);
         st_i32<C>(ws.offsets + e, off);
-        if (cnt > 0) st_i32<C>(ws.touched + tidx, e);
+        if (cnt > 0) {
+          st_i32<C>(ws.touched + tidx, e);
+          int32_t* rec = ws.slot_tab + static_cast<size_t>(tidx) * kSlotInts;
+          st_i32<C>(rec, e);
+          st_i32<C>(rec + 1, cnt);
+          st_i32<C>(rec + 2, off);
+        }
       }
       run += packed[m];
     }
@@ -237,6 +247,9 @@ __device__ inline void build_routes(int T, int E, int k, const Workspace& ws,
       st_i32<C>(ws.offsets + E, total >> 11);
       st_i32<C>(ws.n_touched, total & 0x7ff);
     }
+    const int dmax = R < E ? R : E;
+    for (int d = (total & 0x7ff) + static_cast<int>(threadIdx.x); d < dmax; d += kRouteThreads)
+      st_i32<C>(ws.slot_tab + static_cast<size_t>(d) * kSlotInts, -1);
   }
   __syncthreads();
   // Stable position of every route: its expert's offset plus the number of
@@ -250,6 +263,8 @@ __device__ inline void build_routes(int T, int E, int k, const Workspace& ws,
     const int pos = sm.off[e] + rank;
     st_i32<C>(ws.perm + pos, r);
     st_i32<C>(ws.inv + r, pos);
+    if (rank < kSlotRoutes)
+      st_i32<C>(ws.slot_tab + static_cast<size_t>(sm.slot[e]) * kSlotInts + 4 + rank, r);
   }
 }
 
