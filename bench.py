@@ -377,14 +377,18 @@ def main():
         kern_id = "decode_fused_kernel<"
         kern_bytes = metric_bytes + E * H * 2
     else:
-        # routed gate/up projection: touched experts' w13 + scales, the token
-        # rows in, the SwiGLU rows out (f32, or hi + lo bf16 planes)
+        # gate/up projection: touched experts' w13 + scales, the token rows
+        # in, the SwiGLU rows out (f32, or hi + lo bf16 planes)
         sb = 1 if sh.scale_fmt == "e8m0" else 4
         kern_bytes = (D * (2 * sh.I * H + sb * (2 * sh.I // 128) * (H // 128))
                       + T * H * 2 + T * k * sh.I * 4)
         if path_taken == md.PATH_GROUPED:
-            kern_name = "gate_up_mfma_kernel<U, GR, E8, SHARED=false> (routed experts)"
-            kern_id = "gate_up_mfma_kernel<2, 1, %s, false>" % e8
+            # one launch covers the shared expert's token passes as well
+            kern_name = "gate_up_mfma_kernel<U, GR, E8> (routed + shared experts)"
+            kern_id = "gate_up_mfma_kernel<2, 1, %s>" % e8
+            if sh.Is:
+                kern_bytes += (2 * sh.Is * H + sb * (2 * sh.Is // 128) * (H // 128)
+                               + T * sh.Is * 4)
         else:
             kern_name = "gate_up_kernel<NJ, E8> (routed experts)"
             kern_id = "gate_up_kernel<%d, %s>" % ((H + 1023) // 1024, e8)

@@ -22,12 +22,14 @@
  *     LayerStages._build_mega: the fused MoE stage is built only for sigmoid
  *     scoring, one expert group and normalised top-k; its constructor takes
  *     w13/w2 fp8 weights with their block scales, top_k, swiglu_limit,
- *     routed_scaling_factor and the power-of-two (e8m0) scale flag; buffers
- *     and the shared-expert side stream are made once at build time.
- *   - same page, LayerStages._mega_moe: the shared expert runs on a side
- *     stream forked from and joined back to the caller's stream; the routed
- *     rows come back unfinalized with their expert weights and the shared
- *     output beside them; the router bias is handed to the expert kernel.
+ *     routed_scaling_factor and the power-of-two (e8m0) scale flag; its
+ *     buffers are made once at build time.
+ *   - same page, LayerStages._mega_moe: the shared expert runs beside the
+ *     routed experts; the routed rows come back unfinalized with their
+ *     expert weights and the shared output beside them; the router bias is
+ *     handed to the expert kernel.  (There the shared expert has a second
+ *     stream; here its tiles are extra workgroups of the same launches,
+ *     which costs less on MI355X than a fork and join per step.)
  *   - same page, LayerStages._router: router logits in fp32 from a bf16
  *     router weight.
  *   - page "vllm.models.glm5next.nvidia.specialized_decode.runtime.draft",
@@ -81,10 +83,13 @@ typedef enum {
    * weights (staged through LDS) times bf16 activations in
    * v_mfma_f32_16x16x32_bf16, fp32 accumulation per 128-wide scale block;
    * the SwiGLU output goes to the down projection as hi + lo bf16 parts.
-   * Same kernel sequence and streams as GEMV_SPLIT. */
+   * Kernels: router, gate_up (shared expert's 16-token passes and the
+   * touched experts), down (the same), boundary; above 64 tokens the shared
+   * expert's passes run on the plan's side stream instead. */
   MOE_DECODE_PATH_GROUPED = 2,
-  /* The GEMV kernels launched one after another (router, gate_up, down,
-   * boundary), the shared expert on the plan's side stream. */
+  /* The GEMV kernels launched one after another: router (with the shared
+   * expert's gate_up beside it), routed gate_up, down (shared and routed),
+   * boundary. */
   MOE_DECODE_PATH_GEMV_SPLIT = 3
 } moe_decode_path;
 
@@ -151,25 +156,27 @@ int moe_decode_args_check(const moe_decode_desc* d, const moe_decode_args* a, in
 
 /*
  * Builds a plan on HIP device `device`: validates the descriptor, checks the
- * device is gfx950, allocates the workspace for max_tokens, creates the side
- * stream (default priority) and its events.  On success *out owns them until
- * moe_decode_destroy; on failure *out is set to NULL and nothing is leaked.
+ * device is gfx950, allocates the workspace for max_tokens and creates a side
+ * stream (default priority) with two events.  On success *out owns them
+ * until moe_decode_destroy; on failure *out is set to NULL and nothing is
+ * leaked.
  */
 int moe_decode_plan(const moe_decode_desc* d, int device, moe_decode_plan_t* out);
 
 /*
  * Runs the layer for T tokens, asynchronously on `stream` (a hipStream_t of
  * the plan's device; NULL = the null stream).  No allocation and no host
- * synchronisation, so the call may be captured into a HIP graph.  On the
- * split GEMV path the shared expert runs on the plan's side stream, forked
- * from `stream` at entry and joined back before the boundary; the fused path
- * queues it inside its single kernel.  T = 0 returns OK and launches nothing.
- * On an error after the fork the side stream is joined back first.  Runs on
- * one plan must not overlap (they share its workspace).
+ * synchronisation, so the call may be captured into a HIP graph.  Every
+ * kernel goes to `stream`, except the shared expert's on the MFMA path above
+ * 64 tokens: those run on the plan's side stream, forked from `stream` after
+ * the router and joined back before the boundary (also when an error occurs
+ * after the fork).  T = 0 returns OK and launches nothing.  Runs on one plan
+ * must not overlap (they share its workspace).
  */
 int moe_decode_run(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, void* stream);
 
-/* Frees the plan's workspace, side stream and events.  NULL is a no-op. */
+/* Waits for the plan's device, then frees the plan's workspace, side stream
+ * and events.  NULL is a no-op. */
 int moe_decode_destroy(moe_decode_plan_t p);
 
 /* Static text naming a status code. */

@@ -1,14 +1,21 @@
-// C ABI of the MoE decode layer: validation, plan (workspace, side stream,
-// events), run (fork/join of the shared expert, kernel sequence), destroy.
+// C ABI of the MoE decode layer: validation, plan (workspace, events), run
+// (kernel sequence), destroy.
 //
 // Follows the vLLM API page "vllm.models.glm5next.nvidia.specialized_decode.
 // runtime.decode": LayerStages._build_mega allocates the route-order buffer
-// and the shared-expert stream once, before any capture; LayerStages._mega_moe
-// forks the shared expert onto that stream (it waits on the caller's stream)
-// and joins it back (the caller's stream waits on it) after the routed
-// experts.  Page "vllm.models.deepseek_v41.nvidia.specialized_decode.runtime.
-// draft", DraftDecode.run: on an error the side stream is rejoined before the
-// error is reported, so a graph capture sees no unjoined work.
+// and its other buffers once, before any capture, and LayerStages._mega_moe
+// runs the shared expert beside the routed experts.  There the shared expert
+// gets a second stream; on MI355X a fork and join inside a HIP graph cost
+// about 5 and 10 us per step (measured), more than running the shared
+// expert's tiles as extra workgroups of the same launches, which is what
+// this library does up to 64 tokens: its gate_up rides in the router launch
+// (GEMV path) or in the routed gate_up launch (MFMA path), its down
+// projection in the routed down launch.  Above 64 tokens the shared expert
+// needs several passes over its weights and runs on the plan's side stream
+// (default priority), forked after the router and joined before the
+// boundary; an error after the fork still joins it, as the page "vllm.
+// models.deepseek_v41.nvidia.specialized_decode.runtime.draft",
+// DraftDecode.run, rejoins its side stream before reporting.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -25,7 +32,8 @@ struct moe_decode_plan_s {
   void* ws_base;
   size_t ws_bytes;
   moe::Workspace ws;
-  hipStream_t side;
+  hipStream_t side;      // the shared expert's stream on the MFMA path above
+                         // kMergeSharedMaxTokens tokens
   hipEvent_t fork, join;
   hipEvent_t user_begin, user_end;
   uint32_t fused_grid;  // workgroups of the fused kernel (0: fused path unavailable)
@@ -220,7 +228,10 @@ int moe_decode_destroy(moe_decode_plan_t p) {
   if (p->fork) (void)hipEventDestroy(p->fork);
   if (p->join) (void)hipEventDestroy(p->join);
   if (p->side) (void)hipStreamDestroy(p->side);
-  if (p->ws_base) (void)hipFree(p->ws_base);
+  if (p->ws_base) {
+    (void)hipDeviceSynchronize();  // no launch of this plan may still use the workspace
+    (void)hipFree(p->ws_base);
+  }
   (void)hipSetDevice(prev);
   delete p;
   return MOE_DECODE_OK;
@@ -296,29 +307,39 @@ static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t 
     return err == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;
   }
 
-  // GROUPED: the shared expert on the side stream, forked once the router is
-  // queued (it then streams beside the routed experts, not beside the
-  // latency-bound router) and joined before the boundary.
+  // GROUPED: router, the projections, the boundary.  Up to
+  // kMergeSharedMaxTokens tokens the shared expert's passes are extra rows of
+  // the routed launches; above that they run on the side stream, forked once
+  // the router is queued and joined before the boundary.
   step(moe::launch_router(d, a->hidden, a->router_w, static_cast<const float*>(bias), p->ws,
                           a->topk_ids, a->topk_weights, nullptr, nullptr, s));
   if (err != hipSuccess) return MOE_DECODE_ERR_HIP;
-  if (hipEventRecord(p->fork, s) != hipSuccess) return MOE_DECODE_ERR_HIP;
-  if (hipStreamWaitEvent(p->side, p->fork, 0) != hipSuccess) return MOE_DECODE_ERR_HIP;
-  if (has_shared) {
-    step(moe::launch_gate_up_mfma(d, true, a->hidden, a->sw13, a->sw13_scale, p->ws, p->side));
+  const bool side = has_shared && T > moe::kMergeSharedMaxTokens;
+  const int rows = side ? moe::kRoutedRows : moe::kAllRows;
+  const void* sw13 = has_shared ? a->sw13 : nullptr;
+  const void* sw2 = has_shared ? a->sw2 : nullptr;
+  if (side) {
+    if (hipEventRecord(p->fork, s) != hipSuccess) return MOE_DECODE_ERR_HIP;
+    if (hipStreamWaitEvent(p->side, p->fork, 0) != hipSuccess) return MOE_DECODE_ERR_HIP;
+    step(moe::launch_gate_up_mfma(d, moe::kSharedRows, a->hidden, a->w13, a->w13_scale, sw13,
+                                  a->sw13_scale, p->ws, p->side));
     if (err == hipSuccess)
-      step(moe::launch_down_mfma(d, true, a->sw2, a->sw2_scale, p->ws, p->side));
+      step(moe::launch_down_mfma(d, moe::kSharedRows, a->w2, a->w2_scale, sw2, a->sw2_scale,
+                                 p->ws, p->side));
   }
   if (err == hipSuccess && p->user_begin) step(hipEventRecord(p->user_begin, s));
   if (err == hipSuccess)
-    step(moe::launch_gate_up_mfma(d, false, a->hidden, a->w13, a->w13_scale, p->ws, s));
+    step(moe::launch_gate_up_mfma(d, rows, a->hidden, a->w13, a->w13_scale, sw13, a->sw13_scale,
+                                  p->ws, s));
   if (err == hipSuccess && p->user_end) step(hipEventRecord(p->user_end, s));
-  if (err == hipSuccess) step(moe::launch_down_mfma(d, false, a->w2, a->w2_scale, p->ws, s));
-
-  // Join the side stream on every path, then run the boundary.
-  hipError_t jerr = hipEventRecord(p->join, p->side);
-  if (jerr == hipSuccess) jerr = hipStreamWaitEvent(s, p->join, 0);
-  if (err == hipSuccess) err = jerr;
+  if (err == hipSuccess)
+    step(moe::launch_down_mfma(d, rows, a->w2, a->w2_scale, sw2, a->sw2_scale, p->ws, s));
+  if (side) {
+    // joined on every path, errors included, so a capture sees no loose work
+    hipError_t jerr = hipEventRecord(p->join, p->side);
+    if (jerr == hipSuccess) jerr = hipStreamWaitEvent(s, p->join, 0);
+    if (err == hipSuccess) err = jerr;
+  }
   if (err == hipSuccess)
     step(moe::launch_epilogue(d, a->residual, a->gamma, p->ws, a->out, a->residual_out, s));
   return err == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;

@@ -107,26 +107,30 @@ __device__ __forceinline__ f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, co
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) { return static_cast<uint16_t>(f32_to_bf16(f)); }
 
-// Per-slot expert, token count, permuted base position and this
-// workgroup's token range [p_begin, p_end) (uniform).  Routed: grid row y is
-// the touched-expert slot and the workgroup takes all of its tokens, in
-// passes of 16 * GR.  Shared: grid row y is one pass of 16 * GR tokens.
+// What one grid row works on (uniform).  Rows [0, SP) are the shared
+// expert, one 16 * GR-token pass each (they run in parallel); the rows after
+// them are the touched-expert slots, each taking all of its expert's tokens
+// in passes of 16 * GR.  Tokens [p_begin, p_end) of the row's expert; base =
+// the expert's first permuted position (0 for the shared expert, whose
+// positions are the tokens themselves).
 struct Slot {
-  int e, n, base, p_begin, p_end;
+  bool shared;
+  int e, base, p_begin, p_end;
 };
 
-template <bool SHARED, int GR>
-__device__ __forceinline__ bool slot_of(int T, const Workspace& ws, Slot* s) {
-  if (SHARED) {
-    const int p = blockIdx.y * 16 * GR;
-    *s = {0, T, 0, p, min(T, p + 16 * GR)};
+template <int GR>
+__device__ __forceinline__ bool slot_of(int T, int SP, const Workspace& ws, Slot* s) {
+  const int y = static_cast<int>(blockIdx.y);
+  if (y < SP) {
+    const int p = y * 16 * GR;
+    *s = {true, 0, 0, p, min(T, p + 16 * GR)};
     return p < T;
   }
   // the router's slot record: expert (-1: none this step), count, base
-  const int4 rec = *reinterpret_cast<const int4*>(ws.slot_tab +
-                                                 static_cast<size_t>(blockIdx.y) * kSlotInts);
+  const int4 rec =
+      *reinterpret_cast<const int4*>(ws.slot_tab + static_cast<size_t>(y - SP) * kSlotInts);
   if (rec.x < 0) return false;
-  *s = {rec.x, rec.y, rec.z, 0, rec.y};
+  *s = {false, rec.x, rec.z, 0, rec.y};
   return true;
 }
 
@@ -134,19 +138,27 @@ __device__ __forceinline__ bool slot_of(int T, const Workspace& ws, Slot* s) {
 // expert for all its tokens; writes the hi / lo bf16 planes of
 // act[(base + q) * I + i].  U = scale blocks per round of loads; GR =
 // 16-token groups per pass over the weights.
-template <int U, int GR, bool E8, bool SHARED>
+// ROWS: kAllRows (shared passes and touched experts, chosen per row at run
+// time) or only one kind, fixed at compile time.
+template <int U, int GR, bool E8, int ROWS>
 __global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
     const uint16_t* __restrict__ hidden, const uint8_t* __restrict__ w13,
-    const void* __restrict__ scale, int H, int I, int k, int T, Workspace ws, float limit) {
+    const void* __restrict__ scale13, const uint8_t* __restrict__ sw13,
+    const void* __restrict__ sscale13, int H, int I_r, int Is, int k, int T, int SP,
+    Workspace ws, float limit) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   const int i0 = (blockIdx.x * kWaves + wave) * 16;
   Slot sl;
-  if (!slot_of<SHARED, GR>(T, ws, &sl) || i0 >= I) return;
+  if (!slot_of<GR>(T, SP, ws, &sl)) return;
+  const bool shared = ROWS == kAllRows ? sl.shared : ROWS == kSharedRows;
+  const int I = shared ? Is : I_r;
+  if (i0 >= I) return;
+  const void* scale = shared ? sscale13 : scale13;
   unsigned char* stage = smem + wave * U * kStageBlock;
   const int KB = H / kBlock;
-  const uint8_t* W = w13 + static_cast<size_t>(sl.e) * 2 * I * H;
+  const uint8_t* W = shared ? sw13 : w13 + static_cast<size_t>(sl.e) * 2 * I * H;
   // load rows: instructions 0, 1 = gate rows i0 .. i0+15, 2, 3 = up rows
   const uint8_t* lrow[4];
 #pragma unroll
@@ -155,8 +167,8 @@ __global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
   const size_t sb = static_cast<size_t>(sl.e) * (2 * I / kBlock) * KB;
   const size_t sg0 = sb + static_cast<size_t>(i0 / kBlock) * KB;
   const size_t su0 = sb + static_cast<size_t>((I + i0) / kBlock) * KB;
-  uint16_t* act_hi = reinterpret_cast<uint16_t*>(SHARED ? ws.act_s : ws.act);
-  const size_t plane = static_cast<size_t>(SHARED ? T : T * k) * I;
+  uint16_t* act_hi = reinterpret_cast<uint16_t*>(shared ? ws.act_s : ws.act);
+  const size_t plane = static_cast<size_t>(shared ? T : T * k) * I;
   uint16_t* act_lo = act_hi + plane;
 
   for (int p0 = sl.p_begin; p0 < sl.p_end; p0 += 16 * GR) {
@@ -165,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
 #pragma unroll
     for (int gr = 0; gr < GR; ++gr) {
       const int q = min(p0 + gr * 16 + c, sl.p_end - 1);
-      const int t = SHARED ? q : ws.perm[sl.base + q] / k;
+      const int t = shared ? q : ws.perm[sl.base + q] / k;
       xrow[gr] = hidden + static_cast<size_t>(t) * H + 32 * g;
     }
     f32x4_t fg[GR], fu[GR];
@@ -244,28 +256,32 @@ __global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
 // its tokens, from the hi / lo activation planes; row q goes to
 // out[perm[base + q] * H] (routed: the route index t*k + j) or out[q * H]
 // (shared).
-template <int U, int GR, bool E8, bool SHARED>
+template <int U, int GR, bool E8, int ROWS>
 __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
-    const uint8_t* __restrict__ w2, const void* __restrict__ scale, int H, int I, int k, int T,
-    Workspace ws) {
+    const uint8_t* __restrict__ w2, const void* __restrict__ scale2,
+    const uint8_t* __restrict__ sw2, const void* __restrict__ sscale2, int H, int I_r, int Is,
+    int k, int T, int SP, Workspace ws) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   const int h0 = (blockIdx.x * kWaves + wave) * 32;
   Slot sl;
-  if (!slot_of<SHARED, GR>(T, ws, &sl) || h0 >= H) return;
+  if (!slot_of<GR>(T, SP, ws, &sl) || h0 >= H) return;
+  const bool shared = ROWS == kAllRows ? sl.shared : ROWS == kSharedRows;
+  const int I = shared ? Is : I_r;
+  const void* scale = shared ? sscale2 : scale2;
   unsigned char* stage = smem + wave * U * kStageBlock;
   const int KB = I / kBlock;
-  const uint8_t* W = w2 + static_cast<size_t>(sl.e) * H * I;
+  const uint8_t* W = shared ? sw2 : w2 + static_cast<size_t>(sl.e) * H * I;
   const uint8_t* lrow[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) lrow[i] = W + static_cast<size_t>(h0 + 8 * i + (lane >> 3)) * I;
   const size_t s0 = static_cast<size_t>(sl.e) * (H / kBlock) * KB +
                     static_cast<size_t>(h0 / kBlock) * KB;
-  const uint16_t* act_hi = reinterpret_cast<const uint16_t*>(SHARED ? ws.act_s : ws.act);
-  const size_t plane = static_cast<size_t>(SHARED ? T : T * k) * I;
+  const uint16_t* act_hi = reinterpret_cast<const uint16_t*>(shared ? ws.act_s : ws.act);
+  const size_t plane = static_cast<size_t>(shared ? T : T * k) * I;
   const uint16_t* act_lo = act_hi + plane;
-  float* out = SHARED ? ws.y_s : ws.rows;
+  float* out = shared ? ws.y_s : ws.rows;
 
   for (int p0 = sl.p_begin; p0 < sl.p_end; p0 += 16 * GR) {
     const int G = min(GR, (sl.p_end - p0 + 15) / 16);
@@ -335,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
       for (int i = 0; i < 4; ++i) {
         const int q = p0 + gr * 16 + 4 * g + i;
         if (q < sl.p_end) {
-          const int o = SHARED ? q : ws.perm[sl.base + q];
+          const int o = shared ? q : ws.perm[sl.base + q];
           float* row = out + static_cast<size_t>(o) * H + h0 + c;
           row[0] = f0[gr][i];
           row[16] = f1[gr][i];
@@ -345,65 +361,75 @@ __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
   }
 }
 
-// Routed: U scale blocks per round of loads, one 16-token group per pass
-// (an expert rarely has more than 16 of a step's tokens).  Shared: the same
-// tile shape, one grid row per 16 tokens, so that the passes run in parallel.
+// U scale blocks per round of loads, one 16-token group per pass (a routed
+// expert rarely has more than 16 of a step's tokens; the shared expert gets
+// one grid row per 16 tokens, so that its passes run in parallel).
 constexpr int kU = 2;
-constexpr int kGR = 1;
+constexpr int kGR = 1;  // 16-token groups per shared-expert pass
 constexpr size_t kLds = static_cast<size_t>(kWaves) * kU * kStageBlock;
 
-template <bool E8>
-void launch_gu(dim3 grid, hipStream_t s, bool shared, const uint16_t* x, const uint8_t* w,
-               const void* scale, const LayerDims& d, int I, const Workspace& ws) {
-  if (shared)
-    hipLaunchKernelGGL((gate_up_mfma_kernel<kU, kGR, E8, true>), grid, dim3(kThreads), kLds, s, x,
-                       w, scale, d.H, I, d.k, d.T, ws, d.limit);
-  else
-    hipLaunchKernelGGL((gate_up_mfma_kernel<kU, kGR, E8, false>), grid, dim3(kThreads), kLds, s, x,
-                       w, scale, d.H, I, d.k, d.T, ws, d.limit);
+template <bool E8, int ROWS>
+void launch_gu(dim3 grid, hipStream_t s, const uint16_t* x, const uint8_t* w, const void* scale,
+               const uint8_t* sw, const void* sscale, const LayerDims& d, int SP,
+               const Workspace& ws) {
+  hipLaunchKernelGGL((gate_up_mfma_kernel<kU, kGR, E8, ROWS>), grid, dim3(kThreads), kLds, s, x,
+                     w, scale, sw, sscale, d.H, d.I, d.Is, d.k, d.T, SP, ws, d.limit);
 }
 
-template <bool E8>
-void launch_dn(dim3 grid, hipStream_t s, bool shared, const uint8_t* w, const void* scale,
-               const LayerDims& d, int I, const Workspace& ws) {
-  if (shared)
-    hipLaunchKernelGGL((down_mfma_kernel<kU, kGR, E8, true>), grid, dim3(kThreads), kLds, s, w,
-                       scale, d.H, I, d.k, d.T, ws);
-  else
-    hipLaunchKernelGGL((down_mfma_kernel<kU, kGR, E8, false>), grid, dim3(kThreads), kLds, s, w,
-                       scale, d.H, I, d.k, d.T, ws);
+template <bool E8, int ROWS>
+void launch_dn(dim3 grid, hipStream_t s, const uint8_t* w, const void* scale, const uint8_t* sw,
+               const void* sscale, const LayerDims& d, int SP, const Workspace& ws) {
+  hipLaunchKernelGGL((down_mfma_kernel<kU, kGR, E8, ROWS>), grid, dim3(kThreads), kLds, s, w,
+                     scale, sw, sscale, d.H, d.I, d.Is, d.k, d.T, SP, ws);
 }
 
-int grid_rows(const LayerDims& d, bool shared) {
-  if (shared) return (d.T + 16 * kGR - 1) / (16 * kGR);
-  return d.T * d.k < d.E ? d.T * d.k : d.E;
-}
+// grid rows: the shared expert's passes, then the touched-expert slots
+int shared_rows(const LayerDims& d) { return d.Is > 0 ? (d.T + 16 * kGR - 1) / (16 * kGR) : 0; }
+int slot_rows(const LayerDims& d) { return d.T * d.k < d.E ? d.T * d.k : d.E; }
 
 }  // namespace
 
-hipError_t launch_gate_up_mfma(const LayerDims& d, bool shared, const void* hidden,
-                               const void* w13, const void* w13_scale, const Workspace& ws,
-                               hipStream_t s) {
-  const int I = shared ? d.Is : d.I;
-  dim3 grid((I / 16 + kWaves - 1) / kWaves, grid_rows(d, shared));
+hipError_t launch_gate_up_mfma(const LayerDims& d, int rows, const void* hidden, const void* w13,
+                               const void* w13_scale, const void* sw13, const void* sw13_scale,
+                               const Workspace& ws, hipStream_t s) {
+  const int SP = rows == kRoutedRows ? 0 : shared_rows(d);
+  const int R = rows == kSharedRows ? 0 : slot_rows(d);
+  if (SP + R == 0) return hipSuccess;
+  const int Imax = d.I > d.Is ? d.I : d.Is;
+  dim3 grid((Imax / 16 + kWaves - 1) / kWaves, SP + R);
   const auto* x = static_cast<const uint16_t*>(hidden);
   const auto* w = static_cast<const uint8_t*>(w13);
-  if (d.e8m0)
-    launch_gu<true>(grid, s, shared, x, w, w13_scale, d, I, ws);
-  else
-    launch_gu<false>(grid, s, shared, x, w, w13_scale, d, I, ws);
+  const auto* sw = static_cast<const uint8_t*>(sw13);
+#define MOE_GU(E8, ROWS) launch_gu<E8, ROWS>(grid, s, x, w, w13_scale, sw, sw13_scale, d, SP, ws)
+  if (rows == kAllRows) {
+    if (d.e8m0) MOE_GU(true, kAllRows); else MOE_GU(false, kAllRows);
+  } else if (rows == kSharedRows) {
+    if (d.e8m0) MOE_GU(true, kSharedRows); else MOE_GU(false, kSharedRows);
+  } else {
+    if (d.e8m0) MOE_GU(true, kRoutedRows); else MOE_GU(false, kRoutedRows);
+  }
+#undef MOE_GU
   return hipGetLastError();
 }
 
-hipError_t launch_down_mfma(const LayerDims& d, bool shared, const void* w2,
-                            const void* w2_scale, const Workspace& ws, hipStream_t s) {
-  const int I = shared ? d.Is : d.I;
-  dim3 grid((d.H / 32 + kWaves - 1) / kWaves, grid_rows(d, shared));
+hipError_t launch_down_mfma(const LayerDims& d, int rows, const void* w2, const void* w2_scale,
+                            const void* sw2, const void* sw2_scale, const Workspace& ws,
+                            hipStream_t s) {
+  const int SP = rows == kRoutedRows ? 0 : shared_rows(d);
+  const int R = rows == kSharedRows ? 0 : slot_rows(d);
+  if (SP + R == 0) return hipSuccess;
+  dim3 grid((d.H / 32 + kWaves - 1) / kWaves, SP + R);
   const auto* w = static_cast<const uint8_t*>(w2);
-  if (d.e8m0)
-    launch_dn<true>(grid, s, shared, w, w2_scale, d, I, ws);
-  else
-    launch_dn<false>(grid, s, shared, w, w2_scale, d, I, ws);
+  const auto* sw = static_cast<const uint8_t*>(sw2);
+#define MOE_DN(E8, ROWS) launch_dn<E8, ROWS>(grid, s, w, w2_scale, sw, sw2_scale, d, SP, ws)
+  if (rows == kAllRows) {
+    if (d.e8m0) MOE_DN(true, kAllRows); else MOE_DN(false, kAllRows);
+  } else if (rows == kSharedRows) {
+    if (d.e8m0) MOE_DN(true, kSharedRows); else MOE_DN(false, kSharedRows);
+  } else {
+    if (d.e8m0) MOE_DN(true, kRoutedRows); else MOE_DN(false, kRoutedRows);
+  }
+#undef MOE_DN
   return hipGetLastError();
 }
 

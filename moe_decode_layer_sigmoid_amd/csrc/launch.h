@@ -78,6 +78,10 @@ __host__ __device__ constexpr size_t router_cnt_words() {
 }
 
 constexpr int kFusedMaxTokens = 16;
+// Up to this many tokens the MFMA path runs the shared expert's passes in the
+// routed experts' launches; above it (several 16-token passes, each streaming
+// the shared weights again) on a second stream, beside the routed launches.
+constexpr int kMergeSharedMaxTokens = 64;
 // AUTO takes the MFMA projections from this many tokens on (at 8 to 12
 // tokens the two paths measure the same on MI355X; from 16 on MFMA wins).
 constexpr int kGroupedMinTokens = 8;
@@ -133,12 +137,16 @@ hipError_t launch_down_gemv(const LayerDims& d, const void* w2, const void* w2_s
                             hipStream_t s);
 
 // The same two projections on the matrix cores (bf16 MFMA on exactly
-// converted fp8 weights; SwiGLU activations as hi + lo bf16 planes).
-hipError_t launch_gate_up_mfma(const LayerDims& d, bool shared, const void* hidden,
-                               const void* w13, const void* w13_scale, const Workspace& ws,
-                               hipStream_t s);
-hipError_t launch_down_mfma(const LayerDims& d, bool shared, const void* w2,
-                            const void* w2_scale, const Workspace& ws, hipStream_t s);
+// converted fp8 weights; SwiGLU activations as hi + lo bf16 planes).  Grid
+// rows: the shared expert's 16-token passes, then the touched experts;
+// `rows` launches both or one of the two kinds.
+enum : int { kAllRows = 0, kSharedRows = 1, kRoutedRows = 2 };
+hipError_t launch_gate_up_mfma(const LayerDims& d, int rows, const void* hidden, const void* w13,
+                               const void* w13_scale, const void* sw13, const void* sw13_scale,
+                               const Workspace& ws, hipStream_t s);
+hipError_t launch_down_mfma(const LayerDims& d, int rows, const void* w2, const void* w2_scale,
+                            const void* sw2, const void* sw2_scale, const Workspace& ws,
+                            hipStream_t s);
 
 // Fused persistent kernel of the whole step (T <= kFusedMaxTokens).
 int fused_nj(int H, int I, int Is);

@@ -198,12 +198,14 @@ def test_smaller_T_than_plan_and_zero(c_oracle):
     plan.close()
 
 
-@pytest.mark.parametrize("path", [md.PATH_GEMV, md.PATH_GEMV_SPLIT, md.PATH_GROUPED],
-                         ids=["fused", "split", "grouped"])
-def test_graph_replay_matches_eager(path, c_oracle):
+@pytest.mark.parametrize("path,T", [(md.PATH_GEMV, 16), (md.PATH_GEMV_SPLIT, 16),
+                                    (md.PATH_GROUPED, 16), (md.PATH_GROUPED, 80)],
+                         ids=["fused", "split", "grouped", "grouped-side-stream"])
+def test_graph_replay_matches_eager(path, T, c_oracle):
     """One run captured into a HIP graph, replayed several times with eager
-    work in between; every replay equals the eager result bit for bit."""
-    sh = WORKLOADS["decode_t16"].replace(H=1024, I=512, Is=256, tag=305)
+    work in between; every replay equals the eager result bit for bit.  At
+    80 tokens the MFMA path puts the shared expert on the side stream."""
+    sh = WORKLOADS["decode_t16"].replace(T=T, H=1024, I=512, Is=256, tag=305)
     inp = make_layer(sh)
     dev = to_device(inp)
     plan = make_plan(sh, path=path)
