@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
+MERGE_SHARED_MAX_TOKENS = 64  # the library's kMergeSharedMaxTokens
 METRIC = "µs per MoE layer and effective HBM TB/s (fraction of peak) at 1/16/64/128 tok"
 
 
@@ -383,10 +384,14 @@ def main():
         kern_bytes = (D * (2 * sh.I * H + sb * (2 * sh.I // 128) * (H // 128))
                       + T * H * 2 + T * k * sh.I * 4)
         if path_taken == md.PATH_GROUPED:
-            # one launch covers the shared expert's token passes as well
-            kern_name = "gate_up_mfma_kernel<U, GR, E8> (routed + shared experts)"
-            kern_id = "gate_up_mfma_kernel<2, 1, %s>" % e8
-            if sh.Is:
+            # up to 64 tokens one launch also covers the shared expert's token
+            # passes (ROWS = 0); above, the routed launch has routed rows only
+            # (ROWS = 2) and the shared expert runs beside it
+            merged = T <= MERGE_SHARED_MAX_TOKENS
+            kern_name = "gate_up_mfma_kernel<U, GR, E8, ROWS> (%s)" % (
+                "routed + shared experts" if merged else "routed experts")
+            kern_id = "gate_up_mfma_kernel<2, 1, %s, %d>" % (e8, 0 if merged else 2)
+            if sh.Is and merged:
                 kern_bytes += (2 * sh.Is * H + sb * (2 * sh.Is // 128) * (H // 128)
                                + T * sh.Is * 4)
         else:
