@@ -52,21 +52,22 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kStageBlock = 4096;  // LDS bytes of one 128-wide block of a wave's 32 rows
+constexpr int kSubtileBlock = 2048;  // LDS bytes of one 128-wide block of 16 weight rows
 constexpr unsigned kCpolNT = 2;    // non-temporal: weights are read once per step
 
 // Issues the loads of one 128-wide block (byte offset kofs of every row) of
-// the wave's 32 rows into `stage` (kStageBlock bytes): load instruction i
+// the wave's 8 NI rows into `stage` (NI * 1024 bytes): load instruction i
 // covers rows 8i .. 8i+7, whose start pointers lane l finds in row[i] (its
 // row 8i + l / 8).  Lane l fetches piece (l % 8) ^ (l / 8) of its row and
 // lands at stage + 1024 i + 16 l, so row r's piece p sits at slot
 // p ^ (r % 8) of its 128 bytes.
-__device__ __forceinline__ void stage_block(const uint8_t* const row[4], int kofs,
+template <int NI>
+__device__ __forceinline__ void stage_block(const uint8_t* const row[NI], int kofs,
                                             unsigned char* stage) {
   const int lane = threadIdx.x & 63;
   const int piece = (lane & 7) ^ (lane >> 3);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
     __builtin_amdgcn_global_load_lds(row[i] + kofs + 16 * piece,
                                      (lds_void_t*)(stage + 1024 * i), 16, 0,
                                      kCpolNT);
@@ -134,13 +135,14 @@ __device__ __forceinline__ bool slot_of(int T, int SP, const Workspace& ws, Slot
   return true;
 }
 
-// gate_up + clamped SwiGLU.  Wave: SwiGLU outputs [i0, i0 + 16) of one
-// expert for all its tokens; writes the hi / lo bf16 planes of
-// act[(base + q) * I + i].  U = scale blocks per round of loads; GR =
-// 16-token groups per pass over the weights.
+// gate_up + clamped SwiGLU.  Wave: SwiGLU outputs [i0, i0 + 8 NS) of one
+// expert for all its tokens (NS 16-row subtiles of weights: NS / 2 of gate
+// rows, then the NS / 2 matching subtiles of up rows); writes the hi / lo
+// bf16 planes of act[(base + q) * I + i].  U = scale blocks per round of
+// loads; GR = 16-token groups per pass over the weights.
 // ROWS: kAllRows (shared passes and touched experts, chosen per row at run
 // time) or only one kind, fixed at compile time.
-template <int U, int GR, bool E8, int ROWS>
+template <int NS, int U, int GR, bool E8, int ROWS>
 __global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
     const uint16_t* __restrict__ hidden, const uint8_t* __restrict__ w13,
     const void* __restrict__ scale13, const uint8_t* __restrict__ sw13,
@@ -149,21 +151,23 @@ __global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-  const int i0 = (blockIdx.x * kWaves + wave) * 16;
+  constexpr int NH = NS / 2;  // gate (and up) subtiles
+  const int i0 = (blockIdx.x * kWaves + wave) * 16 * NH;
   Slot sl;
   if (!slot_of<GR>(T, SP, ws, &sl)) return;
   const bool shared = ROWS == kAllRows ? sl.shared : ROWS == kSharedRows;
   const int I = shared ? Is : I_r;
   if (i0 >= I) return;
   const void* scale = shared ? sscale13 : scale13;
-  unsigned char* stage = smem + wave * U * kStageBlock;
+  constexpr int SB = NS * kSubtileBlock;  // stage bytes of one block
+  unsigned char* stage = smem + wave * U * SB;
   const int KB = H / kBlock;
   const uint8_t* W = shared ? sw13 : w13 + static_cast<size_t>(sl.e) * 2 * I * H;
-  // load rows: instructions 0, 1 = gate rows i0 .. i0+15, 2, 3 = up rows
-  const uint8_t* lrow[4];
+  // load rows: instructions [0, NS) = gate rows i0 .. i0 + 8 NS - 1, then up
+  const uint8_t* lrow[2 * NS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    lrow[i] = W + static_cast<size_t>((i < 2 ? i0 : I + i0 - 16) + 8 * i + (lane >> 3)) * H;
+  for (int i = 0; i < 2 * NS; ++i)
+    lrow[i] = W + static_cast<size_t>((i < NS ? i0 : I + i0 - 8 * NS) + 8 * i + (lane >> 3)) * H;
   const size_t sb = static_cast<size_t>(sl.e) * (2 * I / kBlock) * KB;
   const size_t sg0 = sb + static_cast<size_t>(i0 / kBlock) * KB;
   const size_t su0 = sb + static_cast<size_t>((I + i0) / kBlock) * KB;
@@ -180,18 +184,20 @@ __global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
       const int t = shared ? q : ws.perm[sl.base + q] / k;
       xrow[gr] = hidden + static_cast<size_t>(t) * H + 32 * g;
     }
-    f32x4_t fg[GR], fu[GR];
+    f32x4_t fg[GR][NH], fu[GR][NH];
 #pragma unroll
-    for (int gr = 0; gr < GR; ++gr) {
-      fg[gr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      fu[gr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int gr = 0; gr < GR; ++gr)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        fg[gr][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        fu[gr][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
     for (int kb0 = 0; kb0 < KB; kb0 += U) {
       float sg[U], su[U];
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         const int kb = min(kb0 + j, KB - 1);  // a block past the end gets scale 0
-        stage_block(lrow, kb * kBlock, stage + j * kStageBlock);
+        stage_block<2 * NS>(lrow, kb * kBlock, stage + j * SB);
         const float a = load_scale<E8>(scale, sg0 + kb);
         const float b = load_scale<E8>(scale, su0 + kb);
         sg[j] = kb0 + j < KB ? a : 0.f;
@@ -212,27 +218,31 @@ __global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
         }
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-          const unsigned char* st = stage + j * kStageBlock;
-          const uint4 g0 = staged_piece(st, 0, c, 2 * g), g1 = staged_piece(st, 0, c, 2 * g + 1);
-          const uint4 u0 = staged_piece(st, 1, c, 2 * g), u1 = staged_piece(st, 1, c, 2 * g + 1);
-          f32x4_t pg = {0.f, 0.f, 0.f, 0.f}, pu = {0.f, 0.f, 0.f, 0.f};
+          const unsigned char* st = stage + j * SB;
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const bf16x8_t a = as_bf16x8(xa[j][m]);
-            pg = mfma(a, weight_frag(g0, g1, m), pg);
-            pu = mfma(a, weight_frag(u0, u1, m), pu);
-          }
+          for (int h = 0; h < NH; ++h) {
+            const uint4 g0 = staged_piece(st, h, c, 2 * g), g1 = staged_piece(st, h, c, 2 * g + 1);
+            const uint4 u0 = staged_piece(st, NH + h, c, 2 * g),
+                        u1 = staged_piece(st, NH + h, c, 2 * g + 1);
+            f32x4_t pg = {0.f, 0.f, 0.f, 0.f}, pu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            fg[gr][i] = fmaf(sg[j], pg[i], fg[gr][i]);
-            fu[gr][i] = fmaf(su[j], pu[i], fu[gr][i]);
+            for (int m = 0; m < 4; ++m) {
+              const bf16x8_t a = as_bf16x8(xa[j][m]);
+              pg = mfma(a, weight_frag(g0, g1, m), pg);
+              pu = mfma(a, weight_frag(u0, u1, m), pu);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              fg[gr][h][i] = fmaf(sg[j], pg[i], fg[gr][h][i]);
+              fu[gr][h][i] = fmaf(su[j], pu[i], fu[gr][h][i]);
+            }
           }
         }
       }
       // the next round's loads overwrite the stage: its reads must be done
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     }
-    // lane holds tokens p0 + 16 gr + 4 g + i of SwiGLU output i0 + c
+    // lane holds tokens p0 + 16 gr + 4 g + i of SwiGLU outputs i0 + 16 h + c
 #pragma unroll
     for (int gr = 0; gr < GR; ++gr) {
       if (gr >= G) break;
@@ -240,23 +250,26 @@ __global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
       for (int i = 0; i < 4; ++i) {
         const int q = p0 + gr * 16 + 4 * g + i;
         if (q < sl.p_end) {
-          const float a = clamped_swiglu(fg[gr][i], fu[gr][i], limit);
-          const uint16_t hi = bf16_bits(a);
-          const uint16_t lo = bf16_bits(a - bf16_to_f32(hi));
-          const size_t o = static_cast<size_t>(sl.base + q) * I + i0 + c;
-          act_hi[o] = hi;
-          act_lo[o] = lo;
+#pragma unroll
+          for (int h = 0; h < NH; ++h) {
+            const float a = clamped_swiglu(fg[gr][h][i], fu[gr][h][i], limit);
+            const uint16_t hi = bf16_bits(a);
+            const uint16_t lo = bf16_bits(a - bf16_to_f32(hi));
+            const size_t o = static_cast<size_t>(sl.base + q) * I + i0 + 16 * h + c;
+            act_hi[o] = hi;
+            act_lo[o] = lo;
+          }
         }
       }
     }
   }
 }
 
-// down projection.  Wave: output rows [h0, h0 + 32) of one expert for all
+// down projection.  Wave: output rows [h0, h0 + 16 NS) of one expert for all
 // its tokens, from the hi / lo activation planes; row q goes to
 // out[perm[base + q] * H] (routed: the route index t*k + j) or out[q * H]
 // (shared).
-template <int U, int GR, bool E8, int ROWS>
+template <int NS, int U, int GR, bool E8, int ROWS>
 __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
     const uint8_t* __restrict__ w2, const void* __restrict__ scale2,
     const uint8_t* __restrict__ sw2, const void* __restrict__ sscale2, int H, int I_r, int Is,
@@ -264,18 +277,20 @@ __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-  const int h0 = (blockIdx.x * kWaves + wave) * 32;
+  const int h0 = (blockIdx.x * kWaves + wave) * 16 * NS;
   Slot sl;
   if (!slot_of<GR>(T, SP, ws, &sl) || h0 >= H) return;
   const bool shared = ROWS == kAllRows ? sl.shared : ROWS == kSharedRows;
   const int I = shared ? Is : I_r;
   const void* scale = shared ? sscale2 : scale2;
-  unsigned char* stage = smem + wave * U * kStageBlock;
+  constexpr int SB = NS * kSubtileBlock;
+  unsigned char* stage = smem + wave * U * SB;
   const int KB = I / kBlock;
   const uint8_t* W = shared ? sw2 : w2 + static_cast<size_t>(sl.e) * H * I;
-  const uint8_t* lrow[4];
+  const uint8_t* lrow[2 * NS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lrow[i] = W + static_cast<size_t>(h0 + 8 * i + (lane >> 3)) * I;
+  for (int i = 0; i < 2 * NS; ++i)
+    lrow[i] = W + static_cast<size_t>(h0 + 8 * i + (lane >> 3)) * I;
   const size_t s0 = static_cast<size_t>(sl.e) * (H / kBlock) * KB +
                     static_cast<size_t>(h0 / kBlock) * KB;
   const uint16_t* act_hi = reinterpret_cast<const uint16_t*>(shared ? ws.act_s : ws.act);
@@ -291,18 +306,17 @@ __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
       const int q = min(p0 + gr * 16 + c, sl.p_end - 1);
       arow[gr] = static_cast<size_t>(sl.base + q) * I + 32 * g;
     }
-    f32x4_t f0[GR], f1[GR];
+    f32x4_t f[GR][NS];
 #pragma unroll
-    for (int gr = 0; gr < GR; ++gr) {
-      f0[gr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      f1[gr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int gr = 0; gr < GR; ++gr)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) f[gr][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int kb0 = 0; kb0 < KB; kb0 += U) {
       float sc[U];
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         const int kb = min(kb0 + j, KB - 1);
-        stage_block(lrow, kb * kBlock, stage + j * kStageBlock);
+        stage_block<2 * NS>(lrow, kb * kBlock, stage + j * SB);
         const float s = load_scale<E8>(scale, s0 + kb);
         sc[j] = kb0 + j < KB ? s : 0.f;
       }
@@ -322,23 +336,19 @@ __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
         }
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-          const unsigned char* st = stage + j * kStageBlock;
-          const uint4 a0 = staged_piece(st, 0, c, 2 * g), a1 = staged_piece(st, 0, c, 2 * g + 1);
-          const uint4 b0 = staged_piece(st, 1, c, 2 * g), b1 = staged_piece(st, 1, c, 2 * g + 1);
-          f32x4_t p = {0.f, 0.f, 0.f, 0.f}, q = {0.f, 0.f, 0.f, 0.f};
+          const unsigned char* st = stage + j * SB;
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const bf16x8_t wa = weight_frag(a0, a1, m);
-            const bf16x8_t wb = weight_frag(b0, b1, m);
-            p = mfma(as_bf16x8(ah[j][m]), wa, p);
-            p = mfma(as_bf16x8(al[j][m]), wa, p);
-            q = mfma(as_bf16x8(ah[j][m]), wb, q);
-            q = mfma(as_bf16x8(al[j][m]), wb, q);
-          }
+          for (int s = 0; s < NS; ++s) {
+            const uint4 a0 = staged_piece(st, s, c, 2 * g), a1 = staged_piece(st, s, c, 2 * g + 1);
+            f32x4_t p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            f0[gr][i] = fmaf(sc[j], p[i], f0[gr][i]);
-            f1[gr][i] = fmaf(sc[j], q[i], f1[gr][i]);
+            for (int m = 0; m < 4; ++m) {
+              const bf16x8_t wa = weight_frag(a0, a1, m);
+              p = mfma(as_bf16x8(ah[j][m]), wa, p);
+              p = mfma(as_bf16x8(al[j][m]), wa, p);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f[gr][s][i] = fmaf(sc[j], p[i], f[gr][s][i]);
           }
         }
       }
@@ -353,33 +363,36 @@ __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
         if (q < sl.p_end) {
           const int o = shared ? q : ws.perm[sl.base + q];
           float* row = out + static_cast<size_t>(o) * H + h0 + c;
-          row[0] = f0[gr][i];
-          row[16] = f1[gr][i];
+#pragma unroll
+          for (int s = 0; s < NS; ++s) row[16 * s] = f[gr][s][i];
         }
       }
     }
   }
 }
 
-// U scale blocks per round of loads, one 16-token group per pass (a routed
-// expert rarely has more than 16 of a step's tokens; the shared expert gets
-// one grid row per 16 tokens, so that its passes run in parallel).
-constexpr int kU = 2;
+// Per wave: NS 16-row weight subtiles, U scale blocks per round of loads,
+// one 16-token group per pass (a routed expert rarely has more than 16 of a
+// step's tokens; the shared expert gets one grid row per 16 tokens, so that
+// its passes run in parallel).
+constexpr int kNsGu = 4, kUGu = 1;
+constexpr int kNsDn = 4, kUDn = 1;
 constexpr int kGR = 1;  // 16-token groups per shared-expert pass
-constexpr size_t kLds = static_cast<size_t>(kWaves) * kU * kStageBlock;
+constexpr size_t kLdsGu = static_cast<size_t>(kWaves) * kUGu * kNsGu * kSubtileBlock;
+constexpr size_t kLdsDn = static_cast<size_t>(kWaves) * kUDn * kNsDn * kSubtileBlock;
 
 template <bool E8, int ROWS>
 void launch_gu(dim3 grid, hipStream_t s, const uint16_t* x, const uint8_t* w, const void* scale,
                const uint8_t* sw, const void* sscale, const LayerDims& d, int SP,
                const Workspace& ws) {
-  hipLaunchKernelGGL((gate_up_mfma_kernel<kU, kGR, E8, ROWS>), grid, dim3(kThreads), kLds, s, x,
+  hipLaunchKernelGGL((gate_up_mfma_kernel<kNsGu, kUGu, kGR, E8, ROWS>), grid, dim3(kThreads), kLdsGu, s, x,
                      w, scale, sw, sscale, d.H, d.I, d.Is, d.k, d.T, SP, ws, d.limit);
 }
 
 template <bool E8, int ROWS>
 void launch_dn(dim3 grid, hipStream_t s, const uint8_t* w, const void* scale, const uint8_t* sw,
                const void* sscale, const LayerDims& d, int SP, const Workspace& ws) {
-  hipLaunchKernelGGL((down_mfma_kernel<kU, kGR, E8, ROWS>), grid, dim3(kThreads), kLds, s, w,
+  hipLaunchKernelGGL((down_mfma_kernel<kNsDn, kUDn, kGR, E8, ROWS>), grid, dim3(kThreads), kLdsDn, s, w,
                      scale, sw, sscale, d.H, d.I, d.Is, d.k, d.T, SP, ws);
 }
 
@@ -396,7 +409,8 @@ hipError_t launch_gate_up_mfma(const LayerDims& d, int rows, const void* hidden,
   const int R = rows == kSharedRows ? 0 : slot_rows(d);
   if (SP + R == 0) return hipSuccess;
   const int Imax = d.I > d.Is ? d.I : d.Is;
-  dim3 grid((Imax / 16 + kWaves - 1) / kWaves, SP + R);
+  const int per_wg = kWaves * 8 * kNsGu;  // SwiGLU outputs per workgroup
+  dim3 grid((Imax + per_wg - 1) / per_wg, SP + R);
   const auto* x = static_cast<const uint16_t*>(hidden);
   const auto* w = static_cast<const uint8_t*>(w13);
   const auto* sw = static_cast<const uint8_t*>(sw13);
@@ -418,7 +432,8 @@ hipError_t launch_down_mfma(const LayerDims& d, int rows, const void* w2, const 
   const int SP = rows == kRoutedRows ? 0 : shared_rows(d);
   const int R = rows == kSharedRows ? 0 : slot_rows(d);
   if (SP + R == 0) return hipSuccess;
-  dim3 grid((d.H / 32 + kWaves - 1) / kWaves, SP + R);
+  const int per_wg = kWaves * 16 * kNsDn;  // output rows per workgroup
+  dim3 grid((d.H + per_wg - 1) / per_wg, SP + R);
   const auto* w = static_cast<const uint8_t*>(w2);
   const auto* sw = static_cast<const uint8_t*>(sw2);
 #define MOE_DN(E8, ROWS) launch_dn<E8, ROWS>(grid, s, w, w2_scale, sw, sw2_scale, d, SP, ws)
