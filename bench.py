@@ -33,6 +33,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 MERGE_SHARED_MAX_TOKENS = 64  # the library's kMergeSharedMaxTokens
+# template arguments (NS, U, GR) of the library's gate_up MFMA launches (kNsGu, kUGu, kGR)
+MFMA_GATE_UP_TILE = "4, 1, 1"
 METRIC = "µs per MoE layer and effective HBM TB/s (fraction of peak) at 1/16/64/128 tok"
 
 
@@ -388,9 +390,9 @@ def main():
             # passes (ROWS = 0); above, the routed launch has routed rows only
             # (ROWS = 2) and the shared expert runs beside it
             merged = T <= MERGE_SHARED_MAX_TOKENS
-            kern_name = "gate_up_mfma_kernel<U, GR, E8, ROWS> (%s)" % (
+            kern_name = "gate_up_mfma_kernel<NS, U, GR, E8, ROWS> (%s)" % (
                 "routed + shared experts" if merged else "routed experts")
-            kern_id = "gate_up_mfma_kernel<2, 1, %s, %d>" % (e8, 0 if merged else 2)
+            kern_id = "gate_up_mfma_kernel<%s, %s, %d>" % (MFMA_GATE_UP_TILE, e8, 0 if merged else 2)
             if sh.Is and merged:
                 kern_bytes += (2 * sh.Is * H + sb * (2 * sh.Is // 128) * (H // 128)
                                + T * sh.Is * 4)

@@ -108,6 +108,28 @@ __device__ __forceinline__ f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, co
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) { return static_cast<uint16_t>(f32_to_bf16(f)); }
 
+// Up to this many tokens the launches' workgroups all start in about one
+// round, and if every wave walked the contraction from block 0 they would all
+// read the same block columns at once; the waves then drain unevenly.  There
+// each wave starts at its own block (its id modulo the block count) and
+// wraps around; the order of a wave's blocks is fixed by the grid, so results
+// stay deterministic.  With more tokens later workgroups start staggered
+// anyway, and the rotation only scatters the accesses of neighbouring waves
+// (measured slower at 64 and 128 tokens).
+constexpr int kRotateMaxTokens = 32;
+
+__device__ __forceinline__ int first_block(int T, int wave, int KB) {
+  if (T > kRotateMaxTokens) return 0;
+  return static_cast<int>((blockIdx.x * kWaves + wave + 5 * blockIdx.y) % KB);
+}
+
+// Block i of a wave's walk (i past the end: the last block, whose scale the
+// caller zeroes).
+__device__ __forceinline__ int block_at(int i, int KB, int rot) {
+  const int b = min(i, KB - 1) + rot;
+  return b >= KB ? b - KB : b;
+}
+
 // What one grid row works on (uniform).  Rows [0, SP) are the shared
 // expert, one 16 * GR-token pass each (they run in parallel); the rows after
 // them are the touched-expert slots, each taking all of its expert's tokens
@@ -162,6 +184,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
   constexpr int SB = NS * kSubtileBlock;  // stage bytes of one block
   unsigned char* stage = smem + wave * U * SB;
   const int KB = H / kBlock;
+  const int rot = first_block(T, wave, KB);
   const uint8_t* W = shared ? sw13 : w13 + static_cast<size_t>(sl.e) * 2 * I * H;
   // load rows: instructions [0, NS) = gate rows i0 .. i0 + 8 NS - 1, then up
   const uint8_t* lrow[2 * NS];
@@ -196,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
       float sg[U], su[U];
 #pragma unroll
       for (int j = 0; j < U; ++j) {
-        const int kb = min(kb0 + j, KB - 1);  // a block past the end gets scale 0
+        const int kb = block_at(kb0 + j, KB, rot);  // a block past the end gets scale 0
         stage_block<2 * NS>(lrow, kb * kBlock, stage + j * SB);
         const float a = load_scale<E8>(scale, sg0 + kb);
         const float b = load_scale<E8>(scale, su0 + kb);
@@ -211,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
         uint4 xa[U][4];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-          const int kb = min(kb0 + j, KB - 1);
+          const int kb = block_at(kb0 + j, KB, rot);
 #pragma unroll
           for (int m = 0; m < 4; ++m)
             xa[j][m] = *reinterpret_cast<const uint4*>(xrow[gr] + kb * kBlock + 8 * m);
@@ -286,6 +309,7 @@ __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
   constexpr int SB = NS * kSubtileBlock;
   unsigned char* stage = smem + wave * U * SB;
   const int KB = I / kBlock;
+  const int rot = first_block(T, wave, KB);
   const uint8_t* W = shared ? sw2 : w2 + static_cast<size_t>(sl.e) * H * I;
   const uint8_t* lrow[2 * NS];
 #pragma unroll
@@ -315,7 +339,7 @@ __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
       float sc[U];
 #pragma unroll
       for (int j = 0; j < U; ++j) {
-        const int kb = min(kb0 + j, KB - 1);
+        const int kb = block_at(kb0 + j, KB, rot);
         stage_block<2 * NS>(lrow, kb * kBlock, stage + j * SB);
         const float s = load_scale<E8>(scale, s0 + kb);
         sc[j] = kb0 + j < KB ? s : 0.f;
@@ -327,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
         uint4 ah[U][4], al[U][4];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-          const int kb = min(kb0 + j, KB - 1);
+          const int kb = block_at(kb0 + j, KB, rot);
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
             ah[j][m] = *reinterpret_cast<const uint4*>(act_hi + arow[gr] + kb * kBlock + 8 * m);
@@ -375,11 +399,13 @@ __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
 // one 16-token group per pass (a routed expert rarely has more than 16 of a
 // step's tokens; the shared expert gets one grid row per 16 tokens, so that
 // its passes run in parallel).
+// The routed-only down launch (above kMergeSharedMaxTokens, several tokens
+// per expert) takes 128 rows per wave: each activation fragment then feeds
+// eight weight subtiles (measured 8% faster there; no gain at 64 tokens).
 constexpr int kNsGu = 4, kUGu = 1;
-constexpr int kNsDn = 4, kUDn = 1;
+constexpr int kNsDn = 4, kNsDnRouted = 8, kUDn = 1;
 constexpr int kGR = 1;  // 16-token groups per shared-expert pass
 constexpr size_t kLdsGu = static_cast<size_t>(kWaves) * kUGu * kNsGu * kSubtileBlock;
-constexpr size_t kLdsDn = static_cast<size_t>(kWaves) * kUDn * kNsDn * kSubtileBlock;
 
 template <bool E8, int ROWS>
 void launch_gu(dim3 grid, hipStream_t s, const uint16_t* x, const uint8_t* w, const void* scale,
@@ -389,11 +415,14 @@ void launch_gu(dim3 grid, hipStream_t s, const uint16_t* x, const uint8_t* w, co
                      w, scale, sw, sscale, d.H, d.I, d.Is, d.k, d.T, SP, ws, d.limit);
 }
 
-template <bool E8, int ROWS>
-void launch_dn(dim3 grid, hipStream_t s, const uint8_t* w, const void* scale, const uint8_t* sw,
+template <int NS, bool E8, int ROWS>
+void launch_dn(int R, hipStream_t s, const uint8_t* w, const void* scale, const uint8_t* sw,
                const void* sscale, const LayerDims& d, int SP, const Workspace& ws) {
-  hipLaunchKernelGGL((down_mfma_kernel<kNsDn, kUDn, kGR, E8, ROWS>), grid, dim3(kThreads), kLdsDn, s, w,
-                     scale, sw, sscale, d.H, d.I, d.Is, d.k, d.T, SP, ws);
+  const int per_wg = kWaves * 16 * NS;  // output rows per workgroup
+  const dim3 grid((d.H + per_wg - 1) / per_wg, SP + R);
+  const size_t lds = static_cast<size_t>(kWaves) * kUDn * NS * kSubtileBlock;
+  hipLaunchKernelGGL((down_mfma_kernel<NS, kUDn, kGR, E8, ROWS>), grid, dim3(kThreads), lds, s,
+                     w, scale, sw, sscale, d.H, d.I, d.Is, d.k, d.T, SP, ws);
 }
 
 // grid rows: the shared expert's passes, then the touched-expert slots
@@ -432,17 +461,16 @@ hipError_t launch_down_mfma(const LayerDims& d, int rows, const void* w2, const 
   const int SP = rows == kRoutedRows ? 0 : shared_rows(d);
   const int R = rows == kSharedRows ? 0 : slot_rows(d);
   if (SP + R == 0) return hipSuccess;
-  const int per_wg = kWaves * 16 * kNsDn;  // output rows per workgroup
-  dim3 grid((d.H + per_wg - 1) / per_wg, SP + R);
   const auto* w = static_cast<const uint8_t*>(w2);
   const auto* sw = static_cast<const uint8_t*>(sw2);
-#define MOE_DN(E8, ROWS) launch_dn<E8, ROWS>(grid, s, w, w2_scale, sw, sw2_scale, d, SP, ws)
+#define MOE_DN(NS, E8, ROWS) launch_dn<NS, E8, ROWS>(R, s, w, w2_scale, sw, sw2_scale, d, SP, ws)
   if (rows == kAllRows) {
-    if (d.e8m0) MOE_DN(true, kAllRows); else MOE_DN(false, kAllRows);
+    if (d.e8m0) MOE_DN(kNsDn, true, kAllRows); else MOE_DN(kNsDn, false, kAllRows);
   } else if (rows == kSharedRows) {
-    if (d.e8m0) MOE_DN(true, kSharedRows); else MOE_DN(false, kSharedRows);
+    if (d.e8m0) MOE_DN(kNsDn, true, kSharedRows); else MOE_DN(kNsDn, false, kSharedRows);
   } else {
-    if (d.e8m0) MOE_DN(true, kRoutedRows); else MOE_DN(false, kRoutedRows);
+    if (d.e8m0) MOE_DN(kNsDnRouted, true, kRoutedRows);
+    else MOE_DN(kNsDnRouted, false, kRoutedRows);
   }
 #undef MOE_DN
   return hipGetLastError();

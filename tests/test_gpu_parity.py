@@ -137,20 +137,21 @@ def test_route_tables_match_oracle(c_oracle):
     plan.close()
 
 
-@pytest.mark.parametrize("T", [37, 150])
+@pytest.mark.parametrize("T,H,I", [(37, 256, 128), (150, 256, 128), (150, 1152, 640)],
+                         ids=["T37", "T150", "T150-wide"])
 @pytest.mark.parametrize("path", [md.PATH_GEMV_SPLIT, md.PATH_GROUPED], ids=["split", "grouped"])
-def test_same_expert_for_every_token(T, path, c_oracle):
+def test_same_expert_for_every_token(T, H, I, path, c_oracle):
     """All tokens pick the same experts: one expert carries T tokens (the
     GEMV token loop runs several register passes; the MFMA kernels run
-    several 16-token groups and, past 64 tokens, several weight passes)."""
-    sh = LayerShape(T=T, H=256, E=16, k=2, I=128, Is=128, tag=302)
+    several 16-token passes per workgroup, each over the whole contraction)."""
+    sh = LayerShape(T=T, H=H, E=16, k=2, I=I, Is=128, tag=302)
     inp = make_layer(sh)
     # Every token carries token 0's vector x0; router rows 3 and 9 point along
     # x0 (logits |x0| and |x0|/2), every other row is zero (logit 0).
     from synth import f32_to_bf16_bits
     inp.hidden = np.ascontiguousarray(np.tile(inp.hidden[:1], (T, 1)))
     x0 = oracle.bf16_bits_to_f64(inp.hidden[0])
-    wr = np.zeros((16, 256), np.float32)
+    wr = np.zeros((16, H), np.float32)
     wr[3] = (x0 / np.linalg.norm(x0)).astype(np.float32)
     wr[9] = 0.5 * wr[3]
     inp.router_w = f32_to_bf16_bits(wr)
@@ -198,14 +199,22 @@ def test_smaller_T_than_plan_and_zero(c_oracle):
     plan.close()
 
 
-@pytest.mark.parametrize("path,T", [(md.PATH_GEMV, 16), (md.PATH_GEMV_SPLIT, 16),
-                                    (md.PATH_GROUPED, 16), (md.PATH_GROUPED, 80)],
-                         ids=["fused", "split", "grouped", "grouped-side-stream"])
-def test_graph_replay_matches_eager(path, T, c_oracle):
+@pytest.mark.parametrize("path,T,H,I", [(md.PATH_GEMV, 16, 1024, 512),
+                                        (md.PATH_GEMV_SPLIT, 16, 1024, 512),
+                                        (md.PATH_GROUPED, 16, 1024, 512),
+                                        (md.PATH_GROUPED, 80, 1024, 512),
+                                        (md.PATH_GROUPED, 24, 2304, 640),
+                                        (md.PATH_GROUPED, 80, 2304, 640)],
+                         ids=["fused", "split", "grouped", "grouped-side-stream",
+                              "grouped-wide", "grouped-wide-side-stream"])
+def test_graph_replay_matches_eager(path, T, H, I, c_oracle):
     """One run captured into a HIP graph, replayed several times with eager
     work in between; every replay equals the eager result bit for bit.  At
-    80 tokens the MFMA path puts the shared expert on the side stream."""
-    sh = WORKLOADS["decode_t16"].replace(T=T, H=1024, I=512, Is=256, tag=305)
+    80 tokens the MFMA path puts the shared expert on the side stream.  The
+    H = 2304, I = 640 cases give the MFMA kernels contractions of 18 and 5
+    blocks (so at 24 tokens the rotated block walks wrap at odd points) and a
+    shared expert narrower than the routed ones."""
+    sh = WORKLOADS["decode_t16"].replace(T=T, H=H, I=I, Is=256, tag=305)
     inp = make_layer(sh)
     dev = to_device(inp)
     plan = make_plan(sh, path=path)
