@@ -51,7 +51,8 @@ namespace fused {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr uint32_t kSpinLimit = 1u << 22;
-constexpr size_t kRouteSmem = 16 * 16 * 4 + kMaxExperts * 8 + kMaxExperts * 8 + 16;
+constexpr size_t kRouteSmem =
+    kSelBytes + 16 * 16 * 4 + kMaxExperts * 8 + kMaxExperts * 8 + 16;
 constexpr int kMaxRoutes = kFusedMaxTokens * kMaxTopK;  // most touched-expert slots
 static_assert(3 * kMaxRoutes * 4 <= kRouteSmem, "slot table must fit the routing scratch");
 

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
 
   // ---- phase 2: top-k of the block's tokens
   const RouteSmem sm(smem, T, E, k);
-  select_tokens<true>(t0, t0 + nt, E, k, rsf, ws.logits, bias, ws, ids_out, w_out, sm.ids);
+  select_tokens<true>(t0, t0 + nt, E, k, rsf, ws.logits, bias, ws, ids_out, w_out, sm);
   if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (gridDim.y > 1) {
     wait_memory();

@@ -44,6 +44,125 @@ __device__ inline int block_exclusive_scan(int v, int* s_tmp, int* total) {
   return base + inc - v;
 }
 
+// Per-wave LDS scratch of select_token, in 8-byte words: the 64 lane
+// maxima, the candidate keys (kMaxTopK lanes x 16 slots, plus zero padding
+// to a multiple of 8), the picks and the threshold (padded to a 16-byte
+// multiple).
+constexpr int kSelWaveWords = (64 + kMaxTopK * 16 + 8 + kMaxTopK + 1 + 1) & ~1;
+constexpr size_t kSelBytes = static_cast<size_t>(kRouteThreads / 64) * kSelWaveWords * 8;
+
+// Orders the LDS accesses of one wave: the compiler keeps them on their side
+// of this point, and a wave's LDS instructions complete in issue order, so
+// what every lane wrote before it is what every lane reads after it.
+__device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
+
+// Top-k of one token in one wave.  Keys are sigmoid(logit) + bias (bias is
+// never null: a zero vector stands in for no bias); the largest key wins,
+// equal keys go to the lower expert id.  Lane l holds experts l + 64 i
+// (slot i < ceil(E / 64)) as unique 64-bit keys (order-preserving key bits,
+// then ~id; 0 for a slot past E).
+//
+// Selection without serial rounds: tau = the k-th largest of the 64 lane
+// maxima (each lane counts the lane maxima above its own).  The k lanes
+// whose maximum reaches tau hold k keys >= tau, so every top-k key is
+// >= tau, and a key >= tau can only sit in one of those lanes.  They write
+// their keys >= tau to LDS (a k x ceil(E / 64) table, other entries 0), and
+// every candidate's rank is the number of table entries above it: every key
+// above a candidate is itself a candidate.  Rank j < k is the j-th pick.
+// A few LDS round trips replace k rounds of wave arg-max, each of which
+// waits on vector-to-scalar dependencies.  Lane j < k ends with the j-th
+// pick and its weight R * s_j / (s_0 + ... + s_{k-1}), summed in pick
+// order.  sel: this wave's kSelWaveWords words of LDS.
+//
+// NS = slots per lane, a power of two >= ceil(E / 64) (slots past E hold
+// key 0), so that every loop over a lane's keys unrolls with constant
+// indices.
+template <bool C, int NS>
+__device__ inline void select_token_ns(const float* logits, const float* bias, int E, int k,
+                                       float rsf, unsigned long long* sel, int* pick_id,
+                                       float* pick_w) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long* lmax = sel;
+  unsigned long long* cand = sel + 64;
+  unsigned long long* picks = cand + kMaxTopK * 16 + 8;
+  unsigned long long* thr = picks + kMaxTopK;
+  float sc[NS];
+  float bv[NS];
+  unsigned long long key[NS];
+  // every load first (clamped index)
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int e = lane + 64 * i;
+    const int ee = e < E ? e : E - 1;
+    sc[i] = ld_f32<C>(logits + ee);
+    bv[i] = bias[ee];
+  }
+  unsigned long long mx = 0ull;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int e = lane + 64 * i;
+    const float s = sigmoidf_(sc[i]);
+    sc[i] = s;
+    key[i] = e < E ? (static_cast<unsigned long long>(ordered_bits(s + bv[i])) << 32) |
+                         (0xffffffffu - static_cast<uint32_t>(e))
+                   : 0ull;
+    mx = key[i] > mx ? key[i] : mx;
+  }
+  lmax[lane] = mx;
+  wave_lds_order();
+  // lane maxima above this lane's: 16 keys per batch, the batch's loads first
+  int rank = 0;
+#pragma unroll
+  for (int j0 = 0; j0 < 64; j0 += 16) {
+    ulonglong2 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = reinterpret_cast<const ulonglong2*>(lmax + j0)[j];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rank += (v[j].x > mx ? 1 : 0) + (v[j].y > mx ? 1 : 0);
+  }
+  if (rank == k - 1) *thr = mx;
+  wave_lds_order();
+  const unsigned long long tau = *thr;
+  const bool holds = rank < k;  // exactly k lanes
+  if (holds) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) cand[rank * NS + i] = key[i] >= tau ? key[i] : 0ull;
+  }
+  // the table is padded with zeros to a multiple of 8 entries
+  const int nc = k * NS, nc8 = (nc + 7) & ~7;
+  if (lane < nc8 - nc) cand[nc + lane] = 0ull;
+  wave_lds_order();
+  if (holds) {
+    int r[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) r[i] = 0;
+    for (int j0 = 0; j0 < nc8; j0 += 8) {
+      ulonglong2 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = reinterpret_cast<const ulonglong2*>(cand + j0)[j];
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          r[i] += (v[j].x > key[i] ? 1 : 0) + (v[j].y > key[i] ? 1 : 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      if (key[i] >= tau && r[i] < k)
+        picks[r[i]] = (static_cast<unsigned long long>(__float_as_uint(sc[i])) << 32) |
+                      static_cast<uint32_t>(lane + 64 * i);
+  }
+  wave_lds_order();
+  if (lane < k) {
+    const unsigned long long p = picks[lane];
+    float ssum = 0.f;
+    for (int j = 0; j < k; ++j) ssum += __uint_as_float(static_cast<uint32_t>(picks[j] >> 32));
+    *pick_id = static_cast<int>(static_cast<uint32_t>(p));
+    *pick_w = rsf * __uint_as_float(static_cast<uint32_t>(p >> 32)) / ssum;
+  }
+  wave_lds_order();  // the next token's writes come after these reads
+}
+
 // One step of the DPP wave maximum of 64-bit values held as (hi, lo)
 // dwords: lanes take the neighbour's value named by the DPP control when it
 // is larger (one 64-bit compare).
@@ -73,18 +192,14 @@ __device__ __forceinline__ void wave_max_pair(uint32_t& hi, uint32_t& lo) {
   lo = __builtin_amdgcn_readlane(lo, 63);
 }
 
-// Top-k of one token in one wave.  Keys are sigmoid(logit) + bias (bias is
-// never null: a zero vector stands in for no bias); the largest key wins,
-// equal keys go to the lower expert id.  Lane l holds experts l + 64 i
-// (slot i < ceil(E / 64)) as order-preserving key bits, 0 marking a slot
-// that is taken or past E (a real key never maps to 0).  Each of the k
-// rounds takes every lane's best slot (strict >, so the lower slot, i.e. the
-// lower id, wins a tie), then a DPP wave maximum of (key, ~id).  (A radix
-// select over the key bits measures slower on gfx950: its 32 dependent
-// ballot/count steps cost more than k short DPP chains.)  Lane j < k ends
-// with the j-th pick and its weight R * s_j / sum of the k picked scores.
+// The same selection in k rounds, for more than 256 experts (where the
+// threshold table would need more registers than the router kernel can
+// spare).  Keys as above, 32-bit order-preserving bits per slot, 0 marking a
+// slot that is taken or past E (a real key never maps to 0).  Each round
+// takes every lane's best slot (strict >, so the lower slot, i.e. the lower
+// id, wins a tie), then a DPP wave maximum of (key, ~id).
 template <bool C>
-__device__ inline void select_token(const float* logits, const float* bias, int E, int k,
+__device__ inline void select_token_rounds(const float* logits, const float* bias, int E, int k,
                                     float rsf, int* pick_id, float* pick_w) {
   const int lane = threadIdx.x & 63;
   const int ns = (E + 63) >> 6;
@@ -140,16 +255,33 @@ __device__ inline void select_token(const float* logits, const float* bias, int 
   }
 }
 
+template <bool C>
+__device__ inline void select_token(const float* logits, const float* bias, int E, int k,
+                                    float rsf, unsigned long long* sel, int* pick_id,
+                                    float* pick_w) {
+  const int ns = (E + 63) >> 6;  // uniform
+  if (ns <= 1)
+    select_token_ns<C, 1>(logits, bias, E, k, rsf, sel, pick_id, pick_w);
+  else if (ns <= 2)
+    select_token_ns<C, 2>(logits, bias, E, k, rsf, sel, pick_id, pick_w);
+  else if (ns <= 4)
+    select_token_ns<C, 4>(logits, bias, E, k, rsf, sel, pick_id, pick_w);
+  else
+    select_token_rounds<C>(logits, bias, E, k, rsf, pick_id, pick_w);
+}
+
 // LDS bytes select_and_route needs (16-byte aligned base).
 __host__ __device__ inline size_t route_smem_bytes(int T, int E, int k) {
   const size_t R = static_cast<size_t>(T) * k, MW = (T + 63) / 64;
-  return ((R * 4 + 7) & ~static_cast<size_t>(7)) + static_cast<size_t>(E) * MW * 8 +
-         static_cast<size_t>(E) * 8 + 16;
+  return kSelBytes + ((R * 4 + 7) & ~static_cast<size_t>(7)) +
+         static_cast<size_t>(E) * MW * 8 + static_cast<size_t>(E) * 8 + 16;
 }
 
-// LDS carve-up of the routing step: s_ids [T*k], token masks [E * MW],
-// offsets [E], touched slot of each expert [E], scan scratch [4].
+// LDS carve-up of the routing step: the selection scratch of each wave
+// [4 * kSelWaveWords], s_ids [T*k], token masks [E * MW], offsets [E],
+// touched slot of each expert [E], scan scratch [4].
 struct RouteSmem {
+  unsigned long long* sel;
   int* ids;
   unsigned long long* mask;
   int* off;
@@ -157,6 +289,8 @@ struct RouteSmem {
   int* tmp;
   __device__ RouteSmem(unsigned char* smem, int T, int E, int k) {
     const size_t R = static_cast<size_t>(T) * k, MW = (T + 63) / 64;
+    sel = reinterpret_cast<unsigned long long*>(smem);
+    smem += kSelBytes;
     ids = reinterpret_cast<int*>(smem);
     mask = reinterpret_cast<unsigned long long*>(smem + ((R * 4 + 7) & ~static_cast<size_t>(7)));
     off = reinterpret_cast<int*>(mask + static_cast<size_t>(E) * MW);
@@ -171,12 +305,14 @@ struct RouteSmem {
 template <bool C>
 __device__ inline void select_tokens(int t_begin, int t_end, int E, int k, float rsf,
                                      const float* logits, const float* bias, const Workspace& ws,
-                                     int32_t* ids_out, float* w_out, int* s_ids) {
+                                     int32_t* ids_out, float* w_out, const RouteSmem& sm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int* s_ids = sm.ids;
+  unsigned long long* sel = sm.sel + static_cast<size_t>(wave) * kSelWaveWords;
   for (int t = t_begin + wave; t < t_end; t += kRouteThreads / 64) {
     int id = 0;
     float w = 0.f;
-    select_token<C>(logits + static_cast<size_t>(t) * E, bias, E, k, rsf, &id, &w);
+    select_token<C>(logits + static_cast<size_t>(t) * E, bias, E, k, rsf, sel, &id, &w);
     if (lane < k) {
       const int r = t * k + lane;
       s_ids[r] = id;
@@ -276,7 +412,7 @@ __device__ inline void select_and_route(int T, int E, int k, float rsf, const fl
                                         const float* bias, const Workspace& ws,
                                         int32_t* ids_out, float* w_out, unsigned char* smem) {
   const RouteSmem sm(smem, T, E, k);
-  select_tokens<C>(0, T, E, k, rsf, logits, bias, ws, ids_out, w_out, sm.ids);
+  select_tokens<C>(0, T, E, k, rsf, logits, bias, ws, ids_out, w_out, sm);
   build_routes<C>(T, E, k, ws, sm);
 }
 
