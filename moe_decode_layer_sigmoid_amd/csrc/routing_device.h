@@ -20,16 +20,25 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inclusive scan of v over the wave with DPP moves: shifts by 1, 2, 4, 8
+// within rows of 16 lanes (lanes with no source add 0), then the last lane of
+// row 0 is added to row 1 and of row 2 to row 3 (row_bcast:15), and the last
+// lane of row 1 to rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
 // Exclusive scan of v over the 256 threads (4 waves); returns the prefix and
 // writes the total to *total.  s_tmp holds 4 ints.
 __device__ inline int block_exclusive_scan(int v, int* s_tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(inc, off, 64);
-    if (lane >= off) inc += o;
-  }
+  const int inc = wave_inclusive_scan(v);
   if (lane == 63) s_tmp[wave] = inc;
   __syncthreads();
   int base = 0, tot = 0;
