@@ -8,8 +8,9 @@
 // shared expert (SharedExpert) takes the same weight pair and limit.
 //
 // Each touched expert's weights are streamed from HBM once for all of its
-// tokens.  A wave owns 32 weight rows (gate_up: 16 gate rows and the 16
-// matching up rows; down: 32 consecutive output rows) and walks the
+// tokens.  A wave owns 16 NS weight rows (gate_up: 8 NS gate rows and the
+// matching up rows; down: 16 NS consecutive output rows), so that each
+// activation fragment it loads feeds NS MFMA subtiles, and walks the
 // contraction dimension in 128-wide scale blocks.  The weights go from HBM
 // straight to the wave's own LDS area (global_load_lds_dwordx4): eight
 // consecutive lanes read the eight 16-byte pieces of one 128-byte block of
