@@ -69,8 +69,10 @@ __host__ __device__ constexpr size_t sync_words(int E) {
 }
 
 // Arrival counters of the router kernel in Workspace::counter: one 128-byte
-// line per block of kRouterTokBlk tokens, then one for the token blocks.
-constexpr int kRouterTokBlk = 4;   // one token per wave when ranking
+// line per token block, then one for the token blocks.  A block holds at most
+// kRouterTokBlk tokens (one per wave when ranking); launches of few tokens
+// use smaller blocks (router_block_tokens).
+constexpr int kRouterTokBlk = 4;
 constexpr int kRouterMaxBlk = 64;  // 256 tokens
 __host__ __device__ constexpr int router_cnt_line(int b) { return b * kSyncStride; }
 __host__ __device__ constexpr size_t router_cnt_words() {

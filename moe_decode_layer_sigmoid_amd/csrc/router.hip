@@ -11,7 +11,7 @@
 // Grid: x = blocks of 4 experts (one expert row per wave), then, when asked,
 // the shared expert's gate_up tiles (8 SwiGLU rows each, grid row 0 only: it
 // depends on no routing, so its weights stream while the router waits on
-// its memory round trips); y = blocks of kRouterTokBlk tokens.  Phase 1: every wave loads its whole bf16 router row at once
+// its memory round trips); y = blocks of TB tokens (router_block_tokens).  Phase 1: every wave loads its whole bf16 router row at once
 // (one memory round trip), then dots it with the block's token rows.
 // Phase 2: the last workgroup of each token block (an arrival counter per
 // block) ranks that block's tokens, one wave per token.  Phase 3: the last
@@ -34,7 +34,7 @@ constexpr int kThreads = 256;
 template <int NJ2, bool E8>
 __global__ __launch_bounds__(kThreads) void router_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ router_w,
-    const float* __restrict__ bias, int T, int H, int E, int k, float rsf, Workspace ws,
+    const float* __restrict__ bias, int T, int TB, int H, int E, int k, float rsf, Workspace ws,
     int32_t* __restrict__ ids_out, float* __restrict__ w_out, int n_router,
     const uint8_t* __restrict__ sw13, const void* __restrict__ sscale, int Is, float limit) {
   // 16-byte aligned: the 64-bit token masks need 8-byte aligned LDS
@@ -42,8 +42,8 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int s_last;
   const int wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.y * kRouterTokBlk;
-  const int nt = min(kRouterTokBlk, T - t0);
+  const int t0 = blockIdx.y * TB;
+  const int nt = min(TB, T - t0);
 
   // ---- columns past the router's: the shared expert's gate_up + SwiGLU,
   // which needs no routing and so streams in the router's shadow
@@ -93,6 +93,13 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
   build_routes<false>(T, E, k, ws, sm);
 }
 
+// Tokens per block: every wave of a block's workgroups loads all of the
+// block's token rows, so small blocks shorten the logits phase; larger ones
+// read the router weight fewer times (once per block).  One token per block
+// up to 16 tokens (2 us shorter at 16 tokens than blocks of 4), then
+// kRouterTokBlk (blocks of 2 measured slower at 64 and 128 tokens).
+int router_block_tokens(int T) { return T <= 16 ? 1 : kRouterTokBlk; }
+
 }  // namespace
 
 hipError_t launch_router(const LayerDims& d, const void* hidden, const void* router_w,
@@ -102,7 +109,8 @@ hipError_t launch_router(const LayerDims& d, const void* hidden, const void* rou
   if (d.T > kRouterMaxBlk * kRouterTokBlk) return hipErrorInvalidValue;
   const int n_router = (d.E + 3) / 4;
   const int n_shared = sw13 && d.Is > 0 ? d.Is / 8 : 0;  // 8 SwiGLU rows per workgroup
-  dim3 grid(n_router + n_shared, (d.T + kRouterTokBlk - 1) / kRouterTokBlk);
+  const int TB = router_block_tokens(d.T);
+  dim3 grid(n_router + n_shared, (d.T + TB - 1) / TB);
   const size_t smem = route_smem_bytes(d.T, d.E, d.k);
   const auto* x = static_cast<const uint16_t*>(hidden);
   const auto* w = static_cast<const uint16_t*>(router_w);
@@ -112,12 +120,12 @@ hipError_t launch_router(const LayerDims& d, const void* hidden, const void* rou
 #define X(N)                                                                                   \
   case 2 * N:                                                                                  \
     hipLaunchKernelGGL((router_kernel<N, false>), grid, dim3(kThreads), smem, s, x, w, bias,    \
-                       d.T, d.H, d.E, d.k, d.rsf, ws, ids_out, weights_out, n_router, sw,      \
+                       d.T, TB, d.H, d.E, d.k, d.rsf, ws, ids_out, weights_out, n_router, sw,      \
                        sw13_scale, Is, d.limit);                                               \
     break;                                                                                     \
   case 2 * N + 1:                                                                              \
     hipLaunchKernelGGL((router_kernel<N, true>), grid, dim3(kThreads), smem, s, x, w, bias,     \
-                       d.T, d.H, d.E, d.k, d.rsf, ws, ids_out, weights_out, n_router, sw,      \
+                       d.T, TB, d.H, d.E, d.k, d.rsf, ws, ids_out, weights_out, n_router, sw,      \
                        sw13_scale, Is, d.limit);                                               \
     break;
     X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
