@@ -19,20 +19,22 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 1024;  // 8 columns per thread: H <= 8192 in one pass
+constexpr int kMaxThreads = 1024;  // 8 columns per thread: H <= 8192 in one pass
 constexpr int kCols = 8;
 constexpr int kGroup = 8;        // routes whose rows one round of loads fetches
 
-// One workgroup per token.  Every load (top-k weights, the first kGroup
+// One workgroup per token, of ceil(H / 8) threads rounded up to whole waves
+// (a thread past H would only repeat loads of the row's last columns).
+// Every load (top-k weights, the first kGroup
 // routed rows, the shared row, the residual and gamma) is issued before the
 // first is used, and addresses are clamped instead of branched around, so
 // the common case (k <= 8) costs one memory round trip before the sum of
 // squares.  Sums run in a fixed order: routes j = 0..k-1, shared, residual;
-// waves 0..15 for the sum of squares.
-__global__ __launch_bounds__(kThreads) void epilogue_kernel(
+// waves in order for the sum of squares.
+__global__ __launch_bounds__(kMaxThreads) void epilogue_kernel(
     const uint16_t* residual, const uint16_t* __restrict__ gamma, int H, int k, int has_shared,
     float eps, Workspace ws, uint16_t* out, uint16_t* residual_out) {
-  __shared__ float s_part[kThreads / kWave];
+  __shared__ float s_part[kMaxThreads / kWave];
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = kCols * threadIdx.x;
@@ -88,7 +90,8 @@ __global__ __launch_bounds__(kThreads) void epilogue_kernel(
   __syncthreads();
   float tot = 0.f;
 #pragma unroll
-  for (int w = 0; w < kThreads / kWave; ++w) tot += s_part[w];
+  for (int w = 0; w < kMaxThreads / kWave; ++w)
+    if (w < static_cast<int>(blockDim.x) / kWave) tot += s_part[w];
   const float inv_rms = 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
   if (!live) return;
   const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
@@ -110,7 +113,8 @@ __global__ __launch_bounds__(kThreads) void epilogue_kernel(
 
 hipError_t launch_epilogue(const LayerDims& d, const void* residual, const void* gamma,
                            const Workspace& ws, void* out, void* residual_out, hipStream_t s) {
-  hipLaunchKernelGGL(epilogue_kernel, dim3(d.T), dim3(kThreads), 0, s,
+  const int threads = ((d.H / kCols + kWave - 1) / kWave) * kWave;
+  hipLaunchKernelGGL(epilogue_kernel, dim3(d.T), dim3(threads), 0, s,
                      static_cast<const uint16_t*>(residual), static_cast<const uint16_t*>(gamma),
                      d.H, d.k, static_cast<int>(d.Is > 0), d.eps, ws, static_cast<uint16_t*>(out),
                      static_cast<uint16_t*>(residual_out));
