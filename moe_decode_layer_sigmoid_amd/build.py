@@ -16,9 +16,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_decode.so")
 SOURCES = ["api.hip", "router.hip", "experts_gemv.hip", "experts_mfma.hip", "epilogue.hip",
-           "decode_fused.hip"]
+           "decode_fused.hip", "experts_chain.hip"]
 # decode_fused.hip is also compiled once per register chunk count and scale
-# format (the template arguments of its kernel), each into its own object.
+# format (the template arguments of its kernel), each into its own object;
+# experts_chain.hip once per w13 chunk count.
 FUSED_NJ = range(1, 9)
 ARCH = "gfx950"
 
@@ -62,6 +63,10 @@ def build(verbose: bool = False) -> str:
             jobs.append((obj, [hipcc(), *FLAGS, *inc, "-DMOE_FUSED_NJ=%d" % nj,
                                "-DMOE_FUSED_E8=%d" % e8, "-c",
                                os.path.join(CSRC, "decode_fused.hip"), "-o", obj]))
+    for nj in FUSED_NJ:
+        obj = os.path.join(objdir, "experts_chain_njg%d.o" % nj)
+        jobs.append((obj, [hipcc(), *FLAGS, *inc, "-DMOE_CHAIN_NJG=%d" % nj, "-c",
+                           os.path.join(CSRC, "experts_chain.hip"), "-o", obj]))
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", "0")) or os.cpu_count() or 1))
     with ThreadPoolExecutor(workers) as ex:
         results = list(ex.map(lambda j: _run(j[1]), jobs))

@@ -37,6 +37,7 @@ struct moe_decode_plan_s {
   hipEvent_t fork, join;
   hipEvent_t user_begin, user_end;
   uint32_t fused_grid;  // workgroups of the fused kernel (0: fused path unavailable)
+  bool chain;  // the split path's expert chain launch supports this layer shape
 };
 
 namespace {
@@ -85,6 +86,7 @@ size_t layout(const moe_decode_desc& d, char* base, moe::Workspace* ws) {
   w.sync = reinterpret_cast<uint32_t*>(take(moe::sync_words(static_cast<int>(E)) * 4));
   w.zero_bias = reinterpret_cast<float*>(take(E * 4));
   w.slot_tab = reinterpret_cast<int32_t*>(take(E * moe::kSlotInts * 4));
+  w.epi_part = reinterpret_cast<float*>(take(T * moe::kMaxBndSlices * 4));
   if (ws) *ws = w;
   return off;
 }
@@ -208,6 +210,7 @@ int moe_decode_plan(const moe_decode_desc* d, int device, moe_decode_plan_t* out
         moe::fused_nj(d->hidden, d->intermediate, d->shared_intermediate),
         d->scale_fmt == MOE_DECODE_SCALE_E8M0);
     p->fused_grid = static_cast<uint32_t>(per_cu > 0 ? per_cu * prop.multiProcessorCount : 0);
+    p->chain = moe::chain_supported(d->hidden, d->intermediate, d->shared_intermediate);
   }
   if (!rc && hipDeviceSynchronize() != hipSuccess) rc = MOE_DECODE_ERR_HIP;
   (void)hipSetDevice(prev);
@@ -291,11 +294,32 @@ static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t 
   };
 
   if (path == MOE_DECODE_PATH_GEMV_SPLIT) {
-    // router (with the shared expert's gate_up beside it), the routed
-    // gate_up, then the shared and routed down projections in one launch
+    // router (with the shared expert's gate_up beside it), then either the
+    // expert chain launch (shared down, routed gate_up and down, boundary) or,
+    // above its token limit, the routed gate_up, the shared and routed down
+    // projections in one launch, and the boundary
     step(moe::launch_router(d, a->hidden, a->router_w, static_cast<const float*>(bias), p->ws,
                             a->topk_ids, a->topk_weights, has_shared ? a->sw13 : nullptr,
                             a->sw13_scale, s));
+    if (T <= moe::kChainMaxTokens && p->chain) {
+      moe::ChainArgs c{};
+      moe::chain_items(d, &c);
+      c.hidden = static_cast<const uint16_t*>(a->hidden);
+      c.residual = static_cast<const uint16_t*>(a->residual);
+      c.w13 = static_cast<const uint8_t*>(a->w13);
+      c.w13_scale = a->w13_scale;
+      c.w2 = static_cast<const uint8_t*>(a->w2);
+      c.w2_scale = a->w2_scale;
+      c.sw2 = static_cast<const uint8_t*>(a->sw2);
+      c.sw2_scale = a->sw2_scale;
+      c.gamma = static_cast<const uint16_t*>(a->gamma);
+      c.out = static_cast<uint16_t*>(a->out);
+      c.residual_out = static_cast<uint16_t*>(a->residual_out);
+      if (err == hipSuccess && p->user_begin) step(hipEventRecord(p->user_begin, s));
+      if (err == hipSuccess) step(moe::launch_expert_chain(c, p->ws, s));
+      if (err == hipSuccess && p->user_end) step(hipEventRecord(p->user_end, s));
+      return err == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;
+    }
     if (err == hipSuccess && p->user_begin) step(hipEventRecord(p->user_begin, s));
     if (err == hipSuccess)
       step(moe::launch_gate_up_gemv(d, a->hidden, a->w13, a->w13_scale, p->ws, s));

@@ -44,63 +44,17 @@
 #include "gemv_tiles.h"
 #include "launch.h"
 #include "routing_device.h"
+#include "sync_device.h"
 
 namespace moe {
 namespace fused {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr size_t kRouteSmem =
     kSelBytes + 16 * 16 * 4 + kMaxExperts * 8 + kMaxExperts * 8 + 16;
 constexpr int kMaxRoutes = kFusedMaxTokens * kMaxTopK;  // most touched-expert slots
 static_assert(3 * kMaxRoutes * 4 <= kRouteSmem, "slot table must fit the routing scratch");
-
-struct Sync {
-  uint32_t* base;
-  __device__ uint32_t* line(int i) const { return base + static_cast<size_t>(i) * kSyncStride; }
-};
-
-// Sets flag f (all kFlagRep replicas).  Called by one thread.
-__device__ __forceinline__ void raise_flag(const Sync& sy, int f) {
-#pragma unroll
-  for (int r = 0; r < kFlagRep; ++r)
-    __hip_atomic_store(sy.line(f + r), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Publishes this workgroup's coherent stores, then bumps counter `cnt`; the
-// bump that reaches `target` raises flag `f` (f < 0: no flag).  Returns, to
-// every thread, whether this bump completed the counter.
-__device__ __forceinline__ bool signal(const Sync& sy, int cnt, uint32_t target, int f, int* s_flag) {
-  wait_memory();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(sy.line(cnt), 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = prev + 1 == target;
-    if (last && f >= 0) raise_flag(sy, f);
-    *s_flag = last;
-  }
-  __syncthreads();
-  return *s_flag != 0;
-}
-
-// Waits until flag f is up, polling this workgroup's replica (bounded: sets
-// the error word and gives up after kSpinLimit polls).
-__device__ __forceinline__ void wait_flag(const Sync& sy, int f) {
-  if (threadIdx.x == 0) {
-    const uint32_t* p = sy.line(f + static_cast<int>(blockIdx.x % kFlagRep));
-    uint32_t n = 0;
-    while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++n == kSpinLimit) {
-        __hip_atomic_fetch_or(sy.line(kSyncError), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
-  }
-  __syncthreads();
-}
 
 template <int NJ, bool E8>
 hipError_t launch_nj(const FusedArgs& a, const Workspace& ws, hipStream_t s);
@@ -221,28 +175,9 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
     __syncthreads();
   }
 
-  // Two-level exit count; the last workgroup out zeroes every counter and flag
-  // for the next launch (HIP-graph replays included).  The error word stays.
-  if (threadIdx.x == 0) {
-    const uint32_t lines = kSyncExitLines;
-    const uint32_t line = blockIdx.x % lines;
-    const uint32_t share = a.grid / lines + (line < a.grid % lines ? 1u : 0u);
-    const uint32_t prev = __hip_atomic_fetch_add(sy.line(kSyncExit0 + static_cast<int>(line)), 1u,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int last = 0;
-    if (prev == share - 1) {
-      const uint32_t top = __hip_atomic_fetch_add(sy.line(kSyncExitTop), 1u, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-      last = top == (a.grid < lines ? a.grid : lines) - 1;
-    }
-    s_flag = last;
-  }
-  __syncthreads();
-  if (s_flag) {
-    for (int i = threadIdx.x; i < sync_lines(a.dmax); i += kThreads)
-      if (i != kSyncError)
-        __hip_atomic_store(sy.line(i), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  // The last workgroup out zeroes every counter and flag for the next launch
+  // (HIP-graph replays included).  The error word stays.
+  if (last_out(sy, a.grid, &s_flag)) reset_sync(sy, sync_lines(a.dmax));
 }
 
 template <int NJ, bool E8>

@@ -168,36 +168,48 @@ __device__ __forceinline__ void gate_up_wave(const uint16_t* __restrict__ hidden
   }
 }
 
-// down projection of one wave: output rows h0 .. h0+3 (h0 % 4 == 0) of one
-// expert for its n >= 1 SwiGLU rows act[(base + q) * I], written to
-// out[o * H + h0 .. +3] with o = out_route[base + q] (the route index t*k+j),
-// or o = base + q when out_route is null.  fp32 products and sums (the
-// SwiGLU activations stay fp32).  NJ = ceil(I / 1024); TB, C, E8 as above.
-template <int NJ, int TB, bool C, bool E8>
+// No wait between a tile's weight loads and its first use of activations.
+struct NoWait {
+  __device__ void operator()() const {}
+};
+
+// down projection of one wave: output rows h0 .. h0+R-1 (h0 % R == 0, R = 4
+// or 8) of one expert for its n >= 1 SwiGLU rows act[(base + q) * I],
+// written to out[o * H + h0 .. +R-1] with o = out_route[base + q] (the route
+// index t*k+j), or o = base + q when out_route is null.  fp32 products and
+// sums (the SwiGLU activations stay fp32).  NJ = ceil(I / 1024); TB, C, E8
+// as above, C for the stores; CL = coherent loads of act and out_route.
+// wait() runs after the weight loads are issued and before act is read (a
+// workgroup whose activations come from other workgroups of the same launch
+// waits there for them while its weights stream in; it must be called by
+// every wave of the workgroup).
+template <int NJ, int TB, bool C, bool E8, bool CL = C, typename Wait = NoWait, int R = 4>
 __device__ __forceinline__ void down_wave(const uint8_t* __restrict__ W,
                                           const void* __restrict__ scale, size_t sbase, int H,
                                           int I, int h0, int n, int base,
                                           const int32_t* out_route, const float* act,
-                                          float* out) {
+                                          float* out, Wait wait = Wait()) {
+  static_assert(R == 4 || R == 8, "4 or 8 rows per wave");
   const int lane = threadIdx.x & 63;
   const int ib_n = I / kBlock;
   const int nchunk = I / 16;
-  uint4 wv[4][NJ];
+  uint4 wv[R][NJ];
   float sc[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int c = lane + 64 * j;
     const int cc = c < nchunk ? c : nchunk - 1;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < R; ++r)
       wv[r][j] = ld_stream16(W + static_cast<size_t>(h0 + r) * I + 16 * cc);
     const float s0 = load_scale<E8>(scale, sbase + static_cast<size_t>(h0 / kBlock) * ib_n + cc / 8);
     sc[j] = c < nchunk ? s0 : 0.f;
   }
+  wait();
   for (int q0 = 0; q0 < n; q0 += TB) {
-    float acc[4][TB];
+    float acc[R][TB];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int qq = 0; qq < TB; ++qq) acc[r][qq] = 0.f;
 #pragma unroll
@@ -211,30 +223,33 @@ __device__ __forceinline__ void down_wave(const uint8_t* __restrict__ W,
         float af[16];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const float4 v = ld_f32x4<C>(ap + 4 * m);
+          const float4 v = ld_f32x4<CL>(ap + 4 * m);
           af[4 * m] = v.x;
           af[4 * m + 1] = v.y;
           af[4 * m + 2] = v.z;
           af[4 * m + 3] = v.w;
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r][qq] = fmaf(sc[j], dot16_fp8(wv[r][j], af), acc[r][qq]);
+        for (int r = 0; r < R; ++r) acc[r][qq] = fmaf(sc[j], dot16_fp8(wv[r][j], af), acc[r][qq]);
       }
     }
 #pragma unroll
     for (int qq = 0; qq < TB; ++qq) {
       if (q0 + qq >= n) continue;
-      float v[4];
+      float v[R];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = wave_sum(acc[r][qq]);
+      for (int r = 0; r < R; ++r) v[r] = wave_sum(acc[r][qq]);
       if (lane == 0) {
-        const int o = out_route ? ld_i32<C>(out_route + base + q0 + qq) : base + q0 + qq;
-        st_f32x4<C>(out + static_cast<size_t>(o) * H + h0, make_float4(v[0], v[1], v[2], v[3]));
+        const int o = out_route ? ld_i32<CL>(out_route + base + q0 + qq) : base + q0 + qq;
+#pragma unroll
+        for (int r = 0; r < R; r += 4)
+          st_f32x4<C>(out + static_cast<size_t>(o) * H + h0 + r,
+                      make_float4(v[r], v[r + 1], v[r + 2], v[r + 3]));
       }
     }
     if (q0 + TB < n) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) opaque(wv[r][j]);
     }
@@ -301,7 +316,9 @@ constexpr int kEpiGroup = 8;  // routes whose rows one round of loads fetches
 // residual_out = bf16(h), out = bf16(h / sqrt(mean(h^2) + eps) * gamma).
 // Every load of a group of routes is issued before any is used.
 // s_part: 4 floats of LDS.
-template <bool C = false>
+// GRP = routes whose rows one round of loads fetches (fewer registers with a
+// smaller group).
+template <bool C = false, int GRP = kEpiGroup>
 __device__ __forceinline__ void epilogue_token(int t, const uint16_t* residual,
                                                const uint16_t* __restrict__ gamma, int H, int k,
                                                bool has_shared, float eps, const Workspace& ws,
@@ -318,11 +335,11 @@ __device__ __forceinline__ void epilogue_token(int t, const uint16_t* residual,
     float acc[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) acc[m] = 0.f;
-    for (int j0 = 0; j0 < k; j0 += kEpiGroup) {
-      float wj[kEpiGroup];
-      float4 ra[kEpiGroup], rb[kEpiGroup];
+    for (int j0 = 0; j0 < k; j0 += GRP) {
+      float wj[GRP];
+      float4 ra[GRP], rb[GRP];
 #pragma unroll
-      for (int q = 0; q < kEpiGroup; ++q) {
+      for (int q = 0; q < GRP; ++q) {
         const int j = j0 + q < k ? j0 + q : k - 1;  // clamped: no branch around the loads
         const float w = ld_f32<C>(ws.weights + t * k + j);
         wj[q] = j0 + q < k ? w : 0.f;
@@ -331,7 +348,7 @@ __device__ __forceinline__ void epilogue_token(int t, const uint16_t* residual,
         rb[q] = ld_f32x4<C>(row + 4);
       }
 #pragma unroll
-      for (int q = 0; q < kEpiGroup; ++q) {
+      for (int q = 0; q < GRP; ++q) {
         acc[0] = fmaf(wj[q], ra[q].x, acc[0]);
         acc[1] = fmaf(wj[q], ra[q].y, acc[1]);
         acc[2] = fmaf(wj[q], ra[q].z, acc[2]);

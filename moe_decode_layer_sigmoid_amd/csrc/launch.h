@@ -26,6 +26,7 @@ struct Workspace {
   float* zero_bias;    // [E] zeros: the router bias when the caller passes none
   int32_t* slot_tab;   // [E][kSlotInts] touched slot d: expert (-1: no expert), route
                        // count, first permuted position, -, first kSlotRoutes routes
+  float* epi_part;     // [maxT][kMaxBndSlices] boundary slices' sums of squares
 };
 
 // Per-slot record the router leaves for the expert kernels, so that a
@@ -115,6 +116,31 @@ struct FusedArgs {
   uint32_t grid;
 };
 
+// Arguments of the expert chain launch of the few-token GEMV path (see
+// experts_chain.hip): item offsets and counts, the grid (items + 1).
+constexpr int kChainMaxTokens = 16;
+constexpr int kBndCols = 2048;     // columns of one boundary workgroup (8 per thread)
+constexpr int kMaxBndSlices = 4;   // H <= 8192
+struct ChainArgs {
+  const uint16_t* hidden;
+  const uint16_t* residual;
+  const uint8_t* w13;
+  const void* w13_scale;
+  const uint8_t* w2;
+  const void* w2_scale;
+  const uint8_t* sw2;
+  const void* sw2_scale;
+  const uint16_t* gamma;
+  uint16_t* out;
+  uint16_t* residual_out;
+  int T, H, k, I, Is, e8m0;
+  float limit, eps;
+  int gu_per, dn_per, dmax;  // items per slot; touched-slot rows of the grid
+  int o_rgu, o_rdn, n_items, gu_items;
+  int bnd_ns;  // boundary workgroups per token (kBndCols columns each)
+  uint32_t grid;
+};
+
 struct LayerDims {
   int T, H, E, k, I, Is;
   bool e8m0;
@@ -155,6 +181,12 @@ int fused_nj(int H, int I, int Is);
 int fused_blocks_per_cu(int nj, bool e8m0);
 void fused_items(const LayerDims& d, FusedArgs* a);
 hipError_t launch_decode_fused(const FusedArgs& a, const Workspace& ws, hipStream_t s);
+
+// Shared down, routed gate_up, routed down and the boundary in one launch
+// (T <= kChainMaxTokens; H <= 8192; I and I_s <= 4096).
+bool chain_supported(int H, int I, int Is);
+void chain_items(const LayerDims& d, ChainArgs* a);
+hipError_t launch_expert_chain(const ChainArgs& a, const Workspace& ws, hipStream_t s);
 
 // Weighted combine + shared + residual, RMSNorm * gamma, bf16 outputs.
 hipError_t launch_epilogue(const LayerDims& d, const void* residual, const void* gamma,

@@ -72,8 +72,9 @@ def run_layer(plan, dev, T, alias_residual=False, stream=None, keep_device=False
              sw13_scale=dev["sw13_scale"], sw2=dev["sw2"], sw2_scale=dev["sw2_scale"],
              gamma=dev["gamma"], out=out, residual_out=res_out, topk_ids=ids, topk_weights=w)
     torch.cuda.synchronize()
-    if plan.path_for(T) == md.PATH_GEMV:
-        assert not plan.check_waits(), "a bounded wait of the fused kernel gave up"
+    # the persistent launches (the fused kernel, the split path's expert chain)
+    # wait on each other's workgroups with bounded waits
+    assert not plan.check_waits(), "a bounded wait gave up"
     got = dict(out=bf16_to_np(out), residual_out=bf16_to_np(res_out), ids=ids.cpu().numpy(),
                weights=w.cpu().numpy().astype(np.float64))
     if keep_device:

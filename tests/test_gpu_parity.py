@@ -163,6 +163,24 @@ def test_same_expert_for_every_token(T, H, I, path, c_oracle):
     plan.close()
 
 
+@pytest.mark.parametrize("T", [1, 5, 16])
+@pytest.mark.parametrize("path", [md.PATH_GEMV, md.PATH_GEMV_SPLIT, md.PATH_GROUPED],
+                         ids=["fused", "split", "grouped"])
+def test_alternating_inputs_on_one_plan(path, T, c_oracle):
+    """Two different layers (other weights, other tokens) run in turn on one
+    plan: every run matches its own oracle, so nothing a run leaves in the
+    workspace or in the caches (SwiGLU rows, down rows, route tables,
+    counters) leaks into the next one."""
+    sh = WORKLOADS["decode_t16"].replace(T=T, H=2048, I=768, Is=512, E=32, tag=306)
+    inps = [make_layer(sh, seed=s) for s in (0, 1)]
+    devs = [to_device(i) for i in inps]
+    plan = make_plan(sh, path=path)
+    for r in range(4):
+        got = run_layer(plan, devs[r % 2], T)
+        check_layer(inps[r % 2], got, c_oracle=c_oracle)
+    plan.close()
+
+
 @pytest.mark.parametrize("path", [md.PATH_GEMV, md.PATH_GEMV_SPLIT, md.PATH_GROUPED],
                          ids=["fused", "split", "grouped"])
 def test_residual_alias_and_determinism(path, c_oracle):
