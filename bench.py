@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 MERGE_SHARED_MAX_TOKENS = 64  # the library's kMergeSharedMaxTokens
+CHAIN_MAX_TOKENS = 16  # the library's kChainMaxTokens (split path: one expert launch)
 # template arguments (NS, U, GR) of the library's gate_up MFMA launches (kNsGu, kUGu, kGR)
 MFMA_GATE_UP_TILE = "4, 1, 1"
 METRIC = "µs per MoE layer and effective HBM TB/s (fraction of peak) at 1/16/64/128 tok"
@@ -396,6 +397,16 @@ def main():
             if sh.Is and merged:
                 kern_bytes += (2 * sh.Is * H + sb * (2 * sh.Is // 128) * (H // 128)
                                + T * sh.Is * 4)
+        elif T <= CHAIN_MAX_TOKENS:
+            # one launch streams the touched experts' gate_up and down weights
+            # and the shared expert's down weights, and ends with the boundary
+            # (the shared gate_up rides in the router launch)
+            kern_name = "expert_chain_kernel<NJG, NJD, E8> (routed experts, shared down, boundary)"
+            njd = (max(sh.I, sh.Is) + 1023) // 1024
+            kern_id = "expert_chain_kernel<%d, %d, %s>" % ((H + 1023) // 1024, njd, e8)
+            kern_bytes = routed_b + act_b
+            if sh.Is:
+                kern_bytes += H * sh.Is + sb * (H // 128) * (sh.Is // 128)
         else:
             kern_name = "gate_up_kernel<NJ, E8> (routed experts)"
             kern_id = "gate_up_kernel<%d, %s>" % ((H + 1023) // 1024, e8)

@@ -338,9 +338,46 @@ __device__ inline void select_tokens(int t_begin, int t_end, int E, int k, float
 // the slot records ws.slot_tab (expert -1 for slots past the touched count,
 // up to min(T*k, E)) (coherent stores when C).  Its first barrier comes before the first read of
 // sm.ids, so callers may fill sm.ids right before the call.
+// One token: its k picks are k distinct experts, one route each.  Expert e's
+// position is the number of picks with a lower id; every table follows from
+// that without the token masks and the block scan (same tables as below).
+template <bool C>
+__device__ inline void build_routes_one_token(int E, int k, const Workspace& ws,
+                                              const RouteSmem& sm) {
+  __syncthreads();  // sm.ids complete
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+    int below = 0, j_of = -1;
+    for (int j = 0; j < k; ++j) {
+      const int id = sm.ids[j];
+      below += id < e ? 1 : 0;
+      j_of = id == e ? j : j_of;
+    }
+    st_i32<C>(ws.counts + e, j_of >= 0 ? 1 : 0);
+    st_i32<C>(ws.offsets + e, below);
+    if (j_of >= 0) {
+      st_i32<C>(ws.touched + below, e);
+      st_i32<C>(ws.perm + below, j_of);
+      st_i32<C>(ws.inv + j_of, below);
+      int32_t* rec = ws.slot_tab + static_cast<size_t>(below) * kSlotInts;
+      st_i32<C>(rec, e);
+      st_i32<C>(rec + 1, 1);
+      st_i32<C>(rec + 2, below);
+      st_i32<C>(rec + 4, j_of);
+    }
+  }
+  if (threadIdx.x == 0) {
+    st_i32<C>(ws.offsets + E, k);
+    st_i32<C>(ws.n_touched, k);
+  }
+}
+
 template <bool C>
 __device__ inline void build_routes(int T, int E, int k, const Workspace& ws,
                                     const RouteSmem& sm) {
+  if (T == 1) {
+    build_routes_one_token<C>(E, k, ws, sm);
+    return;
+  }
   const int R = T * k;
   const int MW = (T + 63) / 64;
   for (int i = threadIdx.x; i < E * MW; i += kRouteThreads) sm.mask[i] = 0ull;

@@ -113,8 +113,9 @@ def test_paths_agree(T, c_oracle):
         check_layer(inp, r, c_oracle=c_oracle)
 
 
-def test_route_tables_match_oracle(c_oracle):
-    sh = WORKLOADS["decode_t16"].replace(H=1024, I=256, Is=256, tag=301)
+@pytest.mark.parametrize("T", [1, 16])
+def test_route_tables_match_oracle(T, c_oracle):
+    sh = WORKLOADS["decode_t16"].replace(T=T, H=1024, I=256, Is=256, tag=301)
     inp = make_layer(sh)
     dev = to_device(inp)
     plan = make_plan(sh)
