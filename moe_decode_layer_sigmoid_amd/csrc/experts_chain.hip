@@ -35,7 +35,7 @@
 // every wait ends; waits are bounded anyway (a sticky error word,
 // moe_decode_check_waits).  Completion counts are bumped with atomics whose
 // result is not used (no workgroup waits for them); the router launch that
-// precedes every chain launch zeroes them.  SwiGLU rows and down rows are
+// precedes every chain launch zeroes them (and arms the boundary's slots).  SwiGLU rows and down rows are
 // written with agent-scope atomic stores (sync_device.h).
 #include "device_common.h"
 #include "gemv_tiles.h"
@@ -61,55 +61,58 @@ constexpr uint32_t kChainSpin = 1u << 17;
 template <int NJG, int NJD, bool E8>
 hipError_t launch_t(const ChainArgs& a, const Workspace& ws, hipStream_t s);
 
-// Counter line of token t's boundary slices (the flag lines, unused here).
-__host__ __device__ constexpr int token_line(int t) { return kSyncFlags + t; }
-static_assert(kNumFlags * kFlagRep >= kChainMaxTokens, "a line per token");
-
 #ifdef MOE_CHAIN_NJG
 // The boundary of token t, columns [kBndCols * s, +kBndCols) (8 per thread),
-// by one of the token's ns workgroups: h = sum_j w[t, j] * rows[t*k + j] +
-// y_s[t] + residual[t] (fixed order), the slice's sum of squares (waves in
-// order) published in ws.epi_part and counted on the token's line; once all
-// ns slices are in, their sums in slice order give the RMS, and the slice of
-// residual_out = bf16(h), out = bf16(h / sqrt(mean(h^2) + eps) * gamma) is
-// written.  Every load of the slice is issued before the first use.
-__device__ __forceinline__ void boundary_slice(const ChainArgs& a, const Workspace& ws,
-                                               const Sync& sy, int t, int s, float* s_part) {
+// by one of the token's bnd_ns workgroups: h = sum_j w[t, j] * rows[t*k + j]
+// + y_s[t] + residual[t] (fixed order); the slice's sum of squares (waves in
+// order) goes to ws.epi_part[t][s], which the router launch armed with
+// kEpiEmpty; once every slice of the token is in, their sums in slice order
+// give the RMS, and the slice of residual_out = bf16(h), out = bf16(h /
+// sqrt(mean(h^2) + eps) * gamma) is written.  The loads that do not depend on
+// the down rows (top-k weights, residual, gamma) are issued before `wait`;
+// the rest of the slice's loads all before their first use.
+template <typename Wait>
+__device__ __forceinline__ void boundary_slice(const ChainArgs& a, const Workspace& ws, int t,
+                                               int s, float* s_part, float* s_tot, Wait wait) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int H = a.H, k = a.k, ns = a.bnd_ns;
   const int c = kBndCols * s + 8 * static_cast<int>(threadIdx.x);
   const bool live = c < H;
   const int c0 = live ? c : H - 8;  // clamped: loads stay in the row
-  const float* rows_t = ws.rows + static_cast<size_t>(t) * k * H + c0;
-  const float* ys = ws.y_s + static_cast<size_t>(t) * H + c0;
   const uint4 rv = *reinterpret_cast<const uint4*>(a.residual + static_cast<size_t>(t) * H + c0);
   const uint4 gv = *reinterpret_cast<const uint4*>(a.gamma + c0);
+  float wts[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) wts[j] = ws.weights[t * k + (j < k ? j : k - 1)];
+  wait();
+  const float* rows_t = ws.rows + static_cast<size_t>(t) * k * H + c0;
+  const float* ys = ws.y_s + static_cast<size_t>(t) * H + c0;
   const float4 ya = *reinterpret_cast<const float4*>(ys);
   const float4 yb = *reinterpret_cast<const float4*>(ys + 4);
   float acc[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) acc[m] = 0.f;
-  for (int j0 = 0; j0 < k; j0 += 8) {
-    float wj[8];
+#pragma unroll
+  for (int j0 = 0; j0 < kMaxTopK; j0 += 8) {
+    if (j0 >= k) break;  // uniform
     float4 ra[8], rb[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const int j = j0 + q < k ? j0 + q : k - 1;
-      const float w = ws.weights[t * k + j];
-      wj[q] = j0 + q < k ? w : 0.f;
+      const int j = j0 + q < k ? j0 + q : k - 1;  // clamped: no branch around the loads
       ra[q] = *reinterpret_cast<const float4*>(rows_t + static_cast<size_t>(j) * H);
       rb[q] = *reinterpret_cast<const float4*>(rows_t + static_cast<size_t>(j) * H + 4);
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      acc[0] = fmaf(wj[q], ra[q].x, acc[0]);
-      acc[1] = fmaf(wj[q], ra[q].y, acc[1]);
-      acc[2] = fmaf(wj[q], ra[q].z, acc[2]);
-      acc[3] = fmaf(wj[q], ra[q].w, acc[3]);
-      acc[4] = fmaf(wj[q], rb[q].x, acc[4]);
-      acc[5] = fmaf(wj[q], rb[q].y, acc[5]);
-      acc[6] = fmaf(wj[q], rb[q].z, acc[6]);
-      acc[7] = fmaf(wj[q], rb[q].w, acc[7]);
+      const float w = j0 + q < k ? wts[j0 + q] : 0.f;
+      acc[0] = fmaf(w, ra[q].x, acc[0]);
+      acc[1] = fmaf(w, ra[q].y, acc[1]);
+      acc[2] = fmaf(w, ra[q].z, acc[2]);
+      acc[3] = fmaf(w, ra[q].w, acc[3]);
+      acc[4] = fmaf(w, rb[q].x, acc[4]);
+      acc[5] = fmaf(w, rb[q].y, acc[5]);
+      acc[6] = fmaf(w, rb[q].z, acc[6]);
+      acc[7] = fmaf(w, rb[q].w, acc[7]);
     }
   }
   if (a.Is > 0) {
@@ -128,16 +131,30 @@ __device__ __forceinline__ void boundary_slice(const ChainArgs& a, const Workspa
   ss = wave_sum(live ? ss : 0.f);
   if (lane == 0) s_part[wave] = ss;
   __syncthreads();
-  if (threadIdx.x == 0)
-    st_f32<true>(ws.epi_part + t * kMaxBndSlices + s,
-                 (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]));
-  bump(sy, token_line(t));
-  wait_count(sy, token_line(t), 1, static_cast<uint32_t>(ns), kChainSpin);
-  if (static_cast<int>(threadIdx.x) < ns)
-    s_part[threadIdx.x] = ld_f32<true>(ws.epi_part + t * kMaxBndSlices + threadIdx.x);
+  float* part = ws.epi_part + t * kMaxBndSlices;
+  if (wave == 0) {
+    // publish this slice's sum (no wait for the store), then poll the token's
+    // slices, one lane each, until none is empty
+    if (lane == 0) st_f32<true>(part + s, (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]));
+    uint32_t polls = 0;
+    float v = 0.f;
+    for (;;) {
+      v = ld_f32<true>(part + (lane < ns ? lane : 0));
+      const bool in = lane >= ns || __float_as_uint(v) != kEpiEmpty;
+      if (__builtin_amdgcn_ballot_w64(!in) == 0) break;  // uniform over the wave
+      __builtin_amdgcn_s_sleep(1);
+      if (++polls == kChainSpin) {
+        if (lane == 0)
+          __hip_atomic_fetch_or(ws.sync + kSyncError * kSyncStride, 1u, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+    if (lane < ns) s_tot[lane] = v;
+  }
   __syncthreads();
   float tot = 0.f;
-  for (int i = 0; i < ns; ++i) tot += s_part[i];
+  for (int i = 0; i < ns; ++i) tot += s_tot[i];
   const float inv_rms = 1.0f / sqrtf(tot / static_cast<float>(H) + a.eps);
   if (!live) return;
   const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
@@ -215,10 +232,12 @@ __global__ __launch_bounds__(kThreads) void expert_chain_kernel(ChainArgs a, Wor
 
   // ---- the boundary (the last T * bnd_ns workgroups), after every down item
   // (shared and routed, empty slots included)
-  wait_count(sy, kSyncExit0, kSyncExitLines, static_cast<uint32_t>(a.n_items - a.gu_items),
-             kChainSpin);
+  __shared__ float s_tot[kMaxBndSlices];
   const int b = it - a.n_items;
-  boundary_slice(a, ws, sy, b / a.bnd_ns, b % a.bnd_ns, s_part);
+  boundary_slice(a, ws, b / a.bnd_ns, b % a.bnd_ns, s_part, s_tot, [&]() {
+    wait_count(sy, kSyncExit0, kSyncExitLines, static_cast<uint32_t>(a.n_items - a.gu_items),
+               kChainSpin);
+  });
 }
 
 template <int NJG, int NJD, bool E8>

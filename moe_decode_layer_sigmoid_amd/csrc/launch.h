@@ -121,6 +121,8 @@ struct FusedArgs {
 constexpr int kChainMaxTokens = 16;
 constexpr int kBndCols = 2048;     // columns of one boundary workgroup (8 per thread)
 constexpr int kMaxBndSlices = 4;   // H <= 8192
+constexpr uint32_t kEpiEmpty = 0xffffffffu;  // an empty slot of Workspace::epi_part (a NaN
+                                             // no sum of squares takes)
 struct ChainArgs {
   const uint16_t* hidden;
   const uint16_t* residual;
