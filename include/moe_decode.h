@@ -87,9 +87,12 @@ typedef enum {
    * touched experts), down (the same), boundary; above 64 tokens the shared
    * expert's passes run on the plan's side stream instead. */
   MOE_DECODE_PATH_GROUPED = 2,
-  /* The GEMV kernels launched one after another: router (with the shared
-   * expert's gate_up beside it), routed gate_up, down (shared and routed),
-   * boundary. */
+  /* The GEMV kernels launched one after another: the router (with the
+   * shared expert's gate_up beside it), then, up to 16 tokens, one expert
+   * chain launch (the shared expert's down, the touched experts' gate_up and
+   * down, the boundary; its workgroups hand rows to each other through
+   * counters with bounded waits), above 16 tokens the routed gate_up, down
+   * (shared and routed) and boundary kernels. */
   MOE_DECODE_PATH_GEMV_SPLIT = 3
 } moe_decode_path;
 
@@ -196,11 +199,14 @@ int moe_decode_last_routes(moe_decode_plan_t p, int32_t T, int32_t* counts, int3
                            int32_t* perm, int32_t* touched, int32_t* n_touched, void* stream);
 
 /*
- * Measurement hook: when both are non-NULL, each later run records hipEvent_t
- * `begin` on `stream` just before its dominant kernel and `end` just after
- * it: the fused persistent kernel on MOE_DECODE_PATH_GEMV, the routed-expert
- * gate/up projection kernel on MOE_DECODE_PATH_GEMV_SPLIT and
- * MOE_DECODE_PATH_GROUPED.  NULL, NULL switches it off.
+ * Measurement hook: when both are non-NULL, each later run launches its
+ * dominant kernel with hipExtLaunchKernel, which records hipEvent_t `begin`
+ * and `end` (created by the caller, timing enabled) at that kernel's own start
+ * and end.  The dominant kernel is the fused persistent kernel on
+ * MOE_DECODE_PATH_GEMV; on MOE_DECODE_PATH_GEMV_SPLIT the expert chain launch
+ * (up to 16 tokens) or the routed-expert gate/up projection kernel; on
+ * MOE_DECODE_PATH_GROUPED the gate/up projection kernel.  NULL, NULL switches
+ * it off.  Eager runs only: not for use under graph capture.
  */
 int moe_decode_set_expert_events(moe_decode_plan_t p, void* begin, void* end);
 
@@ -210,7 +216,8 @@ int moe_decode_set_expert_events(moe_decode_plan_t p, void* begin, void* end);
 int moe_decode_path_for(moe_decode_plan_t p, int32_t T);
 
 /*
- * Health check of the fused kernel's bounded waits: synchronises the plan's
+ * Health check of the bounded waits (the fused kernel's and the expert
+ * chain launch's): synchronises the plan's
  * device, returns in *gave_up whether any wait since the last check ran out
  * of its spin budget (which would mean a result is not trustworthy) and
  * clears the flag.  Not capturable; for tests and monitoring.

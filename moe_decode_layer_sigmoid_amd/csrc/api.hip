@@ -274,10 +274,7 @@ static int run_fused(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, h
   f.ids_out = a->topk_ids;
   f.w_out = a->topk_weights;
   f.grid = p->fused_grid;
-  hipError_t err = hipSuccess;
-  if (p->user_begin) err = hipEventRecord(p->user_begin, s);
-  if (err == hipSuccess) err = moe::launch_decode_fused(f, p->ws, s);
-  if (err == hipSuccess && p->user_end) err = hipEventRecord(p->user_end, s);
+  const hipError_t err = moe::launch_decode_fused(f, p->ws, s, p->user_begin, p->user_end);
   return err == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;
 }
 
@@ -315,15 +312,13 @@ static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t 
       c.gamma = static_cast<const uint16_t*>(a->gamma);
       c.out = static_cast<uint16_t*>(a->out);
       c.residual_out = static_cast<uint16_t*>(a->residual_out);
-      if (err == hipSuccess && p->user_begin) step(hipEventRecord(p->user_begin, s));
-      if (err == hipSuccess) step(moe::launch_expert_chain(c, p->ws, s));
-      if (err == hipSuccess && p->user_end) step(hipEventRecord(p->user_end, s));
+      if (err == hipSuccess)
+        step(moe::launch_expert_chain(c, p->ws, s, p->user_begin, p->user_end));
       return err == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;
     }
-    if (err == hipSuccess && p->user_begin) step(hipEventRecord(p->user_begin, s));
     if (err == hipSuccess)
-      step(moe::launch_gate_up_gemv(d, a->hidden, a->w13, a->w13_scale, p->ws, s));
-    if (err == hipSuccess && p->user_end) step(hipEventRecord(p->user_end, s));
+      step(moe::launch_gate_up_gemv(d, a->hidden, a->w13, a->w13_scale, p->ws, s,
+                                    p->user_begin, p->user_end));
     if (err == hipSuccess)
       step(moe::launch_down_gemv(d, a->w2, a->w2_scale, a->sw2, a->sw2_scale, p->ws, s));
     if (err == hipSuccess)
@@ -351,11 +346,9 @@ static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t 
       step(moe::launch_down_mfma(d, moe::kSharedRows, a->w2, a->w2_scale, sw2, a->sw2_scale,
                                  p->ws, p->side));
   }
-  if (err == hipSuccess && p->user_begin) step(hipEventRecord(p->user_begin, s));
   if (err == hipSuccess)
     step(moe::launch_gate_up_mfma(d, rows, a->hidden, a->w13, a->w13_scale, sw13, a->sw13_scale,
-                                  p->ws, s));
-  if (err == hipSuccess && p->user_end) step(hipEventRecord(p->user_end, s));
+                                  p->ws, s, p->user_begin, p->user_end));
   if (err == hipSuccess)
     step(moe::launch_down_mfma(d, rows, a->w2, a->w2_scale, sw2, a->sw2_scale, p->ws, s));
   if (side) {

@@ -57,7 +57,8 @@ constexpr int kMaxRoutes = kFusedMaxTokens * kMaxTopK;  // most touched-expert s
 static_assert(3 * kMaxRoutes * 4 <= kRouteSmem, "slot table must fit the routing scratch");
 
 template <int NJ, bool E8>
-hipError_t launch_nj(const FusedArgs& a, const Workspace& ws, hipStream_t s);
+hipError_t launch_nj(const FusedArgs& a, const Workspace& ws, hipStream_t s, hipEvent_t evb,
+                     hipEvent_t eve);
 template <int NJ, bool E8>
 int occupancy_nj();
 
@@ -181,8 +182,9 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
 }
 
 template <int NJ, bool E8>
-hipError_t launch_nj(const FusedArgs& a, const Workspace& ws, hipStream_t s) {
-  hipLaunchKernelGGL((decode_fused_kernel<NJ, E8>), dim3(a.grid), dim3(kThreads), 0, s, a, ws);
+hipError_t launch_nj(const FusedArgs& a, const Workspace& ws, hipStream_t s, hipEvent_t evb,
+                     hipEvent_t eve) {
+  MOE_LAUNCH((decode_fused_kernel<NJ, E8>), dim3(a.grid), dim3(kThreads), 0, s, evb, eve, a, ws);
   return hipGetLastError();
 }
 
@@ -196,7 +198,8 @@ int occupancy_nj() {
 }
 
 template hipError_t launch_nj<MOE_FUSED_NJ, (MOE_FUSED_E8 != 0)>(const FusedArgs&,
-                                                                  const Workspace&, hipStream_t);
+                                                                  const Workspace&, hipStream_t,
+                                                                  hipEvent_t, hipEvent_t);
 template int occupancy_nj<MOE_FUSED_NJ, (MOE_FUSED_E8 != 0)>();
 #endif  // MOE_FUSED_NJ
 
@@ -250,13 +253,14 @@ void fused_items(const LayerDims& d, FusedArgs* a) {
   a->o_rgu = a->o_sdn + a->n_sdn;
 }
 
-hipError_t launch_decode_fused(const FusedArgs& a, const Workspace& ws, hipStream_t s) {
+hipError_t launch_decode_fused(const FusedArgs& a, const Workspace& ws, hipStream_t s,
+                               hipEvent_t evb, hipEvent_t eve) {
   switch (fused_nj(a.H, a.I, a.Is) * 2 + (a.e8m0 ? 1 : 0)) {
 #define X(N)                          \
   case 2 * N:                         \
-    return launch_nj<N, false>(a, ws, s); \
+    return launch_nj<N, false>(a, ws, s, evb, eve); \
   case 2 * N + 1:                     \
-    return launch_nj<N, true>(a, ws, s);
+    return launch_nj<N, true>(a, ws, s, evb, eve);
     X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8)
 #undef X
     default:

@@ -59,7 +59,8 @@ constexpr int kMaxSlots = kChainMaxTokens * kMaxTopK;
 constexpr uint32_t kChainSpin = 1u << 17;
 
 template <int NJG, int NJD, bool E8>
-hipError_t launch_t(const ChainArgs& a, const Workspace& ws, hipStream_t s);
+hipError_t launch_t(const ChainArgs& a, const Workspace& ws, hipStream_t s, hipEvent_t evb,
+                    hipEvent_t eve);
 
 #ifdef MOE_CHAIN_NJG
 // The boundary of token t, columns [kBndCols * s, +kBndCols) (8 per thread),
@@ -241,15 +242,16 @@ __global__ __launch_bounds__(kThreads) void expert_chain_kernel(ChainArgs a, Wor
 }
 
 template <int NJG, int NJD, bool E8>
-hipError_t launch_t(const ChainArgs& a, const Workspace& ws, hipStream_t s) {
-  hipLaunchKernelGGL((expert_chain_kernel<NJG, NJD, E8>), dim3(a.grid), dim3(kThreads), 0, s, a,
-                     ws);
+hipError_t launch_t(const ChainArgs& a, const Workspace& ws, hipStream_t s, hipEvent_t evb,
+                    hipEvent_t eve) {
+  MOE_LAUNCH((expert_chain_kernel<NJG, NJD, E8>), dim3(a.grid), dim3(kThreads), 0, s, evb, eve, a,
+             ws);
   return hipGetLastError();
 }
 
 #define MOE_CHAIN_INST(NJD, E8)                                                              \
   template hipError_t launch_t<MOE_CHAIN_NJG, NJD, E8>(const ChainArgs&, const Workspace&,   \
-                                                        hipStream_t);
+                                                        hipStream_t, hipEvent_t, hipEvent_t);
 MOE_CHAIN_INST(1, false) MOE_CHAIN_INST(1, true)
 MOE_CHAIN_INST(2, false) MOE_CHAIN_INST(2, true)
 MOE_CHAIN_INST(3, false) MOE_CHAIN_INST(3, true)
@@ -305,7 +307,8 @@ void chain_items(const LayerDims& d, ChainArgs* a) {
   a->grid = static_cast<uint32_t>(a->n_items + d.T * a->bnd_ns);
 }
 
-hipError_t launch_expert_chain(const ChainArgs& a, const Workspace& ws, hipStream_t s) {
+hipError_t launch_expert_chain(const ChainArgs& a, const Workspace& ws, hipStream_t s,
+                               hipEvent_t evb, hipEvent_t eve) {
   if (a.T < 1 || a.T > kChainMaxTokens || a.bnd_ns > kMaxBndSlices ||
       a.grid != static_cast<uint32_t>(a.n_items + a.T * a.bnd_ns) ||
       a.dmax > chain::kMaxSlots ||
@@ -314,7 +317,7 @@ hipError_t launch_expert_chain(const ChainArgs& a, const Workspace& ws, hipStrea
   switch (key(chain_njg(a.H), chain_njd(a.I, a.Is), a.e8m0 != 0)) {
 #define X(G, D, E)          \
   case (G * 8 + D) * 2 + E: \
-    return chain::launch_t<G, D, E>(a, ws, s);
+    return chain::launch_t<G, D, E>(a, ws, s, evb, eve);
     MOE_CHAIN_ALL
 #undef X
     default:

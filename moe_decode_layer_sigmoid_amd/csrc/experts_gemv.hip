@@ -97,7 +97,8 @@ static int slot_rows(const LayerDims& d) {
 }
 
 hipError_t launch_gate_up_gemv(const LayerDims& d, const void* hidden, const void* w13,
-                               const void* w13_scale, const Workspace& ws, hipStream_t s) {
+                               const void* w13_scale, const Workspace& ws, hipStream_t s,
+                               hipEvent_t evb, hipEvent_t eve) {
   const int nj = (d.H + 1023) / 1024;
   dim3 grid(d.I / (2 * kWaves), d.T * d.k < d.E ? d.T * d.k : d.E);
   const auto* x = static_cast<const uint16_t*>(hidden);
@@ -105,12 +106,12 @@ hipError_t launch_gate_up_gemv(const LayerDims& d, const void* hidden, const voi
   switch (nj * 2 + (d.e8m0 ? 1 : 0)) {
 #define X(N)                                                                                  \
   case 2 * N:                                                                                 \
-    hipLaunchKernelGGL((gate_up_kernel<N, false>), grid, dim3(kThreads), 0, s, x, w, w13_scale, \
-                       d.H, d.I, d.k, d.T, ws, d.limit);                                      \
+    MOE_LAUNCH((gate_up_kernel<N, false>), grid, dim3(kThreads), 0, s, evb, eve, x, w,        \
+               w13_scale, d.H, d.I, d.k, d.T, ws, d.limit);                                   \
     break;                                                                                    \
   case 2 * N + 1:                                                                             \
-    hipLaunchKernelGGL((gate_up_kernel<N, true>), grid, dim3(kThreads), 0, s, x, w, w13_scale,  \
-                       d.H, d.I, d.k, d.T, ws, d.limit);                                      \
+    MOE_LAUNCH((gate_up_kernel<N, true>), grid, dim3(kThreads), 0, s, evb, eve, x, w,         \
+               w13_scale, d.H, d.I, d.k, d.T, ws, d.limit);                                   \
     break;
     MOE_NJ_CASES(X)
 #undef X

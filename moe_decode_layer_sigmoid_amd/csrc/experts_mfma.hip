@@ -411,9 +411,9 @@ constexpr size_t kLdsGu = static_cast<size_t>(kWaves) * kUGu * kNsGu * kSubtileB
 template <bool E8, int ROWS>
 void launch_gu(dim3 grid, hipStream_t s, const uint16_t* x, const uint8_t* w, const void* scale,
                const uint8_t* sw, const void* sscale, const LayerDims& d, int SP,
-               const Workspace& ws) {
-  hipLaunchKernelGGL((gate_up_mfma_kernel<kNsGu, kUGu, kGR, E8, ROWS>), grid, dim3(kThreads), kLdsGu, s, x,
-                     w, scale, sw, sscale, d.H, d.I, d.Is, d.k, d.T, SP, ws, d.limit);
+               const Workspace& ws, hipEvent_t evb, hipEvent_t eve) {
+  MOE_LAUNCH((gate_up_mfma_kernel<kNsGu, kUGu, kGR, E8, ROWS>), grid, dim3(kThreads), kLdsGu, s,
+             evb, eve, x, w, scale, sw, sscale, d.H, d.I, d.Is, d.k, d.T, SP, ws, d.limit);
 }
 
 template <int NS, bool E8, int ROWS>
@@ -434,7 +434,8 @@ int slot_rows(const LayerDims& d) { return d.T * d.k < d.E ? d.T * d.k : d.E; }
 
 hipError_t launch_gate_up_mfma(const LayerDims& d, int rows, const void* hidden, const void* w13,
                                const void* w13_scale, const void* sw13, const void* sw13_scale,
-                               const Workspace& ws, hipStream_t s) {
+                               const Workspace& ws, hipStream_t s, hipEvent_t evb,
+                               hipEvent_t eve) {
   const int SP = rows == kRoutedRows ? 0 : shared_rows(d);
   const int R = rows == kSharedRows ? 0 : slot_rows(d);
   if (SP + R == 0) return hipSuccess;
@@ -444,7 +445,8 @@ hipError_t launch_gate_up_mfma(const LayerDims& d, int rows, const void* hidden,
   const auto* x = static_cast<const uint16_t*>(hidden);
   const auto* w = static_cast<const uint8_t*>(w13);
   const auto* sw = static_cast<const uint8_t*>(sw13);
-#define MOE_GU(E8, ROWS) launch_gu<E8, ROWS>(grid, s, x, w, w13_scale, sw, sw13_scale, d, SP, ws)
+#define MOE_GU(E8, ROWS) \
+  launch_gu<E8, ROWS>(grid, s, x, w, w13_scale, sw, sw13_scale, d, SP, ws, evb, eve)
   if (rows == kAllRows) {
     if (d.e8m0) MOE_GU(true, kAllRows); else MOE_GU(false, kAllRows);
   } else if (rows == kSharedRows) {

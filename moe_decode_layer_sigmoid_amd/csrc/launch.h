@@ -1,10 +1,23 @@
 // Host-side launchers of the MoE decode kernels (internal to the library).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace moe {
+
+// Launches `kernel`; with a non-null `evb` through hipExtLaunchKernelGGL,
+// which records evb / eve at the kernel's own start and end (the measurement
+// hook: an event recorded on the stream around the launch would also count
+// the dispatch and completion of the launch).
+#define MOE_LAUNCH(kernel, grid, block, lds, s, evb, eve, ...)                             \
+  do {                                                                                   \
+    if (evb)                                                                             \
+      hipExtLaunchKernelGGL(kernel, grid, block, lds, s, evb, eve, 0, __VA_ARGS__);      \
+    else                                                                                 \
+      hipLaunchKernelGGL(kernel, grid, block, lds, s, __VA_ARGS__);                      \
+  } while (0)
 
 // Device workspace of one plan, sized for max_tokens.
 struct Workspace {
@@ -159,7 +172,8 @@ hipError_t launch_router(const LayerDims& d, const void* hidden, const void* rou
 // gate_up + clamped SwiGLU (GEMV) of the touched experts (one grid row
 // each; the shared expert's runs in the router launch).
 hipError_t launch_gate_up_gemv(const LayerDims& d, const void* hidden, const void* w13,
-                               const void* w13_scale, const Workspace& ws, hipStream_t s);
+                               const void* w13_scale, const Workspace& ws, hipStream_t s,
+                               hipEvent_t evb = nullptr, hipEvent_t eve = nullptr);
 
 // down projection (GEMV) of the same slots.
 hipError_t launch_down_gemv(const LayerDims& d, const void* w2, const void* w2_scale,
@@ -173,7 +187,8 @@ hipError_t launch_down_gemv(const LayerDims& d, const void* w2, const void* w2_s
 enum : int { kAllRows = 0, kSharedRows = 1, kRoutedRows = 2 };
 hipError_t launch_gate_up_mfma(const LayerDims& d, int rows, const void* hidden, const void* w13,
                                const void* w13_scale, const void* sw13, const void* sw13_scale,
-                               const Workspace& ws, hipStream_t s);
+                               const Workspace& ws, hipStream_t s, hipEvent_t evb = nullptr,
+                               hipEvent_t eve = nullptr);
 hipError_t launch_down_mfma(const LayerDims& d, int rows, const void* w2, const void* w2_scale,
                             const void* sw2, const void* sw2_scale, const Workspace& ws,
                             hipStream_t s);
@@ -182,13 +197,15 @@ hipError_t launch_down_mfma(const LayerDims& d, int rows, const void* w2, const 
 int fused_nj(int H, int I, int Is);
 int fused_blocks_per_cu(int nj, bool e8m0);
 void fused_items(const LayerDims& d, FusedArgs* a);
-hipError_t launch_decode_fused(const FusedArgs& a, const Workspace& ws, hipStream_t s);
+hipError_t launch_decode_fused(const FusedArgs& a, const Workspace& ws, hipStream_t s,
+                               hipEvent_t evb = nullptr, hipEvent_t eve = nullptr);
 
 // Shared down, routed gate_up, routed down and the boundary in one launch
 // (T <= kChainMaxTokens; H <= 8192; I and I_s <= 4096).
 bool chain_supported(int H, int I, int Is);
 void chain_items(const LayerDims& d, ChainArgs* a);
-hipError_t launch_expert_chain(const ChainArgs& a, const Workspace& ws, hipStream_t s);
+hipError_t launch_expert_chain(const ChainArgs& a, const Workspace& ws, hipStream_t s,
+                               hipEvent_t evb = nullptr, hipEvent_t eve = nullptr);
 
 // Weighted combine + shared + residual, RMSNorm * gamma, bf16 outputs.
 hipError_t launch_epilogue(const LayerDims& d, const void* residual, const void* gamma,
