@@ -139,6 +139,12 @@ typedef struct {
   void* residual_out;       /* [T, H] bf16: h; may alias residual, nothing else */
   int32_t* topk_ids;        /* [T, k] selected experts in rank order, or NULL */
   float* topk_weights;      /* [T, k] their weights (R-scaled), or NULL */
+  /* [T, H] bf16: the finalized MoE output sum_j w_j y_j + y_shared, before
+   * the residual add and the norm (the decode page's LayerStages._grouped_moe
+   * takes this from the grouped kernel with finalize=True, for token counts
+   * whose boundary is not fused), or NULL.  Written by the boundary beside
+   * out and residual_out; it may alias no other tensor. */
+  void* moe_out;
 } moe_decode_args;
 
 typedef struct moe_decode_plan_s* moe_decode_plan_t;

@@ -46,7 +46,7 @@ class Args(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "hidden", "residual", "router_w", "router_bias", "w13", "w13_scale", "w2", "w2_scale",
         "sw13", "sw13_scale", "sw2", "sw2_scale", "gamma", "out", "residual_out",
-        "topk_ids", "topk_weights")]
+        "topk_ids", "topk_weights", "moe_out")]
 
 
 _lib = None
@@ -151,10 +151,11 @@ class Plan:
 
     def make_args(self, *, hidden, residual, router_w, w13, w13_scale, w2, w2_scale, gamma,
                   out, residual_out, router_bias=None, sw13=None, sw13_scale=None, sw2=None,
-                  sw2_scale=None, topk_ids=None, topk_weights=None) -> Args:
+                  sw2_scale=None, topk_ids=None, topk_weights=None, moe_out=None) -> Args:
         return Args(*[_ptr(t) for t in (
             hidden, residual, router_w, router_bias, w13, w13_scale, w2, w2_scale, sw13,
-            sw13_scale, sw2, sw2_scale, gamma, out, residual_out, topk_ids, topk_weights)])
+            sw13_scale, sw2, sw2_scale, gamma, out, residual_out, topk_ids, topk_weights,
+            moe_out)])
 
     def run_args(self, args: Args, T: int, stream=None) -> None:
         rc = lib().moe_decode_run(self._h, ctypes.byref(args), T, _stream(stream))

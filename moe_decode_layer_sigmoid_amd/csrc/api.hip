@@ -158,12 +158,15 @@ int moe_decode_args_check(const moe_decode_desc* d, const moe_decode_args* a, in
     return MOE_DECODE_ERR_INVALID_ARG;
   // 16-byte vector loads and stores need 16-byte aligned tensors.
   const void* vec[] = {a->hidden, a->residual, a->router_w, a->w13, a->w2, a->gamma,
-                       a->out, a->residual_out, a->sw13, a->sw2};
+                       a->out, a->residual_out, a->sw13, a->sw2, a->moe_out};
   for (const void* p : vec)
     if (p && !aligned16(p)) return MOE_DECODE_ERR_INVALID_ARG;
   // out is written while hidden/residual/gamma are still being read.
   if (a->out == a->hidden || a->out == a->residual || a->out == a->residual_out ||
       a->residual_out == a->hidden)
+    return MOE_DECODE_ERR_INVALID_ARG;
+  if (a->moe_out && (a->moe_out == a->hidden || a->moe_out == a->residual ||
+                     a->moe_out == a->out || a->moe_out == a->residual_out))
     return MOE_DECODE_ERR_INVALID_ARG;
   return MOE_DECODE_OK;
 }
@@ -270,6 +273,7 @@ static int run_fused(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, h
   f.sw2_scale = a->sw2_scale;
   f.gamma = static_cast<const uint16_t*>(a->gamma);
   f.out = static_cast<uint16_t*>(a->out);
+  f.moe_out = static_cast<uint16_t*>(a->moe_out);
   f.residual_out = static_cast<uint16_t*>(a->residual_out);
   f.ids_out = a->topk_ids;
   f.w_out = a->topk_weights;
@@ -311,6 +315,7 @@ static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t 
       c.sw2_scale = a->sw2_scale;
       c.gamma = static_cast<const uint16_t*>(a->gamma);
       c.out = static_cast<uint16_t*>(a->out);
+      c.moe_out = static_cast<uint16_t*>(a->moe_out);
       c.residual_out = static_cast<uint16_t*>(a->residual_out);
       if (err == hipSuccess)
         step(moe::launch_expert_chain(c, p->ws, s, p->user_begin, p->user_end));
@@ -322,7 +327,8 @@ static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t 
     if (err == hipSuccess)
       step(moe::launch_down_gemv(d, a->w2, a->w2_scale, a->sw2, a->sw2_scale, p->ws, s));
     if (err == hipSuccess)
-      step(moe::launch_epilogue(d, a->residual, a->gamma, p->ws, a->out, a->residual_out, s));
+      step(moe::launch_epilogue(d, a->residual, a->gamma, p->ws, a->out, a->residual_out,
+                                a->moe_out, s));
     return err == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;
   }
 
@@ -358,7 +364,8 @@ static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t 
     if (err == hipSuccess) err = jerr;
   }
   if (err == hipSuccess)
-    step(moe::launch_epilogue(d, a->residual, a->gamma, p->ws, a->out, a->residual_out, s));
+    step(moe::launch_epilogue(d, a->residual, a->gamma, p->ws, a->out, a->residual_out,
+                                a->moe_out, s));
   return err == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;
 }
 

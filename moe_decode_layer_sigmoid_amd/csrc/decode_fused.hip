@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
   }
   for (; it < total; it += G) {
     epilogue_token<true>(it - o_epi, a.residual, a.gamma, H, k, Is > 0, a.eps, ws, a.out,
-                         a.residual_out, s_part);
+                         a.residual_out, a.moe_out, s_part);
     __syncthreads();
   }
 

@@ -28,6 +28,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// Eight floats -> eight bf16 (RNE) in one 16-byte store (p 16-byte aligned).
+__device__ __forceinline__ void store_bf16x8(uint16_t* p, const float* v) {
+  uint32_t w[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) w[m] = f32_to_bf16(v[2 * m]) | (f32_to_bf16(v[2 * m + 1]) << 16);
+  *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Four e4m3fn codes (one dword, byte 0 first) -> four floats (exact).
 __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {
   auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);

@@ -1,5 +1,8 @@
 // The MoE layer's boundary on gfx950: weighted combine of the routed rows,
-// plus the shared expert and the residual, then RMSNorm * gamma.
+// plus the shared expert and the residual, then RMSNorm * gamma; optionally
+// also the finalized MoE output (the combine plus the shared expert, before
+// the residual: what the decode page's LayerStages._grouped_moe takes from
+// the grouped kernel with finalize=True).
 //
 // Follows the vLLM API page "vllm.models.glm5next.nvidia.specialized_decode.
 // runtime.draft", SpecializedDraft.reduced_norm and _build_ar_norm: the
@@ -33,7 +36,7 @@ constexpr int kGroup = 8;        // routes whose rows one round of loads fetches
 // waves in order for the sum of squares.
 __global__ __launch_bounds__(kMaxThreads) void epilogue_kernel(
     const uint16_t* residual, const uint16_t* __restrict__ gamma, int H, int k, int has_shared,
-    float eps, Workspace ws, uint16_t* out, uint16_t* residual_out) {
+    float eps, Workspace ws, uint16_t* out, uint16_t* residual_out, uint16_t* moe_out) {
   __shared__ float s_part[kMaxThreads / kWave];
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -76,6 +79,7 @@ __global__ __launch_bounds__(kMaxThreads) void epilogue_kernel(
     acc[0] += ya.x; acc[1] += ya.y; acc[2] += ya.z; acc[3] += ya.w;
     acc[4] += yb.x; acc[5] += yb.y; acc[6] += yb.z; acc[7] += yb.w;
   }
+  if (moe_out && live) store_bf16x8(moe_out + static_cast<size_t>(t) * H + c, acc);
   const uint32_t u[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -112,12 +116,13 @@ __global__ __launch_bounds__(kMaxThreads) void epilogue_kernel(
 }  // namespace
 
 hipError_t launch_epilogue(const LayerDims& d, const void* residual, const void* gamma,
-                           const Workspace& ws, void* out, void* residual_out, hipStream_t s) {
+                           const Workspace& ws, void* out, void* residual_out, void* moe_out,
+                           hipStream_t s) {
   const int threads = ((d.H / kCols + kWave - 1) / kWave) * kWave;
   hipLaunchKernelGGL(epilogue_kernel, dim3(d.T), dim3(threads), 0, s,
                      static_cast<const uint16_t*>(residual), static_cast<const uint16_t*>(gamma),
                      d.H, d.k, static_cast<int>(d.Is > 0), d.eps, ws, static_cast<uint16_t*>(out),
-                     static_cast<uint16_t*>(residual_out));
+                     static_cast<uint16_t*>(residual_out), static_cast<uint16_t*>(moe_out));
   return hipGetLastError();
 }
 

@@ -65,7 +65,8 @@ hipError_t launch_t(const ChainArgs& a, const Workspace& ws, hipStream_t s, hipE
 #ifdef MOE_CHAIN_NJG
 // The boundary of token t, columns [kBndCols * s, +kBndCols) (8 per thread),
 // by one of the token's bnd_ns workgroups: h = sum_j w[t, j] * rows[t*k + j]
-// + y_s[t] + residual[t] (fixed order); the slice's sum of squares (waves in
+// + y_s[t] + residual[t] (fixed order; with moe_out, the sum before the
+// residual goes there too); the slice's sum of squares (waves in
 // order) goes to ws.epi_part[t][s], which the router launch armed with
 // kEpiEmpty; once every slice of the token is in, their sums in slice order
 // give the RMS, and the slice of residual_out = bf16(h), out = bf16(h /
@@ -120,6 +121,7 @@ __device__ __forceinline__ void boundary_slice(const ChainArgs& a, const Workspa
     acc[0] += ya.x; acc[1] += ya.y; acc[2] += ya.z; acc[3] += ya.w;
     acc[4] += yb.x; acc[5] += yb.y; acc[6] += yb.z; acc[7] += yb.w;
   }
+  if (a.moe_out && live) store_bf16x8(a.moe_out + static_cast<size_t>(t) * H + c, acc);
   const uint32_t u[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
   for (int m = 0; m < 4; ++m) {

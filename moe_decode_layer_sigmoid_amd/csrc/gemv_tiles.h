@@ -313,8 +313,10 @@ constexpr int kEpiGroup = 8;  // routes whose rows one round of loads fetches
 
 // The boundary for token t, by one 256-thread workgroup:
 // h = sum_j w[t, j] * rows[t*k + j] + y_s[t] + residual[t] (fixed order),
-// residual_out = bf16(h), out = bf16(h / sqrt(mean(h^2) + eps) * gamma).
-// Every load of a group of routes is issued before any is used.
+// residual_out = bf16(h), out = bf16(h / sqrt(mean(h^2) + eps) * gamma),
+// and, when moe_out is not null, moe_out = bf16(h - residual) (the sum before
+// the residual is added).  Every load of a group of routes is issued before
+// any is used.
 // s_part: 4 floats of LDS.
 // GRP = routes whose rows one round of loads fetches (fewer registers with a
 // smaller group).
@@ -323,7 +325,7 @@ __device__ __forceinline__ void epilogue_token(int t, const uint16_t* residual,
                                                const uint16_t* __restrict__ gamma, int H, int k,
                                                bool has_shared, float eps, const Workspace& ws,
                                                uint16_t* out, uint16_t* residual_out,
-                                               float* s_part) {
+                                               uint16_t* moe_out, float* s_part) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* rows_t = ws.rows + static_cast<size_t>(t) * k * H;
   float hv[kEpiPass][8];
@@ -366,6 +368,7 @@ __device__ __forceinline__ void epilogue_token(int t, const uint16_t* residual,
       acc[0] += ya.x; acc[1] += ya.y; acc[2] += ya.z; acc[3] += ya.w;
       acc[4] += yb.x; acc[5] += yb.y; acc[6] += yb.z; acc[7] += yb.w;
     }
+    if (moe_out) store_bf16x8(moe_out + static_cast<size_t>(t) * H + c0, acc);
     const uint32_t u[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {

@@ -119,6 +119,7 @@ struct FusedArgs {
   const uint16_t* gamma;
   uint16_t* out;
   uint16_t* residual_out;
+  uint16_t* moe_out;  // nullable
   int32_t* ids_out;
   float* w_out;
   int T, H, E, k, I, Is, e8m0;
@@ -148,6 +149,7 @@ struct ChainArgs {
   const uint16_t* gamma;
   uint16_t* out;
   uint16_t* residual_out;
+  uint16_t* moe_out;  // nullable
   int T, H, k, I, Is, e8m0;
   float limit, eps;
   int gu_per, dn_per, dmax;  // items per slot; touched-slot rows of the grid
@@ -208,7 +210,9 @@ hipError_t launch_expert_chain(const ChainArgs& a, const Workspace& ws, hipStrea
                                hipEvent_t evb = nullptr, hipEvent_t eve = nullptr);
 
 // Weighted combine + shared + residual, RMSNorm * gamma, bf16 outputs.
+// moe_out (nullable): also the finalized MoE output (before the residual).
 hipError_t launch_epilogue(const LayerDims& d, const void* residual, const void* gamma,
-                           const Workspace& ws, void* out, void* residual_out, hipStream_t s);
+                           const Workspace& ws, void* out, void* residual_out, void* moe_out,
+                           hipStream_t s);
 
 }  // namespace moe

@@ -43,7 +43,8 @@ def _p(a):
 
 def moe_layer(inp, forced_ids=None, rows=None, threads: int = 0) -> dict:
     """The layer on the listed token rows (all when None); same outputs as the
-    NumPy oracle's moe_layer: ids, weights, gaps, logits, h, out."""
+    NumPy oracle's moe_layer: ids, weights, gaps, logits, moe, h, out (moe =
+    h - residual: the finalized MoE output before the residual add)."""
     sh = inp.shape
     lib = _load()
     rows_arr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
@@ -68,4 +69,7 @@ def moe_layer(inp, forced_ids=None, rows=None, threads: int = 0) -> dict:
         c.c_int(threads))
     if rc != 0:
         raise ValueError("moe_oracle_layer rejected its arguments (%d)" % rc)
-    return dict(ids=ids, weights=w, gaps=gaps, logits=logits, h=h, out=out)
+    from .moe_oracle import bf16_bits_to_f64
+
+    res = bf16_bits_to_f64(inp.residual if rows_arr is None else inp.residual[rows_arr])
+    return dict(ids=ids, weights=w, gaps=gaps, logits=logits, moe=h - res, h=h, out=out)

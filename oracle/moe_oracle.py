@@ -188,8 +188,12 @@ def moe_layer(inp, forced_ids=None, rows=None) -> dict:
     rows        optional token rows to compute (all when None); the outputs
                 then hold only those rows, in that order
 
-    Returns a dict with logits, scores, ids, weights, gaps, y_shared, h
-    (= the new residual before rounding) and out (the normalised output).
+    Returns a dict with logits, scores, ids, weights, gaps, y_shared, moe
+    (the finalized MoE output: the weighted routed rows plus the shared
+    expert, before the residual; what the decode page's LayerStages.
+    _grouped_moe gets from the grouped kernel with finalize=True), h (= moe +
+    residual, the new residual before rounding) and out (the normalised
+    output).
     """
     sh = inp.shape
     rows = np.arange(sh.T) if rows is None else np.asarray(rows)
@@ -221,7 +225,8 @@ def moe_layer(inp, forced_ids=None, rows=None) -> dict:
     else:
         y_shared = np.zeros((n, sh.H))
 
-    h = routed + y_shared + res
+    moe = routed + y_shared
+    h = moe + res
     out = rms_norm(h, gamma, sh.eps)
     return dict(logits=logits, scores=scores, ids=ids, weights=weights,
-                gaps=score_gaps(scores, bias, sh.k), y_shared=y_shared, h=h, out=out)
+                gaps=score_gaps(scores, bias, sh.k), y_shared=y_shared, moe=moe, h=h, out=out)

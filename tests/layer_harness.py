@@ -64,18 +64,21 @@ def run_layer(plan, dev, T, alias_residual=False, stream=None, keep_device=False
     else:
         res_out = torch.empty((T, H), dtype=torch.int16, device=device)
         residual = dev["residual"]
+    moe = torch.empty((T, H), dtype=torch.int16, device=device)
     ids = torch.full((T, k), -1, dtype=torch.int32, device=device)
     w = torch.full((T, k), float("nan"), dtype=torch.float32, device=device)
     plan.run(T, stream=stream, hidden=dev["hidden"], residual=residual, router_w=dev["router_w"],
              router_bias=dev["router_bias"], w13=dev["w13"], w13_scale=dev["w13_scale"],
              w2=dev["w2"], w2_scale=dev["w2_scale"], sw13=dev["sw13"],
              sw13_scale=dev["sw13_scale"], sw2=dev["sw2"], sw2_scale=dev["sw2_scale"],
-             gamma=dev["gamma"], out=out, residual_out=res_out, topk_ids=ids, topk_weights=w)
+             gamma=dev["gamma"], out=out, residual_out=res_out, topk_ids=ids, topk_weights=w,
+             moe_out=moe)
     torch.cuda.synchronize()
     # the persistent launches (the fused kernel, the split path's expert chain)
     # wait on each other's workgroups with bounded waits
     assert not plan.check_waits(), "a bounded wait gave up"
-    got = dict(out=bf16_to_np(out), residual_out=bf16_to_np(res_out), ids=ids.cpu().numpy(),
+    got = dict(out=bf16_to_np(out), residual_out=bf16_to_np(res_out), moe=bf16_to_np(moe),
+               ids=ids.cpu().numpy(),
                weights=w.cpu().numpy().astype(np.float64))
     if keep_device:
         got["dev"] = dict(out=out, residual_out=res_out, ids=ids, weights=w)
@@ -141,5 +144,7 @@ def check_layer(inp, got, rows=None, use_c=None, c_oracle=None):
     assert np.allclose(got["weights"].sum(1), sh.rsf, rtol=1e-5)
     e_out = assert_close(got["out"][rows_list], ref["out"], "out")
     e_res = assert_close(got["residual_out"][rows_list], ref["h"], "residual_out")
+    if "moe" in got:
+        assert_close(got["moe"][rows_list], ref["moe"], "moe_out")
     return dict(n_tie=n_tie, out_rel_l2=e_out[0], out_max=e_out[1], res_rel_l2=e_res[0],
                 res_max=e_res[1], w_rel=float(w_rel.max()))

@@ -102,6 +102,11 @@ def test_args_check_codes():
     assert md.args_check(d, full_args(out=a.hidden), 1) == md.ERR_INVALID_ARG
     assert md.args_check(d, full_args(residual_out=a.residual), 1) == md.OK
     assert md.args_check(d, full_args(residual_out=a.hidden), 1) == md.ERR_INVALID_ARG
+    # the finalized MoE output is optional, aligned, and aliases nothing
+    assert md.args_check(d, full_args(moe_out=None), 1) == md.OK
+    assert md.args_check(d, full_args(moe_out=0x10008), 1) == md.ERR_INVALID_ARG
+    for n in ["hidden", "residual", "out", "residual_out"]:
+        assert md.args_check(d, full_args(moe_out=getattr(a, n)), 1) == md.ERR_INVALID_ARG, n
 
 
 def test_strerror_and_null_plan():

@@ -274,6 +274,9 @@ def test_hand_two_expert_example(k, which, c_oracle):
     assert np.allclose(r["weights"][0], w, rtol=1e-14)
     assert np.allclose(r["h"][0, :4], h4, rtol=1e-14)
     assert np.all(r["h"][0, 4:] == 0)
+    # the finalized MoE output: h without the residual (e3)
+    assert np.allclose(r["moe"][0, :4], h4[:3] + [0.0], rtol=1e-14, atol=1e-15)
+    assert np.all(r["moe"][0, 4:] == 0)
     assert np.allclose(r["out"][0, :4], out4, rtol=1e-13)
     # the numbers themselves (k = 2): 2.2019926949447, 0.2980073050553, ...
     if k == 2:
