@@ -72,7 +72,7 @@ typedef enum { MOE_DECODE_SCALE_FP32 = 0, MOE_DECODE_SCALE_E8M0 = 1 } moe_decode
 /* Expert kernel family.  AUTO picks by token count; the others force one. */
 typedef enum {
   /* The faster path for the token count as measured on MI355X: GEMV_SPLIT
-   * below 8 tokens, GROUPED from 8 tokens on. */
+   * below 4 tokens, GROUPED from 4 tokens on. */
   MOE_DECODE_PATH_AUTO = 0,
   /* fp8 dequant-FMA GEMV, one weight pass per touched expert.  Up to 16
    * tokens the whole step is one persistent kernel (router, shared expert,

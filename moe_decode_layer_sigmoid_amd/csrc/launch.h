@@ -98,9 +98,11 @@ constexpr int kFusedMaxTokens = 16;
 // routed experts' launches; above it (several 16-token passes, each streaming
 // the shared weights again) on a second stream, beside the routed launches.
 constexpr int kMergeSharedMaxTokens = 64;
-// AUTO takes the MFMA projections from this many tokens on (at 8 to 12
-// tokens the two paths measure the same on MI355X; from 16 on MFMA wins).
-constexpr int kGroupedMinTokens = 8;
+// AUTO takes the MFMA projections from this many tokens on.  Measured on
+// MI355X at the 4096 x 1536, 128-expert decode shape (µs per step, split /
+// grouped): 1 token 46.5 / 74.2, 2: 75.3 / 87.0, 3: 103.1 / 109.9,
+// 4: 127.9 / 118.9, 8: 215.8 / 183.5, 16: 378.8 / 295.6.
+constexpr int kGroupedMinTokens = 4;
 
 // Arguments of the fused persistent kernel (see decode_fused.hip).
 struct FusedArgs {
