@@ -352,11 +352,19 @@ static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t 
       step(moe::launch_down_mfma(d, moe::kSharedRows, a->w2, a->w2_scale, sw2, a->sw2_scale,
                                  p->ws, p->side));
   }
-  if (err == hipSuccess)
-    step(moe::launch_gate_up_mfma(d, rows, a->hidden, a->w13, a->w13_scale, sw13, a->sw13_scale,
-                                  p->ws, s, p->user_begin, p->user_end));
-  if (err == hipSuccess)
-    step(moe::launch_down_mfma(d, rows, a->w2, a->w2_scale, sw2, a->sw2_scale, p->ws, s));
+  if (!side && moe::grouped_chain_supported(d)) {
+    // gate_up and down in one launch (the down tiles start in the gate_up drain)
+    if (err == hipSuccess)
+      step(moe::launch_grouped_chain(d, a->hidden, a->w13, a->w13_scale, sw13, a->sw13_scale,
+                                     a->w2, a->w2_scale, sw2, a->sw2_scale, p->ws, s,
+                                     p->user_begin, p->user_end));
+  } else {
+    if (err == hipSuccess)
+      step(moe::launch_gate_up_mfma(d, rows, a->hidden, a->w13, a->w13_scale, sw13,
+                                    a->sw13_scale, p->ws, s, p->user_begin, p->user_end));
+    if (err == hipSuccess)
+      step(moe::launch_down_mfma(d, rows, a->w2, a->w2_scale, sw2, a->sw2_scale, p->ws, s));
+  }
   if (side) {
     // joined on every path, errors included, so a capture sees no loose work
     hipError_t jerr = hipEventRecord(p->join, p->side);

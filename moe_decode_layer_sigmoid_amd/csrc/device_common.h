@@ -88,6 +88,11 @@ __device__ __forceinline__ void st_f32(float* p, float v) {
   else *p = v;
 }
 template <bool C>
+__device__ __forceinline__ void st_u32(uint32_t* p, uint32_t v) {
+  if (C) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool C>
 __device__ __forceinline__ void st_i32(int* p, int v) {
   if (C) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   else *p = v;

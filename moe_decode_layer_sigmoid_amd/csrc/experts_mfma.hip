@@ -37,6 +37,7 @@
 // and its activation loads follow the same order, so A and B agree.
 #include "device_common.h"
 #include "launch.h"
+#include "sync_device.h"
 
 namespace moe {
 namespace {
@@ -119,9 +120,9 @@ __device__ __forceinline__ uint16_t bf16_bits(float f) { return static_cast<uint
 // (measured slower at 64 and 128 tokens).
 constexpr int kRotateMaxTokens = 32;
 
-__device__ __forceinline__ int first_block(int T, int wave, int KB) {
+__device__ __forceinline__ int first_block(int T, int wave, int KB, int bx, int by) {
   if (T > kRotateMaxTokens) return 0;
-  return static_cast<int>((blockIdx.x * kWaves + wave + 5 * blockIdx.y) % KB);
+  return (bx * kWaves + wave + 5 * by) % KB;
 }
 
 // Block i of a wave's walk (i past the end: the last block, whose scale the
@@ -143,8 +144,7 @@ struct Slot {
 };
 
 template <int GR>
-__device__ __forceinline__ bool slot_of(int T, int SP, const Workspace& ws, Slot* s) {
-  const int y = static_cast<int>(blockIdx.y);
+__device__ __forceinline__ bool slot_of(int T, int SP, const Workspace& ws, int y, Slot* s) {
   if (y < SP) {
     const int p = y * 16 * GR;
     *s = {true, 0, 0, p, min(T, p + 16 * GR)};
@@ -165,27 +165,32 @@ __device__ __forceinline__ bool slot_of(int T, int SP, const Workspace& ws, Slot
 // loads; GR = 16-token groups per pass over the weights.
 // ROWS: kAllRows (shared passes and touched experts, chosen per row at run
 // time) or only one kind, fixed at compile time.
-template <int NS, int U, int GR, bool E8, int ROWS>
-__global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
-    const uint16_t* __restrict__ hidden, const uint8_t* __restrict__ w13,
-    const void* __restrict__ scale13, const uint8_t* __restrict__ sw13,
-    const void* __restrict__ sscale13, int H, int I_r, int Is, int k, int T, int SP,
-    Workspace ws, float limit) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+// The tile of workgroup (bx, by) of that grid; returns whether it worked
+// (false: an empty slot or a tile past the row's end).  C: the SwiGLU planes
+// are written with agent-scope atomic stores (write-through, two bf16 of
+// neighbouring lanes per 32-bit store), for readers in the same launch: a
+// plain store leaves the line in the writer's L2, possibly filled with stale
+// bytes of the part other workgroups write.
+template <int NS, int U, int GR, bool E8, int ROWS, bool C = false>
+__device__ __forceinline__ bool gate_up_tile(
+    int bx, int by, unsigned char* smem, const uint16_t* __restrict__ hidden,
+    const uint8_t* __restrict__ w13, const void* __restrict__ scale13,
+    const uint8_t* __restrict__ sw13, const void* __restrict__ sscale13, int H, int I_r, int Is,
+    int k, int T, int SP, const Workspace& ws, float limit) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   constexpr int NH = NS / 2;  // gate (and up) subtiles
-  const int i0 = (blockIdx.x * kWaves + wave) * 16 * NH;
+  const int i0 = (bx * kWaves + wave) * 16 * NH;
   Slot sl;
-  if (!slot_of<GR>(T, SP, ws, &sl)) return;
+  if (!slot_of<GR>(T, SP, ws, by, &sl)) return false;
   const bool shared = ROWS == kAllRows ? sl.shared : ROWS == kSharedRows;
   const int I = shared ? Is : I_r;
-  if (i0 >= I) return;
+  if (i0 >= I) return false;
   const void* scale = shared ? sscale13 : scale13;
   constexpr int SB = NS * kSubtileBlock;  // stage bytes of one block
   unsigned char* stage = smem + wave * U * SB;
   const int KB = H / kBlock;
-  const int rot = first_block(T, wave, KB);
+  const int rot = first_block(T, wave, KB, bx, by);
   const uint8_t* W = shared ? sw13 : w13 + static_cast<size_t>(sl.e) * 2 * I * H;
   // load rows: instructions [0, NS) = gate rows i0 .. i0 + 8 NS - 1, then up
   const uint8_t* lrow[2 * NS];
@@ -240,6 +245,11 @@ __global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
           for (int m = 0; m < 4; ++m)
             xa[j][m] = *reinterpret_cast<const uint4*>(xrow[gr] + kb * kBlock + 8 * m);
         }
+        // The staged weights land in LDS through the loads' own path: the
+        // compiler does not order the LDS reads below after them, so wait
+        // for every load of the wave here (the activation loads above are
+        // issued by then).
+        wait_memory();
 #pragma unroll
         for (int j = 0; j < U; ++j) {
           const unsigned char* st = stage + j * SB;
@@ -280,37 +290,64 @@ __global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
             const uint16_t hi = bf16_bits(a);
             const uint16_t lo = bf16_bits(a - bf16_to_f32(hi));
             const size_t o = static_cast<size_t>(sl.base + q) * I + i0 + 16 * h + c;
-            act_hi[o] = hi;
-            act_lo[o] = lo;
+            if (C) {
+              // lanes c and c ^ 1 hold neighbouring outputs of the same token
+              // (the condition above is uniform over the 16 lanes of g)
+              const uint32_t hi2 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), 1));
+              const uint32_t lo2 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), 1));
+              if ((c & 1) == 0) {
+                st_u32<true>(reinterpret_cast<uint32_t*>(act_hi + o), hi | (hi2 << 16));
+                st_u32<true>(reinterpret_cast<uint32_t*>(act_lo + o), lo | (lo2 << 16));
+              }
+            } else {
+              act_hi[o] = hi;
+              act_lo[o] = lo;
+            }
           }
         }
       }
     }
   }
+  return true;
+}
+
+template <int NS, int U, int GR, bool E8, int ROWS>
+__global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
+    const uint16_t* __restrict__ hidden, const uint8_t* __restrict__ w13,
+    const void* __restrict__ scale13, const uint8_t* __restrict__ sw13,
+    const void* __restrict__ sscale13, int H, int I_r, int Is, int k, int T, int SP,
+    Workspace ws, float limit) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  gate_up_tile<NS, U, GR, E8, ROWS>(blockIdx.x, blockIdx.y, smem, hidden, w13, scale13, sw13,
+                                    sscale13, H, I_r, Is, k, T, SP, ws, limit);
 }
 
 // down projection.  Wave: output rows [h0, h0 + 16 NS) of one expert for all
 // its tokens, from the hi / lo activation planes; row q goes to
 // out[perm[base + q] * H] (routed: the route index t*k + j) or out[q * H]
 // (shared).
-template <int NS, int U, int GR, bool E8, int ROWS>
-__global__ __launch_bounds__(kThreads) void down_mfma_kernel(
-    const uint8_t* __restrict__ w2, const void* __restrict__ scale2,
-    const uint8_t* __restrict__ sw2, const void* __restrict__ sscale2, int H, int I_r, int Is,
-    int k, int T, int SP, Workspace ws) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+// The tile of workgroup (bx, by) of that grid.  wait() runs once, after the
+// first round of weight loads is issued and before the first activation is
+// read (every wave of the workgroup calls it); the kernel of its own passes
+// NoWait.
+template <int NS, int U, int GR, bool E8, int ROWS, typename Wait>
+__device__ __forceinline__ void down_tile(
+    int bx, int by, unsigned char* smem, const uint8_t* __restrict__ w2,
+    const void* __restrict__ scale2, const uint8_t* __restrict__ sw2,
+    const void* __restrict__ sscale2, int H, int I_r, int Is, int k, int T, int SP,
+    const Workspace& ws, Wait wait) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-  const int h0 = (blockIdx.x * kWaves + wave) * 16 * NS;
+  const int h0 = (bx * kWaves + wave) * 16 * NS;
   Slot sl;
-  if (!slot_of<GR>(T, SP, ws, &sl) || h0 >= H) return;
+  if (!slot_of<GR>(T, SP, ws, by, &sl) || h0 >= H) return;
   const bool shared = ROWS == kAllRows ? sl.shared : ROWS == kSharedRows;
   const int I = shared ? Is : I_r;
   const void* scale = shared ? sscale2 : scale2;
   constexpr int SB = NS * kSubtileBlock;
   unsigned char* stage = smem + wave * U * SB;
   const int KB = I / kBlock;
-  const int rot = first_block(T, wave, KB);
+  const int rot = first_block(T, wave, KB, bx, by);
   const uint8_t* W = shared ? sw2 : w2 + static_cast<size_t>(sl.e) * H * I;
   const uint8_t* lrow[2 * NS];
 #pragma unroll
@@ -322,6 +359,7 @@ __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
   const size_t plane = static_cast<size_t>(shared ? T : T * k) * I;
   const uint16_t* act_lo = act_hi + plane;
   float* out = shared ? ws.y_s : ws.rows;
+  bool waited = false;
 
   for (int p0 = sl.p_begin; p0 < sl.p_end; p0 += 16 * GR) {
     const int G = min(GR, (sl.p_end - p0 + 15) / 16);
@@ -346,6 +384,10 @@ __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
         sc[j] = kb0 + j < KB ? s : 0.f;
       }
       asm volatile("" ::: "memory");
+      if (!waited) {  // uniform
+        wait();
+        waited = true;
+      }
 #pragma unroll
       for (int gr = 0; gr < GR; ++gr) {
         if (gr >= G) break;
@@ -359,6 +401,7 @@ __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
             al[j][m] = *reinterpret_cast<const uint4*>(act_lo + arow[gr] + kb * kBlock + 8 * m);
           }
         }
+        wait_memory();  // the staged weights are in LDS (see gate_up_tile)
 #pragma unroll
         for (int j = 0; j < U; ++j) {
           const unsigned char* st = stage + j * SB;
@@ -396,6 +439,20 @@ __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
   }
 }
 
+struct NoWaitMfma {
+  __device__ void operator()() const {}
+};
+
+template <int NS, int U, int GR, bool E8, int ROWS>
+__global__ __launch_bounds__(kThreads) void down_mfma_kernel(
+    const uint8_t* __restrict__ w2, const void* __restrict__ scale2,
+    const uint8_t* __restrict__ sw2, const void* __restrict__ sscale2, int H, int I_r, int Is,
+    int k, int T, int SP, Workspace ws) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  down_tile<NS, U, GR, E8, ROWS>(blockIdx.x, blockIdx.y, smem, w2, scale2, sw2, sscale2, H, I_r,
+                                 Is, k, T, SP, ws, NoWaitMfma());
+}
+
 // Per wave: NS 16-row weight subtiles, U scale blocks per round of loads,
 // one 16-token group per pass (a routed expert rarely has more than 16 of a
 // step's tokens; the shared expert gets one grid row per 16 tokens, so that
@@ -424,6 +481,48 @@ void launch_dn(int R, hipStream_t s, const uint8_t* w, const void* scale, const 
   const size_t lds = static_cast<size_t>(kWaves) * kUDn * NS * kSubtileBlock;
   hipLaunchKernelGGL((down_mfma_kernel<NS, kUDn, kGR, E8, ROWS>), grid, dim3(kThreads), lds, s,
                      w, scale, sw, sscale, d.H, d.I, d.Is, d.k, d.T, SP, ws);
+}
+
+// The gate_up and down tiles of the merged launch (shared passes and touched
+// slots, up to kMergeSharedMaxTokens tokens) as one launch: workgroups
+// [0, n_gu) are the gate_up tiles (row-major over grid rows), the rest the
+// down tiles.  A down tile issues its first round of weight loads, then waits
+// until every gate_up tile of its row has published its SwiGLU planes, so
+// the down weights stream while the gate_up tiles drain (their waves end over
+// a wide window: 130 to 187 us at 16 tokens).  A gate_up tile writes its
+// SwiGLU planes with write-through (agent-scope atomic) stores, waits for
+// them, and then bumps its row's count; the down tile reads the planes with
+// plain loads (no L2 holds their lines when the launch starts, and nothing
+// reads them before the count is complete).  A workgroup waits only for workgroups of
+// lower index, which the dispatcher starts first; waits are bounded (the
+// sticky error word).  The router launch zeroes the counts.
+constexpr uint32_t kGChainSpin = 1u << 17;
+
+// Counter line of grid row y: the shared passes on the flag lines, the
+// touched slots on their gate_up count lines.
+__device__ __forceinline__ int gchain_line(int y, int SP) {
+  return y < SP ? kSyncFlags + y : sync_gu_cnt(y - SP);
+}
+
+template <bool E8>
+__global__ __launch_bounds__(kThreads, 4) void grouped_chain_kernel(GChainArgs a, Workspace ws) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const Sync sy{ws.sync};
+  const int it = blockIdx.x;
+  if (it < a.n_gu) {
+    const int by = it / a.gx, bx = it - by * a.gx;
+    if (gate_up_tile<kNsGu, kUGu, kGR, E8, kAllRows, true>(
+            bx, by, smem, a.hidden, a.w13, a.w13_scale, a.sw13, a.sw13_scale, a.H, a.I, a.Is,
+            a.k, a.T, a.SP, ws, a.limit))
+      bump(sy, gchain_line(by, a.SP));
+    return;
+  }
+  const int v = it - a.n_gu;
+  const int by = v / a.dx, bx = v - by * a.dx;
+  const uint32_t target = static_cast<uint32_t>((by < a.SP ? a.Is : a.I) / kBlock);
+  auto wait = [&]() { wait_count(sy, gchain_line(by, a.SP), 1, target, kGChainSpin); };
+  down_tile<kNsDn, kUDn, kGR, E8, kAllRows>(bx, by, smem, a.w2, a.w2_scale, a.sw2, a.sw2_scale,
+                                            a.H, a.I, a.Is, a.k, a.T, a.SP, ws, wait);
 }
 
 // grid rows: the shared expert's passes, then the touched-expert slots
@@ -476,6 +575,56 @@ hipError_t launch_down_mfma(const LayerDims& d, int rows, const void* w2, const 
     else MOE_DN(kNsDnRouted, false, kRoutedRows);
   }
 #undef MOE_DN
+  return hipGetLastError();
+}
+
+}  // namespace moe
+
+namespace moe {
+
+bool grouped_chain_supported(const LayerDims& d) {
+  // whole down tiles (every wave of a tile reaches the wait) and whole
+  // gate_up tiles; the shared passes fit the flag lines
+  return d.T <= kMergeSharedMaxTokens && d.H % (kWaves * 16 * kNsDn) == 0 &&
+         d.I % (kWaves * 8 * kNsGu) == 0 && d.Is % (kWaves * 8 * kNsGu) == 0 &&
+         kNsDn * kWaves * 16 == 256 && shared_rows(d) <= kNumFlags * kFlagRep &&
+         kLdsGu == static_cast<size_t>(kWaves) * kUDn * kNsDn * kSubtileBlock;
+}
+
+hipError_t launch_grouped_chain(const LayerDims& d, const void* hidden, const void* w13,
+                                const void* w13_scale, const void* sw13, const void* sw13_scale,
+                                const void* w2, const void* w2_scale, const void* sw2,
+                                const void* sw2_scale, const Workspace& ws, hipStream_t s,
+                                hipEvent_t evb, hipEvent_t eve) {
+  if (!grouped_chain_supported(d)) return hipErrorInvalidValue;
+  GChainArgs a{};
+  a.hidden = static_cast<const uint16_t*>(hidden);
+  a.w13 = static_cast<const uint8_t*>(w13);
+  a.w13_scale = w13_scale;
+  a.sw13 = static_cast<const uint8_t*>(sw13);
+  a.sw13_scale = sw13_scale;
+  a.w2 = static_cast<const uint8_t*>(w2);
+  a.w2_scale = w2_scale;
+  a.sw2 = static_cast<const uint8_t*>(sw2);
+  a.sw2_scale = sw2_scale;
+  a.H = d.H;
+  a.I = d.I;
+  a.Is = d.Is;
+  a.k = d.k;
+  a.T = d.T;
+  a.SP = shared_rows(d);
+  a.limit = d.limit;
+  const int rows = a.SP + slot_rows(d);
+  const int Imax = d.I > d.Is ? d.I : d.Is;
+  a.gx = Imax / (kWaves * 8 * kNsGu);
+  a.dx = d.H / (kWaves * 16 * kNsDn);
+  a.n_gu = a.gx * rows;
+  const int n = a.n_gu + a.dx * rows;
+  if (d.e8m0)
+    MOE_LAUNCH((grouped_chain_kernel<true>), dim3(n), dim3(kThreads), kLdsGu, s, evb, eve, a, ws);
+  else
+    MOE_LAUNCH((grouped_chain_kernel<false>), dim3(n), dim3(kThreads), kLdsGu, s, evb, eve, a,
+               ws);
   return hipGetLastError();
 }
 

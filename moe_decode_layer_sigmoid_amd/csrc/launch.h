@@ -160,6 +160,23 @@ struct ChainArgs {
   uint32_t grid;
 };
 
+// Arguments of the grouped path's merged gate_up + down launch (see
+// experts_mfma.hip, grouped_chain_kernel).
+struct GChainArgs {
+  const uint16_t* hidden;
+  const uint8_t* w13;
+  const void* w13_scale;
+  const uint8_t* sw13;
+  const void* sw13_scale;
+  const uint8_t* w2;
+  const void* w2_scale;
+  const uint8_t* sw2;
+  const void* sw2_scale;
+  int H, I, Is, k, T, SP;
+  float limit;
+  int gx, dx, n_gu;  // tiles per grid row (gate_up, down); gate_up workgroups
+};
+
 struct LayerDims {
   int T, H, E, k, I, Is;
   bool e8m0;
@@ -196,6 +213,16 @@ hipError_t launch_gate_up_mfma(const LayerDims& d, int rows, const void* hidden,
 hipError_t launch_down_mfma(const LayerDims& d, int rows, const void* w2, const void* w2_scale,
                             const void* sw2, const void* sw2_scale, const Workspace& ws,
                             hipStream_t s);
+
+// The same gate_up and down projections (shared passes and touched slots,
+// T <= kMergeSharedMaxTokens) as one launch whose down tiles wait for their
+// row's gate_up tiles; grouped_chain_supported tells whether the shape fits.
+bool grouped_chain_supported(const LayerDims& d);
+hipError_t launch_grouped_chain(const LayerDims& d, const void* hidden, const void* w13,
+                                const void* w13_scale, const void* sw13, const void* sw13_scale,
+                                const void* w2, const void* w2_scale, const void* sw2,
+                                const void* sw2_scale, const Workspace& ws, hipStream_t s,
+                                hipEvent_t evb = nullptr, hipEvent_t eve = nullptr);
 
 // Fused persistent kernel of the whole step (T <= kFusedMaxTokens).
 int fused_nj(int H, int I, int Is);
