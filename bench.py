@@ -386,17 +386,17 @@ def main():
         sb = 1 if sh.scale_fmt == "e8m0" else 4
         kern_bytes = (D * (2 * sh.I * H + sb * (2 * sh.I // 128) * (H // 128))
                       + T * H * 2 + T * k * sh.I * 4)
-        if path_taken == md.PATH_GROUPED:
-            # up to 64 tokens one launch also covers the shared expert's token
-            # passes (ROWS = 0); above, the routed launch has routed rows only
-            # (ROWS = 2) and the shared expert runs beside it
-            merged = T <= MERGE_SHARED_MAX_TOKENS
-            kern_name = "gate_up_mfma_kernel<NS, U, GR, E8, ROWS> (%s)" % (
-                "routed + shared experts" if merged else "routed experts")
-            kern_id = "gate_up_mfma_kernel<%s, %s, %d>" % (MFMA_GATE_UP_TILE, e8, 0 if merged else 2)
-            if sh.Is and merged:
-                kern_bytes += (2 * sh.Is * H + sb * (2 * sh.Is // 128) * (H // 128)
-                               + T * sh.Is * 4)
+        if path_taken == md.PATH_GROUPED and T <= MERGE_SHARED_MAX_TOKENS and H % 256 == 0:
+            # one launch: the gate_up and down tiles of the touched experts and
+            # of the shared expert's token passes (the boundary follows apart)
+            kern_name = "grouped_chain_kernel<E8> (routed + shared experts, gate_up and down)"
+            kern_id = "grouped_chain_kernel<%s>" % e8
+            kern_bytes = routed_b + shared_b + T * H * 2
+        elif path_taken == md.PATH_GROUPED:
+            # above 64 tokens the routed launch has routed rows only (ROWS =
+            # 2) and the shared expert runs beside it
+            kern_name = "gate_up_mfma_kernel<NS, U, GR, E8, ROWS> (routed experts)"
+            kern_id = "gate_up_mfma_kernel<%s, %s, 2>" % (MFMA_GATE_UP_TILE, e8)
         elif T <= CHAIN_MAX_TOKENS:
             # one launch streams the touched experts' gate_up and down weights
             # and the shared expert's down weights, and ends with the boundary

@@ -83,9 +83,11 @@ typedef enum {
    * weights (staged through LDS) times bf16 activations in
    * v_mfma_f32_16x16x32_bf16, fp32 accumulation per 128-wide scale block;
    * the SwiGLU output goes to the down projection as hi + lo bf16 parts.
-   * Kernels: router, gate_up (shared expert's 16-token passes and the
-   * touched experts), down (the same), boundary; above 64 tokens the shared
-   * expert's passes run on the plan's side stream instead. */
+   * Kernels: router; up to 64 tokens one launch of the gate_up and down tiles
+   * (shared expert's 16-token passes and the touched experts; a down tile
+   * waits for its row's gate_up tiles through a bounded wait); boundary.
+   * Above 64 tokens: separate gate_up and down launches of the touched
+   * experts, and the shared expert's passes on the plan's side stream. */
   MOE_DECODE_PATH_GROUPED = 2,
   /* The GEMV kernels launched one after another: the router (with the
    * shared expert's gate_up beside it), then, up to 16 tokens, one expert
@@ -211,7 +213,8 @@ int moe_decode_last_routes(moe_decode_plan_t p, int32_t T, int32_t* counts, int3
  * and end.  The dominant kernel is the fused persistent kernel on
  * MOE_DECODE_PATH_GEMV; on MOE_DECODE_PATH_GEMV_SPLIT the expert chain launch
  * (up to 16 tokens) or the routed-expert gate/up projection kernel; on
- * MOE_DECODE_PATH_GROUPED the gate/up projection kernel.  NULL, NULL switches
+ * MOE_DECODE_PATH_GROUPED the gate_up + down launch (up to 64 tokens) or the
+ * routed gate/up projection kernel.  NULL, NULL switches
  * it off.  Eager runs only: not for use under graph capture.
  */
 int moe_decode_set_expert_events(moe_decode_plan_t p, void* begin, void* end);
@@ -222,8 +225,8 @@ int moe_decode_set_expert_events(moe_decode_plan_t p, void* begin, void* end);
 int moe_decode_path_for(moe_decode_plan_t p, int32_t T);
 
 /*
- * Health check of the bounded waits (the fused kernel's and the expert
- * chain launch's): synchronises the plan's
+ * Health check of the bounded waits (the fused kernel's, the expert chain
+ * launch's and the grouped gate_up + down launch's): synchronises the plan's
  * device, returns in *gave_up whether any wait since the last check ran out
  * of its spin budget (which would mean a result is not trustworthy) and
  * clears the flag.  Not capturable; for tests and monitoring.
