@@ -519,7 +519,8 @@ __global__ __launch_bounds__(kThreads, 4) void grouped_chain_kernel(GChainArgs a
   }
   const int v = it - a.n_gu;
   const int by = v / a.dx, bx = v - by * a.dx;
-  const uint32_t target = static_cast<uint32_t>((by < a.SP ? a.Is : a.I) / kBlock);
+  // the row's gate_up tiles (a tile covers kWaves * 8 * kNsGu SwiGLU outputs)
+  const uint32_t target = static_cast<uint32_t>((by < a.SP ? a.Is : a.I) / (kWaves * 8 * kNsGu));
   auto wait = [&]() { wait_count(sy, gchain_line(by, a.SP), 1, target, kGChainSpin); };
   down_tile<kNsDn, kUDn, kGR, E8, kAllRows>(bx, by, smem, a.w2, a.w2_scale, a.sw2, a.sw2_scale,
                                             a.H, a.I, a.Is, a.k, a.T, a.SP, ws, wait);
