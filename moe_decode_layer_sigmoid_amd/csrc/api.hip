@@ -49,6 +49,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // hand-off sits on the critical path); GEMV asks for the fused kernel.
 int path_for(const moe_decode_plan_s& p, int32_t T) {
   const int want = p.desc.path;
+  if (p.desc.num_experts == 0)  // a dense layer: the GEMV or the MFMA kernels
+    return want == MOE_DECODE_PATH_GROUPED ||
+                   (want == MOE_DECODE_PATH_AUTO && T >= moe::kGroupedMinTokens)
+               ? MOE_DECODE_PATH_GROUPED
+               : MOE_DECODE_PATH_GEMV_SPLIT;
   if (want == MOE_DECODE_PATH_GEMV_SPLIT || want == MOE_DECODE_PATH_GROUPED) return want;
   if (want == MOE_DECODE_PATH_GEMV && T <= moe::kFusedMaxTokens && p.fused_grid > 0)
     return MOE_DECODE_PATH_GEMV;
@@ -126,8 +131,12 @@ const char* moe_decode_strerror(int code) {
 
 int moe_decode_desc_check(const moe_decode_desc* d) {
   if (!d) return MOE_DECODE_ERR_INVALID_ARG;
-  if (d->hidden <= 0 || d->num_experts <= 0 || d->top_k <= 0 || d->intermediate <= 0 ||
+  if (d->hidden <= 0 || d->num_experts < 0 || d->top_k < 0 || d->intermediate < 0 ||
       d->shared_intermediate < 0 || d->max_tokens <= 0)
+    return MOE_DECODE_ERR_INVALID_ARG;
+  // a dense layer (no routed experts) has its MLP in the shared-expert slot
+  if (d->num_experts == 0 ? (d->top_k != 0 || d->shared_intermediate == 0)
+                          : (d->top_k == 0 || d->intermediate == 0))
     return MOE_DECODE_ERR_INVALID_ARG;
   if (d->scale_fmt != MOE_DECODE_SCALE_FP32 && d->scale_fmt != MOE_DECODE_SCALE_E8M0)
     return MOE_DECODE_ERR_INVALID_ARG;
@@ -150,10 +159,13 @@ int moe_decode_desc_check(const moe_decode_desc* d) {
 int moe_decode_args_check(const moe_decode_desc* d, const moe_decode_args* a, int32_t T) {
   if (!d || !a) return MOE_DECODE_ERR_INVALID_ARG;
   if (T < 0 || T > d->max_tokens) return MOE_DECODE_ERR_INVALID_ARG;
-  const void* req[] = {a->hidden, a->residual, a->router_w, a->w13, a->w13_scale, a->w2,
-                       a->w2_scale, a->gamma, a->out, a->residual_out};
+  const void* req[] = {a->hidden, a->residual, a->gamma, a->out, a->residual_out};
   for (const void* p : req)
     if (!p) return MOE_DECODE_ERR_INVALID_ARG;
+  const void* routed[] = {a->router_w, a->w13, a->w13_scale, a->w2, a->w2_scale};
+  if (d->num_experts > 0)
+    for (const void* p : routed)
+      if (!p) return MOE_DECODE_ERR_INVALID_ARG;
   if (d->shared_intermediate > 0 && (!a->sw13 || !a->sw13_scale || !a->sw2 || !a->sw2_scale))
     return MOE_DECODE_ERR_INVALID_ARG;
   // 16-byte vector loads and stores need 16-byte aligned tensors.
@@ -282,8 +294,40 @@ static int run_fused(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, h
   return err == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;
 }
 
+// A dense layer (no routed experts): the shared-expert slot's MLP and the
+// boundary with no routed rows.  The decode page's LayerStages._build_dense
+// builds such layers' DenseMlp from the same fp8 weight pair with block
+// scales and swiglu_limit, and LayerStages.mlp sends dense(x) to the same
+// boundary as the MoE output.  GEMV path: the router kernel with no router
+// rows (only the gate_up tiles), the down kernel's shared row, the boundary;
+// MFMA path: the shared-row gate_up and down launches, the boundary.
+static int run_dense(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, hipStream_t s) {
+  const moe::LayerDims d = dims(p->desc, T);
+  hipError_t err = hipSuccess;
+  auto step = [&](hipError_t e) {
+    if (err == hipSuccess && e != hipSuccess) err = e;
+  };
+  if (path_for(*p, T) == MOE_DECODE_PATH_GROUPED) {
+    step(moe::launch_gate_up_mfma(d, moe::kSharedRows, a->hidden, nullptr, nullptr, a->sw13,
+                                  a->sw13_scale, p->ws, s, p->user_begin, p->user_end));
+    if (err == hipSuccess)
+      step(moe::launch_down_mfma(d, moe::kSharedRows, nullptr, nullptr, a->sw2, a->sw2_scale,
+                                 p->ws, s));
+  } else {
+    step(moe::launch_router(d, a->hidden, nullptr, p->ws.zero_bias, p->ws, nullptr, nullptr,
+                            a->sw13, a->sw13_scale, s, p->user_begin, p->user_end));
+    if (err == hipSuccess)
+      step(moe::launch_down_gemv(d, nullptr, nullptr, a->sw2, a->sw2_scale, p->ws, s));
+  }
+  if (err == hipSuccess)
+    step(moe::launch_epilogue(d, a->residual, a->gamma, p->ws, a->out, a->residual_out,
+                              a->moe_out, s));
+  return err == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;
+}
+
 static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t T,
                          hipStream_t s) {
+  if (p->desc.num_experts == 0) return run_dense(p, a, T, s);
   const int path = path_for(*p, T);
   if (path == MOE_DECODE_PATH_GEMV) return run_fused(p, a, T, s);
   const moe::LayerDims d = dims(p->desc, T);

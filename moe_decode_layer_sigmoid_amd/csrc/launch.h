@@ -185,10 +185,12 @@ struct LayerDims {
 
 // Router logits, sigmoid, top-k, weights and the route tables; with sw13
 // non-null also the shared expert's gate_up + SwiGLU (into ws.act_s).
+// With d.E == 0 (a dense layer) only the gate_up tiles run.  evb / eve: the
+// measurement hook (MOE_LAUNCH).
 hipError_t launch_router(const LayerDims& d, const void* hidden, const void* router_w,
                          const float* bias, const Workspace& ws, int32_t* ids_out,
                          float* weights_out, const void* sw13, const void* sw13_scale,
-                         hipStream_t s);
+                         hipStream_t s, hipEvent_t evb = nullptr, hipEvent_t eve = nullptr);
 
 // gate_up + clamped SwiGLU (GEMV) of the touched experts (one grid row
 // each; the shared expert's runs in the router launch).

@@ -116,12 +116,13 @@ int router_block_tokens(int T) { return T <= 16 ? 1 : kRouterTokBlk; }
 hipError_t launch_router(const LayerDims& d, const void* hidden, const void* router_w,
                          const float* bias, const Workspace& ws, int32_t* ids_out,
                          float* weights_out, const void* sw13, const void* sw13_scale,
-                         hipStream_t s) {
+                         hipStream_t s, hipEvent_t evb, hipEvent_t eve) {
   if (d.T > kRouterMaxBlk * kRouterTokBlk) return hipErrorInvalidValue;
   const int n_router = (d.E + 3) / 4;
   const int n_shared = sw13 && d.Is > 0 ? d.Is / 8 : 0;  // 8 SwiGLU rows per workgroup
   const int TB = router_block_tokens(d.T);
-  dim3 grid(n_router + n_shared, (d.T + TB - 1) / TB);
+  // no routed experts (a dense layer): only the gate_up tiles, one grid row
+  dim3 grid(n_router + n_shared, d.E > 0 ? (d.T + TB - 1) / TB : 1);
   const size_t smem = route_smem_bytes(d.T, d.E, d.k);
   const auto* x = static_cast<const uint16_t*>(hidden);
   const auto* w = static_cast<const uint16_t*>(router_w);
@@ -130,14 +131,14 @@ hipError_t launch_router(const LayerDims& d, const void* hidden, const void* rou
   switch (((d.H + 511) / 512) * 2 + (d.e8m0 ? 1 : 0)) {
 #define X(N)                                                                                   \
   case 2 * N:                                                                                  \
-    hipLaunchKernelGGL((router_kernel<N, false>), grid, dim3(kThreads), smem, s, x, w, bias,    \
-                       d.T, TB, d.H, d.E, d.k, d.rsf, ws, ids_out, weights_out, n_router, sw,      \
-                       sw13_scale, Is, d.limit);                                               \
+    MOE_LAUNCH((router_kernel<N, false>), grid, dim3(kThreads), smem, s, evb, eve, x, w, bias, \
+               d.T, TB, d.H, d.E, d.k, d.rsf, ws, ids_out, weights_out, n_router, sw,          \
+               sw13_scale, Is, d.limit);                                                       \
     break;                                                                                     \
   case 2 * N + 1:                                                                              \
-    hipLaunchKernelGGL((router_kernel<N, true>), grid, dim3(kThreads), smem, s, x, w, bias,     \
-                       d.T, TB, d.H, d.E, d.k, d.rsf, ws, ids_out, weights_out, n_router, sw,      \
-                       sw13_scale, Is, d.limit);                                               \
+    MOE_LAUNCH((router_kernel<N, true>), grid, dim3(kThreads), smem, s, evb, eve, x, w, bias,  \
+               d.T, TB, d.H, d.E, d.k, d.rsf, ws, ids_out, weights_out, n_router, sw,          \
+               sw13_scale, Is, d.limit);                                                       \
     break;
     X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16)
 #undef X

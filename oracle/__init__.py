@@ -28,5 +28,6 @@ from .moe_oracle import (  # noqa: F401
     route_table,
     rms_norm,
     moe_layer,
+    dense_layer,
     score_gaps,
 )

@@ -178,8 +178,34 @@ def rms_norm(h: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
 
 # -------------------------------------------------------------------- layer
 
+def dense_layer(inp, rows=None) -> dict:
+    """A dense layer step in float64: no router and no routed experts (E = 0);
+    the layer's MLP is held in the shared-expert weights (sw13, sw2).
+
+    The decode page's LayerStages._build_dense builds a DenseMlp from a dense
+    layer's fp8 gate_up / down weights with their weight_scale_inv, the
+    swiglu_limit and the e8m0 flag, and LayerStages.mlp returns dense(x) as
+    the layer's FFN output, which goes through the same boundary as the MoE
+    output (the draft page's reduced_norm).  So y = W2 a with a =
+    silu(min(g, L)) clamp(u, -L, L), [g; u] = W13 x; h = y + residual; out =
+    RMSNorm(h) * gamma.  Returns moe (= y), h and out (ids and weights empty).
+    """
+    sh = inp.shape
+    rows = np.arange(sh.T) if rows is None else np.asarray(rows)
+    x = bf16_bits_to_f64(inp.hidden[rows])
+    res = bf16_bits_to_f64(inp.residual[rows])
+    gamma = bf16_bits_to_f64(inp.gamma)
+    y = expert_mlp(dequantize(inp.sw13, inp.sw13_scale), dequantize(inp.sw2, inp.sw2_scale), x,
+                   sh.limit)
+    h = y + res
+    n = len(rows)
+    return dict(ids=np.zeros((n, 0), np.int32), weights=np.zeros((n, 0)), y_shared=y, moe=y, h=h,
+                out=rms_norm(h, gamma, sh.eps))
+
+
 def moe_layer(inp, forced_ids=None, rows=None) -> dict:
-    """The whole layer step in float64.
+    """The whole layer step in float64 (a dense layer when the shape has no
+    routed experts: dense_layer).
 
     inp         synth.LayerInputs (device bytes of every input)
     forced_ids  optional [T, k] expert ids (indexed by token) to use instead
@@ -196,6 +222,8 @@ def moe_layer(inp, forced_ids=None, rows=None) -> dict:
     output).
     """
     sh = inp.shape
+    if sh.E == 0:
+        return dense_layer(inp, rows)
     rows = np.arange(sh.T) if rows is None else np.asarray(rows)
     x = bf16_bits_to_f64(inp.hidden[rows])
     res = bf16_bits_to_f64(inp.residual[rows])

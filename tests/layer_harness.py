@@ -131,8 +131,15 @@ def check_layer(inp, got, rows=None, use_c=None, c_oracle=None):
     """Full comparison of one run; rows = token rows to compute with the
     oracle (all when None).  Returns a dict of the measured errors."""
     sh = inp.shape
-    n_tie = check_ids(inp, got["ids"])
     rows_list = np.arange(sh.T) if rows is None else np.asarray(rows)
+    if sh.E == 0:
+        # a dense layer: no routing to check; the NumPy oracle computes it
+        ref = mo.moe_layer(inp, rows=rows_list)
+        e_out = assert_close(got["out"][rows_list], ref["out"], "out")
+        e_res = assert_close(got["residual_out"][rows_list], ref["h"], "residual_out")
+        assert_close(got["moe"][rows_list], ref["moe"], "moe_out")
+        return dict(n_tie=0, out_rel_l2=e_out[0], out_max=e_out[1], res_rel_l2=e_res[0])
+    n_tie = check_ids(inp, got["ids"])
     if use_c is None:
         use_c = sh.H * sh.I * len(rows_list) > 2 ** 24
     if use_c:

@@ -71,6 +71,30 @@ def test_desc_check_codes():
     assert md.lib().moe_decode_desc_check(None) == md.ERR_INVALID_ARG
 
 
+def test_dense_layer_descriptors():
+    """No routed experts (E = 0, k = 0): a dense layer whose MLP sits in the
+    shared-expert slot; it needs that slot, and a MoE layer needs k and I."""
+    d = good_desc()
+    d.num_experts, d.top_k, d.intermediate = 0, 0, 0
+    assert md.desc_check(d) == md.OK
+    d.top_k = 1
+    assert md.desc_check(d) == md.ERR_INVALID_ARG
+    d.top_k, d.shared_intermediate = 0, 0
+    assert md.desc_check(d) == md.ERR_INVALID_ARG
+    d = good_desc()
+    d.top_k = 0
+    assert md.desc_check(d) == md.ERR_INVALID_ARG
+    d = good_desc()
+    d.intermediate = 0
+    assert md.desc_check(d) == md.ERR_INVALID_ARG
+    # a dense layer's run needs no router or routed-expert pointers
+    d = good_desc()
+    d.num_experts, d.top_k, d.intermediate = 0, 0, 0
+    none = dict(router_w=None, w13=None, w13_scale=None, w2=None, w2_scale=None)
+    assert md.args_check(d, full_args(**none), 1) == md.OK
+    assert md.args_check(d, full_args(sw13=None, **none), 1) == md.ERR_INVALID_ARG
+
+
 def full_args(**kw):
     names = [f for f, _ in md.Args._fields_]
     vals = {n: 0x10000 * (i + 1) for i, n in enumerate(names)}

@@ -284,6 +284,31 @@ def test_hand_two_expert_example(k, which, c_oracle):
         assert abs(out4[2] - 11.17142897897562) < 1e-12
 
 
+def test_hand_dense_layer():
+    """A dense layer (no routed experts): the shared-expert weights of the
+    hand-built layer above as the layer's MLP.  x = 2 e0, gate = up = 4 on
+    column 0 give g = u = 8, clamped to 7; down = 1 at [2, 0]; residual e3:
+    h = (0, 0, silu(7) * 7, 1, 0, ...)."""
+    base = _hand_layer(2)
+    sh = base.shape.replace(E=0, k=0, I=0)
+    inp = make_layer_from_arrays(
+        sh, hidden=base.hidden, residual=base.residual, sw13=base.sw13,
+        sw13_scale=base.sw13_scale, sw2=base.sw2, sw2_scale=base.sw2_scale, gamma=base.gamma)
+    r = oracle.moe_layer(inp)
+    sig = lambda z: 1 / (1 + math.exp(-z))
+    a_s = 7 * sig(7) * 7
+    h4 = [0.0, 0.0, a_s, 1.0]
+    assert r["ids"].shape == (1, 0)
+    assert np.allclose(r["h"][0, :4], h4, rtol=1e-14, atol=0)
+    assert np.all(r["h"][0, 4:] == 0)
+    assert np.allclose(r["moe"][0, :4], [0.0, 0.0, a_s, 0.0], rtol=1e-14, atol=0)
+    ms = sum(v * v for v in h4) / 128
+    assert np.allclose(r["out"][0, :4], [v / math.sqrt(ms + 1e-5) for v in h4], rtol=1e-13)
+    # the same numbers as the shared part of the two-expert example
+    full = oracle.moe_layer(base)
+    assert np.allclose(r["h"][0, 2], full["h"][0, 2], rtol=1e-15)
+
+
 # ---------------------------------------------- the two oracles agree
 
 @pytest.mark.parametrize("fmt", ["fp32", "e8m0"])
