@@ -58,10 +58,26 @@ def step_bytes(sh, D):
 
 
 def cpu_baseline(inp, sh, metric_bytes, seconds):
+    import oracle
     from oracle import c_oracle
 
     c_oracle.build(force=False)
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
+    if sh.E == 0:
+        # a dense layer: the NumPy oracle (the C oracle is the MoE layer's)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.moe_layer(inp)
+            reps += 1
+            elapsed = time.perf_counter() - t0
+            if elapsed >= seconds:
+                break
+        per_step = elapsed / reps
+        return {"value": metric_bytes / per_step / 1e12, "unit": "TB/s",
+                "us_per_layer": per_step * 1e6, "cores": threads, "kind": "oracle",
+                "sample": "NumPy float64 dense-layer oracle, %d repetition(s) of the %s layer, "
+                          "%.1f s (BLAS threads: up to %d)" % (reps, sh_name(sh), elapsed,
+                                                               threads)}
     # token rows per repetition: whole step for small T, else a prefix
     rows = list(range(sh.T))
     t0 = time.perf_counter()
@@ -279,15 +295,18 @@ def main():
     from oracle import c_oracle
 
     c_oracle.build(force=False)
-    ref = c_oracle.moe_layer(inp, forced_ids=got_ids, rows=[0])
+    ref = (oracle.moe_layer(inp, rows=[0]) if E == 0 else
+           c_oracle.moe_layer(inp, forced_ids=got_ids, rows=[0]))
     got0 = oracle.bf16_bits_to_f64(out[:1].cpu().numpy().view(np.uint16))
     rel0 = float(np.linalg.norm(got0 - ref["out"]) / np.linalg.norm(ref["out"]))
-    x = oracle.bf16_bits_to_f64(inp.hidden)
-    sc = oracle.sigmoid(oracle.router_logits(x, oracle.bf16_bits_to_f64(inp.router_w)))
-    oids = oracle.select_experts(sc, None, k)
-    gaps = oracle.score_gaps(sc, None, k)
-    ids_ok = all(set(a) == set(b) for a, b, g in zip(got_ids.tolist(), oids.tolist(), gaps)
-                 if g > 1e-4)
+    ids_ok = True
+    if E > 0:
+        x = oracle.bf16_bits_to_f64(inp.hidden)
+        sc = oracle.sigmoid(oracle.router_logits(x, oracle.bf16_bits_to_f64(inp.router_w)))
+        oids = oracle.select_experts(sc, None, k)
+        gaps = oracle.score_gaps(sc, None, k)
+        ids_ok = all(set(a) == set(b) for a, b, g in zip(got_ids.tolist(), oids.tolist(), gaps)
+                     if g > 1e-4)
     log("check: distinct experts %d, ids match %s, row-0 rel L2 %.2e" % (D, ids_ok, rel0))
 
     # ---- weight copies so that no step finds its weights cached
@@ -375,7 +394,19 @@ def main():
         log("note: the GPU caught up with the host during the bracketed launches")
     path_taken = plan.path_for(T)
     e8 = "true" if sh.scale_fmt == "e8m0" else "false"
-    if path_taken == md.PATH_GEMV:
+    sb = 1 if sh.scale_fmt == "e8m0" else 4
+    if E == 0:
+        # a dense layer: the gate/up projection of its MLP (the router
+        # kernel's gate_up tiles on the GEMV path, the shared-row MFMA launch)
+        kern_bytes = (2 * sh.Is * H + sb * (2 * sh.Is // 128) * (H // 128) + T * H * 2
+                      + T * sh.Is * 4)
+        if path_taken == md.PATH_GROUPED:
+            kern_name = "gate_up_mfma_kernel<NS, U, GR, E8, ROWS> (dense MLP)"
+            kern_id = "gate_up_mfma_kernel<%s, %s, 1>" % (MFMA_GATE_UP_TILE, e8)
+        else:
+            kern_name = "router_kernel<NJ2, E8> (dense MLP gate_up tiles)"
+            kern_id = "router_kernel<%d, %s>" % ((H + 511) // 512, e8)
+    elif path_taken == md.PATH_GEMV:
         # one persistent kernel runs the whole step: its bytes are the step's
         kern_name = "decode_fused_kernel (router, shared + routed experts, boundary)"
         kern_id = "decode_fused_kernel<"

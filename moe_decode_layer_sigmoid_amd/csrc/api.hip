@@ -51,7 +51,7 @@ int path_for(const moe_decode_plan_s& p, int32_t T) {
   const int want = p.desc.path;
   if (p.desc.num_experts == 0)  // a dense layer: the GEMV or the MFMA kernels
     return want == MOE_DECODE_PATH_GROUPED ||
-                   (want == MOE_DECODE_PATH_AUTO && T >= moe::kGroupedMinTokens)
+                   (want == MOE_DECODE_PATH_AUTO && T >= moe::kDenseGroupedMinTokens)
                ? MOE_DECODE_PATH_GROUPED
                : MOE_DECODE_PATH_GEMV_SPLIT;
   if (want == MOE_DECODE_PATH_GEMV_SPLIT || want == MOE_DECODE_PATH_GROUPED) return want;

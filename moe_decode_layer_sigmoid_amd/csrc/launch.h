@@ -103,6 +103,12 @@ constexpr int kMergeSharedMaxTokens = 64;
 // grouped): 1 token 46.5 / 74.2, 2: 75.3 / 87.0, 3: 103.1 / 109.9,
 // 4: 127.9 / 118.9, 8: 215.8 / 183.5, 16: 378.8 / 295.6.
 constexpr int kGroupedMinTokens = 4;
+// The same for a dense layer (no routed experts).  Its MFMA launches have
+// only I_s / 128 tiles per 16-token pass, so they win only where the GEMV
+// tiles' per-token work has grown (MI355X, H = 4096, I_s = 8192, µs per step
+// split / grouped: 2 tokens 37.9 / 121.6, 8: 87.5 / 128.7, 16: 152.6 / 139.7,
+// 64: 546.5 / 137.8).
+constexpr int kDenseGroupedMinTokens = 16;
 
 // Arguments of the fused persistent kernel (see decode_fused.hip).
 struct FusedArgs {

@@ -68,6 +68,10 @@ WORKLOADS = {
     "decode_t16": LayerShape(T=16, H=4096, E=128, k=8, I=1536, Is=1536, scale_fmt="fp32", tag=2),
     "wide_t64_e8m0": LayerShape(T=64, H=6144, E=256, k=8, I=2048, Is=2048, scale_fmt="e8m0", tag=3),
     "verify_t128": LayerShape(T=128, H=6144, E=256, k=8, I=2048, Is=2048, scale_fmt="fp32", tag=4),
+    # a dense layer's MLP (no routed experts; the MLP in the shared-expert
+    # slot) at the decode hidden size, intermediate 2 x hidden (the library's
+    # largest): a synthetic choice, the pages give no dense-layer sizes
+    "dense_t1": LayerShape(T=1, H=4096, E=0, k=0, I=0, Is=8192, scale_fmt="fp32", tag=5),
 }
 WORKLOAD_ORDER = ["tiny_t1", "decode_t1", "decode_t16", "wide_t64_e8m0", "verify_t128"]
 

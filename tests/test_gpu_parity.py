@@ -169,7 +169,7 @@ def test_same_expert_for_every_token(T, H, I, path, c_oracle):
 def test_dense_layer(T, fmt, c_oracle):
     """No routed experts: the layer's fp8 clamped-SwiGLU MLP (in the shared-
     expert slot) and the boundary, on the GEMV kernels (few tokens) and the
-    MFMA kernels (AUTO from 4 tokens), against the dense oracle; each path
+    MFMA kernels (AUTO from 16 tokens), against the dense oracle; each path
     forced at T = 3 and 16 as well."""
     sh = LayerShape(T=T, H=2048, E=0, k=0, I=0, Is=3072, scale_fmt=fmt, tag=320 + T)
     inp = make_layer(sh)
@@ -178,7 +178,7 @@ def test_dense_layer(T, fmt, c_oracle):
     for path in paths:
         _log("dense", sh, "path", path)
         plan = make_plan(sh, path=path)
-        want = (md.PATH_GROUPED if T >= 4 else md.PATH_GEMV_SPLIT) if path == md.PATH_AUTO else path
+        want = (md.PATH_GROUPED if T >= 16 else md.PATH_GEMV_SPLIT) if path == md.PATH_AUTO else path
         assert plan.path_for(T) == want
         got = run_layer(plan, dev, T)
         err = check_layer(inp, got)
