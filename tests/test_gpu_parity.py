@@ -78,6 +78,9 @@ SMALL = [
     (64, 256, 128, 8, 128, 128, "e8m0"),
     (130, 128, 200, 6, 128, 0, "fp32"),  # more than two 64-token mask words
     (1, 8192, 16, 2, 128, 128, "fp32"),  # widest hidden
+    (3, 256, 1024, 8, 128, 0, "fp32"),  # most experts: top-k by rounds of wave arg-max
+    (40, 256, 1024, 16, 128, 128, "e8m0"),  # most experts with the largest k
+    (256, 256, 64, 8, 128, 128, "fp32"),  # most tokens (four 64-token mask words)
 ]
 
 
