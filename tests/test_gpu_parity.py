@@ -243,22 +243,9 @@ def test_smaller_T_than_plan_and_zero(c_oracle):
     plan.close()
 
 
-@pytest.mark.parametrize("path,T,H,I", [(md.PATH_GEMV, 16, 1024, 512),
-                                        (md.PATH_GEMV_SPLIT, 16, 1024, 512),
-                                        (md.PATH_GROUPED, 16, 1024, 512),
-                                        (md.PATH_GROUPED, 80, 1024, 512),
-                                        (md.PATH_GROUPED, 24, 2304, 640),
-                                        (md.PATH_GROUPED, 80, 2304, 640)],
-                         ids=["fused", "split", "grouped", "grouped-side-stream",
-                              "grouped-wide", "grouped-wide-side-stream"])
-def test_graph_replay_matches_eager(path, T, H, I, c_oracle):
-    """One run captured into a HIP graph, replayed several times with eager
-    work in between; every replay equals the eager result bit for bit.  At
-    80 tokens the MFMA path puts the shared expert on the side stream.  The
-    H = 2304, I = 640 cases give the MFMA kernels contractions of 18 and 5
-    blocks (so at 24 tokens the rotated block walks wrap at odd points) and a
-    shared expert narrower than the routed ones."""
-    sh = WORKLOADS["decode_t16"].replace(T=T, H=H, I=I, Is=256, tag=305)
+def _graph_vs_eager(sh, path):
+    """One run captured into a HIP graph, replayed four times with eager runs
+    in between; every replay equals the eager result bit for bit."""
     inp = make_layer(sh)
     dev = to_device(inp)
     plan = make_plan(sh, path=path)
@@ -294,3 +281,30 @@ def test_graph_replay_matches_eager(path, T, H, I, c_oracle):
         # eager work between replays
         run_layer(plan, dev, T)
     plan.close()
+
+
+@pytest.mark.parametrize("path,T,H,I", [(md.PATH_GEMV, 16, 1024, 512),
+                                        (md.PATH_GEMV_SPLIT, 16, 1024, 512),
+                                        (md.PATH_GROUPED, 16, 1024, 512),
+                                        (md.PATH_GROUPED, 80, 1024, 512),
+                                        (md.PATH_GROUPED, 24, 2304, 640),
+                                        (md.PATH_GROUPED, 80, 2304, 640)],
+                         ids=["fused", "split", "grouped", "grouped-side-stream",
+                              "grouped-wide", "grouped-wide-side-stream"])
+def test_graph_replay_matches_eager(path, T, H, I, c_oracle):
+    """One run captured into a HIP graph, replayed several times with eager
+    work in between; every replay equals the eager result bit for bit.  At
+    80 tokens the MFMA path puts the shared expert on the side stream.  The
+    H = 2304, I = 640 cases give the MFMA kernels contractions of 18 and 5
+    blocks (so at 24 tokens the rotated block walks wrap at odd points) and a
+    shared expert narrower than the routed ones."""
+    _graph_vs_eager(WORKLOADS["decode_t16"].replace(T=T, H=H, I=I, Is=256, tag=305), path)
+
+
+@pytest.mark.parametrize("name", ["decode_t1", "decode_t16"])
+def test_workload_graph_replay(name, c_oracle):
+    """The decode workloads at full size on the AUTO path (the launches the
+    benchmark times: the expert chain at one token, the grouped merged launch
+    at 16), captured and replayed: every replay equals the eager run, which
+    the oracle checks (test_decode_layers_full)."""
+    _graph_vs_eager(WORKLOADS[name], md.PATH_AUTO)
