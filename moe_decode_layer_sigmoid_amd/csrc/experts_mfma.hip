@@ -110,18 +110,25 @@ __device__ __forceinline__ f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, co
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) { return static_cast<uint16_t>(f32_to_bf16(f)); }
 
-// Up to this many tokens the launches' workgroups all start in about one
-// round, and if every wave walked the contraction from block 0 they would all
-// read the same block columns at once; the waves then drain unevenly.  There
-// each wave starts at its own block (its id modulo the block count) and
-// wraps around; the order of a wave's blocks is fixed by the grid, so results
-// stay deterministic.  With more tokens later workgroups start staggered
-// anyway, and the rotation only scatters the accesses of neighbouring waves
-// (measured slower at 64 and 128 tokens).
+// Each wave walks the contraction in blocks of 128 columns.  If every wave
+// started at block 0, the waves would read the same block columns at once:
+// up to this many tokens the launches' workgroups all start in about one
+// round and then drain unevenly; and where the gate_up rows are a power of
+// two bytes long (H = 4096) those columns of all rows share the same few
+// memory channels, at any token count (the down tiles follow the same rule).
+// There each wave starts at its own
+// block (its id modulo the block count) and wraps around; the order of a
+// wave's blocks is fixed by the grid, so results stay deterministic.
+// Measured at H = 4096, E = 128: 64 tokens 472 -> 430 us, 128 tokens 515 ->
+// 472 us, 256 tokens 649 -> 633 us.  Otherwise, with more tokens, later
+// workgroups start staggered anyway, and the rotation only scatters the
+// accesses of neighbouring waves (measured slower at H = 6144 with 64 and
+// 128 tokens; rotating by the down rows' length, I = 2048 there, changed
+// nothing).
 constexpr int kRotateMaxTokens = 32;
 
-__device__ __forceinline__ int first_block(int T, int wave, int KB, int bx, int by) {
-  if (T > kRotateMaxTokens) return 0;
+__device__ __forceinline__ int first_block(int T, int H, int wave, int KB, int bx, int by) {
+  if (T > kRotateMaxTokens && (H & (H - 1)) != 0) return 0;
   return (bx * kWaves + wave + 5 * by) % KB;
 }
 
@@ -190,7 +197,7 @@ __device__ __forceinline__ bool gate_up_tile(
   constexpr int SB = NS * kSubtileBlock;  // stage bytes of one block
   unsigned char* stage = smem + wave * U * SB;
   const int KB = H / kBlock;
-  const int rot = first_block(T, wave, KB, bx, by);
+  const int rot = first_block(T, H, wave, KB, bx, by);
   const uint8_t* W = shared ? sw13 : w13 + static_cast<size_t>(sl.e) * 2 * I * H;
   // load rows: instructions [0, NS) = gate rows i0 .. i0 + 8 NS - 1, then up
   const uint8_t* lrow[2 * NS];
@@ -347,7 +354,7 @@ __device__ __forceinline__ void down_tile(
   constexpr int SB = NS * kSubtileBlock;
   unsigned char* stage = smem + wave * U * SB;
   const int KB = I / kBlock;
-  const int rot = first_block(T, wave, KB, bx, by);
+  const int rot = first_block(T, H, wave, KB, bx, by);
   const uint8_t* W = shared ? sw2 : w2 + static_cast<size_t>(sl.e) * H * I;
   const uint8_t* lrow[2 * NS];
 #pragma unroll
@@ -454,32 +461,39 @@ __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
 }
 
 // Per wave: NS 16-row weight subtiles, U scale blocks per round of loads,
-// one 16-token group per pass (a routed expert rarely has more than 16 of a
-// step's tokens; the shared expert gets one grid row per 16 tokens, so that
-// its passes run in parallel).
+// one 16-token group per pass (the shared expert gets one grid row per 16
+// tokens, so that its passes run in parallel).
 // The routed-only down launch (above kMergeSharedMaxTokens, several tokens
 // per expert) takes 128 rows per wave: each activation fragment then feeds
 // eight weight subtiles (measured 8% faster there; no gain at 64 tokens).
+// Every pass streams the expert's weights again, so once the routes average
+// kGr2MinMean tokens per expert (many experts then hold more than 16) the
+// routed-only launches take two 16-token groups per pass: the extra
+// accumulators cost occupancy, which is a net loss below that mean (measured
+// at H = 4096, E = 128: 256 tokens 827 -> 647 us, 192 tokens 643 -> 578 us,
+// 128 tokens 514 -> 517 us; neutral at H = 6144, E = 256 up to 256 tokens).
 constexpr int kNsGu = 4, kUGu = 1;
 constexpr int kNsDn = 4, kNsDnRouted = 8, kUDn = 1;
-constexpr int kGR = 1;  // 16-token groups per shared-expert pass
+constexpr int kGR = 1;  // 16-token groups per pass
+constexpr int kGr2MinMean = 12;
+bool routed_gr2(const LayerDims& d) { return d.T * d.k >= kGr2MinMean * d.E; }
 constexpr size_t kLdsGu = static_cast<size_t>(kWaves) * kUGu * kNsGu * kSubtileBlock;
 
-template <bool E8, int ROWS>
+template <bool E8, int ROWS, int GR = kGR>
 void launch_gu(dim3 grid, hipStream_t s, const uint16_t* x, const uint8_t* w, const void* scale,
                const uint8_t* sw, const void* sscale, const LayerDims& d, int SP,
                const Workspace& ws, hipEvent_t evb, hipEvent_t eve) {
-  MOE_LAUNCH((gate_up_mfma_kernel<kNsGu, kUGu, kGR, E8, ROWS>), grid, dim3(kThreads), kLdsGu, s,
+  MOE_LAUNCH((gate_up_mfma_kernel<kNsGu, kUGu, GR, E8, ROWS>), grid, dim3(kThreads), kLdsGu, s,
              evb, eve, x, w, scale, sw, sscale, d.H, d.I, d.Is, d.k, d.T, SP, ws, d.limit);
 }
 
-template <int NS, bool E8, int ROWS>
+template <int NS, bool E8, int ROWS, int GR = kGR>
 void launch_dn(int R, hipStream_t s, const uint8_t* w, const void* scale, const uint8_t* sw,
                const void* sscale, const LayerDims& d, int SP, const Workspace& ws) {
   const int per_wg = kWaves * 16 * NS;  // output rows per workgroup
   const dim3 grid((d.H + per_wg - 1) / per_wg, SP + R);
   const size_t lds = static_cast<size_t>(kWaves) * kUDn * NS * kSubtileBlock;
-  hipLaunchKernelGGL((down_mfma_kernel<NS, kUDn, kGR, E8, ROWS>), grid, dim3(kThreads), lds, s,
+  hipLaunchKernelGGL((down_mfma_kernel<NS, kUDn, GR, E8, ROWS>), grid, dim3(kThreads), lds, s,
                      w, scale, sw, sscale, d.H, d.I, d.Is, d.k, d.T, SP, ws);
 }
 
@@ -545,14 +559,16 @@ hipError_t launch_gate_up_mfma(const LayerDims& d, int rows, const void* hidden,
   const auto* x = static_cast<const uint16_t*>(hidden);
   const auto* w = static_cast<const uint8_t*>(w13);
   const auto* sw = static_cast<const uint8_t*>(sw13);
-#define MOE_GU(E8, ROWS) \
-  launch_gu<E8, ROWS>(grid, s, x, w, w13_scale, sw, sw13_scale, d, SP, ws, evb, eve)
+#define MOE_GU(E8, ROWS, GR) \
+  launch_gu<E8, ROWS, GR>(grid, s, x, w, w13_scale, sw, sw13_scale, d, SP, ws, evb, eve)
   if (rows == kAllRows) {
-    if (d.e8m0) MOE_GU(true, kAllRows); else MOE_GU(false, kAllRows);
+    if (d.e8m0) MOE_GU(true, kAllRows, kGR); else MOE_GU(false, kAllRows, kGR);
   } else if (rows == kSharedRows) {
-    if (d.e8m0) MOE_GU(true, kSharedRows); else MOE_GU(false, kSharedRows);
+    if (d.e8m0) MOE_GU(true, kSharedRows, kGR); else MOE_GU(false, kSharedRows, kGR);
+  } else if (routed_gr2(d)) {
+    if (d.e8m0) MOE_GU(true, kRoutedRows, 2); else MOE_GU(false, kRoutedRows, 2);
   } else {
-    if (d.e8m0) MOE_GU(true, kRoutedRows); else MOE_GU(false, kRoutedRows);
+    if (d.e8m0) MOE_GU(true, kRoutedRows, kGR); else MOE_GU(false, kRoutedRows, kGR);
   }
 #undef MOE_GU
   return hipGetLastError();
@@ -566,14 +582,19 @@ hipError_t launch_down_mfma(const LayerDims& d, int rows, const void* w2, const 
   if (SP + R == 0) return hipSuccess;
   const auto* w = static_cast<const uint8_t*>(w2);
   const auto* sw = static_cast<const uint8_t*>(sw2);
-#define MOE_DN(NS, E8, ROWS) launch_dn<NS, E8, ROWS>(R, s, w, w2_scale, sw, sw2_scale, d, SP, ws)
+#define MOE_DN(NS, E8, ROWS, GR) \
+  launch_dn<NS, E8, ROWS, GR>(R, s, w, w2_scale, sw, sw2_scale, d, SP, ws)
   if (rows == kAllRows) {
-    if (d.e8m0) MOE_DN(kNsDn, true, kAllRows); else MOE_DN(kNsDn, false, kAllRows);
+    if (d.e8m0) MOE_DN(kNsDn, true, kAllRows, kGR); else MOE_DN(kNsDn, false, kAllRows, kGR);
   } else if (rows == kSharedRows) {
-    if (d.e8m0) MOE_DN(kNsDn, true, kSharedRows); else MOE_DN(kNsDn, false, kSharedRows);
+    if (d.e8m0) MOE_DN(kNsDn, true, kSharedRows, kGR);
+    else MOE_DN(kNsDn, false, kSharedRows, kGR);
+  } else if (routed_gr2(d)) {
+    if (d.e8m0) MOE_DN(kNsDnRouted, true, kRoutedRows, 2);
+    else MOE_DN(kNsDnRouted, false, kRoutedRows, 2);
   } else {
-    if (d.e8m0) MOE_DN(kNsDnRouted, true, kRoutedRows);
-    else MOE_DN(kNsDnRouted, false, kRoutedRows);
+    if (d.e8m0) MOE_DN(kNsDnRouted, true, kRoutedRows, kGR);
+    else MOE_DN(kNsDnRouted, false, kRoutedRows, kGR);
   }
 #undef MOE_DN
   return hipGetLastError();
