@@ -67,6 +67,22 @@ def test_wide_layers_sampled(name, path, c_oracle):
     _case(sh, c_oracle, rows=rows, path=path)
 
 
+@pytest.mark.parametrize("T", [48, 192, 256])
+def test_decode_shape_many_tokens_sampled(T, c_oracle):
+    """The decode shape (H = 4096, E = 128) with more tokens, at full size:
+    the rotated block walk past 32 tokens (H is a power of two), the shared
+    expert on its own stream past 64 tokens, and from 192 tokens (12 or more
+    tokens per expert on average) the routed launches' two 16-token groups
+    per pass over the weights."""
+    sh = WORKLOADS["decode_t16"].replace(T=T)
+    rows = [0, 1, T // 2, T - 1]
+    _, got, _ = _case(sh, c_oracle, rows=rows)
+    counts = np.bincount(got["ids"].ravel(), minlength=sh.E)
+    _log("  most tokens on one expert", counts.max())
+    if T >= 192:
+        assert counts.max() > 16  # some pass carries two 16-token groups
+
+
 SMALL = [
     # T, H, E, k, I, Is, fmt
     (1, 128, 4, 1, 128, 0, "fp32"),
