@@ -83,6 +83,15 @@ def test_decode_shape_many_tokens_sampled(T, c_oracle):
         assert counts.max() > 16  # some pass carries two 16-token groups
 
 
+def test_wide_shape_max_tokens_sampled(c_oracle):
+    """H = 6144, E = 256, e8m0 scales at the plan's 256-token maximum, full
+    size: sixteen shared-expert passes on the side stream beside the routed
+    launches, and one 16-token group per pass (8 tokens per expert on
+    average)."""
+    sh = WORKLOADS["wide_t64_e8m0"].replace(T=256)
+    _case(sh, c_oracle, rows=[0, 1, 128, 255])
+
+
 SMALL = [
     # T, H, E, k, I, Is, fmt
     (1, 128, 4, 1, 128, 0, "fp32"),
