@@ -10,7 +10,7 @@ Expert ids must equal the oracle's selection (as sets) for every token whose
 k-th / (k+1)-th ranking-key gap exceeds 1e-4; for the other tokens any
 selection whose keys are all within 1e-4 of the oracle's k-th key is valid.
 Outputs are always compared with the oracle run on the GPU's own ids (forced
-routing), so a valid near-tie choice is judged on its own arithmetic.
+routing), so a valid near-tie choice is checked on its own arithmetic.
 """
 
 from __future__ import annotations
