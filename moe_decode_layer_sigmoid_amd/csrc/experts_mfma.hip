@@ -241,41 +241,56 @@ __device__ __forceinline__ bool gate_up_tile(
       }
       // every load of the round is issued before the first wait
       asm volatile("" ::: "memory");
+      uint4 xa[GR][U][4];
 #pragma unroll
       for (int gr = 0; gr < GR; ++gr) {
         if (gr >= G) break;
-        uint4 xa[U][4];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
           const int kb = block_at(kb0 + j, KB, rot);
 #pragma unroll
           for (int m = 0; m < 4; ++m)
-            xa[j][m] = *reinterpret_cast<const uint4*>(xrow[gr] + kb * kBlock + 8 * m);
+            xa[gr][j][m] = *reinterpret_cast<const uint4*>(xrow[gr] + kb * kBlock + 8 * m);
         }
-        // The staged weights land in LDS through the loads' own path: the
-        // compiler does not order the LDS reads below after them, so wait
-        // for every load of the wave here (the activation loads above are
-        // issued by then).
-        wait_memory();
+      }
+      // The staged weights land in LDS through the loads' own path: the
+      // compiler does not order the LDS reads below after them, so wait
+      // for every load of the wave here (the activation loads above are
+      // issued by then).
+      wait_memory();
 #pragma unroll
-        for (int j = 0; j < U; ++j) {
-          const unsigned char* st = stage + j * SB;
+      for (int j = 0; j < U; ++j) {
+        const unsigned char* st = stage + j * SB;
 #pragma unroll
-          for (int h = 0; h < NH; ++h) {
-            const uint4 g0 = staged_piece(st, h, c, 2 * g), g1 = staged_piece(st, h, c, 2 * g + 1);
-            const uint4 u0 = staged_piece(st, NH + h, c, 2 * g),
-                        u1 = staged_piece(st, NH + h, c, 2 * g + 1);
-            f32x4_t pg = {0.f, 0.f, 0.f, 0.f}, pu = {0.f, 0.f, 0.f, 0.f};
+        for (int h = 0; h < NH; ++h) {
+          const uint4 g0 = staged_piece(st, h, c, 2 * g), g1 = staged_piece(st, h, c, 2 * g + 1);
+          const uint4 u0 = staged_piece(st, NH + h, c, 2 * g),
+                      u1 = staged_piece(st, NH + h, c, 2 * g + 1);
+          f32x4_t pg[GR], pu[GR];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              const bf16x8_t a = as_bf16x8(xa[j][m]);
-              pg = mfma(a, weight_frag(g0, g1, m), pg);
-              pu = mfma(a, weight_frag(u0, u1, m), pu);
+          for (int gr = 0; gr < GR; ++gr) {
+            pg[gr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            pu[gr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            // each weight fragment is converted once for every group of the pass
+            const bf16x8_t wg = weight_frag(g0, g1, m), wu = weight_frag(u0, u1, m);
+#pragma unroll
+            for (int gr = 0; gr < GR; ++gr) {
+              if (gr >= G) break;
+              const bf16x8_t a = as_bf16x8(xa[gr][j][m]);
+              pg[gr] = mfma(a, wg, pg[gr]);
+              pu[gr] = mfma(a, wu, pu[gr]);
             }
+          }
+#pragma unroll
+          for (int gr = 0; gr < GR; ++gr) {
+            if (gr >= G) break;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              fg[gr][h][i] = fmaf(sg[j], pg[i], fg[gr][h][i]);
-              fu[gr][h][i] = fmaf(su[j], pu[i], fu[gr][h][i]);
+              fg[gr][h][i] = fmaf(sg[j], pg[gr][i], fg[gr][h][i]);
+              fu[gr][h][i] = fmaf(su[j], pu[gr][i], fu[gr][h][i]);
             }
           }
         }
@@ -472,6 +487,8 @@ __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
 // accumulators cost occupancy, which is a net loss below that mean (measured
 // at H = 4096, E = 128: 256 tokens 827 -> 647 us, 192 tokens 643 -> 578 us,
 // 128 tokens 514 -> 517 us; neutral at H = 6144, E = 256 up to 256 tokens).
+// gate_up converts each staged weight fragment once for both groups (256
+// tokens 632 -> 609 us, though the fp32-scale kernel then holds 144 VGPRs).
 constexpr int kNsGu = 4, kUGu = 1;
 constexpr int kNsDn = 4, kNsDnRouted = 8, kUDn = 1;
 constexpr int kGR = 1;  // 16-token groups per pass
