@@ -410,35 +410,46 @@ __device__ __forceinline__ void down_tile(
         wait();
         waited = true;
       }
+      uint4 ah[GR][U][4], al[GR][U][4];
 #pragma unroll
       for (int gr = 0; gr < GR; ++gr) {
         if (gr >= G) break;
-        uint4 ah[U][4], al[U][4];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
           const int kb = block_at(kb0 + j, KB, rot);
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            ah[j][m] = *reinterpret_cast<const uint4*>(act_hi + arow[gr] + kb * kBlock + 8 * m);
-            al[j][m] = *reinterpret_cast<const uint4*>(act_lo + arow[gr] + kb * kBlock + 8 * m);
+            ah[gr][j][m] = *reinterpret_cast<const uint4*>(act_hi + arow[gr] + kb * kBlock + 8 * m);
+            al[gr][j][m] = *reinterpret_cast<const uint4*>(act_lo + arow[gr] + kb * kBlock + 8 * m);
           }
         }
-        wait_memory();  // the staged weights are in LDS (see gate_up_tile)
+      }
+      wait_memory();  // the staged weights are in LDS (see gate_up_tile)
 #pragma unroll
-        for (int j = 0; j < U; ++j) {
-          const unsigned char* st = stage + j * SB;
+      for (int j = 0; j < U; ++j) {
+        const unsigned char* st = stage + j * SB;
 #pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            const uint4 a0 = staged_piece(st, s, c, 2 * g), a1 = staged_piece(st, s, c, 2 * g + 1);
-            f32x4_t p = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < NS; ++s) {
+          const uint4 a0 = staged_piece(st, s, c, 2 * g), a1 = staged_piece(st, s, c, 2 * g + 1);
+          f32x4_t p[GR];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              const bf16x8_t wa = weight_frag(a0, a1, m);
-              p = mfma(as_bf16x8(ah[j][m]), wa, p);
-              p = mfma(as_bf16x8(al[j][m]), wa, p);
+          for (int gr = 0; gr < GR; ++gr) p[gr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            // each weight fragment is converted once for every group of the pass
+            const bf16x8_t wa = weight_frag(a0, a1, m);
+#pragma unroll
+            for (int gr = 0; gr < GR; ++gr) {
+              if (gr >= G) break;
+              p[gr] = mfma(as_bf16x8(ah[gr][j][m]), wa, p[gr]);
+              p[gr] = mfma(as_bf16x8(al[gr][j][m]), wa, p[gr]);
             }
+          }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) f[gr][s][i] = fmaf(sc[j], p[i], f[gr][s][i]);
+          for (int gr = 0; gr < GR; ++gr) {
+            if (gr >= G) break;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f[gr][s][i] = fmaf(sc[j], p[gr][i], f[gr][s][i]);
           }
         }
       }
@@ -487,8 +498,9 @@ __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
 // accumulators cost occupancy, which is a net loss below that mean (measured
 // at H = 4096, E = 128: 256 tokens 827 -> 647 us, 192 tokens 643 -> 578 us,
 // 128 tokens 514 -> 517 us; neutral at H = 6144, E = 256 up to 256 tokens).
-// gate_up converts each staged weight fragment once for both groups (256
-// tokens 632 -> 609 us, though the fp32-scale kernel then holds 144 VGPRs).
+// Both tiles convert each staged weight fragment once for both groups
+// (256 tokens 632 -> 609 us for gate_up, though its fp32-scale kernel then
+// holds 144 VGPRs; then 611 -> 591 us for down).
 constexpr int kNsGu = 4, kUGu = 1;
 constexpr int kNsDn = 4, kNsDnRouted = 8, kUDn = 1;
 constexpr int kGR = 1;  // 16-token groups per pass
