@@ -37,7 +37,7 @@ CHAIN_MAX_TOKENS = 16  # the library's kChainMaxTokens (split path: one expert l
 # template arguments (NS, U, GR) of the library's gate_up MFMA launches (kNsGu, kUGu, kGR)
 MFMA_GATE_UP_TILE = "4, 1, 1"
 MFMA_ROUTED_TILE = "4, 1"  # NS, U of the routed-only gate_up launch
-GR2_MIN_MEAN = 12  # the library's kGr2MinMean
+GR2_MIN_MEAN = 10  # the library's kGr2MinMean
 METRIC = "µs per MoE layer and effective HBM TB/s (fraction of peak) at 1/16/64/128 tok"
 
 
@@ -428,7 +428,7 @@ def main():
         elif path_taken == md.PATH_GROUPED:
             # above 64 tokens the routed launch has routed rows only (ROWS =
             # 2) and the shared expert runs beside it
-            # (two 16-token groups per pass once the routes average 12 or
+            # (two 16-token groups per pass once the routes average 10 or
             # more tokens per expert)
             kern_name = "gate_up_mfma_kernel<NS, U, GR, E8, ROWS> (routed experts)"
             gr = 2 if T * sh.k >= GR2_MIN_MEAN * sh.E else 1

@@ -500,11 +500,13 @@ __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
 // 128 tokens 514 -> 517 us; neutral at H = 6144, E = 256 up to 256 tokens).
 // Both tiles convert each staged weight fragment once for both groups
 // (256 tokens 632 -> 609 us for gate_up, though its fp32-scale kernel then
-// holds 144 VGPRs; then 611 -> 591 us for down).
+// holds 144 VGPRs; then 611 -> 591 us for down).  With that, two groups pay
+// from a mean of 10 (160 tokens at E = 128: 523 -> 510 us) and still lose
+// at 8 (128 tokens: 472 -> 483 us) and 6 (96 tokens: 450 -> 457 us).
 constexpr int kNsGu = 4, kUGu = 1;
 constexpr int kNsDn = 4, kNsDnRouted = 8, kUDn = 1;
 constexpr int kGR = 1;  // 16-token groups per pass
-constexpr int kGr2MinMean = 12;
+constexpr int kGr2MinMean = 10;
 bool routed_gr2(const LayerDims& d) { return d.T * d.k >= kGr2MinMean * d.E; }
 constexpr size_t kLdsGu = static_cast<size_t>(kWaves) * kUGu * kNsGu * kSubtileBlock;
 

@@ -71,7 +71,7 @@ def test_wide_layers_sampled(name, path, c_oracle):
 def test_decode_shape_many_tokens_sampled(T, c_oracle):
     """The decode shape (H = 4096, E = 128) with more tokens, at full size:
     the rotated block walk past 32 tokens (H is a power of two), the shared
-    expert on its own stream past 64 tokens, and from 192 tokens (12 or more
+    expert on its own stream past 64 tokens, and from 160 tokens (10 or more
     tokens per expert on average) the routed launches' two 16-token groups
     per pass over the weights."""
     sh = WORKLOADS["decode_t16"].replace(T=T)
