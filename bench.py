@@ -38,6 +38,7 @@ CHAIN_MAX_TOKENS = 16  # the library's kChainMaxTokens (split path: one expert l
 MFMA_GATE_UP_TILE = "4, 1, 1"
 MFMA_ROUTED_TILE = "4, 1"  # NS, U of the routed-only gate_up launch
 GR2_MIN_MEAN = 10  # the library's kGr2MinMean
+MFMA_DENSE_TILE = "2, 1, 1"  # NS, U, GR of a dense layer's gate_up launch (kNsGuDense)
 METRIC = "µs per MoE layer and effective HBM TB/s (fraction of peak) at 1/16/64/128 tok"
 
 
@@ -404,7 +405,7 @@ def main():
                       + T * sh.Is * 4)
         if path_taken == md.PATH_GROUPED:
             kern_name = "gate_up_mfma_kernel<NS, U, GR, E8, ROWS> (dense MLP)"
-            kern_id = "gate_up_mfma_kernel<%s, %s, 1>" % (MFMA_GATE_UP_TILE, e8)
+            kern_id = "gate_up_mfma_kernel<%s, %s, 1>" % (MFMA_DENSE_TILE, e8)
         else:
             kern_name = "router_kernel<NJ2, E8> (dense MLP gate_up tiles)"
             kern_id = "router_kernel<%d, %s>" % ((H + 511) // 512, e8)

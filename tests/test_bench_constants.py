@@ -1,6 +1,6 @@
 """bench.py names the kernel it times (and prices its bytes) from copies of a
 few of the library's launch constants: the token limits of the chain and
-merged launches, the gate_up MFMA tile, and the mean tokens per expert from
+merged launches, the gate_up MFMA tiles, and the mean tokens per expert from
 which the routed launches take two 16-token groups per pass.  A copy that
 drifts from the source makes bench.py time or price the wrong kernel, so
 this reads each constant from the C++ sources and compares."""
@@ -38,5 +38,7 @@ def test_mfma_tile_matches_library():
     ns_r, u_r = (int(x) for x in bench.MFMA_ROUTED_TILE.split(","))
     assert (ns_r, u_r) == (ns, u)
     assert bench.GR2_MIN_MEAN == _const(mfma, "kGr2MinMean")
+    ns_d, u_d, gr_d = (int(x) for x in bench.MFMA_DENSE_TILE.split(","))
+    assert (ns_d, u_d, gr_d) == (_const(mfma, "kNsGuDense"), u, gr)
     # the rule bench.py applies is the library's: T * k >= kGr2MinMean * E
     assert re.search(r"d\.T \* d\.k >= kGr2MinMean \* d\.E", mfma)
