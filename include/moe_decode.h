@@ -108,8 +108,8 @@ typedef enum {
  * DenseMlp, LayerStages._build_dense) goes in the shared-expert slot
  * (sw13, sw2 and their scales), the router and routed-expert pointers may be
  * NULL, and a run computes out, residual_out and moe_out (= the MLP output)
- * through the same boundary.  AUTO: GEMV kernels below 16 tokens, MFMA
- * kernels from 16.
+ * through the same boundary.  AUTO: GEMV kernels below 8 tokens, MFMA
+ * kernels from 8.
  */
 typedef struct {
   int32_t hidden;              /* H */
@@ -178,6 +178,14 @@ int moe_decode_args_check(const moe_decode_desc* d, const moe_decode_args* a, in
  * stream (default priority) with two events.  On success *out owns them
  * until moe_decode_destroy; on failure *out is set to NULL and nothing is
  * leaked.
+ *
+ * Defined by the decode page's LayerStages._build_mega: the MoE stage is
+ * built once per layer from the layer constants (top_k, swiglu_limit,
+ * routed_scaling_factor, the e8m0 flag), and its route-order buffer and the
+ * shared expert's stream are made once at build time, sized for the largest
+ * token count, before any graph capture.  Errors: INVALID_ARG (null out, bad
+ * descriptor or device index), UNSUPPORTED (a size outside the limits, or a
+ * device that is not gfx950), NO_MEMORY, HIP.
  */
 int moe_decode_plan(const moe_decode_desc* d, int device, moe_decode_plan_t* out);
 
@@ -190,14 +198,33 @@ int moe_decode_plan(const moe_decode_desc* d, int device, moe_decode_plan_t* out
  * the router and joined back before the boundary (also when an error occurs
  * after the fork).  T = 0 returns OK and launches nothing.  Runs on one plan
  * must not overlap (they share its workspace).
+ *
+ * Defined by the decode page's LayerStages._mega_moe (router logits, the
+ * routed experts as one stage, the shared expert beside them, the routed
+ * rows handed on with their weights and route order) and LayerStages._router
+ * (fp32 logits from the bf16 router weight), followed by the draft page's
+ * SpecializedDraft.reduced_norm (norm(x + residual) and the new residual).
+ * An error after the fork still joins the side stream before it returns, as
+ * the v41 draft page's DraftDecode.run rejoins its side stream before it
+ * reports an error, so a capture sees no unjoined work.
+ *
+ * Errors: INVALID_ARG (moe_decode_args_check), HIP (a launch failed).  The
+ * launches hand work between workgroups through bounded waits; if one ever
+ * gave up, the run still returns OK but out, residual_out and moe_out are
+ * not trustworthy: the boundary then writes NaN to out, and
+ * moe_decode_check_waits reports it.
  */
 int moe_decode_run(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, void* stream);
 
 /* Waits for the plan's device, then frees the plan's workspace, side stream
- * and events.  NULL is a no-op. */
+ * and events (what LayerStages._build_mega made for the stage).  NULL is a
+ * no-op; always returns OK. */
 int moe_decode_destroy(moe_decode_plan_t p);
 
-/* Static text naming a status code. */
+/* Static text naming a status code.  Where the decode page's
+ * LayerStages._build_mega meets a routing it does not support it warns and
+ * runs the stock layers; this library has no second compute path, so it
+ * returns the reason to the caller, and this names it. */
 const char* moe_decode_strerror(int code);
 
 /*
@@ -232,16 +259,30 @@ int moe_decode_set_expert_events(moe_decode_plan_t p, void* begin, void* end);
 int moe_decode_path_for(moe_decode_plan_t p, int32_t T);
 
 /*
- * Health check of the bounded waits (the fused kernel's, the expert chain
- * launch's and the grouped gate_up + down launch's): synchronises the plan's
- * device, returns in *gave_up whether any wait since the last check ran out
- * of its spin budget (which would mean a result is not trustworthy) and
- * clears the flag.  Not capturable; for tests and monitoring.
+ * Health check of the bounded waits (the single-launch path's, the expert
+ * chain launch's and the grouped gate_up + down launch's): synchronises the
+ * plan's device, returns in *gave_up whether any wait since the last check
+ * ran out of its spin budget (outputs of the runs since the last check are
+ * then not trustworthy) and clears the flag.  After a give-up it also
+ * re-zeroes the plan's counters, so later runs start from a clean state.
+ * Not capturable; for tests and monitoring.
  */
 int moe_decode_check_waits(moe_decode_plan_t p, int32_t* gave_up);
 
 /* Device bytes the plan holds for its workspace. */
 size_t moe_decode_workspace_bytes(moe_decode_plan_t p);
+
+
+/*
+ * Measurement only (not part of the layer): one streaming read of `bytes`
+ * bytes at device pointer `buf` (16-byte aligned; bytes a non-zero multiple
+ * of 64 MiB) with the non-temporal 16-byte loads the expert kernels stream
+ * their weights with, queued on `stream`.  `sink` (device, 256 uint32) is
+ * written only to keep the loads live.  A benchmark times it with events to
+ * state layer times as a fraction of a measured read ceiling besides the
+ * published peak.  Errors: INVALID_ARG, HIP.
+ */
+int moe_decode_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

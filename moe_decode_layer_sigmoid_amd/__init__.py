@@ -28,5 +28,7 @@ from .binding import (  # noqa: F401
     desc_check,
     lib,
     make_desc,
+    read_probe,
     strerror,
+    PROBE_STEP,
 )

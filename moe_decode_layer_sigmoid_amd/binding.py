@@ -20,6 +20,9 @@ SCALE_FP32, SCALE_E8M0 = 0, 1
 PATH_AUTO, PATH_GEMV, PATH_GROUPED, PATH_GEMV_SPLIT = 0, 1, 2, 3
 
 
+PROBE_STEP = 64 << 20  # moe_decode_read_probe reads a multiple of this many bytes
+
+
 class MoeDecodeError(RuntimeError):
     def __init__(self, code: int, what: str):
         super().__init__("%s: %s (%d)" % (what, strerror(code), code))
@@ -75,8 +78,9 @@ def lib():
         L.moe_decode_check_waits.argtypes = [vp, ctypes.POINTER(i32)]
         L.moe_decode_workspace_bytes.argtypes = [vp]
         L.moe_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_decode_read_probe.argtypes = [vp, ctypes.c_size_t, vp, vp]
         for f in ("desc_check", "args_check", "plan", "run", "destroy", "last_routes",
-                  "set_expert_events", "path_for", "check_waits"):
+                  "set_expert_events", "path_for", "check_waits", "read_probe"):
             getattr(L, "moe_decode_" + f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -85,7 +89,7 @@ def lib():
 EXPORTED = ["moe_decode_desc_check", "moe_decode_args_check", "moe_decode_plan",
             "moe_decode_run", "moe_decode_destroy", "moe_decode_strerror",
             "moe_decode_last_routes", "moe_decode_set_expert_events", "moe_decode_path_for",
-            "moe_decode_check_waits", "moe_decode_workspace_bytes"]
+            "moe_decode_check_waits", "moe_decode_workspace_bytes", "moe_decode_read_probe"]
 
 
 def strerror(code: int) -> str:
@@ -194,3 +198,12 @@ class Plan:
 
     def workspace_bytes(self) -> int:
         return lib().moe_decode_workspace_bytes(self._h)
+
+
+def read_probe(buf, nbytes: int, sink, stream=None) -> None:
+    """moe_decode_read_probe: one streaming read of `nbytes` of `buf` (a
+    measurement kernel for the benchmark's read ceiling)."""
+    rc = lib().moe_decode_read_probe(_ptr(buf), nbytes, _ptr(sink), _stream(stream))
+    if rc:
+        raise MoeDecodeError(rc, "moe_decode_read_probe")
+

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_decode.so")
 SOURCES = ["api.hip", "router.hip", "experts_gemv.hip", "experts_mfma.hip", "epilogue.hip",
-           "decode_fused.hip", "experts_chain.hip"]
+           "decode_fused.hip", "experts_chain.hip", "probe.hip"]
 # decode_fused.hip is also compiled once per register chunk count and scale
 # format (the template arguments of its kernel), each into its own object;
 # experts_chain.hip once per w13 chunk count.

@@ -31,6 +31,7 @@ struct moe_decode_plan_s {
   int device;
   void* ws_base;
   size_t ws_bytes;
+  size_t state_bytes;  // the leading workspace regions that carry state between runs
   moe::Workspace ws;
   hipStream_t side;      // the shared expert's stream on the MFMA path above
                          // kMergeSharedMaxTokens tokens
@@ -63,8 +64,12 @@ int path_for(const moe_decode_plan_s& p, int32_t T) {
 
 size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
-// Lays the workspace out from `base` (nullptr: only sizes it).
-size_t layout(const moe_decode_desc& d, char* base, moe::Workspace* ws) {
+// Lays the workspace out from `base` (nullptr: only sizes it).  The regions
+// that carry state from one run to the next (counters, flags, the boundary
+// slots, the zero bias) come first, `state_bytes` of them: they must be zero
+// before the first run.
+size_t layout(const moe_decode_desc& d, char* base, moe::Workspace* ws,
+              size_t* state_bytes = nullptr) {
   const size_t T = d.max_tokens, E = d.num_experts, k = d.top_k, H = d.hidden;
   const size_t I = d.intermediate, Is = d.shared_intermediate;
   size_t off = 0;
@@ -74,6 +79,11 @@ size_t layout(const moe_decode_desc& d, char* base, moe::Workspace* ws) {
     return p;
   };
   moe::Workspace w{};
+  w.counter = reinterpret_cast<uint32_t*>(take(moe::router_cnt_words() * 4));
+  w.sync = reinterpret_cast<uint32_t*>(take(moe::sync_words(static_cast<int>(E)) * 4));
+  w.zero_bias = reinterpret_cast<float*>(take(E * 4));
+  w.epi_part = reinterpret_cast<float*>(take(T * moe::kMaxBndSlices * 4));
+  if (state_bytes) *state_bytes = off;
   w.logits = reinterpret_cast<float*>(take(T * E * 4));
   w.ids = reinterpret_cast<int32_t*>(take(T * k * 4));
   w.weights = reinterpret_cast<float*>(take(T * k * 4));
@@ -87,11 +97,7 @@ size_t layout(const moe_decode_desc& d, char* base, moe::Workspace* ws) {
   w.act_s = reinterpret_cast<float*>(take(T * (Is ? Is : 1) * 4));
   w.rows = reinterpret_cast<float*>(take(T * k * H * 4));
   w.y_s = reinterpret_cast<float*>(take(T * H * 4));
-  w.counter = reinterpret_cast<uint32_t*>(take(moe::router_cnt_words() * 4));
-  w.sync = reinterpret_cast<uint32_t*>(take(moe::sync_words(static_cast<int>(E)) * 4));
-  w.zero_bias = reinterpret_cast<float*>(take(E * 4));
   w.slot_tab = reinterpret_cast<int32_t*>(take(E * moe::kSlotInts * 4));
-  w.epi_part = reinterpret_cast<float*>(take(T * moe::kMaxBndSlices * 4));
   if (ws) *ws = w;
   return off;
 }
@@ -205,7 +211,7 @@ int moe_decode_plan(const moe_decode_desc* d, int device, moe_decode_plan_t* out
   }
   p->desc = *d;
   p->device = device;
-  p->ws_bytes = layout(*d, nullptr, nullptr);
+  p->ws_bytes = layout(*d, nullptr, nullptr, &p->state_bytes);
   rc = MOE_DECODE_OK;
   if (hipMalloc(&p->ws_base, p->ws_bytes) != hipSuccess) {
     p->ws_base = nullptr;
@@ -464,9 +470,13 @@ int moe_decode_check_waits(moe_decode_plan_t p, int32_t* gave_up) {
   if (hipDeviceSynchronize() != hipSuccess ||
       hipMemcpy(&flag, p->ws.sync + moe::kSyncError * moe::kSyncStride, 4,
                 hipMemcpyDeviceToHost) != hipSuccess ||
-      hipMemset(p->ws.sync + moe::kSyncError * moe::kSyncStride, 0, 4) != hipSuccess ||
-      hipDeviceSynchronize() != hipSuccess)
+      hipMemset(p->ws.sync + moe::kSyncError * moe::kSyncStride, 0, 4) != hipSuccess)
     rc = MOE_DECODE_ERR_HIP;
+  // a wait that gave up may have left counters part-way: start the next run
+  // from the zeroed state a new plan has
+  if (!rc && flag && hipMemset(p->ws_base, 0, p->state_bytes) != hipSuccess)
+    rc = MOE_DECODE_ERR_HIP;
+  if (!rc && hipDeviceSynchronize() != hipSuccess) rc = MOE_DECODE_ERR_HIP;
   (void)hipSetDevice(prev);
   *gave_up = flag != 0;
   return rc;
@@ -475,3 +485,4 @@ int moe_decode_check_waits(moe_decode_plan_t p, int32_t* gave_up) {
 size_t moe_decode_workspace_bytes(moe_decode_plan_t p) { return p ? p->ws_bytes : 0; }
 
 }  // extern "C"
+

@@ -110,7 +110,8 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
   for (; it < a.o_rgu; it += G) {
     wait_flag(sy, sync_flag(kFlagSgu));
     const int h0 = (it - a.o_sdn) * 4 * kWaves + 4 * wave;
-    down_wave<NJ, 1, true, E8>(a.sw2, a.sw2_scale, 0, H, Is, h0, T, 0, nullptr, ws.act_s, ws.y_s);
+    down_wave<NJ, 1, true, E8>(a.sw2, a.sw2_scale, 0, H, Is, h0, T, 0, RouteIdentity{},
+                               ws.act_s, ws.y_s);
     signal(sy, kSyncSdnCnt, static_cast<uint32_t>(a.n_sdn), sync_flag(kFlagSdn), &s_flag);
   }
 
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs a, Wor
     const int h0 = tile * 4 * kWaves + 4 * wave;
     down_wave<NJ, 1, true, E8>(a.w2 + static_cast<size_t>(e) * H * I, a.w2_scale,
                                static_cast<size_t>(e) * (H / kBlock) * (I / kBlock), H, I, h0,
-                               s_n[d], s_b[d], ws.perm, ws.act, ws.rows);
+                               s_n[d], s_b[d], RouteTable<true>{ws.perm}, ws.act, ws.rows);
     if (signal(sy, sync_dn_cnt(d), static_cast<uint32_t>(a.dn_per), -1, &s_flag) &&
         threadIdx.x == 0) {
       // this expert is complete; the last expert to complete raises the flag

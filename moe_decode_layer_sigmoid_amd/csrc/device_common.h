@@ -28,6 +28,10 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// Two bf16 quiet NaNs in one dword: what a boundary writes to `out` when a
+// bounded wait of the run gave up.
+constexpr uint32_t kBf16NanPair = 0x7fc07fc0u;
+
 // Eight floats -> eight bf16 (RNE) in one 16-byte store (p 16-byte aligned).
 __device__ __forceinline__ void store_bf16x8(uint16_t* p, const float* v) {
   uint32_t w[4];

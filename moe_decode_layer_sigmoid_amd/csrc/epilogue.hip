@@ -47,6 +47,10 @@ __global__ __launch_bounds__(kMaxThreads) void epilogue_kernel(
   const float* ys = ws.y_s + static_cast<size_t>(t) * H + c0;
   const uint4 rv = *reinterpret_cast<const uint4*>(residual + static_cast<size_t>(t) * H + c0);
   const uint4 gv = *reinterpret_cast<const uint4*>(gamma + c0);
+  // set when a bounded wait of an earlier launch of this run gave up: the
+  // rows may then be incomplete, and out is written as NaN
+  const uint32_t gave_up = ld_i32<true>(reinterpret_cast<const int*>(ws.sync) +
+                                        kSyncError * kSyncStride);
   const float4 ya = *reinterpret_cast<const float4*>(ys);
   const float4 yb = *reinterpret_cast<const float4*>(ys + 4);
   float acc[kCols];
@@ -106,6 +110,7 @@ __global__ __launch_bounds__(kMaxThreads) void epilogue_kernel(
     o[m] = f32_to_bf16(h0 * inv_rms * bf16_lo(g[m])) |
            (f32_to_bf16(h1 * inv_rms * bf16_hi(g[m])) << 16);
     r[m] = f32_to_bf16(h0) | (f32_to_bf16(h1) << 16);
+    if (gave_up) o[m] = kBf16NanPair;
   }
   *reinterpret_cast<uint4*>(out + static_cast<size_t>(t) * H + c) =
       make_uint4(o[0], o[1], o[2], o[3]);

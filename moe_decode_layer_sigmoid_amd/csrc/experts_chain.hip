@@ -135,14 +135,20 @@ __device__ __forceinline__ void boundary_slice(const ChainArgs& a, const Workspa
   if (lane == 0) s_part[wave] = ss;
   __syncthreads();
   float* part = ws.epi_part + t * kMaxBndSlices;
+  __shared__ uint32_t s_bad;
   if (wave == 0) {
     // publish this slice's sum (no wait for the store), then poll the token's
-    // slices, one lane each, until none is empty
+    // slices, one lane each, until none is empty; lane 63 reads the error
+    // word in the same round trips (a wait of the launch that gave up)
     if (lane == 0) st_f32<true>(part + s, (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]));
+    const float* src = lane < ns ? part + lane
+                                 : (lane == 63 ? reinterpret_cast<const float*>(
+                                                     ws.sync + kSyncError * kSyncStride)
+                                               : part);
     uint32_t polls = 0;
     float v = 0.f;
     for (;;) {
-      v = ld_f32<true>(part + (lane < ns ? lane : 0));
+      v = ld_f32<true>(src);
       const bool in = lane >= ns || __float_as_uint(v) != kEpiEmpty;
       if (__builtin_amdgcn_ballot_w64(!in) == 0) break;  // uniform over the wave
       __builtin_amdgcn_s_sleep(1);
@@ -154,8 +160,10 @@ __device__ __forceinline__ void boundary_slice(const ChainArgs& a, const Workspa
       }
     }
     if (lane < ns) s_tot[lane] = v;
+    if (lane == 63) s_bad = (__float_as_uint(v) != 0u || polls == kChainSpin) ? 1u : 0u;
   }
   __syncthreads();
+  const bool gave_up = s_bad != 0u;
   float tot = 0.f;
   for (int i = 0; i < ns; ++i) tot += s_tot[i];
   const float inv_rms = 1.0f / sqrtf(tot / static_cast<float>(H) + a.eps);
@@ -168,6 +176,7 @@ __device__ __forceinline__ void boundary_slice(const ChainArgs& a, const Workspa
     o[m] = f32_to_bf16(h0 * inv_rms * bf16_lo(g[m])) |
            (f32_to_bf16(h1 * inv_rms * bf16_hi(g[m])) << 16);
     r[m] = f32_to_bf16(h0) | (f32_to_bf16(h1) << 16);
+    if (gave_up) o[m] = kBf16NanPair;
   }
   *reinterpret_cast<uint4*>(a.out + static_cast<size_t>(t) * H + c) =
       make_uint4(o[0], o[1], o[2], o[3]);
@@ -189,8 +198,8 @@ __global__ __launch_bounds__(kThreads) void expert_chain_kernel(ChainArgs a, Wor
   if (it < a.o_rgu) {
     // ---- shared down: rows RD * (4 * it + wave) .. +RD-1 of y_s
     down_wave<NJD, 1, true, E8, false, NoWait, RD>(a.sw2, a.sw2_scale, 0, H, a.Is,
-                                                   (it * kWaves + wave) * RD, a.T, 0, nullptr,
-                                                   ws.act_s, ws.y_s);
+                                                   (it * kWaves + wave) * RD, a.T, 0,
+                                                   RouteIdentity{}, ws.act_s, ws.y_s);
     bump(sy, kSyncExit0 + it % kSyncExitLines);
     return;
   }
@@ -226,8 +235,8 @@ __global__ __launch_bounds__(kThreads) void expert_chain_kernel(ChainArgs a, Wor
       down_wave<NJD, 1, true, E8, false, decltype(wait), RD>(
           a.w2 + static_cast<size_t>(e) * H * I, a.w2_scale,
           static_cast<size_t>(e) * (H / kBlock) * (I / kBlock), H, I,
-          ((v - d * a.dn_per) * kWaves + wave) * RD, rec.y, rec.z, ws.perm, ws.act, ws.rows,
-          wait);
+          ((v - d * a.dn_per) * kWaves + wave) * RD, rec.y, rec.z, RouteTable<false>{ws.perm},
+          ws.act, ws.rows, wait);
     }
     bump(sy, kSyncExit0 + it % kSyncExitLines);
     return;

@@ -84,8 +84,8 @@ __global__ __launch_bounds__(kThreads) void down_kernel(
   const uint8_t* W = sl.shared ? sw2 : w2 + static_cast<size_t>(sl.e) * H * II;
   const size_t sbase = static_cast<size_t>(sl.e) * (H / kBlock) * (II / kBlock);
   down_wave<NJ, 1, false, E8>(W, sl.shared ? sscale : scale, sbase, H, II, h0, sl.n, sl.base,
-                              sl.shared ? nullptr : ws.perm, sl.shared ? ws.act_s : ws.act,
-                              sl.shared ? ws.y_s : ws.rows);
+                              RouteTable<false>{sl.shared ? nullptr : ws.perm},
+                              sl.shared ? ws.act_s : ws.act, sl.shared ? ws.y_s : ws.rows);
 }
 
 }  // namespace

@@ -173,22 +173,36 @@ struct NoWait {
   __device__ void operator()() const {}
 };
 
+// Where the down output of SwiGLU row `pos` goes: out row route_of(pos).
+struct RouteIdentity {  // row pos itself (the shared expert: token pos)
+  __device__ int operator()(int pos) const { return pos; }
+};
+template <bool C>
+struct RouteTable {  // perm[pos]: the route index t*k+j (C: coherent load); pos when
+                     // perm is null (the shared expert)
+  const int32_t* perm;
+  __device__ int operator()(int pos) const { return perm ? ld_i32<C>(perm + pos) : pos; }
+};
+struct RouteFixed {  // one known route (a slot with one route)
+  int route;
+  __device__ int operator()(int) const { return route; }
+};
+
 // down projection of one wave: output rows h0 .. h0+R-1 (h0 % R == 0, R = 4
 // or 8) of one expert for its n >= 1 SwiGLU rows act[(base + q) * I],
-// written to out[o * H + h0 .. +R-1] with o = out_route[base + q] (the route
-// index t*k+j), or o = base + q when out_route is null.  fp32 products and
-// sums (the SwiGLU activations stay fp32).  NJ = ceil(I / 1024); TB, C, E8
-// as above, C for the stores; CL = coherent loads of act and out_route.
-// wait() runs after the weight loads are issued and before act is read (a
-// workgroup whose activations come from other workgroups of the same launch
-// waits there for them while its weights stream in; it must be called by
-// every wave of the workgroup).
-template <int NJ, int TB, bool C, bool E8, bool CL = C, typename Wait = NoWait, int R = 4>
+// written to out[o * H + h0 .. +R-1] with o = route_of(base + q) (the route
+// index t*k+j, or base + q).  fp32 products and sums (the SwiGLU activations
+// stay fp32).  NJ = ceil(I / 1024); TB, C, E8 as above, C for the stores;
+// CL = coherent loads of act.  wait() runs after the weight loads are issued
+// and before act is read (a workgroup whose activations come from other
+// workgroups of the same launch waits there for them while its weights
+// stream in; it must be called by every wave of the workgroup).
+template <int NJ, int TB, bool C, bool E8, bool CL = C, typename Wait = NoWait, int R = 4,
+          typename RouteOf = RouteIdentity>
 __device__ __forceinline__ void down_wave(const uint8_t* __restrict__ W,
                                           const void* __restrict__ scale, size_t sbase, int H,
-                                          int I, int h0, int n, int base,
-                                          const int32_t* out_route, const float* act,
-                                          float* out, Wait wait = Wait()) {
+                                          int I, int h0, int n, int base, RouteOf route_of,
+                                          const float* act, float* out, Wait wait = Wait()) {
   static_assert(R == 4 || R == 8, "4 or 8 rows per wave");
   const int lane = threadIdx.x & 63;
   const int ib_n = I / kBlock;
@@ -240,7 +254,7 @@ __device__ __forceinline__ void down_wave(const uint8_t* __restrict__ W,
 #pragma unroll
       for (int r = 0; r < R; ++r) v[r] = wave_sum(acc[r][qq]);
       if (lane == 0) {
-        const int o = out_route ? ld_i32<CL>(out_route + base + q0 + qq) : base + q0 + qq;
+        const int o = route_of(base + q0 + qq);
 #pragma unroll
         for (int r = 0; r < R; r += 4)
           st_f32x4<C>(out + static_cast<size_t>(o) * H + h0 + r,
@@ -262,7 +276,7 @@ constexpr int kRouterTokB = 2;  // tokens per register pass of a router wave
 // logits[t * E + e] = sum_h hidden[t, h] * router_w[e, h] in fp32.
 // The row stays in registers; tokens go in passes of kRouterTokB.
 // NJ2 = 16-byte chunks per lane = ceil(H / 512).
-template <int NJ2, bool C = false>
+template <int NJ2, bool C = false, bool ENC = false>
 __device__ __forceinline__ void router_wave(const uint16_t* __restrict__ hidden,
                                             const uint16_t* __restrict__ row, int H, int T,
                                             int E, int e, float* logits) {
@@ -298,7 +312,10 @@ __device__ __forceinline__ void router_wave(const uint16_t* __restrict__ hidden,
     for (int q = 0; q < kRouterTokB; ++q) {
       if (t0 + q >= T) continue;
       const float v = wave_sum(acc[q]);
-      if (lane == 0) st_f32<C>(logits + static_cast<size_t>(t0 + q) * E + e, v);
+      // ENC: stored with its bits inverted (see load_logit)
+      if (lane == 0)
+        st_f32<C>(logits + static_cast<size_t>(t0 + q) * E + e,
+                  ENC ? __uint_as_float(~__float_as_uint(v)) : v);
     }
   }
 }

@@ -104,11 +104,12 @@ constexpr int kMergeSharedMaxTokens = 64;
 // 4: 127.9 / 118.9, 8: 215.8 / 183.5, 16: 378.8 / 295.6.
 constexpr int kGroupedMinTokens = 4;
 // The same for a dense layer (no routed experts).  Its MFMA launches have
-// only I_s / 128 tiles per 16-token pass, so they win only where the GEMV
-// tiles' per-token work has grown (MI355X, H = 4096, I_s = 8192, µs per step
-// split / grouped: 2 tokens 37.9 / 121.6, 8: 87.5 / 128.7, 16: 152.6 / 139.7,
-// 64: 546.5 / 137.8).
-constexpr int kDenseGroupedMinTokens = 16;
+// few tiles per 16-token pass (I_s / 64 gate_up and H / 64 down tiles with
+// the dense tile sizes), so they win only where the GEMV tiles' per-token
+// work has grown (MI355X, H = 4096, I_s = 8192, µs per step GEMV / MFMA:
+// 8 tokens 94.8 / 93.6, 10: 110.9 / 95.3, 12: 128.5 / 98.1, 14: 143.7 /
+// 100.3, 16: 160.0 / 106.7).
+constexpr int kDenseGroupedMinTokens = 8;
 
 // Arguments of the fused persistent kernel (see decode_fused.hip).
 struct FusedArgs {

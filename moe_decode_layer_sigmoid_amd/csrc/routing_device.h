@@ -15,6 +15,16 @@ namespace moe {
 
 constexpr int kRouteThreads = 256;
 
+// A logit as stored by the router: plain fp32, or (ENC) its bits inverted,
+// so that zeroed memory reads as "not written yet" (inverted bits of 0 are a
+// NaN pattern no dot product produces) and a consumer can poll the logits
+// themselves instead of a counter.
+template <bool C, bool ENC>
+__device__ __forceinline__ float load_logit(const float* p) {
+  const float v = ld_f32<C>(p);
+  return ENC ? __uint_as_float(~__float_as_uint(v)) : v;
+}
+
 __device__ __forceinline__ uint32_t ordered_bits(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -86,7 +96,7 @@ __device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory")
 // NS = slots per lane, a power of two >= ceil(E / 64) (slots past E hold
 // key 0), so that every loop over a lane's keys unrolls with constant
 // indices.
-template <bool C, int NS>
+template <bool C, int NS, bool ENC = false>
 __device__ inline void select_token_ns(const float* logits, const float* bias, int E, int k,
                                        float rsf, unsigned long long* sel, int* pick_id,
                                        float* pick_w) {
@@ -103,7 +113,7 @@ __device__ inline void select_token_ns(const float* logits, const float* bias, i
   for (int i = 0; i < NS; ++i) {
     const int e = lane + 64 * i;
     const int ee = e < E ? e : E - 1;
-    sc[i] = ld_f32<C>(logits + ee);
+    sc[i] = load_logit<C, ENC>(logits + ee);
     bv[i] = bias[ee];
   }
   unsigned long long mx = 0ull;
@@ -207,7 +217,7 @@ __device__ __forceinline__ void wave_max_pair(uint32_t& hi, uint32_t& lo) {
 // slot that is taken or past E (a real key never maps to 0).  Each round
 // takes every lane's best slot (strict >, so the lower slot, i.e. the lower
 // id, wins a tie), then a DPP wave maximum of (key, ~id).
-template <bool C>
+template <bool C, bool ENC = false>
 __device__ inline void select_token_rounds(const float* logits, const float* bias, int E, int k,
                                     float rsf, int* pick_id, float* pick_w) {
   const int lane = threadIdx.x & 63;
@@ -219,7 +229,7 @@ __device__ inline void select_token_rounds(const float* logits, const float* bia
   for (int i = 0; i < 16; ++i) {
     const int e = lane + 64 * i;
     const int ee = e < E ? e : E - 1;
-    const float s = sigmoidf_(ld_f32<C>(logits + ee));
+    const float s = sigmoidf_(load_logit<C, ENC>(logits + ee));
     sc[i] = s;
     kb[i] = e < E ? ordered_bits(s + bias[ee]) : 0u;
   }
@@ -264,19 +274,19 @@ __device__ inline void select_token_rounds(const float* logits, const float* bia
   }
 }
 
-template <bool C>
+template <bool C, bool ENC = false>
 __device__ inline void select_token(const float* logits, const float* bias, int E, int k,
                                     float rsf, unsigned long long* sel, int* pick_id,
                                     float* pick_w) {
   const int ns = (E + 63) >> 6;  // uniform
   if (ns <= 1)
-    select_token_ns<C, 1>(logits, bias, E, k, rsf, sel, pick_id, pick_w);
+    select_token_ns<C, 1, ENC>(logits, bias, E, k, rsf, sel, pick_id, pick_w);
   else if (ns <= 2)
-    select_token_ns<C, 2>(logits, bias, E, k, rsf, sel, pick_id, pick_w);
+    select_token_ns<C, 2, ENC>(logits, bias, E, k, rsf, sel, pick_id, pick_w);
   else if (ns <= 4)
-    select_token_ns<C, 4>(logits, bias, E, k, rsf, sel, pick_id, pick_w);
+    select_token_ns<C, 4, ENC>(logits, bias, E, k, rsf, sel, pick_id, pick_w);
   else
-    select_token_rounds<C>(logits, bias, E, k, rsf, pick_id, pick_w);
+    select_token_rounds<C, ENC>(logits, bias, E, k, rsf, pick_id, pick_w);
 }
 
 // LDS bytes select_and_route needs (16-byte aligned base).
@@ -311,7 +321,7 @@ struct RouteSmem {
 // Top-k of tokens [t_begin, t_end), one wave per token.  Writes ws.ids and
 // ws.weights (coherent stores when C), the optional caller outputs and the
 // LDS copy of the ids (route r = t*k + j).
-template <bool C>
+template <bool C, bool ENC = false>
 __device__ inline void select_tokens(int t_begin, int t_end, int E, int k, float rsf,
                                      const float* logits, const float* bias, const Workspace& ws,
                                      int32_t* ids_out, float* w_out, const RouteSmem& sm) {
@@ -321,7 +331,7 @@ __device__ inline void select_tokens(int t_begin, int t_end, int E, int k, float
   for (int t = t_begin + wave; t < t_end; t += kRouteThreads / 64) {
     int id = 0;
     float w = 0.f;
-    select_token<C>(logits + static_cast<size_t>(t) * E, bias, E, k, rsf, sel, &id, &w);
+    select_token<C, ENC>(logits + static_cast<size_t>(t) * E, bias, E, k, rsf, sel, &id, &w);
     if (lane < k) {
       const int r = t * k + lane;
       s_ids[r] = id;

@@ -333,6 +333,22 @@ def test_c_and_numpy_oracles_agree(fmt, with_bias, c_oracle):
     assert np.abs(d["out"] - a["out"]).max() <= 1e-12 * np.abs(a["out"]).max()
 
 
+@pytest.mark.parametrize("name", ["tiny_t1", "decode_t1"])
+def test_c_and_numpy_oracles_agree_on_workloads(name, c_oracle):
+    """The two independent oracles on the tiny layer and the one-token decode
+    layer (H = 4096, 128 experts, top-8, I = 1536) at their real sizes: the
+    same experts and weights, and every output element within float64
+    rounding of each other."""
+    inp = make_layer(WORKLOADS[name])
+    a = oracle.moe_layer(inp)
+    b = c_oracle.moe_layer(inp)
+    assert np.array_equal(a["ids"], b["ids"])
+    assert np.allclose(a["weights"], b["weights"], rtol=1e-13)
+    assert np.allclose(a["logits"], b["logits"], rtol=1e-12, atol=1e-14)
+    for key in ("out", "h", "moe"):
+        assert np.abs(a[key] - b[key]).max() <= 1e-12 * np.abs(a[key]).max(), key
+
+
 def test_no_shared_expert(c_oracle):
     sh = LayerShape(T=2, H=128, E=4, k=2, I=128, Is=0, tag=501)
     inp = make_layer(sh)
