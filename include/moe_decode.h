@@ -64,7 +64,9 @@ typedef enum {
   MOE_DECODE_ERR_INVALID_ARG = 1, /* null required pointer, T out of range, bad enum */
   MOE_DECODE_ERR_UNSUPPORTED = 2, /* a size or device this library does not handle */
   MOE_DECODE_ERR_HIP = 3,         /* a HIP runtime call failed */
-  MOE_DECODE_ERR_NO_MEMORY = 4    /* workspace allocation failed at plan time */
+  MOE_DECODE_ERR_NO_MEMORY = 4,   /* workspace allocation failed at plan time */
+  MOE_DECODE_ERR_SCRATCH = 5      /* moe_decode_run_static: the workspace for this size
+                                     exceeds the static scratch array */
 } moe_decode_status;
 
 typedef enum { MOE_DECODE_SCALE_FP32 = 0, MOE_DECODE_SCALE_E8M0 = 1 } moe_decode_scale_fmt;
@@ -272,6 +274,34 @@ int moe_decode_check_waits(moe_decode_plan_t p, int32_t* gave_up);
 /* Device bytes the plan holds for its workspace. */
 size_t moe_decode_workspace_bytes(moe_decode_plan_t p);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer as moe_decode_run, on the current HIP device, without a plan.  It
+ * calls no allocating routine.  Its workspace is a static device array of
+ * 64 MiB (MOE_DECODE_STATIC_SCRATCH_BYTES) that every GPU the library runs on
+ * holds, one copy each, until the process ends; the first call on a device
+ * looks up that device's copy (and checks the device is gfx950).
+ *
+ * Arguments as moe_decode_run, with the descriptor in place of a plan
+ * (d->max_tokens bounds T as before; the workspace is laid out for T).
+ * Differences: the shared expert's passes above 64 tokens run on `stream`
+ * ahead of the routed launches (there is no side stream);
+ * MOE_DECODE_PATH_GEMV takes the GEMV_SPLIT kernels; no measurement hook and
+ * no moe_decode_check_waits (a bounded wait that gives up shows as NaN in
+ * out).  Every call clears the array's counters and flags first, so a call
+ * never depends on the one before it.  Calls on one GPU share its array:
+ * calls that overlap on one GPU (other streams, other threads) race and give
+ * undefined results; serialise them.
+ *
+ * Errors: INVALID_ARG, UNSUPPORTED (as moe_decode_plan; also a device index
+ * of 64 or more), SCRATCH (the workspace for this descriptor and T exceeds
+ * the array: for example 128 tokens at H = 6144, k = 8, I = 2048 need about
+ * 38 MiB and fit, 256 tokens do not), HIP.
+ */
+#define MOE_DECODE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_decode_run_static(const moe_decode_desc* d, const moe_decode_args* a, int32_t T,
+                          void* stream);
 
 /*
  * Measurement only (not part of the layer): one streaming read of `bytes`

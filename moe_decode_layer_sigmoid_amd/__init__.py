@@ -17,6 +17,8 @@ from .binding import (  # noqa: F401
     ERR_HIP,
     ERR_INVALID_ARG,
     ERR_NO_MEMORY,
+    ERR_SCRATCH,
+    STATIC_SCRATCH_BYTES,
     ERR_UNSUPPORTED,
     PATH_AUTO,
     PATH_GEMV,
@@ -29,6 +31,7 @@ from .binding import (  # noqa: F401
     lib,
     make_desc,
     read_probe,
+    run_static,
     strerror,
     PROBE_STEP,
 )

@@ -15,7 +15,8 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_decode.so")
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_NO_MEMORY = range(5)
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_NO_MEMORY, ERR_SCRATCH = range(6)
+STATIC_SCRATCH_BYTES = 64 << 20  # MOE_DECODE_STATIC_SCRATCH_BYTES
 SCALE_FP32, SCALE_E8M0 = 0, 1
 PATH_AUTO, PATH_GEMV, PATH_GROUPED, PATH_GEMV_SPLIT = 0, 1, 2, 3
 
@@ -79,8 +80,9 @@ def lib():
         L.moe_decode_workspace_bytes.argtypes = [vp]
         L.moe_decode_workspace_bytes.restype = ctypes.c_size_t
         L.moe_decode_read_probe.argtypes = [vp, ctypes.c_size_t, vp, vp]
+        L.moe_decode_run_static.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Args), i32, vp]
         for f in ("desc_check", "args_check", "plan", "run", "destroy", "last_routes",
-                  "set_expert_events", "path_for", "check_waits", "read_probe"):
+                  "set_expert_events", "path_for", "check_waits", "read_probe", "run_static"):
             getattr(L, "moe_decode_" + f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -89,7 +91,8 @@ def lib():
 EXPORTED = ["moe_decode_desc_check", "moe_decode_args_check", "moe_decode_plan",
             "moe_decode_run", "moe_decode_destroy", "moe_decode_strerror",
             "moe_decode_last_routes", "moe_decode_set_expert_events", "moe_decode_path_for",
-            "moe_decode_check_waits", "moe_decode_workspace_bytes", "moe_decode_read_probe"]
+            "moe_decode_check_waits", "moe_decode_workspace_bytes", "moe_decode_read_probe",
+            "moe_decode_run_static"]
 
 
 def strerror(code: int) -> str:
@@ -207,3 +210,13 @@ def read_probe(buf, nbytes: int, sink, stream=None) -> None:
     if rc:
         raise MoeDecodeError(rc, "moe_decode_read_probe")
 
+
+def run_static(desc: Desc, T: int, stream=None, **tensors) -> None:
+    """moe_decode_run_static: the layer without a plan, its workspace in the
+    library's static scratch array (no device allocation)."""
+    fields = {n: None for n, _ in Args._fields_}
+    fields.update(tensors)
+    args = Args(*[_ptr(fields[n]) for n, _ in Args._fields_])
+    rc = lib().moe_decode_run_static(ctypes.byref(desc), ctypes.byref(args), T, _stream(stream))
+    if rc:
+        raise MoeDecodeError(rc, "moe_decode_run_static")

@@ -18,8 +18,10 @@
 // DraftDecode.run, rejoins its side stream before reporting.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "moe_decode.h"
@@ -131,6 +133,8 @@ const char* moe_decode_strerror(int code) {
     case MOE_DECODE_ERR_UNSUPPORTED: return "unsupported size or device";
     case MOE_DECODE_ERR_HIP: return "HIP runtime error";
     case MOE_DECODE_ERR_NO_MEMORY: return "device allocation failed";
+    case MOE_DECODE_ERR_SCRATCH:
+      return "workspace for this size exceeds the static scratch (moe_decode_run_static)";
     default: return "unknown status";
   }
 }
@@ -393,14 +397,20 @@ static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t 
   const int rows = side ? moe::kRoutedRows : moe::kAllRows;
   const void* sw13 = has_shared ? a->sw13 : nullptr;
   const void* sw2 = has_shared ? a->sw2 : nullptr;
+  // a run without a side stream (moe_decode_run_static) queues the shared
+  // passes on `s`, ahead of the routed launches
+  const bool fork = side && p->side != nullptr;
+  const hipStream_t ss = fork ? p->side : s;
   if (side) {
-    if (hipEventRecord(p->fork, s) != hipSuccess) return MOE_DECODE_ERR_HIP;
-    if (hipStreamWaitEvent(p->side, p->fork, 0) != hipSuccess) return MOE_DECODE_ERR_HIP;
+    if (fork) {
+      if (hipEventRecord(p->fork, s) != hipSuccess) return MOE_DECODE_ERR_HIP;
+      if (hipStreamWaitEvent(p->side, p->fork, 0) != hipSuccess) return MOE_DECODE_ERR_HIP;
+    }
     step(moe::launch_gate_up_mfma(d, moe::kSharedRows, a->hidden, a->w13, a->w13_scale, sw13,
-                                  a->sw13_scale, p->ws, p->side));
+                                  a->sw13_scale, p->ws, ss));
     if (err == hipSuccess)
       step(moe::launch_down_mfma(d, moe::kSharedRows, a->w2, a->w2_scale, sw2, a->sw2_scale,
-                                 p->ws, p->side));
+                                 p->ws, ss));
   }
   if (!side && moe::grouped_chain_supported(d)) {
     // gate_up and down in one launch (the down tiles start in the gate_up drain)
@@ -415,7 +425,7 @@ static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t 
     if (err == hipSuccess)
       step(moe::launch_down_mfma(d, rows, a->w2, a->w2_scale, sw2, a->sw2_scale, p->ws, s));
   }
-  if (side) {
+  if (fork) {
     // joined on every path, errors included, so a capture sees no loose work
     hipError_t jerr = hipEventRecord(p->join, p->side);
     if (jerr == hipSuccess) jerr = hipStreamWaitEvent(s, p->join, 0);
@@ -486,3 +496,89 @@ size_t moe_decode_workspace_bytes(moe_decode_plan_t p) { return p ? p->ws_bytes 
 
 }  // extern "C"
 
+// ---- the entry point that allocates nothing ---------------------------------
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops, harnesses that forbid it).  Its workspace is
+// `scratch`, a file-scope device array: every GPU the library runs on holds
+// its own copy, at its own address, until the process ends.
+namespace {
+constexpr size_t kStaticScratchBytes = MOE_DECODE_STATIC_SCRATCH_BYTES;
+constexpr int kStaticMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+// The device address of `scratch` on each device (nullptr: not set up yet).
+// Host code uses these, never the array's name, which on the host is only a
+// stand-in for the symbol.
+void* g_scratch_ptr[kStaticMaxDevices];
+
+// Sets up device `dev` (current) once: checks it is gfx950 and takes the
+// address of its copy of `scratch`.
+int scratch_for_device(int dev, void** out) {
+  if (dev < 0 || dev >= kStaticMaxDevices) return MOE_DECODE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_DECODE_ERR_HIP;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MOE_DECODE_ERR_UNSUPPORTED;
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+      return MOE_DECODE_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_DECODE_OK;
+}
+
+// Zeroes n 32-bit words (a kernel, not hipMemsetAsync, so that a captured
+// graph replays it correctly).
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, size_t n) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+    p[i] = 0u;
+}
+
+}  // namespace
+
+extern "C" int moe_decode_run_static(const moe_decode_desc* d, const moe_decode_args* a,
+                                     int32_t T, void* stream) {
+  int rc = moe_decode_desc_check(d);
+  if (rc) return rc;
+  rc = moe_decode_args_check(d, a, T);
+  if (rc) return rc;
+  if (T == 0) return MOE_DECODE_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_DECODE_ERR_HIP;
+  void* base = nullptr;
+  rc = scratch_for_device(dev, &base);
+  if (rc) return rc;
+
+  // a plan on the host stack: workspace in the scratch array, sized for T
+  moe_decode_plan_s p{};
+  p.desc = *d;
+  p.desc.max_tokens = T;
+  p.device = dev;
+  size_t state = 0;
+  p.ws_bytes = layout(p.desc, nullptr, nullptr, &state);
+  p.state_bytes = state;
+  if (p.ws_bytes > kStaticScratchBytes) return MOE_DECODE_ERR_SCRATCH;
+  layout(p.desc, static_cast<char*>(base), &p.ws);
+  p.ws_base = base;
+  p.side = nullptr;  // the shared expert's passes go on `stream` too
+  p.fused_grid = 0;  // the persistent kernel needs the plan's measured residency
+  p.chain = moe::chain_supported(d->hidden, d->intermediate, d->shared_intermediate);
+
+  // The array keeps the last call's contents: clear the counters, flags,
+  // boundary slots, zero bias and error word that a run expects at zero.
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t words = state / 4;
+  const unsigned blocks = static_cast<unsigned>(std::min<size_t>((words + 255) / 256, 1024));
+  hipLaunchKernelGGL(zero_words_kernel, dim3(blocks), dim3(256), 0, s,
+                     static_cast<uint32_t*>(base), words);
+  if (hipGetLastError() != hipSuccess) return MOE_DECODE_ERR_HIP;
+  return run_on_device(&p, a, T, s);
+}
