@@ -325,9 +325,12 @@ def dominant_kernel(md, sh, path_taken, D, routed_b, shared_b, act_b):
         return ("router_kernel<NJ2, E8> (dense MLP gate_up tiles)",
                 "router_kernel<%d, %s>" % ((H + 511) // 512, e8), kb, fl)
     if path_taken == md.PATH_GEMV:
-        # one persistent kernel runs the whole step: its bytes are the step's
-        return ("decode_fused_kernel (router, shared + routed experts, boundary)",
-                "decode_fused_kernel<", routed_b + shared_b + act_b + sh.E * H * 2,
+        # one launch runs the whole step: its bytes are the step's (and the
+        # router weight's)
+        njd = (max(sh.I, sh.Is) + 1023) // 1024
+        return ("decode_step_kernel<NJG, NJD, E8> (router, shared + routed experts, boundary)",
+                "decode_step_kernel<%d, %d, %s>" % ((H + 1023) // 1024, njd, e8),
+                routed_b + shared_b + act_b + sh.E * H * 2,
                 6 * T * H * (k * sh.I + sh.Is) + 2 * T * sh.E * H)
     # gate/up projection: touched experts' w13 + scales, the token rows in,
     # the SwiGLU rows out (f32, or hi + lo bf16 planes)
@@ -434,7 +437,7 @@ def measure_point(name, args, ceiling):
     ids = torch.empty((T, max(k, 1)), dtype=torch.int32, device="cuda")
     wts = torch.empty((T, max(k, 1)), dtype=torch.float32, device="cuda")
 
-    path = {"auto": md.PATH_AUTO, "fused": md.PATH_GEMV, "grouped": md.PATH_GROUPED,
+    path = {"auto": md.PATH_AUTO, "step": md.PATH_GEMV, "grouped": md.PATH_GROUPED,
             "split": md.PATH_GEMV_SPLIT}[args.path]
     plan = md.Plan(md.make_desc(H, E, k, sh.I, sh.Is, T, sh.scale_fmt, path, sh.limit, sh.rsf,
                                 sh.eps), torch.cuda.current_device())
@@ -599,7 +602,7 @@ def measure_point(name, args, ceiling):
     point = {
         "workload": wname, "tokens": T, "hidden": H, "experts": E, "top_k": k,
         "intermediate": sh.I, "shared_intermediate": sh.Is, "scale_fmt": sh.scale_fmt,
-        "expert_path": {1: "gemv-fused", 2: "grouped", 3: "gemv-split"}.get(path_taken, "?"),
+        "expert_path": {1: "gemv-step", 2: "grouped", 3: "gemv-split"}.get(path_taken, "?"),
         "distinct_experts": D, "metric_bytes_per_step": metric_bytes, "router_bytes": E * H * 2,
         "weight_copies": copies,
         "us_per_layer": round(ms_per_step * 1e3, 3),
@@ -647,7 +650,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip the read-ceiling probe")
-    ap.add_argument("--path", default="auto", choices=["auto", "fused", "grouped", "split"])
+    ap.add_argument("--path", default="auto", choices=["auto", "step", "grouped", "split"])
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 10 plain device copies of MIB MiB (a known-size reference "

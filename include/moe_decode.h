@@ -77,8 +77,9 @@ typedef enum {
    * below 4 tokens, GROUPED from 4 tokens on. */
   MOE_DECODE_PATH_AUTO = 0,
   /* fp8 dequant-FMA GEMV, one weight pass per touched expert.  Up to 16
-   * tokens the whole step is one persistent kernel (router, shared expert,
-   * routed experts and boundary as ordered work items); above that the
+   * tokens and 256 experts the whole step is one launch of ordered work
+   * items: router, shared expert, routed experts, boundary; at one token
+   * each routed item selects its own expert from the logits.  Otherwise the
    * GEMV_SPLIT kernels run. */
   MOE_DECODE_PATH_GEMV = 1,
   /* Tokens grouped by expert on the matrix cores: exactly converted fp8
@@ -246,7 +247,7 @@ int moe_decode_last_routes(moe_decode_plan_t p, int32_t T, int32_t* counts, int3
  * Measurement hook: when both are non-NULL, each later run launches its
  * dominant kernel with hipExtLaunchKernel, which records hipEvent_t `begin`
  * and `end` (created by the caller, timing enabled) at that kernel's own start
- * and end.  The dominant kernel is the fused persistent kernel on
+ * and end.  The dominant kernel is the single-launch step on
  * MOE_DECODE_PATH_GEMV; on MOE_DECODE_PATH_GEMV_SPLIT the expert chain launch
  * (up to 16 tokens) or the routed-expert gate/up projection kernel; on
  * MOE_DECODE_PATH_GROUPED the gate_up + down launch (up to 64 tokens) or the
@@ -255,8 +256,8 @@ int moe_decode_last_routes(moe_decode_plan_t p, int32_t T, int32_t* counts, int3
  */
 int moe_decode_set_expert_events(moe_decode_plan_t p, void* begin, void* end);
 
-/* Which kernels a run with T tokens takes: MOE_DECODE_PATH_GEMV (the fused
- * persistent kernel), MOE_DECODE_PATH_GEMV_SPLIT or MOE_DECODE_PATH_GROUPED;
+/* Which kernels a run with T tokens takes: MOE_DECODE_PATH_GEMV (the
+ * single-launch step), MOE_DECODE_PATH_GEMV_SPLIT or MOE_DECODE_PATH_GROUPED;
  * negative status on a bad argument. */
 int moe_decode_path_for(moe_decode_plan_t p, int32_t T);
 
@@ -286,10 +287,9 @@ size_t moe_decode_workspace_bytes(moe_decode_plan_t p);
  * Arguments as moe_decode_run, with the descriptor in place of a plan
  * (d->max_tokens bounds T as before; the workspace is laid out for T).
  * Differences: the shared expert's passes above 64 tokens run on `stream`
- * ahead of the routed launches (there is no side stream);
- * MOE_DECODE_PATH_GEMV takes the GEMV_SPLIT kernels; no measurement hook and
- * no moe_decode_check_waits (a bounded wait that gives up shows as NaN in
- * out).  Every call clears the array's counters and flags first, so a call
+ * ahead of the routed launches (there is no side stream); no measurement
+ * hook and no moe_decode_check_waits (a bounded wait that gives up shows as
+ * NaN in out).  Every call clears the array's counters and flags first, so a call
  * never depends on the one before it.  Calls on one GPU share its array:
  * calls that overlap on one GPU (other streams, other threads) race and give
  * undefined results; serialise them.

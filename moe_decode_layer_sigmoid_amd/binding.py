@@ -191,7 +191,7 @@ class Plan:
         return lib().moe_decode_path_for(self._h, T)
 
     def check_waits(self) -> bool:
-        """True when a bounded wait of the fused kernel gave up since the
+        """True when a bounded wait of a run gave up since the
         last check (synchronises the device; clears the flag)."""
         flag = ctypes.c_int32(0)
         rc = lib().moe_decode_check_waits(self._h, ctypes.byref(flag))

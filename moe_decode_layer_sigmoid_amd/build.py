@@ -16,11 +16,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_decode.so")
 SOURCES = ["api.hip", "router.hip", "experts_gemv.hip", "experts_mfma.hip", "epilogue.hip",
-           "decode_fused.hip", "experts_chain.hip", "probe.hip"]
-# decode_fused.hip is also compiled once per register chunk count and scale
-# format (the template arguments of its kernel), each into its own object;
-# experts_chain.hip once per w13 chunk count.
-FUSED_NJ = range(1, 9)
+           "experts_chain.hip", "probe.hip"]
+# experts_chain.hip is also compiled once per w13 chunk count (the first
+# template argument of its kernels), each into its own object, in parallel.
+CHAIN_NJG = range(1, 9)
 ARCH = "gfx950"
 
 
@@ -57,13 +56,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         jobs.append((obj, [hipcc(), *FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj]))
-    for nj in FUSED_NJ:
-        for e8 in (0, 1):
-            obj = os.path.join(objdir, "decode_fused_nj%d_e%d.o" % (nj, e8))
-            jobs.append((obj, [hipcc(), *FLAGS, *inc, "-DMOE_FUSED_NJ=%d" % nj,
-                               "-DMOE_FUSED_E8=%d" % e8, "-c",
-                               os.path.join(CSRC, "decode_fused.hip"), "-o", obj]))
-    for nj in FUSED_NJ:
+    for nj in CHAIN_NJG:
         obj = os.path.join(objdir, "experts_chain_njg%d.o" % nj)
         jobs.append((obj, [hipcc(), *FLAGS, *inc, "-DMOE_CHAIN_NJG=%d" % nj, "-c",
                            os.path.join(CSRC, "experts_chain.hip"), "-o", obj]))

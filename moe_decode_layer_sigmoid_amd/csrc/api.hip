@@ -39,17 +39,20 @@ struct moe_decode_plan_s {
                          // kMergeSharedMaxTokens tokens
   hipEvent_t fork, join;
   hipEvent_t user_begin, user_end;
-  uint32_t fused_grid;  // workgroups of the fused kernel (0: fused path unavailable)
-  bool chain;  // the split path's expert chain launch supports this layer shape
+  bool chain;  // the expert chain and the single-launch step support this layer shape
 };
 
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// AUTO takes the separate GEMV kernels: on MI355X they currently beat the
-// fused persistent kernel at 1 and 16 tokens (the fused kernel's routing
-// hand-off sits on the critical path); GEMV asks for the fused kernel.
+// Whether the single-launch step runs T tokens of this layer.
+bool step_fits(const moe_decode_plan_s& p, int32_t T) {
+  return p.chain && T <= moe::kChainMaxTokens && p.desc.num_experts <= moe::kStepMaxExperts;
+}
+
+// AUTO: the single-launch step below kGroupedMinTokens tokens (where it fits;
+// else the router launch and the chain), the MFMA kernels from there.
 int path_for(const moe_decode_plan_s& p, int32_t T) {
   const int want = p.desc.path;
   if (p.desc.num_experts == 0)  // a dense layer: the GEMV or the MFMA kernels
@@ -58,9 +61,9 @@ int path_for(const moe_decode_plan_s& p, int32_t T) {
                ? MOE_DECODE_PATH_GROUPED
                : MOE_DECODE_PATH_GEMV_SPLIT;
   if (want == MOE_DECODE_PATH_GEMV_SPLIT || want == MOE_DECODE_PATH_GROUPED) return want;
-  if (want == MOE_DECODE_PATH_GEMV && T <= moe::kFusedMaxTokens && p.fused_grid > 0)
-    return MOE_DECODE_PATH_GEMV;
   if (want == MOE_DECODE_PATH_AUTO && T >= moe::kGroupedMinTokens) return MOE_DECODE_PATH_GROUPED;
+  if ((want == MOE_DECODE_PATH_GEMV || T <= moe::kStepAutoMaxTokens) && step_fits(p, T))
+    return MOE_DECODE_PATH_GEMV;
   return MOE_DECODE_PATH_GEMV_SPLIT;
 }
 
@@ -85,6 +88,12 @@ size_t layout(const moe_decode_desc& d, char* base, moe::Workspace* ws,
   w.sync = reinterpret_cast<uint32_t*>(take(moe::sync_words(static_cast<int>(E)) * 4));
   w.zero_bias = reinterpret_cast<float*>(take(E * 4));
   w.epi_part = reinterpret_cast<float*>(take(T * moe::kMaxBndSlices * 4));
+  // the single-launch step's state (at most kChainMaxTokens tokens)
+  const size_t Ts = T < moe::kChainMaxTokens ? T : moe::kChainMaxTokens;
+  const int dmax_s = static_cast<int>(Ts * k < E ? Ts * k : E);
+  w.msync = reinterpret_cast<uint32_t*>(take(moe::step_sync_lines(dmax_s) * moe::kSyncStride * 4));
+  w.mlogits = reinterpret_cast<float*>(take(moe::kFlagRep * Ts * E * 4));
+  w.mepi = reinterpret_cast<float*>(take(Ts * moe::kMaxBndSlices * 4));
   if (state_bytes) *state_bytes = off;
   w.logits = reinterpret_cast<float*>(take(T * E * 4));
   w.ids = reinterpret_cast<int32_t*>(take(T * k * 4));
@@ -230,13 +239,7 @@ int moe_decode_plan(const moe_decode_desc* d, int device, moe_decode_plan_t* out
   if (!rc && (hipEventCreateWithFlags(&p->fork, hipEventDisableTiming) != hipSuccess ||
               hipEventCreateWithFlags(&p->join, hipEventDisableTiming) != hipSuccess))
     rc = MOE_DECODE_ERR_HIP;
-  if (!rc) {
-    const int per_cu = moe::fused_blocks_per_cu(
-        moe::fused_nj(d->hidden, d->intermediate, d->shared_intermediate),
-        d->scale_fmt == MOE_DECODE_SCALE_E8M0);
-    p->fused_grid = static_cast<uint32_t>(per_cu > 0 ? per_cu * prop.multiProcessorCount : 0);
-    p->chain = moe::chain_supported(d->hidden, d->intermediate, d->shared_intermediate);
-  }
+  if (!rc) p->chain = moe::chain_supported(d->hidden, d->intermediate, d->shared_intermediate);
   if (!rc && hipDeviceSynchronize() != hipSuccess) rc = MOE_DECODE_ERR_HIP;
   (void)hipSetDevice(prev);
   if (rc) {
@@ -278,29 +281,30 @@ int moe_decode_run(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, voi
   return rc;
 }
 
-static int run_fused(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, hipStream_t s) {
-  moe::FusedArgs f{};
-  moe::fused_items(dims(p->desc, T), &f);
-  f.hidden = static_cast<const uint16_t*>(a->hidden);
-  f.residual = static_cast<const uint16_t*>(a->residual);
-  f.router_w = static_cast<const uint16_t*>(a->router_w);
-  f.bias = a->router_bias ? a->router_bias : p->ws.zero_bias;
-  f.w13 = static_cast<const uint8_t*>(a->w13);
-  f.w13_scale = a->w13_scale;
-  f.w2 = static_cast<const uint8_t*>(a->w2);
-  f.w2_scale = a->w2_scale;
-  f.sw13 = static_cast<const uint8_t*>(a->sw13);
-  f.sw13_scale = a->sw13_scale;
-  f.sw2 = static_cast<const uint8_t*>(a->sw2);
-  f.sw2_scale = a->sw2_scale;
-  f.gamma = static_cast<const uint16_t*>(a->gamma);
-  f.out = static_cast<uint16_t*>(a->out);
-  f.moe_out = static_cast<uint16_t*>(a->moe_out);
-  f.residual_out = static_cast<uint16_t*>(a->residual_out);
-  f.ids_out = a->topk_ids;
-  f.w_out = a->topk_weights;
-  f.grid = p->fused_grid;
-  const hipError_t err = moe::launch_decode_fused(f, p->ws, s, p->user_begin, p->user_end);
+// The whole step in one launch (router, shared expert, routed experts,
+// boundary: decode_step_kernel).
+static int run_step(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, hipStream_t s) {
+  moe::StepArgs st{};
+  moe::step_items(dims(p->desc, T), &st);
+  st.hidden = static_cast<const uint16_t*>(a->hidden);
+  st.residual = static_cast<const uint16_t*>(a->residual);
+  st.router_w = static_cast<const uint16_t*>(a->router_w);
+  st.bias = a->router_bias ? a->router_bias : p->ws.zero_bias;
+  st.w13 = static_cast<const uint8_t*>(a->w13);
+  st.w13_scale = a->w13_scale;
+  st.w2 = static_cast<const uint8_t*>(a->w2);
+  st.w2_scale = a->w2_scale;
+  st.sw13 = static_cast<const uint8_t*>(a->sw13);
+  st.sw13_scale = a->sw13_scale;
+  st.sw2 = static_cast<const uint8_t*>(a->sw2);
+  st.sw2_scale = a->sw2_scale;
+  st.gamma = static_cast<const uint16_t*>(a->gamma);
+  st.out = static_cast<uint16_t*>(a->out);
+  st.residual_out = static_cast<uint16_t*>(a->residual_out);
+  st.moe_out = static_cast<uint16_t*>(a->moe_out);
+  st.ids_out = a->topk_ids;
+  st.w_out = a->topk_weights;
+  const hipError_t err = moe::launch_decode_step(st, p->ws, s, p->user_begin, p->user_end);
   return err == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;
 }
 
@@ -339,7 +343,7 @@ static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t 
                          hipStream_t s) {
   if (p->desc.num_experts == 0) return run_dense(p, a, T, s);
   const int path = path_for(*p, T);
-  if (path == MOE_DECODE_PATH_GEMV) return run_fused(p, a, T, s);
+  if (path == MOE_DECODE_PATH_GEMV) return run_step(p, a, T, s);
   const moe::LayerDims d = dims(p->desc, T);
   const bool has_shared = d.Is > 0;
   const void* bias = a->router_bias ? a->router_bias : p->ws.zero_bias;
@@ -569,7 +573,6 @@ extern "C" int moe_decode_run_static(const moe_decode_desc* d, const moe_decode_
   layout(p.desc, static_cast<char*>(base), &p.ws);
   p.ws_base = base;
   p.side = nullptr;  // the shared expert's passes go on `stream` too
-  p.fused_grid = 0;  // the persistent kernel needs the plan's measured residency
   p.chain = moe::chain_supported(d->hidden, d->intermediate, d->shared_intermediate);
 
   // The array keeps the last call's contents: clear the counters, flags,

@@ -1,45 +1,74 @@
-// The expert projections and the boundary of a few-token decode step in one
-// launch on gfx950 (after the router launch).
+// The few-token decode step on gfx950 as one or two launches of ordered work
+// items: the expert chain (after the router launch), and the whole step in
+// one launch with the router's items in front.
 //
 // Follows the vLLM API page "vllm.models.glm5next.nvidia.specialized_decode.
 // runtime.decode": LayerStages._build_mega (fp8 w13 / w2 with 128x128 block
-// scales, swiglu_limit), LayerStages._mega_moe (the shared expert beside the
-// routed experts; the boundary receives the unfinalized rows with the route
-// order) and the page "...runtime.draft", SpecializedDraft.reduced_norm
-// (norm(x + residual) with the new residual).
+// scales, swiglu_limit; the MoE layer logged as one kernel),
+// LayerStages._mega_moe (router logits, the shared expert beside the routed
+// experts; the boundary receives the unfinalized rows with the route order),
+// LayerStages._router (fp32 logits from the bf16 router weight) and the page
+// "...runtime.draft", SpecializedDraft.reduced_norm (norm(x + residual) with
+// the new residual).
 //
 // At one token the step is a chain of short weight streams (gate_up 100 MB,
 // down 57 MB at the 4096 x 1536 decode shape).  As separate launches each
 // pays its own ramp and tail; here one launch streams them back to back, one
-// workgroup per item, in this order of workgroup index:
-//   shared down      32 output rows of the shared expert (16 when I_s >
-//                    2048; its SwiGLU rows come from the router launch)
+// workgroup per item, in this order of workgroup index.
+//
+// expert_chain_kernel (after the router launch, which also ran the shared
+// expert's gate_up):
+//   shared down      32 output rows of the shared expert (16 when I_s > 2048)
 //   routed gate_up   8 SwiGLU rows of one touched slot
-//   routed down      32 (or 16) output rows of one touched slot; it issues its weight
-//                    loads first and then waits for the slot's gate_up
+//   routed down      32 (or 16) output rows of one touched slot; it issues its
+//                    weight loads first and then waits for the slot's gate_up
 //                    count, so the down weights stream while gate_up ends
 //   boundary         the last T * ceil(H / 2048) workgroups: after every
 //                    down item, combine + shared + residual of a 2048-column
 //                    slice of one token, the slices' sums of squares
 //                    exchanged, then RMSNorm * gamma of the slice
-// The down items read the SwiGLU rows, and the boundary the down rows, with
-// plain (L2-cached) loads: they are written with write-through stores that
-// complete before the writer's count is bumped, the L2s hold no line of them
-// when the launch starts (every launch begins with an L2 invalidate), and no
-// workgroup touches them (whole 128-byte lines per slot and per route) before
-// the count that covers them is complete.  Coherent loads instead would
-// fetch a slot's SwiGLU rows from memory once per down workgroup (50 MB at
-// one token, as much as the down weights).
+// decode_step_kernel (the whole step):
+//   router           logits of 4 experts (one per wave) for one token, stored
+//                    with inverted bits so that zeroed memory means "not
+//                    written yet"; the last router item then selects every
+//                    token's top-k, builds the route tables and raises the
+//                    route flag
+//   shared gate_up   8 SwiGLU rows of the shared expert (no routing needed:
+//                    its weights stream while the router runs)
+//   shared down      as above, after every shared gate_up item
+//   routed gate_up, routed down, boundary: as above.  At one token each
+//                    routed item finds its slot's expert itself, from the
+//                    logits (it polls them until every router item has
+//                    stored its logits, then runs the same selection as the
+//                    last router item on the same bits), so no routed item
+//                    waits for the route tables; above one token they wait
+//                    for the route flag and read the slot's record.
+// The step launch leaves its counters, flags, logits and boundary slots
+// zeroed for the next step launch: the last boundary slice to finish clears
+// them, once every other workgroup is past its last use of them.
+//
+// Hand-offs.  The down items read the SwiGLU rows, and the boundary the down
+// rows, with plain (L2-cached) loads: they are written with write-through
+// stores that complete before the writer's count is bumped, the L2s hold no
+// line of them when the launch starts (every launch begins with an L2
+// invalidate), and no workgroup touches them (whole 128-byte lines per slot
+// and per route) before the count that covers them is complete.  Coherent
+// loads instead would fetch a slot's SwiGLU rows from memory once per down
+// workgroup (50 MB at one token, as much as the down weights).  Everything
+// else handed over inside a launch (logits, route tables, top-k weights,
+// counters, the boundary slots) is written and read coherently.
 // A workgroup waits only for workgroups of lower index, which the dispatcher
-// has started before it (workgroups are dispatched in index order), so
-// every wait ends; waits are bounded anyway (a sticky error word,
-// moe_decode_check_waits).  Completion counts are bumped with atomics whose
-// result is not used (no workgroup waits for them); the router launch that
-// precedes every chain launch zeroes them (and arms the boundary's slots).  SwiGLU rows and down rows are
-// written with agent-scope atomic stores (sync_device.h).
+// has started before it (workgroups are dispatched in index order), except
+// that a token's boundary slices wait for each other: all T * ceil(H / 2048)
+// (at most 64) boundary workgroups must be resident together, which they are
+// once every other item has ended.  Every wait is bounded anyway: an
+// exhausted wait sets the sticky error word (moe_decode_check_waits) and
+// goes on, and the boundary then writes NaN to out.  Completion counts are
+// bumped with atomics whose result is not used.
 #include "device_common.h"
 #include "gemv_tiles.h"
 #include "launch.h"
+#include "routing_device.h"
 #include "sync_device.h"
 
 namespace moe {
@@ -52,8 +81,8 @@ constexpr int kWaves = kThreads / kWave;
 // gate_up wave's), else 4.
 __host__ __device__ constexpr int rows_dn_wave(int njd) { return njd <= 2 ? 8 : 4; }
 constexpr int kRowsGu = 2 * kWaves;  // SwiGLU rows per gate_up item
-constexpr int kMaxNjd = 4;           // I, I_s <= 4096
-constexpr int kMaxSlots = kChainMaxTokens * kMaxTopK;
+[[maybe_unused]] constexpr int kMaxNjd = 4;  // I, I_s <= 4096
+[[maybe_unused]] constexpr int kMaxSlots = kChainMaxTokens * kMaxTopK;
 // Polls before a wait gives up: a legitimate wait here lasts microseconds
 // (a poll is a memory round trip plus a short sleep).
 constexpr uint32_t kChainSpin = 1u << 17;
@@ -61,32 +90,72 @@ constexpr uint32_t kChainSpin = 1u << 17;
 template <int NJG, int NJD, bool E8>
 hipError_t launch_t(const ChainArgs& a, const Workspace& ws, hipStream_t s, hipEvent_t evb,
                     hipEvent_t eve);
+template <int NJG, int NJD, bool E8>
+hipError_t step_launch_t(const StepArgs& a, const Workspace& ws, size_t smem, hipStream_t s,
+                         hipEvent_t evb, hipEvent_t eve);
 
 #ifdef MOE_CHAIN_NJG
+// What a boundary slice reads and writes besides the workspace rows.
+struct BndArgs {
+  const uint16_t* residual;
+  const uint16_t* gamma;
+  uint16_t* out;
+  uint16_t* residual_out;
+  uint16_t* moe_out;  // nullable
+  int H, k, Is, ns;   // ns = slices per token
+  float eps;
+  float* part;        // [T][kMaxBndSlices] slice sums of squares, inverted bits (0 = empty)
+  uint32_t* err;      // the error word
+};
+
+// What the step launch's last boundary slice clears for the next launch.
+struct StepTail {
+  uint32_t* bnd;      // the boundary slices' count (msync line kStepBnd)
+  uint32_t total;     // boundary slices of the launch
+  uint32_t* sync;     // msync
+  int sync_lines;
+  float* logits;      // mlogits, n_logits words
+  int n_logits;
+  int n_part;         // words of the boundary slots
+};
+
 // The boundary of token t, columns [kBndCols * s, +kBndCols) (8 per thread),
-// by one of the token's bnd_ns workgroups: h = sum_j w[t, j] * rows[t*k + j]
+// by one of the token's ns workgroups: h = sum_j w[t, j] * rows[t*k + j]
 // + y_s[t] + residual[t] (fixed order; with moe_out, the sum before the
-// residual goes there too); the slice's sum of squares (waves in
-// order) goes to ws.epi_part[t][s], which the router launch armed with
-// kEpiEmpty; once every slice of the token is in, their sums in slice order
-// give the RMS, and the slice of residual_out = bf16(h), out = bf16(h /
-// sqrt(mean(h^2) + eps) * gamma) is written.  The loads that do not depend on
-// the down rows (top-k weights, residual, gamma) are issued before `wait`;
-// the rest of the slice's loads all before their first use.
-template <typename Wait>
-__device__ __forceinline__ void boundary_slice(const ChainArgs& a, const Workspace& ws, int t,
-                                               int s, float* s_part, float* s_tot, Wait wait) {
+// residual goes there too); the slice's sum of squares (waves in order) goes
+// to part[t][s] as inverted bits; once every slice of the token is in, their
+// sums in slice order give the RMS, and the slice of residual_out = bf16(h),
+// out = bf16(h / sqrt(mean(h^2) + eps) * gamma) is written (NaN if a bounded
+// wait of the launch gave up).  The loads that do not depend on the down rows
+// are issued before `wait`: the residual, gamma and, in the chain launch,
+// the top-k weights (the step launch writes those itself, so it loads them
+// after the wait, coherently); the rest of the slice's loads all before
+// their first use.  STEP: the step launch's slice, which afterwards counts
+// itself done, and the last one clears the launch's state (`tail`).
+template <bool STEP, typename Wait>
+__device__ __forceinline__ void boundary_slice(const BndArgs& b, const Workspace& ws, int t,
+                                               int s, Wait wait, const StepTail& tail) {
+  __shared__ float s_part[kWaves];
+  __shared__ float s_tot[kMaxBndSlices];
+  __shared__ uint32_t s_bad;
+  __shared__ int s_last;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int H = a.H, k = a.k, ns = a.bnd_ns;
+  const int H = b.H, k = b.k, ns = b.ns;
   const int c = kBndCols * s + 8 * static_cast<int>(threadIdx.x);
   const bool live = c < H;
   const int c0 = live ? c : H - 8;  // clamped: loads stay in the row
-  const uint4 rv = *reinterpret_cast<const uint4*>(a.residual + static_cast<size_t>(t) * H + c0);
-  const uint4 gv = *reinterpret_cast<const uint4*>(a.gamma + c0);
+  const uint4 rv = *reinterpret_cast<const uint4*>(b.residual + static_cast<size_t>(t) * H + c0);
+  const uint4 gv = *reinterpret_cast<const uint4*>(b.gamma + c0);
   float wts[kMaxTopK];
+  if (!STEP) {
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) wts[j] = ws.weights[t * k + (j < k ? j : k - 1)];
+    for (int j = 0; j < kMaxTopK; ++j) wts[j] = ws.weights[t * k + (j < k ? j : k - 1)];
+  }
   wait();
+  if (STEP) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) wts[j] = ld_f32<true>(ws.weights + t * k + (j < k ? j : k - 1));
+  }
   const float* rows_t = ws.rows + static_cast<size_t>(t) * k * H + c0;
   const float* ys = ws.y_s + static_cast<size_t>(t) * H + c0;
   const float4 ya = *reinterpret_cast<const float4*>(ys);
@@ -117,11 +186,11 @@ __device__ __forceinline__ void boundary_slice(const ChainArgs& a, const Workspa
       acc[7] = fmaf(w, rb[q].w, acc[7]);
     }
   }
-  if (a.Is > 0) {
+  if (b.Is > 0) {
     acc[0] += ya.x; acc[1] += ya.y; acc[2] += ya.z; acc[3] += ya.w;
     acc[4] += yb.x; acc[5] += yb.y; acc[6] += yb.z; acc[7] += yb.w;
   }
-  if (a.moe_out && live) store_bf16x8(a.moe_out + static_cast<size_t>(t) * H + c, acc);
+  if (b.moe_out && live) store_bf16x8(b.moe_out + static_cast<size_t>(t) * H + c, acc);
   const uint32_t u[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -134,61 +203,77 @@ __device__ __forceinline__ void boundary_slice(const ChainArgs& a, const Workspa
   ss = wave_sum(live ? ss : 0.f);
   if (lane == 0) s_part[wave] = ss;
   __syncthreads();
-  float* part = ws.epi_part + t * kMaxBndSlices;
-  __shared__ uint32_t s_bad;
+  float* part = b.part + t * kMaxBndSlices;
   if (wave == 0) {
     // publish this slice's sum (no wait for the store), then poll the token's
     // slices, one lane each, until none is empty; lane 63 reads the error
-    // word in the same round trips (a wait of the launch that gave up)
-    if (lane == 0) st_f32<true>(part + s, (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]));
+    // word in the same round trips
+    if (lane == 0) {
+      const float mine = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+      st_u32<true>(reinterpret_cast<uint32_t*>(part + s), ~__float_as_uint(mine));
+    }
     const float* src = lane < ns ? part + lane
-                                 : (lane == 63 ? reinterpret_cast<const float*>(
-                                                     ws.sync + kSyncError * kSyncStride)
-                                               : part);
+                                 : (lane == 63 ? reinterpret_cast<const float*>(b.err) : part);
     uint32_t polls = 0;
-    float v = 0.f;
+    uint32_t v = 0;
     for (;;) {
-      v = ld_f32<true>(src);
-      const bool in = lane >= ns || __float_as_uint(v) != kEpiEmpty;
+      v = __float_as_uint(ld_f32<true>(src));
+      const bool in = lane >= ns || v != 0u;
       if (__builtin_amdgcn_ballot_w64(!in) == 0) break;  // uniform over the wave
       __builtin_amdgcn_s_sleep(1);
       if (++polls == kChainSpin) {
-        if (lane == 0)
-          __hip_atomic_fetch_or(ws.sync + kSyncError * kSyncStride, 1u, __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) __hip_atomic_fetch_or(b.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
     }
-    if (lane < ns) s_tot[lane] = v;
-    if (lane == 63) s_bad = (__float_as_uint(v) != 0u || polls == kChainSpin) ? 1u : 0u;
+    if (lane < ns) s_tot[lane] = __uint_as_float(~v);
+    if (lane == 63) s_bad = (v != 0u || polls == kChainSpin) ? 1u : 0u;
   }
   __syncthreads();
+  // step launch: this slice is done with the shared state; the count comes
+  // back while the outputs are computed and stored
+  uint32_t prev = 0;
+  if (STEP && threadIdx.x == 0)
+    prev = __hip_atomic_fetch_add(tail.bnd, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const bool gave_up = s_bad != 0u;
   float tot = 0.f;
   for (int i = 0; i < ns; ++i) tot += s_tot[i];
-  const float inv_rms = 1.0f / sqrtf(tot / static_cast<float>(H) + a.eps);
-  if (!live) return;
-  const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
-  uint32_t o[4], r[4];
+  const float inv_rms = 1.0f / sqrtf(tot / static_cast<float>(H) + b.eps);
+  if (live) {
+    const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
+    uint32_t o[4], r[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const float h0 = acc[2 * m], h1 = acc[2 * m + 1];
-    o[m] = f32_to_bf16(h0 * inv_rms * bf16_lo(g[m])) |
-           (f32_to_bf16(h1 * inv_rms * bf16_hi(g[m])) << 16);
-    r[m] = f32_to_bf16(h0) | (f32_to_bf16(h1) << 16);
-    if (gave_up) o[m] = kBf16NanPair;
+    for (int m = 0; m < 4; ++m) {
+      const float h0 = acc[2 * m], h1 = acc[2 * m + 1];
+      o[m] = f32_to_bf16(h0 * inv_rms * bf16_lo(g[m])) |
+             (f32_to_bf16(h1 * inv_rms * bf16_hi(g[m])) << 16);
+      r[m] = f32_to_bf16(h0) | (f32_to_bf16(h1) << 16);
+      if (gave_up) o[m] = kBf16NanPair;
+    }
+    *reinterpret_cast<uint4*>(b.out + static_cast<size_t>(t) * H + c) =
+        make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(b.residual_out + static_cast<size_t>(t) * H + c) =
+        make_uint4(r[0], r[1], r[2], r[3]);
   }
-  *reinterpret_cast<uint4*>(a.out + static_cast<size_t>(t) * H + c) =
-      make_uint4(o[0], o[1], o[2], o[3]);
-  *reinterpret_cast<uint4*>(a.residual_out + static_cast<size_t>(t) * H + c) =
-      make_uint4(r[0], r[1], r[2], r[3]);
+  if (STEP) {
+    if (threadIdx.x == 0) s_last = prev + 1 == tail.total;
+    __syncthreads();
+    if (s_last) {
+      // every other workgroup of the launch is past its last use of these
+      for (int i = threadIdx.x; i < tail.sync_lines; i += kThreads)
+        st_u32<true>(tail.sync + static_cast<size_t>(i) * kSyncStride, 0u);
+      for (int i = threadIdx.x; i < tail.n_logits; i += kThreads)
+        st_u32<true>(reinterpret_cast<uint32_t*>(tail.logits) + i, 0u);
+      for (int i = threadIdx.x; i < tail.n_part; i += kThreads)
+        st_u32<true>(reinterpret_cast<uint32_t*>(b.part) + i, 0u);
+    }
+  }
 }
 
 // NJG = 16-byte chunks per lane of a w13 row (ceil(H / 1024)); NJD = the same
 // for w2 rows (ceil(max(I, I_s) / 1024)); E8 = e8m0 scales.
 template <int NJG, int NJD, bool E8>
 __global__ __launch_bounds__(kThreads) void expert_chain_kernel(ChainArgs a, Workspace ws) {
-  __shared__ float s_part[kWaves];
   const Sync sy{ws.sync};
   const int wave = threadIdx.x >> 6;
   const int H = a.H, I = a.I, k = a.k;
@@ -244,12 +329,202 @@ __global__ __launch_bounds__(kThreads) void expert_chain_kernel(ChainArgs a, Wor
 
   // ---- the boundary (the last T * bnd_ns workgroups), after every down item
   // (shared and routed, empty slots included)
-  __shared__ float s_tot[kMaxBndSlices];
   const int b = it - a.n_items;
-  boundary_slice(a, ws, b / a.bnd_ns, b % a.bnd_ns, s_part, s_tot, [&]() {
+  const BndArgs bn{a.residual, a.gamma, a.out, a.residual_out, a.moe_out, H, k, a.Is, a.bnd_ns,
+                   a.eps, ws.epi_part, sy.line(kSyncError)};
+  boundary_slice<false>(bn, ws, b / a.bnd_ns, b % a.bnd_ns, [&]() {
     wait_count(sy, kSyncExit0, kSyncExitLines, static_cast<uint32_t>(a.n_items - a.gu_items),
                kChainSpin);
-  });
+  }, StepTail{});
+}
+
+// ---------------------------------------------------------------- step launch
+
+// Where a routed down item of the step launch writes its rows: the slot's
+// route table (several tokens) or its one route (one token).
+struct RouteStep {
+  const int32_t* perm;  // null: `fixed`
+  int fixed;
+  __device__ int operator()(int pos) const { return perm ? ld_i32<true>(perm + pos) : fixed; }
+};
+
+// Counts this item done once its coherent stores have completed: `cnt`
+// (a counter line of msync, or -1) and its exit line.  Every thread calls it.
+__device__ __forceinline__ void item_done(const Sync& sy, int it, int cnt) {
+  wait_memory();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (cnt >= 0)
+      (void)__hip_atomic_fetch_add(sy.line(cnt), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    (void)__hip_atomic_fetch_add(sy.line(kStepExit0 + it % kSyncExitLines), 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Waits (wave 0, bounded) for the route flag's replica of this workgroup.
+__device__ __forceinline__ void wait_route(const Sync& sy, uint32_t* err) {
+  if (threadIdx.x < 64) {
+    const uint32_t* p = sy.line(kStepRoute + static_cast<int>(blockIdx.x % kFlagRep));
+    uint32_t polls = 0;
+    while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++polls == kChainSpin) {
+        if (threadIdx.x == 0)
+          __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// One token: the expert and route of every slot, from the logits, in wave 0
+// (polling replica blockIdx % kFlagRep of the logits until every router item
+// has stored them).  It is the selection the last router item runs, on the
+// same bits, so all workgroups agree with the route tables.  Slots are the
+// picks in ascending expert order (the route tables' order): s_slot[d] =
+// expert of slot d, s_slot[kMaxTopK + d] = its route j (rank in the top-k).
+__device__ __forceinline__ void route_one_token(const StepArgs& a, const Workspace& ws,
+                                                unsigned long long* sel, int* s_slot,
+                                                uint32_t* err) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    const float* logits = ws.mlogits + static_cast<size_t>(blockIdx.x % kFlagRep) * a.T * a.E;
+    int id = 0;
+    float w = 0.f;
+    select_token<true, true, true, false>(logits, a.bias, a.E, a.k, a.rsf, sel, &id, &w, err);
+    int* ids = reinterpret_cast<int*>(sel);  // the selection is done with its scratch
+    if (lane < a.k) ids[lane] = id;
+    wave_lds_order();
+    if (lane < a.k) {
+      int below = 0;
+      for (int i = 0; i < a.k; ++i) below += ids[i] < id ? 1 : 0;
+      s_slot[below] = id;
+      s_slot[kMaxTopK + below] = lane;
+    }
+  }
+  __syncthreads();
+}
+
+template <int NJG, int NJD, bool E8>
+__global__ __launch_bounds__(kThreads) void decode_step_kernel(StepArgs a, Workspace ws) {
+  // routing scratch (route_smem_bytes(T, E, k)): the last router item's, or
+  // wave 0's selection scratch at one token
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int s_slot[2 * kMaxTopK];
+  const Sync sy{ws.msync};
+  uint32_t* err = ws.sync + kSyncError * kSyncStride;
+  const int wave = threadIdx.x >> 6;
+  const int H = a.H, I = a.I, k = a.k, T = a.T, E = a.E;
+  const int it = blockIdx.x;
+  constexpr int RD = rows_dn_wave(NJD);
+
+  if (it < a.o_sgu) {
+    // ---- router: experts 4 * eb + wave for token t; logits go to every
+    // replica (inverted bits)
+    const int t = it / a.n_eb;
+    const int e = (it - t * a.n_eb) * kWaves + wave;
+    if (e < E)
+      router_wave<2 * NJG, true, true>(a.hidden + static_cast<size_t>(t) * H,
+                                       a.router_w + static_cast<size_t>(e) * H, H, 1, E, e,
+                                       ws.mlogits + static_cast<size_t>(t) * E, kFlagRep,
+                                       static_cast<size_t>(T) * E);
+    if (it == a.o_sgu - 1) {
+      // the last router item: top-k of every token (polling replica 0 of its
+      // logits), the route tables and the caller's ids / weights, then the
+      // route flag
+      const RouteSmem sm(smem, T, E, k);
+      select_tokens<true, true, true, false>(0, T, E, k, a.rsf, ws.mlogits, a.bias, ws,
+                                             a.ids_out, a.w_out, sm, err);
+      build_routes<true>(T, E, k, ws, sm);
+      wait_memory();
+      __syncthreads();
+      if (threadIdx.x < kFlagRep)
+        st_u32<true>(sy.line(kStepRoute + static_cast<int>(threadIdx.x)), 1u);
+    }
+    item_done(sy, it, -1);
+    return;
+  }
+  if (it < a.o_sdn) {
+    // ---- shared gate_up + SwiGLU: SwiGLU rows 8 * item + 2 * wave, +1
+    const int i0 = ((it - a.o_sgu) * kWaves + wave) * 2;
+    gate_up_wave<NJG, 1, true, E8>(a.hidden, a.sw13, a.sw13_scale, 0, H, a.Is, i0, T, nullptr, 0,
+                                   k, ws.act_s, a.limit);
+    item_done(sy, it, kStepSgu);
+    return;
+  }
+  if (it < a.o_rgu) {
+    // ---- shared down: rows RD * (4 * item + wave) .. +RD-1 of y_s, after
+    // every shared gate_up item (its weights stream meanwhile)
+    auto wait = [&]() {
+      wait_count(sy, kStepSgu, 1, static_cast<uint32_t>(a.sgu_n), kChainSpin, err);
+    };
+    down_wave<NJD, 1, true, E8, false, decltype(wait), RD>(
+        a.sw2, a.sw2_scale, 0, H, a.Is, ((it - a.o_sdn) * kWaves + wave) * RD, T, 0,
+        RouteIdentity{}, ws.act_s, ws.y_s, wait);
+    item_done(sy, it, -1);
+    return;
+  }
+  if (it < a.n_items) {
+    // ---- routed items: slot d's expert e, its route count n, first
+    // position base (and, at one token, its route j)
+    const bool gu = it < a.o_rdn;
+    const int u = gu ? it - a.o_rgu : it - a.o_rdn;
+    const int per = gu ? a.gu_per : a.dn_per;
+    const int d = u / per;
+    int e, n, base, j = 0;
+    if (T == 1) {
+      route_one_token(a, ws, reinterpret_cast<unsigned long long*>(smem), s_slot, err);
+      // clamped: only a selection on logits that never arrived (a wait that
+      // gave up, out then NaN) could leave a slot unset
+      e = min(max(s_slot[d], 0), E - 1);
+      j = min(max(s_slot[kMaxTopK + d], 0), k - 1);
+      n = 1;
+      base = d;
+    } else {
+      wait_route(sy, err);
+      const int32_t* rec = ws.slot_tab + static_cast<size_t>(d) * kSlotInts;
+      e = ld_i32<true>(rec);
+      n = ld_i32<true>(rec + 1);
+      base = ld_i32<true>(rec + 2);
+    }
+    if (gu) {
+      // gate_up + SwiGLU: SwiGLU rows 8 * tile + 2 * wave, +1
+      if (e >= 0)
+        gate_up_wave<NJG, 1, true, E8>(
+            a.hidden, a.w13 + static_cast<size_t>(e) * 2 * I * H, a.w13_scale,
+            static_cast<size_t>(e) * (2 * I / kBlock) * (H / kBlock), H, I,
+            (u - d * per) * kRowsGu + 2 * wave, n, T == 1 ? nullptr : ws.perm, base, k, ws.act,
+            a.limit);
+      item_done(sy, it, e >= 0 ? kStepSlot0 + d : -1);
+      return;
+    }
+    // down: rows RD * (4 * tile + wave) .. +RD-1 at route index t * k + j,
+    // the weights in flight while the slot's gate_up ends
+    if (e >= 0) {
+      auto wait = [&]() {
+        wait_count(sy, kStepSlot0 + d, 1, static_cast<uint32_t>(a.gu_per), kChainSpin, err);
+      };
+      down_wave<NJD, 1, true, E8, false, decltype(wait), RD>(
+          a.w2 + static_cast<size_t>(e) * H * I, a.w2_scale,
+          static_cast<size_t>(e) * (H / kBlock) * (I / kBlock), H, I,
+          ((u - d * per) * kWaves + wave) * RD, n, base,
+          RouteStep{T == 1 ? nullptr : ws.perm, j}, ws.act, ws.rows, wait);
+    }
+    item_done(sy, it, -1);
+    return;
+  }
+
+  // ---- the boundary (the last T * bnd_ns workgroups), after every other item
+  const int b = it - a.n_items;
+  const BndArgs bn{a.residual, a.gamma, a.out, a.residual_out, a.moe_out, H, k, a.Is, a.bnd_ns,
+                   a.eps, ws.mepi, err};
+  const StepTail tail{sy.line(kStepBnd), static_cast<uint32_t>(T * a.bnd_ns), ws.msync,
+                      step_sync_lines(a.dmax), ws.mlogits, kFlagRep * T * E,
+                      T * kMaxBndSlices};
+  boundary_slice<true>(bn, ws, b / a.bnd_ns, b % a.bnd_ns, [&]() {
+    wait_count(sy, kStepExit0, kSyncExitLines, static_cast<uint32_t>(a.n_items), kChainSpin, err);
+  }, tail);
 }
 
 template <int NJG, int NJD, bool E8>
@@ -260,9 +535,19 @@ hipError_t launch_t(const ChainArgs& a, const Workspace& ws, hipStream_t s, hipE
   return hipGetLastError();
 }
 
+template <int NJG, int NJD, bool E8>
+hipError_t step_launch_t(const StepArgs& a, const Workspace& ws, size_t smem, hipStream_t s,
+                         hipEvent_t evb, hipEvent_t eve) {
+  MOE_LAUNCH((decode_step_kernel<NJG, NJD, E8>), dim3(a.grid), dim3(kThreads), smem, s, evb, eve,
+             a, ws);
+  return hipGetLastError();
+}
+
 #define MOE_CHAIN_INST(NJD, E8)                                                              \
   template hipError_t launch_t<MOE_CHAIN_NJG, NJD, E8>(const ChainArgs&, const Workspace&,   \
-                                                        hipStream_t, hipEvent_t, hipEvent_t);
+                                                        hipStream_t, hipEvent_t, hipEvent_t); \
+  template hipError_t step_launch_t<MOE_CHAIN_NJG, NJD, E8>(                                 \
+      const StepArgs&, const Workspace&, size_t, hipStream_t, hipEvent_t, hipEvent_t);
 MOE_CHAIN_INST(1, false) MOE_CHAIN_INST(1, true)
 MOE_CHAIN_INST(2, false) MOE_CHAIN_INST(2, true)
 MOE_CHAIN_INST(3, false) MOE_CHAIN_INST(3, true)
@@ -329,6 +614,54 @@ hipError_t launch_expert_chain(const ChainArgs& a, const Workspace& ws, hipStrea
 #define X(G, D, E)          \
   case (G * 8 + D) * 2 + E: \
     return chain::launch_t<G, D, E>(a, ws, s, evb, eve);
+    MOE_CHAIN_ALL
+#undef X
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+void step_items(const LayerDims& d, StepArgs* a) {
+  a->T = d.T;
+  a->H = d.H;
+  a->E = d.E;
+  a->k = d.k;
+  a->I = d.I;
+  a->Is = d.Is;
+  a->e8m0 = d.e8m0 ? 1 : 0;
+  a->limit = d.limit;
+  a->rsf = d.rsf;
+  a->eps = d.eps;
+  a->n_eb = (d.E + chain::kWaves - 1) / chain::kWaves;
+  const int rd = chain::kWaves * chain::rows_dn_wave(chain_njd(d.I, d.Is));
+  a->sgu_n = d.Is ? d.Is / chain::kRowsGu : 0;
+  a->sdn_n = d.Is ? d.H / rd : 0;
+  a->gu_per = d.I / chain::kRowsGu;
+  a->dn_per = d.H / rd;
+  a->dmax = d.T * d.k < d.E ? d.T * d.k : d.E;
+  a->o_sgu = a->n_eb * d.T;
+  a->o_sdn = a->o_sgu + a->sgu_n;
+  a->o_rgu = a->o_sdn + a->sdn_n;
+  a->o_rdn = a->o_rgu + a->dmax * a->gu_per;
+  a->n_items = a->o_rdn + a->dmax * a->dn_per;
+  a->bnd_ns = (d.H + kBndCols - 1) / kBndCols;
+  a->grid = static_cast<uint32_t>(a->n_items + d.T * a->bnd_ns);
+}
+
+size_t step_smem_bytes(const LayerDims& d) { return route_smem_bytes(d.T, d.E, d.k); }
+
+hipError_t launch_decode_step(const StepArgs& a, const Workspace& ws, hipStream_t s,
+                              hipEvent_t evb, hipEvent_t eve) {
+  if (a.T < 1 || a.T > kChainMaxTokens || a.E < 1 || a.E > kStepMaxExperts || a.k < 1 ||
+      a.k > kMaxTopK || a.k > a.E || a.bnd_ns > kMaxBndSlices || a.dmax > chain::kMaxSlots ||
+      a.grid != static_cast<uint32_t>(a.n_items + a.T * a.bnd_ns) ||
+      !chain_supported(a.H, a.I, a.Is))
+    return hipErrorInvalidValue;
+  const size_t smem = route_smem_bytes(a.T, a.E, a.k);
+  switch (key(chain_njg(a.H), chain_njd(a.I, a.Is), a.e8m0 != 0)) {
+#define X(G, D, E)          \
+  case (G * 8 + D) * 2 + E: \
+    return chain::step_launch_t<G, D, E>(a, ws, smem, s, evb, eve);
     MOE_CHAIN_ALL
 #undef X
     default:

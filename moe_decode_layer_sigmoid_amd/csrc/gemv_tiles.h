@@ -276,10 +276,13 @@ constexpr int kRouterTokB = 2;  // tokens per register pass of a router wave
 // logits[t * E + e] = sum_h hidden[t, h] * router_w[e, h] in fp32.
 // The row stays in registers; tokens go in passes of kRouterTokB.
 // NJ2 = 16-byte chunks per lane = ceil(H / 512).
+// ENC: stored with inverted bits (load_logit); reps copies, rep_stride
+// floats apart (pollers spread over the copies).
 template <int NJ2, bool C = false, bool ENC = false>
 __device__ __forceinline__ void router_wave(const uint16_t* __restrict__ hidden,
                                             const uint16_t* __restrict__ row, int H, int T,
-                                            int E, int e, float* logits) {
+                                            int E, int e, float* logits, int reps = 1,
+                                            size_t rep_stride = 0) {
   const int lane = threadIdx.x & 63;
   const int nchunk = H / 8;
   uint4 wv[NJ2];
@@ -312,10 +315,9 @@ __device__ __forceinline__ void router_wave(const uint16_t* __restrict__ hidden,
     for (int q = 0; q < kRouterTokB; ++q) {
       if (t0 + q >= T) continue;
       const float v = wave_sum(acc[q]);
-      // ENC: stored with its bits inverted (see load_logit)
-      if (lane == 0)
-        st_f32<C>(logits + static_cast<size_t>(t0 + q) * E + e,
-                  ENC ? __uint_as_float(~__float_as_uint(v)) : v);
+      const float stored = ENC ? __uint_as_float(~__float_as_uint(v)) : v;
+      if (lane < reps)
+        st_f32<C>(logits + lane * rep_stride + static_cast<size_t>(t0 + q) * E + e, stored);
     }
   }
 }

@@ -35,11 +35,18 @@ struct Workspace {
   float* rows;         // [maxT * k, H]   routed down output, at route index t*k+j
   float* y_s;          // [maxT, H]       shared expert output
   uint32_t* counter;   // router arrival counters, router_cnt_words() (self-resetting)
-  uint32_t* sync;      // [sync_words(E)] counters of the fused kernel (self-resetting)
+  uint32_t* sync;      // [sync_words(E)] counters of the expert chain and grouped merged
+                       // launches (zeroed by the router launch before them); the error word
   float* zero_bias;    // [E] zeros: the router bias when the caller passes none
   int32_t* slot_tab;   // [E][kSlotInts] touched slot d: expert (-1: no expert), route
                        // count, first permuted position, -, first kSlotRoutes routes
-  float* epi_part;     // [maxT][kMaxBndSlices] boundary slices' sums of squares
+  float* epi_part;     // [maxT][kMaxBndSlices] boundary slices' sums of squares (inverted
+                       // bits; 0 = not published yet)
+  // State of the single-launch step (decode_step_kernel), left zeroed by
+  // every such launch for the next one:
+  uint32_t* msync;     // [step_sync_lines(dmax)] lines: route flag, counts, exit lines
+  float* mlogits;      // [min(maxT, kChainMaxTokens), E] logits, inverted bits (0 = not yet)
+  float* mepi;         // [min(maxT, kChainMaxTokens)][kMaxBndSlices] like epi_part
 };
 
 // Per-slot record the router leaves for the expert kernels, so that a
@@ -93,7 +100,6 @@ __host__ __device__ constexpr size_t router_cnt_words() {
   return static_cast<size_t>(kRouterMaxBlk + 1) * kSyncStride;
 }
 
-constexpr int kFusedMaxTokens = 16;
 // Up to this many tokens the MFMA path runs the shared expert's passes in the
 // routed experts' launches; above it (several 16-token passes, each streaming
 // the shared weights again) on a second stream, beside the routed launches.
@@ -103,6 +109,16 @@ constexpr int kMergeSharedMaxTokens = 64;
 // grouped): 1 token 46.5 / 74.2, 2: 75.3 / 87.0, 3: 103.1 / 109.9,
 // 4: 127.9 / 118.9, 8: 215.8 / 183.5, 16: 378.8 / 295.6.
 constexpr int kGroupedMinTokens = 4;
+// AUTO takes the single-launch step up to this many tokens (where it fits).
+// Measured on MI355X at the decode shape (H = 4096, E = 128, k = 8,
+// I = 1536), µs per step, single launch / router launch + expert chain:
+// 1 token 53.8 / 47.0, 2: 80.7 / 73.1, 3: 117.2 / 103.1.  A per-workgroup
+// timeline of the single launch showed why: every routed item there learns
+// its expert from coherent reads of the logits plus its own selection
+// (2.4-3 us), where an expert chain item reads the finished route tables
+// from L2 (1.1 us), and the routing delay (about 5 us) is more than the
+// shared expert's weights can fill.  So AUTO keeps the two launches.
+constexpr int kStepAutoMaxTokens = 0;
 // The same for a dense layer (no routed experts).  Its MFMA launches have
 // few tiles per 16-token pass (I_s / 64 gate_up and H / 64 down tiles with
 // the dense tile sizes), so they win only where the GEMV tiles' per-token
@@ -111,41 +127,11 @@ constexpr int kGroupedMinTokens = 4;
 // 100.3, 16: 160.0 / 106.7).
 constexpr int kDenseGroupedMinTokens = 8;
 
-// Arguments of the fused persistent kernel (see decode_fused.hip).
-struct FusedArgs {
-  const uint16_t* hidden;
-  const uint16_t* residual;
-  const uint16_t* router_w;
-  const float* bias;
-  const uint8_t* w13;
-  const void* w13_scale;
-  const uint8_t* w2;
-  const void* w2_scale;
-  const uint8_t* sw13;
-  const void* sw13_scale;
-  const uint8_t* sw2;
-  const void* sw2_scale;
-  const uint16_t* gamma;
-  uint16_t* out;
-  uint16_t* residual_out;
-  uint16_t* moe_out;  // nullable
-  int32_t* ids_out;
-  float* w_out;
-  int T, H, E, k, I, Is, e8m0;
-  float limit, rsf, eps;
-  // work-queue layout: item offsets and counts
-  int n_router, n_sgu, n_sdn, gu_per, dn_per, dmax;
-  int o_sgu, o_sdn, o_rgu;  // routed items follow o_rgu once the touched count is known
-  uint32_t grid;
-};
-
 // Arguments of the expert chain launch of the few-token GEMV path (see
 // experts_chain.hip): item offsets and counts, the grid (items + 1).
 constexpr int kChainMaxTokens = 16;
 constexpr int kBndCols = 2048;     // columns of one boundary workgroup (8 per thread)
 constexpr int kMaxBndSlices = 4;   // H <= 8192
-constexpr uint32_t kEpiEmpty = 0xffffffffu;  // an empty slot of Workspace::epi_part (a NaN
-                                             // no sum of squares takes)
 struct ChainArgs {
   const uint16_t* hidden;
   const uint16_t* residual;
@@ -166,6 +152,52 @@ struct ChainArgs {
   int bnd_ns;  // boundary workgroups per token (kBndCols columns each)
   uint32_t grid;
 };
+
+// Arguments of the single-launch step (experts_chain.hip, decode_step_kernel):
+// router items, the shared expert's gate_up and down items, the touched
+// slots' gate_up and down items, the boundary slices, in this index order.
+struct StepArgs {
+  const uint16_t* hidden;
+  const uint16_t* residual;
+  const uint16_t* router_w;
+  const float* bias;  // never null (the zero bias stands in)
+  const uint8_t* w13;
+  const void* w13_scale;
+  const uint8_t* w2;
+  const void* w2_scale;
+  const uint8_t* sw13;
+  const void* sw13_scale;
+  const uint8_t* sw2;
+  const void* sw2_scale;
+  const uint16_t* gamma;
+  uint16_t* out;
+  uint16_t* residual_out;
+  uint16_t* moe_out;  // nullable
+  int32_t* ids_out;   // nullable
+  float* w_out;       // nullable
+  int T, H, E, k, I, Is, e8m0;
+  float limit, rsf, eps;
+  int n_eb;                  // router expert blocks (4 experts each); n_eb * T router items
+  int sgu_n, sdn_n;          // shared gate_up and down items
+  int gu_per, dn_per, dmax;  // items per slot; slots
+  int o_sgu, o_sdn, o_rgu, o_rdn, n_items;
+  int bnd_ns;
+  uint32_t grid;
+};
+
+// Most experts the single-launch step routes (its top-k holds at most four
+// keys per lane; wider routers take the router launch and the chain).
+constexpr int kStepMaxExperts = 256;
+
+// Lines of Workspace::msync (one 128-byte line each).
+enum : int {
+  kStepRoute = 0,                     // route flag, kFlagRep replicas (T > 1)
+  kStepSgu = kStepRoute + kFlagRep,   // shared gate_up items done
+  kStepExit0 = kStepSgu + 1,          // kSyncExitLines lines: items done
+  kStepBnd = kStepExit0 + kSyncExitLines,  // boundary slices done
+  kStepSlot0 = kStepBnd + 1           // gate_up items done, one line per slot
+};
+__host__ __device__ constexpr int step_sync_lines(int dmax) { return kStepSlot0 + dmax; }
 
 // Arguments of the grouped path's merged gate_up + down launch (see
 // experts_mfma.hip, grouped_chain_kernel).
@@ -233,19 +265,19 @@ hipError_t launch_grouped_chain(const LayerDims& d, const void* hidden, const vo
                                 const void* sw2_scale, const Workspace& ws, hipStream_t s,
                                 hipEvent_t evb = nullptr, hipEvent_t eve = nullptr);
 
-// Fused persistent kernel of the whole step (T <= kFusedMaxTokens).
-int fused_nj(int H, int I, int Is);
-int fused_blocks_per_cu(int nj, bool e8m0);
-void fused_items(const LayerDims& d, FusedArgs* a);
-hipError_t launch_decode_fused(const FusedArgs& a, const Workspace& ws, hipStream_t s,
-                               hipEvent_t evb = nullptr, hipEvent_t eve = nullptr);
-
 // Shared down, routed gate_up, routed down and the boundary in one launch
 // (T <= kChainMaxTokens; H <= 8192; I and I_s <= 4096).
 bool chain_supported(int H, int I, int Is);
 void chain_items(const LayerDims& d, ChainArgs* a);
 hipError_t launch_expert_chain(const ChainArgs& a, const Workspace& ws, hipStream_t s,
                                hipEvent_t evb = nullptr, hipEvent_t eve = nullptr);
+
+// The whole step in one launch: the router items and the chain's items
+// (T <= kChainMaxTokens, E <= kStepMaxExperts, chain_supported).
+void step_items(const LayerDims& d, StepArgs* a);
+size_t step_smem_bytes(const LayerDims& d);
+hipError_t launch_decode_step(const StepArgs& a, const Workspace& ws, hipStream_t s,
+                              hipEvent_t evb = nullptr, hipEvent_t eve = nullptr);
 
 // Weighted combine + shared + residual, RMSNorm * gamma, bf16 outputs.
 // moe_out (nullable): also the finalized MoE output (before the residual).

@@ -92,15 +92,15 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
   // ---- phase 3: route tables (read by later kernels)
   build_routes<false>(T, E, k, ws, sm);
   // The counters of the launch that follows (the split path's expert chain)
-  // start from zero and its boundary slots empty: it never resets them
-  // itself.  The error word stays.
+  // start from zero and its boundary slots empty (zero): it never resets
+  // them itself.  The error word stays.
   const int lines = sync_lines(T * k < E ? T * k : E);
   for (int i = threadIdx.x; i < lines; i += kThreads)
     if (i != kSyncError)
       __hip_atomic_store(ws.sync + static_cast<size_t>(i) * kSyncStride, 0u, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   for (int i = threadIdx.x; i < T * kMaxBndSlices; i += kThreads)
-    __hip_atomic_store(reinterpret_cast<uint32_t*>(ws.epi_part) + i, kEpiEmpty, __ATOMIC_RELAXED,
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(ws.epi_part) + i, 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -25,6 +25,42 @@ __device__ __forceinline__ float load_logit(const float* p) {
   return ENC ? __uint_as_float(~__float_as_uint(v)) : v;
 }
 
+// Polls before a wait for logits gives up (a poll is a memory round trip
+// plus a short sleep; a legitimate wait lasts microseconds).
+constexpr uint32_t kLogitPolls = 1u << 17;
+
+// Lane l's logits of experts l + 64 i (i < N) of one token into sc (clamped
+// index past E).  POLL (encoded logits only): the wave repeats the loads
+// until every logit of the token has been stored (none reads 0); after
+// kLogitPolls rounds it sets *err and goes on.  Then ENC decodes them.
+template <bool C, bool ENC, bool POLL, int N>
+__device__ __forceinline__ void load_token_logits(const float* logits, int E, float* sc,
+                                                  uint32_t* err) {
+  static_assert(!POLL || ENC, "only encoded logits can be polled");
+  const int lane = threadIdx.x & 63;
+  uint32_t polls = 0;
+  for (;;) {
+    bool have = true;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int e = lane + 64 * i;
+      sc[i] = ld_f32<C>(logits + (e < E ? e : E - 1));
+      have = have && (e >= E || __float_as_uint(sc[i]) != 0u);
+    }
+    if (!POLL || __builtin_amdgcn_ballot_w64(!have) == 0) break;  // uniform
+    if (++polls == kLogitPolls) {
+      if (lane == 0)
+        __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (ENC) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) sc[i] = __uint_as_float(~__float_as_uint(sc[i]));
+  }
+}
+
 __device__ __forceinline__ uint32_t ordered_bits(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -96,10 +132,10 @@ __device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory")
 // NS = slots per lane, a power of two >= ceil(E / 64) (slots past E hold
 // key 0), so that every loop over a lane's keys unrolls with constant
 // indices.
-template <bool C, int NS, bool ENC = false>
+template <bool C, int NS, bool ENC = false, bool POLL = false>
 __device__ inline void select_token_ns(const float* logits, const float* bias, int E, int k,
                                        float rsf, unsigned long long* sel, int* pick_id,
-                                       float* pick_w) {
+                                       float* pick_w, uint32_t* err = nullptr) {
   const int lane = threadIdx.x & 63;
   unsigned long long* lmax = sel;
   unsigned long long* cand = sel + 64;
@@ -112,10 +148,9 @@ __device__ inline void select_token_ns(const float* logits, const float* bias, i
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
     const int e = lane + 64 * i;
-    const int ee = e < E ? e : E - 1;
-    sc[i] = load_logit<C, ENC>(logits + ee);
-    bv[i] = bias[ee];
+    bv[i] = bias[e < E ? e : E - 1];
   }
+  load_token_logits<C, ENC, POLL, NS>(logits, E, sc, err);
   unsigned long long mx = 0ull;
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
@@ -217,21 +252,28 @@ __device__ __forceinline__ void wave_max_pair(uint32_t& hi, uint32_t& lo) {
 // slot that is taken or past E (a real key never maps to 0).  Each round
 // takes every lane's best slot (strict >, so the lower slot, i.e. the lower
 // id, wins a tie), then a DPP wave maximum of (key, ~id).
-template <bool C, bool ENC = false>
+template <bool C, bool ENC = false, bool POLL = false>
 __device__ inline void select_token_rounds(const float* logits, const float* bias, int E, int k,
-                                    float rsf, int* pick_id, float* pick_w) {
+                                    float rsf, int* pick_id, float* pick_w,
+                                    uint32_t* err = nullptr) {
   const int lane = threadIdx.x & 63;
   const int ns = (E + 63) >> 6;
   float sc[16];
   uint32_t kb[16];
   // Branch-free loads (clamped index).
+  float bv[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int e = lane + 64 * i;
-    const int ee = e < E ? e : E - 1;
-    const float s = sigmoidf_(load_logit<C, ENC>(logits + ee));
+    bv[i] = bias[e < E ? e : E - 1];
+  }
+  load_token_logits<C, ENC, POLL, 16>(logits, E, sc, err);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = lane + 64 * i;
+    const float s = sigmoidf_(sc[i]);
     sc[i] = s;
-    kb[i] = e < E ? ordered_bits(s + bias[ee]) : 0u;
+    kb[i] = e < E ? ordered_bits(s + bv[i]) : 0u;
   }
   float ssum = 0.f, my_s = 0.f;
   int my_id = -1;
@@ -274,19 +316,22 @@ __device__ inline void select_token_rounds(const float* logits, const float* bia
   }
 }
 
-template <bool C, bool ENC = false>
+// WIDE = false leaves out the path for more than 256 experts (its sixteen
+// keys and scores per lane raise a kernel's register count; a caller that
+// sets it must not pass E > 256).
+template <bool C, bool ENC = false, bool POLL = false, bool WIDE = true>
 __device__ inline void select_token(const float* logits, const float* bias, int E, int k,
                                     float rsf, unsigned long long* sel, int* pick_id,
-                                    float* pick_w) {
+                                    float* pick_w, uint32_t* err = nullptr) {
   const int ns = (E + 63) >> 6;  // uniform
   if (ns <= 1)
-    select_token_ns<C, 1, ENC>(logits, bias, E, k, rsf, sel, pick_id, pick_w);
+    select_token_ns<C, 1, ENC, POLL>(logits, bias, E, k, rsf, sel, pick_id, pick_w, err);
   else if (ns <= 2)
-    select_token_ns<C, 2, ENC>(logits, bias, E, k, rsf, sel, pick_id, pick_w);
-  else if (ns <= 4)
-    select_token_ns<C, 4, ENC>(logits, bias, E, k, rsf, sel, pick_id, pick_w);
+    select_token_ns<C, 2, ENC, POLL>(logits, bias, E, k, rsf, sel, pick_id, pick_w, err);
+  else if (!WIDE || ns <= 4)
+    select_token_ns<C, 4, ENC, POLL>(logits, bias, E, k, rsf, sel, pick_id, pick_w, err);
   else
-    select_token_rounds<C, ENC>(logits, bias, E, k, rsf, pick_id, pick_w);
+    select_token_rounds<C, ENC, POLL>(logits, bias, E, k, rsf, pick_id, pick_w, err);
 }
 
 // LDS bytes select_and_route needs (16-byte aligned base).
@@ -321,17 +366,19 @@ struct RouteSmem {
 // Top-k of tokens [t_begin, t_end), one wave per token.  Writes ws.ids and
 // ws.weights (coherent stores when C), the optional caller outputs and the
 // LDS copy of the ids (route r = t*k + j).
-template <bool C, bool ENC = false>
+template <bool C, bool ENC = false, bool POLL = false, bool WIDE = true>
 __device__ inline void select_tokens(int t_begin, int t_end, int E, int k, float rsf,
                                      const float* logits, const float* bias, const Workspace& ws,
-                                     int32_t* ids_out, float* w_out, const RouteSmem& sm) {
+                                     int32_t* ids_out, float* w_out, const RouteSmem& sm,
+                                     uint32_t* err = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int* s_ids = sm.ids;
   unsigned long long* sel = sm.sel + static_cast<size_t>(wave) * kSelWaveWords;
   for (int t = t_begin + wave; t < t_end; t += kRouteThreads / 64) {
     int id = 0;
     float w = 0.f;
-    select_token<C, ENC>(logits + static_cast<size_t>(t) * E, bias, E, k, rsf, sel, &id, &w);
+    select_token<C, ENC, POLL, WIDE>(logits + static_cast<size_t>(t) * E, bias, E, k, rsf, sel,
+                                     &id, &w, err);
     if (lane < k) {
       const int r = t * k + lane;
       s_ids[r] = id;

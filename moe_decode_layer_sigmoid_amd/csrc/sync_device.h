@@ -78,9 +78,10 @@ __device__ __forceinline__ void bump(const Sync& sy, int line) {
 // Waits until the sum of the counters on lines [first, first + n) (n <= 64)
 // reaches `target`: wave 0 polls them, one lane per line, then the
 // workgroup meets at a barrier.  Bounded by `limit` polls (then the error
-// word is set and the wait gives up).  Called by every thread.
+// word -- `err`, or line kSyncError of sy -- is set and the wait gives up).
+// Called by every thread.
 __device__ __forceinline__ void wait_count(const Sync& sy, int first, int n, uint32_t target,
-                                           uint32_t limit) {
+                                           uint32_t limit, uint32_t* err = nullptr) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const uint32_t* p = sy.line(first + (lane < n ? lane : 0));
@@ -94,7 +95,7 @@ __device__ __forceinline__ void wait_count(const Sync& sy, int first, int n, uin
       __builtin_amdgcn_s_sleep(2);
       if (++polls == limit) {
         if (lane == 0)
-          __hip_atomic_fetch_or(sy.line(kSyncError), 1u, __ATOMIC_RELAXED,
+          __hip_atomic_fetch_or(err ? err : sy.line(kSyncError), 1u, __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_AGENT);
         break;
       }

@@ -74,8 +74,8 @@ def run_layer(plan, dev, T, alias_residual=False, stream=None, keep_device=False
              gamma=dev["gamma"], out=out, residual_out=res_out, topk_ids=ids, topk_weights=w,
              moe_out=moe)
     torch.cuda.synchronize()
-    # the persistent launches (the fused kernel, the split path's expert chain)
-    # wait on each other's workgroups with bounded waits
+    # the single-launch step, the expert chain and the grouped merged launch
+    # hand work between workgroups through bounded waits
     assert not plan.check_waits(), "a bounded wait gave up"
     got = dict(out=bf16_to_np(out), residual_out=bf16_to_np(res_out), moe=bf16_to_np(moe),
                ids=ids.cpu().numpy(),

@@ -49,7 +49,7 @@ def test_tiny_layer(c_oracle):
 
 @pytest.mark.parametrize("name", ["decode_t1", "decode_t16"])
 @pytest.mark.parametrize("path", [md.PATH_GEMV, md.PATH_GEMV_SPLIT, md.PATH_GROUPED],
-                         ids=["fused", "split", "grouped"])
+                         ids=["step", "split", "grouped"])
 def test_decode_layers_full(name, path, c_oracle):
     inp, got, err = _case(WORKLOADS[name], c_oracle, path=path)
     if name == "decode_t16":
@@ -107,13 +107,17 @@ SMALL = [
     # every limit at once: 256 tokens, 1024 experts, k = 16 (4096 routes, the
     # routing step's largest LDS carve-up and packed route scan)
     (256, 256, 1024, 16, 128, 128, "fp32"),
+    # the single-launch step's widest router (four keys per lane) at one and
+    # two tokens
+    (1, 512, 256, 8, 256, 256, "e8m0"),
+    (2, 384, 150, 6, 128, 0, "fp32"),
 ]
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[str(c) for c in SMALL])
 @pytest.mark.parametrize("with_bias", [False, True])
 @pytest.mark.parametrize("path", [md.PATH_GEMV, md.PATH_GEMV_SPLIT, md.PATH_GROUPED],
-                         ids=["fused", "split", "grouped"])
+                         ids=["step", "split", "grouped"])
 def test_small_layers(case, with_bias, path, c_oracle):
     T, H, E, k, I, Is, fmt = case
     sh = LayerShape(T=T, H=H, E=E, k=k, I=I, Is=Is, scale_fmt=fmt, tag=300 + sum(case[:6]))
@@ -122,7 +126,7 @@ def test_small_layers(case, with_bias, path, c_oracle):
 
 @pytest.mark.parametrize("T", [1, 3, 16, 40])
 def test_paths_agree(T, c_oracle):
-    """The fused persistent kernel, the separate GEMV kernels and the MFMA
+    """The single-launch step, the separate GEMV kernels and the MFMA
     kernels compute the same layer (same ids, outputs within the oracle
     tolerance of each other)."""
     sh = WORKLOADS["decode_t16"].replace(T=T, H=2048, I=768, Is=512, tag=310 + T)
@@ -218,7 +222,7 @@ def test_dense_layer(T, fmt, c_oracle):
 
 @pytest.mark.parametrize("T", [1, 5, 16])
 @pytest.mark.parametrize("path", [md.PATH_GEMV, md.PATH_GEMV_SPLIT, md.PATH_GROUPED],
-                         ids=["fused", "split", "grouped"])
+                         ids=["step", "split", "grouped"])
 def test_alternating_inputs_on_one_plan(path, T, c_oracle):
     """Two different layers (other weights, other tokens) run in turn on one
     plan: every run matches its own oracle, so nothing a run leaves in the
@@ -234,8 +238,25 @@ def test_alternating_inputs_on_one_plan(path, T, c_oracle):
     plan.close()
 
 
+def test_step_token_counts_in_turn(c_oracle):
+    """The single-launch step leaves its counters, flags, logits and
+    boundary slots zeroed for the next launch; runs of 1, 3, 16, 1, 2 and 1
+    tokens in turn on one plan (other layers' inputs each time) each match
+    their own oracle, with the route tables of the multi-token runs and the
+    self-routed one-token runs agreeing with the oracle's selection."""
+    base = WORKLOADS["decode_t16"].replace(H=1024, I=256, Is=256, E=64, tag=307)
+    plan = make_plan(base.replace(T=16), path=md.PATH_GEMV)
+    for i, T in enumerate([1, 3, 16, 1, 2, 1]):
+        sh = base.replace(T=T, tag=307 + i)
+        inp = make_layer(sh, with_bias=(i % 2 == 0), bias_std=0.1)
+        assert plan.path_for(T) == md.PATH_GEMV
+        got = run_layer(plan, to_device(inp), T)
+        check_layer(inp, got, c_oracle=c_oracle)
+    plan.close()
+
+
 @pytest.mark.parametrize("path", [md.PATH_GEMV, md.PATH_GEMV_SPLIT, md.PATH_GROUPED],
-                         ids=["fused", "split", "grouped"])
+                         ids=["step", "split", "grouped"])
 def test_residual_alias_and_determinism(path, c_oracle):
     sh = WORKLOADS["decode_t16"].replace(H=2048, I=512, Is=512, tag=303)
     inp = make_layer(sh)
@@ -316,7 +337,7 @@ def _graph_vs_eager(sh, path):
                                         (md.PATH_GROUPED, 80, 1024, 512),
                                         (md.PATH_GROUPED, 24, 2304, 640),
                                         (md.PATH_GROUPED, 80, 2304, 640)],
-                         ids=["fused", "split", "grouped", "grouped-side-stream",
+                         ids=["step", "split", "grouped", "grouped-side-stream",
                               "grouped-wide", "grouped-wide-side-stream"])
 def test_graph_replay_matches_eager(path, T, H, I, c_oracle):
     """One run captured into a HIP graph, replayed several times with eager
