@@ -94,6 +94,12 @@ size_t layout(const moe_decode_desc& d, char* base, moe::Workspace* ws,
   w.msync = reinterpret_cast<uint32_t*>(take(moe::step_sync_lines(dmax_s) * moe::kSyncStride * 4));
   w.mlogits = reinterpret_cast<float*>(take(moe::kFlagRep * Ts * E * 4));
   w.mepi = reinterpret_cast<float*>(take(Ts * moe::kMaxBndSlices * 4));
+  // the matrix-core router's counters (many tokens only)
+  const bool rmfma = T >= moe::kRouterMfmaMinTokens && E > 0;
+  w.rcnt = reinterpret_cast<uint32_t*>(
+      take(rmfma ? moe::router_mfma_count_lines(static_cast<int>(T), static_cast<int>(E)) *
+                       moe::kSyncStride * 4
+                 : 0));
   if (state_bytes) *state_bytes = off;
   w.logits = reinterpret_cast<float*>(take(T * E * 4));
   w.ids = reinterpret_cast<int32_t*>(take(T * k * 4));
@@ -109,6 +115,12 @@ size_t layout(const moe_decode_desc& d, char* base, moe::Workspace* ws,
   w.rows = reinterpret_cast<float*>(take(T * k * H * 4));
   w.y_s = reinterpret_cast<float*>(take(T * H * 4));
   w.slot_tab = reinterpret_cast<int32_t*>(take(E * moe::kSlotInts * 4));
+  w.rpart = reinterpret_cast<float*>(
+      take(rmfma ? static_cast<size_t>(moe::router_mfma_slices(static_cast<int>(T),
+                                                               static_cast<int>(E),
+                                                               static_cast<int>(H))) *
+                       E * moe::router_mfma_tokens_padded(static_cast<int>(T)) * 4
+                 : 0));
   if (ws) *ws = w;
   return off;
 }
@@ -393,9 +405,17 @@ static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t 
   // GROUPED: router, the projections, the boundary.  Up to
   // kMergeSharedMaxTokens tokens the shared expert's passes are extra rows of
   // the routed launches; above that they run on the side stream, forked once
-  // the router is queued and joined before the boundary.
-  step(moe::launch_router(d, a->hidden, a->router_w, static_cast<const float*>(bias), p->ws,
-                          a->topk_ids, a->topk_weights, nullptr, nullptr, s));
+  // the router is queued and joined before the boundary.  Many tokens take
+  // the matrix-core router.
+  if (T >= moe::kRouterMfmaMinTokens)
+    step(moe::launch_router_mfma(
+        d, a->hidden, a->router_w, static_cast<const float*>(bias), p->ws,
+        moe::router_mfma_tokens_padded(p->desc.max_tokens),
+        T <= moe::kMergeSharedMaxTokens ? moe::sync_lines(T * d.k < d.E ? T * d.k : d.E) : 0,
+        a->topk_ids, a->topk_weights, s));
+  else
+    step(moe::launch_router(d, a->hidden, a->router_w, static_cast<const float*>(bias), p->ws,
+                            a->topk_ids, a->topk_weights, nullptr, nullptr, s));
   if (err != hipSuccess) return MOE_DECODE_ERR_HIP;
   const bool side = has_shared && T > moe::kMergeSharedMaxTokens;
   const int rows = side ? moe::kRoutedRows : moe::kAllRows;

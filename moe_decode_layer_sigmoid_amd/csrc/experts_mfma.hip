@@ -658,7 +658,7 @@ bool grouped_chain_supported(const LayerDims& d) {
   // gate_up tiles; the shared passes fit the flag lines
   return d.T <= kMergeSharedMaxTokens && d.H % (kWaves * 16 * kNsDn) == 0 &&
          d.I % (kWaves * 8 * kNsGu) == 0 && d.Is % (kWaves * 8 * kNsGu) == 0 &&
-         kNsDn * kWaves * 16 == 256 && shared_rows(d) <= kNumFlags * kFlagRep &&
+         kNsDn * kWaves * 16 == 256 && shared_rows(d) <= kSyncSlot0 - kSyncFlags &&
          kLdsGu == static_cast<size_t>(kWaves) * kUDn * kNsDn * kSubtileBlock;
 }
 

@@ -47,6 +47,10 @@ struct Workspace {
   uint32_t* msync;     // [step_sync_lines(dmax)] lines: route flag, counts, exit lines
   float* mlogits;      // [min(maxT, kChainMaxTokens), E] logits, inverted bits (0 = not yet)
   float* mepi;         // [min(maxT, kChainMaxTokens)][kMaxBndSlices] like epi_part
+  // The matrix-core router (many tokens): partial logits [slices][E][Tp]
+  // and its arrival counters (one line each, self-resetting).
+  float* rpart;
+  uint32_t* rcnt;
 };
 
 // Per-slot record the router leaves for the expert kernels, so that a
@@ -55,36 +59,23 @@ struct Workspace {
 constexpr int kSlotInts = 16;
 constexpr int kSlotRoutes = 12;
 
-// Counters and flags of the fused kernel in Workspace::sync, one 128-byte
-// line each: atomics and polls on one line serialise, separate lines proceed
-// in parallel.  Producers bump a counter (only producers touch it); the one
-// that completes it sets a flag replicated over kFlagRep lines, and waiting
-// workgroups poll the replica of their own (so no line is polled by many).
+// Counters and flags in Workspace::sync, one 128-byte line each: atomics and
+// polls on one line serialise, separate lines proceed in parallel.  Lines:
+// the sticky error word; the exit lines of the expert chain launch; lines
+// kSyncFlags + y for the grouped merged launch's shared-expert rows; one
+// line per touched slot (its gate_up items done).  Waiting workgroups poll
+// replicas of a flag (kFlagRep lines) so that no line is polled by many.
 constexpr int kSyncStride = 32;  // uint32 words per line
-constexpr int kFlagRep = 8;      // replicas of every flag
+constexpr int kFlagRep = 8;      // replicas of a polled flag
 enum : int {
-  kSyncRouterCnt = 0,   // router items done
-  kSyncSguCnt = 1,      // shared gate_up tiles done
-  kSyncSdnCnt = 2,      // shared down tiles done
-  kSyncDnSlots = 3,     // touched experts whose down tiles are all done
   kSyncError = 4,       // sticky: set when a bounded wait gave up
-  kSyncExit0 = 5,       // kSyncExitLines first-level exit counters
+  kSyncExit0 = 5,       // kSyncExitLines exit counters
   kSyncExitLines = 8,
-  kSyncExitTop = kSyncExit0 + kSyncExitLines,
-  kSyncFlags = 16,      // global flags, kFlagRep lines each:
-  kFlagRoute = 0,       //   route tables ready
-  kFlagSgu = 1,         //   shared gate_up done
-  kFlagSdn = 2,         //   shared down done
-  kFlagDnAll = 3,       //   every touched expert's down done
-  kNumFlags = 4,
-  kSyncSlot0 = kSyncFlags + kNumFlags * kFlagRep,  // per touched-expert slot:
-  kSlotLines = 2 + kFlagRep                        //   gate_up count, down count, gate_up flag
+  kSyncFlags = 16,      // lines of the grouped merged launch's shared rows
+  kSyncSlot0 = 48,      // per touched slot: gate_up items done
 };
-__host__ __device__ constexpr int sync_flag(int f) { return kSyncFlags + f * kFlagRep; }
-__host__ __device__ constexpr int sync_gu_cnt(int d) { return kSyncSlot0 + d * kSlotLines; }
-__host__ __device__ constexpr int sync_dn_cnt(int d) { return kSyncSlot0 + d * kSlotLines + 1; }
-__host__ __device__ constexpr int sync_gu_flag(int d) { return kSyncSlot0 + d * kSlotLines + 2; }
-__host__ __device__ constexpr int sync_lines(int slots) { return kSyncSlot0 + slots * kSlotLines; }
+__host__ __device__ constexpr int sync_gu_cnt(int d) { return kSyncSlot0 + d; }
+__host__ __device__ constexpr int sync_lines(int slots) { return kSyncSlot0 + slots; }
 __host__ __device__ constexpr size_t sync_words(int E) {
   return static_cast<size_t>(sync_lines(E)) * kSyncStride;
 }
@@ -230,6 +221,21 @@ hipError_t launch_router(const LayerDims& d, const void* hidden, const void* rou
                          const float* bias, const Workspace& ws, int32_t* ids_out,
                          float* weights_out, const void* sw13, const void* sw13_scale,
                          hipStream_t s, hipEvent_t evb = nullptr, hipEvent_t eve = nullptr);
+
+// The router for many tokens on the matrix cores (logits as 16 x 64 MFMA
+// tiles over 512-column slices of the contraction), then the same top-k and
+// route tables; no shared-expert tiles.  Tp_alloc: the token stride of
+// ws.rpart (router_mfma_tokens_padded of the plan's max tokens).
+// zero_lines: lines of ws.sync the launch that follows expects at zero.
+int router_mfma_slices(int T, int E, int H);
+int router_mfma_tokens_padded(int T);
+int router_mfma_count_lines(int T, int E);
+hipError_t launch_router_mfma(const LayerDims& d, const void* hidden, const void* router_w,
+                              const float* bias, const Workspace& ws, int Tp_alloc,
+                              int zero_lines, int32_t* ids_out, float* weights_out,
+                              hipStream_t s);
+// The matrix-core router takes over from this many tokens.
+constexpr int kRouterMfmaMinTokens = 17;
 
 // gate_up + clamped SwiGLU (GEMV) of the touched experts (one grid row
 // each; the shared expert's runs in the router launch).

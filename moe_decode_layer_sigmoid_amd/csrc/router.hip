@@ -23,6 +23,7 @@
 #include "gemv_tiles.h"
 #include "launch.h"
 #include "routing_device.h"
+#include "sync_device.h"
 
 namespace moe {
 namespace {
@@ -111,7 +112,205 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
 // kRouterTokBlk (blocks of 2 measured slower at 64 and 128 tokens).
 int router_block_tokens(int T) { return T <= 16 ? 1 : kRouterTokBlk; }
 
+// ---------------------------------------------------------------------------
+// The router for many tokens on the matrix cores.  The logits are a small
+// GEMM, x [T, H] . W_r^T [H, E]; read one row at a time per wave (above),
+// every wave re-reads its block's token rows, which at 128 tokens and
+// H = 6144 moves hundreds of MB through L2.  Here each workgroup computes a
+// tile of 16 tokens x 64 experts (one v_mfma_f32_16x16x32_bf16 per wave per
+// 32 columns: bf16 products are exact, sums fp32) over one slice of the
+// contraction, so each operand row is read once per tile.  Phases:
+//   1 partials   workgroup (expert tile, token tile, slice): the tile's
+//                partial logits to ws.rpart[slice][expert][token]
+//   2 logits     the last slice of a (token tile, expert tile) to finish
+//                sums the slices in slice order (deterministic) into
+//                ws.logits
+//   3 top-k      that workgroup then waits for the token tile's other
+//                expert tiles (every workgroup of the launch is resident:
+//                the grid is capped at kRtMaxGrid) and ranks its share of
+//                the tile's tokens, one token per wave while the share
+//                allows
+//   4 routes     the last of those to finish builds the route tables and
+//                empties the counters of the launch that follows
+// The MFMA takes any one-to-one assignment of contraction columns to lanes
+// as long as both operands use it: lane (g, c) holds, for steps 2j and
+// 2j + 1, columns 64 j + 16 g + [0, 8) and [8, 16) of its row, so that it
+// loads 32 contiguous bytes per two steps (the four lanes of a row cover a
+// whole 128-byte line).
+// Counts are arrival counters (one 128-byte line each) in ws.rcnt that are
+// reset once nothing reads them; partials and logits are handed over with
+// write-through stores, read after the count that covers them.
+constexpr int kRtTok = 16;     // tokens per tile (MFMA rows)
+constexpr int kRtExp = 64;     // experts per workgroup (16 per wave)
+constexpr int kRtSteps = 16;   // MFMA steps (32 columns each) per round of loads
+constexpr int kRtMaxGrid = 384;  // workgroups: all resident at once (2 or more per CU)
+constexpr uint32_t kRtSpin = 1u << 17;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kThreads) void router_mfma_kernel(
+    const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ router_w,
+    const float* __restrict__ bias, int T, int H, int E, int k, float rsf, int S, int Ks,
+    int Tp, int zero_lines, Workspace ws, int32_t* __restrict__ ids_out,
+    float* __restrict__ w_out) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int s_last;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int et = blockIdx.x, tt = blockIdx.y, sl = blockIdx.z;
+  const int n_et = gridDim.x, n_tt = gridDim.y;
+  const int t0 = tt * kRtTok;
+  const int e0 = et * kRtExp + wave * 16;
+  uint32_t* err = ws.sync + kSyncError * kSyncStride;
+
+  // ---- phase 1: partial logits of tokens t0.., experts e0.. over the slice
+  if (e0 < E) {  // uniform per wave
+    const int kb = sl * Ks;
+    const int nst = (min(H, kb + Ks) - kb) / 32;  // even: H and Ks are multiples of 64
+    // rows past T or E repeat the last one (loads stay in bounds; never stored)
+    const uint16_t* xa = hidden + static_cast<size_t>(min(t0 + c, T - 1)) * H + kb + 16 * g;
+    const uint16_t* wb = router_w + static_cast<size_t>(min(e0 + c, E - 1)) * H + kb + 16 * g;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int r0 = 0; r0 < nst; r0 += kRtSteps) {
+      uint4 av[kRtSteps], bv[kRtSteps];
+#pragma unroll
+      for (int i = 0; i < kRtSteps; ++i) {
+        // step i of the round: columns 64 (i / 2) + 16 g + 8 (i % 2), clamped
+        const int st = min(r0 + i, nst - 1);
+        const int col = 64 * (st >> 1) + 8 * (st & 1);
+        av[i] = *reinterpret_cast<const uint4*>(xa + col);
+        bv[i] = *reinterpret_cast<const uint4*>(wb + col);
+      }
+#pragma unroll
+      for (int i = 0; i < kRtSteps; ++i)
+        if (r0 + i < nst)  // uniform
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[i]),
+                                                        __builtin_bit_cast(bf16x8_t, bv[i]),
+                                                        acc, 0, 0, 0);
+    }
+    // lane holds tokens t0 + 4g .. +3 of expert e0 + c
+    if (e0 + c < E)
+      st_f32x4<true>(ws.rpart + (static_cast<size_t>(sl) * E + e0 + c) * Tp + t0 + 4 * g,
+                     make_float4(acc[0], acc[1], acc[2], acc[3]));
+  }
+  wait_memory();
+  __syncthreads();
+  uint32_t* cnt1 = ws.rcnt + static_cast<size_t>(tt * n_et + et) * kSyncStride;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(cnt1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             static_cast<uint32_t>(S) - 1;
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- phase 2: the tile's logits, slices summed in slice order; thread:
+  // expert et * 64 + tid / 4, tokens t0 + 4 (tid % 4) .. +3
+  if (threadIdx.x == 0) __hip_atomic_store(cnt1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  {
+    const int e = et * kRtExp + static_cast<int>(threadIdx.x >> 2);
+    const int tq = t0 + 4 * static_cast<int>(threadIdx.x & 3);
+    if (e < E) {
+      float4 v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)  // S <= 16; clamped, masked below
+        v[i] = *reinterpret_cast<const float4*>(
+            ws.rpart + (static_cast<size_t>(i < S ? i : S - 1) * E + e) * Tp + tq);
+      float4 sum = v[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i)
+        if (i < S) {
+          sum.x += v[i].x; sum.y += v[i].y; sum.z += v[i].z; sum.w += v[i].w;
+        }
+      const float r[4] = {sum.x, sum.y, sum.z, sum.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (tq + i < T) st_f32<true>(ws.logits + static_cast<size_t>(tq + i) * E + e, r[i]);
+    }
+  }
+
+  // ---- phase 3: once every expert tile of the token tile has its logits,
+  // this workgroup ranks tokens t0 + et, t0 + et + n_et, ... (one per wave)
+  uint32_t* cnt2 = ws.rcnt + static_cast<size_t>(n_tt * n_et + tt) * kSyncStride;
+  bump(Sync{cnt2}, 0);
+  wait_count(Sync{cnt2}, 0, 1, static_cast<uint32_t>(n_et), kRtSpin, err);
+  const RouteSmem sm(smem, T, E, k);
+  {
+    unsigned long long* sel = sm.sel + static_cast<size_t>(wave) * kSelWaveWords;
+    for (int j = wave; et + j * n_et < kRtTok; j += kThreads / 64) {
+      const int t = t0 + et + j * n_et;
+      if (t >= T) break;  // uniform
+      int id = 0;
+      float w = 0.f;
+      select_token<true>(ws.logits + static_cast<size_t>(t) * E, bias, E, k, rsf, sel, &id, &w);
+      if (lane < k) {
+        const int r = t * k + lane;
+        st_i32<true>(ws.ids + r, id);
+        st_f32<true>(ws.weights + r, w);
+        if (ids_out) ids_out[r] = id;
+        if (w_out) w_out[r] = w;
+      }
+    }
+  }
+  wait_memory();
+  __syncthreads();
+  uint32_t* top = ws.rcnt + static_cast<size_t>(n_tt * n_et + n_tt) * kSyncStride;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             static_cast<uint32_t>(n_tt * n_et) - 1;
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- phase 4: route tables (read by later kernels); every other
+  // workgroup is past its waits, so the tile counts reset here
+  for (int i = threadIdx.x; i <= n_tt; i += kThreads)
+    __hip_atomic_store(ws.rcnt + static_cast<size_t>(n_tt * n_et + i) * kSyncStride, 0u,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int r = threadIdx.x; r < T * k; r += kThreads) sm.ids[r] = ld_i32<true>(ws.ids + r);
+  build_routes<false>(T, E, k, ws, sm);
+  // the counters of the grouped merged launch that follows (zero_lines of
+  // them; none when separate launches follow)
+  for (int i = threadIdx.x; i < zero_lines; i += kThreads)
+    if (i != kSyncError)
+      __hip_atomic_store(ws.sync + static_cast<size_t>(i) * kSyncStride, 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace
+
+int router_mfma_tokens_padded(int T) { return (T + kRtTok - 1) / kRtTok * kRtTok; }
+int router_mfma_count_lines(int T, int E) {
+  const int n_tt = (T + kRtTok - 1) / kRtTok, n_et = (E + kRtExp - 1) / kRtExp;
+  return n_tt * n_et + n_tt + 1;
+}
+// Contraction slices: one per 512 columns, fewer where the grid would pass
+// kRtMaxGrid (at most 16: H <= 8192).
+int router_mfma_slices(int T, int E, int H) {
+  const int tiles = ((T + kRtTok - 1) / kRtTok) * ((E + kRtExp - 1) / kRtExp);
+  int S = (H + 511) / 512;
+  const int cap = kRtMaxGrid / tiles;
+  if (S > cap) S = cap > 1 ? cap : 1;
+  return S;
+}
+
+hipError_t launch_router_mfma(const LayerDims& d, const void* hidden, const void* router_w,
+                              const float* bias, const Workspace& ws, int Tp_alloc,
+                              int zero_lines, int32_t* ids_out, float* weights_out,
+                              hipStream_t s) {
+  const int S = router_mfma_slices(d.T, d.E, d.H);
+  // slice width: a multiple of 64 columns
+  const int Ks = ((d.H + S - 1) / S + 63) / 64 * 64;
+  const int n_tt = (d.T + kRtTok - 1) / kRtTok, n_et = (d.E + kRtExp - 1) / kRtExp;
+  if (d.T < 1 || d.E < 1 || d.k < 1 || d.H % 64 || S > 16 || n_tt * n_et * S > kRtMaxGrid ||
+      router_mfma_tokens_padded(d.T) > Tp_alloc)
+    return hipErrorInvalidValue;
+  dim3 grid(n_et, n_tt, (d.H + Ks - 1) / Ks);
+  const size_t smem = route_smem_bytes(d.T, d.E, d.k);
+  hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(kThreads), smem, s,
+                     static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(router_w),
+                     bias, d.T, d.H, d.E, d.k, d.rsf, static_cast<int>(grid.z), Ks, Tp_alloc,
+                     zero_lines, ws, ids_out, weights_out);
+  return hipGetLastError();
+}
 
 hipError_t launch_router(const LayerDims& d, const void* hidden, const void* router_w,
                          const float* bias, const Workspace& ws, int32_t* ids_out,
