@@ -46,8 +46,8 @@ CHAIN_MAX_TOKENS = 16  # the library's kChainMaxTokens (split path: one expert l
 # template arguments (NS, U, GR) of the library's gate_up MFMA launches (kNsGu, kUGu, kGR)
 MFMA_GATE_UP_TILE = "4, 1, 1"
 MFMA_ROUTED_TILE = "4, 1"  # NS, U of the routed-only gate_up launch
+DENSE_MAX_GROUPS = 4  # 16-token groups per dense gate_up workgroup (kDenseMaxGroups)
 GR2_MIN_MEAN = 10  # the library's kGr2MinMean
-MFMA_DENSE_TILE = "2, 1, 1"  # NS, U, GR of a dense layer's gate_up launch (kNsGuDense)
 METRIC = "µs per MoE layer and effective HBM TB/s (fraction of peak) at 1/16/64/128 tok"
 
 
@@ -320,8 +320,10 @@ def dominant_kernel(md, sh, path_taken, D, routed_b, shared_b, act_b):
         kb = (2 * sh.Is * H + sb * (2 * sh.Is // 128) * (H // 128) + T * H * 2 + T * sh.Is * 4)
         fl = 2 * T * 2 * sh.Is * H
         if path_taken == md.PATH_GROUPED:
-            return ("gate_up_mfma_kernel<NS, U, GR, E8, ROWS> (dense MLP)",
-                    "gate_up_mfma_kernel<%s, %s, 1>" % (MFMA_DENSE_TILE, e8), kb, fl)
+            groups = (T + 15) // 16
+            gr = DENSE_MAX_GROUPS if groups >= DENSE_MAX_GROUPS else (2 if groups >= 2 else 1)
+            return ("dense_gate_up_mfma_kernel<E8, GR> (dense MLP)",
+                    "dense_gate_up_mfma_kernel<%s, %d>" % (e8, gr), kb, fl)
         return ("router_kernel<NJ2, E8> (dense MLP gate_up tiles)",
                 "router_kernel<%d, %s>" % ((H + 511) // 512, e8), kb, fl)
     if path_taken == md.PATH_GEMV:

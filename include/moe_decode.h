@@ -111,8 +111,10 @@ typedef enum {
  * DenseMlp, LayerStages._build_dense) goes in the shared-expert slot
  * (sw13, sw2 and their scales), the router and routed-expert pointers may be
  * NULL, and a run computes out, residual_out and moe_out (= the MLP output)
- * through the same boundary.  AUTO: GEMV kernels below 8 tokens, MFMA
- * kernels from 8.
+ * through the same boundary.  AUTO takes the MFMA kernels at every token
+ * count: gate_up with each workgroup's contraction split over its four
+ * waves, then down with the contraction also split over up to eight
+ * workgroups, whose partial outputs the boundary adds in a fixed order.
  */
 typedef struct {
   int32_t hidden;              /* H */

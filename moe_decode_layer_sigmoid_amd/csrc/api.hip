@@ -113,7 +113,7 @@ size_t layout(const moe_decode_desc& d, char* base, moe::Workspace* ws,
   w.act = reinterpret_cast<float*>(take(T * k * I * 4));
   w.act_s = reinterpret_cast<float*>(take(T * (Is ? Is : 1) * 4));
   w.rows = reinterpret_cast<float*>(take(T * k * H * 4));
-  w.y_s = reinterpret_cast<float*>(take(T * H * 4));
+  w.y_s = reinterpret_cast<float*>(take((E == 0 ? moe::kDenseDnMaxSplits : 1) * T * H * 4));
   w.slot_tab = reinterpret_cast<int32_t*>(take(E * moe::kSlotInts * 4));
   w.rpart = reinterpret_cast<float*>(
       take(rmfma ? static_cast<size_t>(moe::router_mfma_slices(static_cast<int>(T),
@@ -333,12 +333,11 @@ static int run_dense(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, h
   auto step = [&](hipError_t e) {
     if (err == hipSuccess && e != hipSuccess) err = e;
   };
+  int planes = 1;
   if (path_for(*p, T) == MOE_DECODE_PATH_GROUPED) {
-    step(moe::launch_gate_up_mfma(d, moe::kSharedRows, a->hidden, nullptr, nullptr, a->sw13,
-                                  a->sw13_scale, p->ws, s, p->user_begin, p->user_end));
-    if (err == hipSuccess)
-      step(moe::launch_down_mfma(d, moe::kSharedRows, nullptr, nullptr, a->sw2, a->sw2_scale,
-                                 p->ws, s));
+    step(moe::launch_dense_mfma(d, a->hidden, a->sw13, a->sw13_scale, a->sw2, a->sw2_scale,
+                                p->ws, s, p->user_begin, p->user_end));
+    planes = moe::dense_down_splits(d);
   } else {
     step(moe::launch_router(d, a->hidden, nullptr, p->ws.zero_bias, p->ws, nullptr, nullptr,
                             a->sw13, a->sw13_scale, s, p->user_begin, p->user_end));
@@ -347,7 +346,7 @@ static int run_dense(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, h
   }
   if (err == hipSuccess)
     step(moe::launch_epilogue(d, a->residual, a->gamma, p->ws, a->out, a->residual_out,
-                              a->moe_out, s));
+                              a->moe_out, s, planes));
   return err == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;
 }
 

@@ -507,12 +507,6 @@ constexpr int kNsGu = 4, kUGu = 1;
 constexpr int kNsDn = 4, kNsDnRouted = 8, kUDn = 1;
 constexpr int kGR = 1;  // 16-token groups per pass
 constexpr int kGr2MinMean = 10;
-// A dense layer (no routed experts) has only the MLP's tiles: I/128 gate_up
-// and H/256 down workgroups per 16-token pass at the tiles above (64 and 16
-// at I = 8192, H = 4096).  Its launches take the smallest tiles instead, 16
-// gate + 16 up rows and 16 down rows per wave, for 2x and 4x the workgroups:
-// 16 tokens 139 -> 102 us, 32 tokens 140 -> 104 us, 64 tokens 145 -> 121 us.
-constexpr int kNsGuDense = 2, kNsDnDense = 1;
 bool routed_gr2(const LayerDims& d) { return d.T * d.k >= kGr2MinMean * d.E; }
 constexpr size_t kLdsGu = static_cast<size_t>(kWaves) * kUGu * kNsGu * kSubtileBlock;
 
@@ -578,6 +572,319 @@ __global__ __launch_bounds__(kThreads, 4) void grouped_chain_kernel(GChainArgs a
                                             a.H, a.I, a.Is, a.k, a.T, a.SP, ws, wait);
 }
 
+// Dense layers (no routed experts).  The MLP is one expert of I_s rows that
+// every token takes, so a 16-token pass of the tiles above has only I_s / 64
+// gate_up and H / 64 down workgroups (128 and 64 at I_s = 8192, H = 4096):
+// too few loads in flight for HBM.  The kernels below give a workgroup a
+// narrow row tile and let its four waves split the contraction into four
+// contiguous ranges instead.  gate_up: 16 gate + 16 up rows per workgroup,
+// I_s / 16 workgroups per pass.  down: 32 output rows per workgroup, with
+// the contraction also split over S workgroups (dense_down_splits), each
+// writing an fp32 partial plane of the output that the boundary adds up in
+// plane order.  The waves' sums meet in LDS and are added in wave order, so
+// results stay deterministic.  Every 16-token pass streams the weights
+// again; workgroup b runs on XCD b % 8 (the dispatcher's round robin), so the
+// grid puts all passes of a tile on one XCD and next to each other in
+// dispatch order, where the later passes find the weight lines in that
+// XCD's L2.
+constexpr int kDenseUGu = 2, kDenseUDn = 1;  // scale blocks per round of loads
+constexpr int kDenseMaxGroups = 4;           // 16-token groups per workgroup
+constexpr int kDenseDnRows = 32;             // down rows per workgroup (8 per 16-row subtile pair)
+constexpr int kXcds = 8;
+
+// blocks [*b0, *b0 + *nb) of range u of n equal contiguous ranges over KB blocks
+__device__ __forceinline__ void k_range(int u, int n, int KB, int* b0, int* nb) {
+  const int a = u * KB / n, b = (u + 1) * KB / n;
+  *b0 = a;
+  *nb = b - a;
+}
+
+// Workgroup b -> (tile, pass), with every pass of a tile on one XCD and
+// adjacent in dispatch order (the grid holds ceil(tiles / 8) * 8 * P).
+__device__ __forceinline__ void xcd_tile_pass(int b, int P, int* tile, int* pass) {
+  const int x = b % kXcds, r = b / kXcds;
+  *pass = r % P;
+  *tile = (r / P) * kXcds + x;
+}
+
+// Block i of a wave's range (i past the end: the last, whose scale the
+// caller zeroes), rotated by rot so that the workgroups' first loads spread
+// over the row's columns.
+__device__ __forceinline__ int range_block(int i, int b0, int nb, int rot) {
+  const int j = min(i, nb - 1) + rot;
+  return b0 + (j >= nb ? j - nb : j);
+}
+
+// The dense kernels read their activations line by line: load m of lane
+// (g, c) takes the 16 bytes at 64 m + 16 g of token c's 256-byte block row,
+// so the four lanes of a token read 64 contiguous bytes per load (the tiles
+// above, whose lanes read 64 bytes each over four loads, touch twice the
+// cache lines per load).  MFMA m then covers the block's columns
+// [32 m, 32 m + 32), lane group g its columns 32 m + 8 g .. + 7, and the
+// weight side follows: lane (g, c) reads the 8 bytes at 32 m + 8 g of row c,
+// half (g & 1) of staged piece 2 m + (g >> 1).
+__device__ __forceinline__ uint2 staged_half(const unsigned char* stage, int s, int c, int m,
+                                             int g) {
+  const int r8 = c & 7, p = 2 * m + (g >> 1);
+  return *reinterpret_cast<const uint2*>(stage + 1024 * (2 * s + (c >> 3)) + 128 * r8 +
+                                         16 * (p ^ r8) + 8 * (g & 1));
+}
+
+// gate_up + clamped SwiGLU of a dense layer: SwiGLU outputs [i0, i0 + 16),
+// tokens [16 GR pass, 16 GR (pass + 1)) as GR 16-token groups that share
+// each staged block of weights, into the hi / lo planes of ws.act_s.
+template <bool E8, int GR>
+__global__ __launch_bounds__(kThreads, 2) void dense_gate_up_mfma_kernel(
+    const uint16_t* __restrict__ hidden, const uint8_t* __restrict__ sw13,
+    const void* __restrict__ sscale13, int H, int Is, int T, int P, Workspace ws, float limit) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  int tile, pass;
+  xcd_tile_pass(blockIdx.x, P, &tile, &pass);
+  const int i0 = tile * 16;
+  if (i0 >= Is) return;  // uniform over the workgroup
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  constexpr int SB = 2 * kSubtileBlock;  // 16 gate + 16 up rows of one block
+  unsigned char* stage = smem + wave * kDenseUGu * SB;
+  const int KB = H / kBlock;
+  int b0, nb;
+  k_range(wave, kWaves, KB, &b0, &nb);
+  const int rot = nb > 0 ? tile % nb : 0;
+  // load rows: instructions 0, 1 = gate rows i0 .. i0 + 15, 2, 3 = up rows
+  const uint8_t* lrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    lrow[i] = sw13 + static_cast<size_t>((i < 2 ? i0 : Is + i0 - 16) + 8 * i + (lane >> 3)) * H;
+  const size_t sg0 = static_cast<size_t>(i0 / kBlock) * KB;
+  const size_t su0 = static_cast<size_t>((Is + i0) / kBlock) * KB;
+  const int p0 = pass * 16 * GR;
+  const int G = min(GR, (T - p0 + 15) / 16);  // groups holding tokens (uniform)
+  const uint16_t* xrow[GR];
+#pragma unroll
+  for (int gr = 0; gr < GR; ++gr)
+    xrow[gr] = hidden + static_cast<size_t>(min(p0 + 16 * gr + c, T - 1)) * H + 8 * g;
+  f32x4_t fg[GR], fu[GR];
+#pragma unroll
+  for (int gr = 0; gr < GR; ++gr) {
+    fg[gr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    fu[gr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int i = 0; i < nb; i += kDenseUGu) {
+    float sg[kDenseUGu], su[kDenseUGu];
+    int kbs[kDenseUGu];
+#pragma unroll
+    for (int j = 0; j < kDenseUGu; ++j) {
+      const int kb = range_block(i + j, b0, nb, rot);
+      kbs[j] = kb;
+      stage_block<4>(lrow, kb * kBlock, stage + j * SB);
+      const float a = load_scale<E8>(sscale13, sg0 + kb);
+      const float b = load_scale<E8>(sscale13, su0 + kb);
+      sg[j] = i + j < nb ? a : 0.f;
+      su[j] = i + j < nb ? b : 0.f;
+    }
+    asm volatile("" ::: "memory");
+    uint4 xa[GR][kDenseUGu][4];
+#pragma unroll
+    for (int gr = 0; gr < GR; ++gr) {
+      if (gr >= G) break;
+#pragma unroll
+      for (int j = 0; j < kDenseUGu; ++j)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          xa[gr][j][m] = *reinterpret_cast<const uint4*>(xrow[gr] + kbs[j] * kBlock + 32 * m);
+    }
+    wait_memory();  // the staged weights are in LDS (see gate_up_tile)
+#pragma unroll
+    for (int j = 0; j < kDenseUGu; ++j) {
+      const unsigned char* st = stage + j * SB;
+      f32x4_t pg[GR], pu[GR];
+#pragma unroll
+      for (int gr = 0; gr < GR; ++gr) {
+        pg[gr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        pu[gr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint2 hg = staged_half(st, 0, c, m, g), hu = staged_half(st, 1, c, m, g);
+        const bf16x8_t wg = fp8x8_to_bf16x8(hg.x, hg.y), wu = fp8x8_to_bf16x8(hu.x, hu.y);
+#pragma unroll
+        for (int gr = 0; gr < GR; ++gr) {
+          if (gr >= G) break;
+          const bf16x8_t a = as_bf16x8(xa[gr][j][m]);
+          pg[gr] = mfma(a, wg, pg[gr]);
+          pu[gr] = mfma(a, wu, pu[gr]);
+        }
+      }
+#pragma unroll
+      for (int gr = 0; gr < GR; ++gr) {
+        if (gr >= G) break;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          fg[gr][e] = fmaf(sg[j], pg[gr][e], fg[gr][e]);
+          fu[gr][e] = fmaf(su[j], pu[gr][e], fu[gr][e]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): stage reads done
+  }
+  // The four ranges meet in LDS (the stage is free once every wave is past
+  // its last round): lane (g, c) of each wave holds tokens p0 + 16 gr + 4 g + e
+  // of SwiGLU output i0 + c; wave w then finishes e = w in wave order.
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int gr = 0; gr < GR; ++gr)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      red[((wave * GR + gr) * 8 + e) * kWave + lane] = fg[gr][e];
+      red[((wave * GR + gr) * 8 + 4 + e) * kWave + lane] = fu[gr][e];
+    }
+  __syncthreads();
+  uint16_t* act_hi = reinterpret_cast<uint16_t*>(ws.act_s);
+#pragma unroll
+  for (int gr = 0; gr < GR; ++gr) {
+    const int q = p0 + 16 * gr + 4 * g + wave;
+    if (q < T) {
+      float ga = 0.f, ua = 0.f;
+#pragma unroll
+      for (int v = 0; v < kWaves; ++v) {
+        ga += red[((v * GR + gr) * 8 + wave) * kWave + lane];
+        ua += red[((v * GR + gr) * 8 + 4 + wave) * kWave + lane];
+      }
+      const float a = clamped_swiglu(ga, ua, limit);
+      const uint16_t hi = bf16_bits(a);
+      const uint16_t lo = bf16_bits(a - bf16_to_f32(hi));
+      const size_t o = static_cast<size_t>(q) * Is + i0 + c;
+      act_hi[o] = hi;
+      act_hi[static_cast<size_t>(T) * Is + o] = lo;
+    }
+  }
+}
+
+// down projection of a dense layer: output rows [h0, h0 + 32), tokens
+// [16 GR pass, 16 GR (pass + 1)) as GR groups, contraction range s of S, into
+// the fp32 partial plane s of ws.y_s ([S][T][H]).
+template <bool E8, int GR>
+__global__ __launch_bounds__(kThreads, 2) void dense_down_mfma_kernel(
+    const uint8_t* __restrict__ sw2, const void* __restrict__ sscale2, int H, int Is, int T,
+    int P, int S, Workspace ws) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  int unit, pass;
+  xcd_tile_pass(blockIdx.x, P, &unit, &pass);
+  if (unit >= (H / kDenseDnRows) * S) return;  // uniform over the workgroup
+  const int rt = unit / S, s = unit - rt * S;
+  const int h0 = rt * kDenseDnRows;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  constexpr int SB = 2 * kSubtileBlock;  // 32 rows of one block
+  unsigned char* stage = smem + wave * kDenseUDn * SB;
+  const int KB = Is / kBlock;
+  int b0, nb;
+  k_range(s * kWaves + wave, S * kWaves, KB, &b0, &nb);
+  const int rot = nb > 0 ? rt % nb : 0;
+  const uint8_t* lrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    lrow[i] = sw2 + static_cast<size_t>(h0 + 8 * i + (lane >> 3)) * Is;
+  const size_t s0 = static_cast<size_t>(h0 / kBlock) * KB;
+  const int p0 = pass * 16 * GR;
+  const int G = min(GR, (T - p0 + 15) / 16);
+  const uint16_t* act_hi = reinterpret_cast<const uint16_t*>(ws.act_s);
+  const uint16_t* act_lo = act_hi + static_cast<size_t>(T) * Is;
+  size_t arow[GR];
+#pragma unroll
+  for (int gr = 0; gr < GR; ++gr)
+    arow[gr] = static_cast<size_t>(min(p0 + 16 * gr + c, T - 1)) * Is + 8 * g;
+  f32x4_t f[GR][2];
+#pragma unroll
+  for (int gr = 0; gr < GR; ++gr) {
+    f[gr][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f[gr][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int i = 0; i < nb; i += kDenseUDn) {
+    float sc[kDenseUDn];
+    int kbs[kDenseUDn];
+#pragma unroll
+    for (int j = 0; j < kDenseUDn; ++j) {
+      const int kb = range_block(i + j, b0, nb, rot);
+      kbs[j] = kb;
+      stage_block<4>(lrow, kb * kBlock, stage + j * SB);
+      const float a = load_scale<E8>(sscale2, s0 + kb);
+      sc[j] = i + j < nb ? a : 0.f;
+    }
+    asm volatile("" ::: "memory");
+    uint4 ah[GR][kDenseUDn][4], al[GR][kDenseUDn][4];
+#pragma unroll
+    for (int gr = 0; gr < GR; ++gr) {
+      if (gr >= G) break;
+#pragma unroll
+      for (int j = 0; j < kDenseUDn; ++j)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const size_t o = arow[gr] + kbs[j] * kBlock + 32 * m;
+          ah[gr][j][m] = *reinterpret_cast<const uint4*>(act_hi + o);
+          al[gr][j][m] = *reinterpret_cast<const uint4*>(act_lo + o);
+        }
+    }
+    wait_memory();  // the staged weights are in LDS (see gate_up_tile)
+#pragma unroll
+    for (int j = 0; j < kDenseUDn; ++j) {
+      const unsigned char* st = stage + j * SB;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        f32x4_t p[GR];
+#pragma unroll
+        for (int gr = 0; gr < GR; ++gr) p[gr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint2 hw = staged_half(st, sub, c, m, g);
+          const bf16x8_t wa = fp8x8_to_bf16x8(hw.x, hw.y);
+#pragma unroll
+          for (int gr = 0; gr < GR; ++gr) {
+            if (gr >= G) break;
+            p[gr] = mfma(as_bf16x8(ah[gr][j][m]), wa, p[gr]);
+            p[gr] = mfma(as_bf16x8(al[gr][j][m]), wa, p[gr]);
+          }
+        }
+#pragma unroll
+        for (int gr = 0; gr < GR; ++gr) {
+          if (gr >= G) break;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[gr][sub][e] = fmaf(sc[j], p[gr][e], f[gr][sub][e]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): stage reads done
+  }
+  // as in the gate_up kernel: lane (g, c) holds tokens p0 + 16 gr + 4 g + e
+  // of rows h0 + 16 sub + c; wave w adds up e = w over the waves, in wave order
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int gr = 0; gr < GR; ++gr)
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        red[((wave * GR + gr) * 8 + 4 * sub + e) * kWave + lane] = f[gr][sub][e];
+  __syncthreads();
+#pragma unroll
+  for (int gr = 0; gr < GR; ++gr) {
+    const int q = p0 + 16 * gr + 4 * g + wave;
+    if (q < T) {
+      float* out = ws.y_s + (static_cast<size_t>(s) * T + q) * H + h0 + c;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        float y = 0.f;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v)
+          y += red[((v * GR + gr) * 8 + 4 * sub + wave) * kWave + lane];
+        out[16 * sub] = y;
+      }
+    }
+  }
+}
+
 // grid rows: the shared expert's passes, then the touched-expert slots
 int shared_rows(const LayerDims& d) { return d.Is > 0 ? (d.T + 16 * kGR - 1) / (16 * kGR) : 0; }
 int slot_rows(const LayerDims& d) { return d.T * d.k < d.E ? d.T * d.k : d.E; }
@@ -592,8 +899,7 @@ hipError_t launch_gate_up_mfma(const LayerDims& d, int rows, const void* hidden,
   const int R = rows == kSharedRows ? 0 : slot_rows(d);
   if (SP + R == 0) return hipSuccess;
   const int Imax = d.I > d.Is ? d.I : d.Is;
-  const bool dense = d.E == 0;
-  const int per_wg = kWaves * 8 * (dense ? kNsGuDense : kNsGu);  // SwiGLU outputs per workgroup
+  const int per_wg = kWaves * 8 * kNsGu;  // SwiGLU outputs per workgroup
   dim3 grid((Imax + per_wg - 1) / per_wg, SP + R);
   const auto* x = static_cast<const uint16_t*>(hidden);
   const auto* w = static_cast<const uint8_t*>(w13);
@@ -602,13 +908,6 @@ hipError_t launch_gate_up_mfma(const LayerDims& d, int rows, const void* hidden,
   launch_gu<E8, ROWS, GR>(grid, s, x, w, w13_scale, sw, sw13_scale, d, SP, ws, evb, eve)
   if (rows == kAllRows) {
     if (d.e8m0) MOE_GU(true, kAllRows, kGR); else MOE_GU(false, kAllRows, kGR);
-  } else if (rows == kSharedRows && dense) {
-    if (d.e8m0)
-      launch_gu<true, kSharedRows, kGR, kNsGuDense>(grid, s, x, w, w13_scale, sw, sw13_scale, d,
-                                                    SP, ws, evb, eve);
-    else
-      launch_gu<false, kSharedRows, kGR, kNsGuDense>(grid, s, x, w, w13_scale, sw, sw13_scale, d,
-                                                     SP, ws, evb, eve);
   } else if (rows == kSharedRows) {
     if (d.e8m0) MOE_GU(true, kSharedRows, kGR); else MOE_GU(false, kSharedRows, kGR);
   } else if (routed_gr2(d)) {
@@ -617,6 +916,54 @@ hipError_t launch_gate_up_mfma(const LayerDims& d, int rows, const void* hidden,
     if (d.e8m0) MOE_GU(true, kRoutedRows, kGR); else MOE_GU(false, kRoutedRows, kGR);
   }
 #undef MOE_GU
+  return hipGetLastError();
+}
+
+int dense_down_splits(const LayerDims& d) {
+  // two rounds of loads per wave at least
+  const int S = d.Is / kBlock / (kWaves * 2 * kDenseUDn);
+  return S < 1 ? 1 : (S > kDenseDnMaxSplits ? kDenseDnMaxSplits : S);
+}
+
+template <bool E8, int GR>
+static void launch_dense(const LayerDims& d, int P, const uint16_t* x, const uint8_t* w13,
+                         const void* s13, const uint8_t* w2, const void* s2, const Workspace& ws,
+                         hipStream_t s, hipEvent_t evb, hipEvent_t eve) {
+  const int n_gu = d.Is / 16;
+  const dim3 g1(static_cast<unsigned>((n_gu + kXcds - 1) / kXcds * kXcds * P));
+  // the stage, or the waves' sums after it (4 waves x GR groups x 8 x 64 floats)
+  const size_t red = static_cast<size_t>(kWaves) * GR * 8 * kWave * 4;
+  const size_t st1 = static_cast<size_t>(kWaves) * kDenseUGu * 2 * kSubtileBlock;
+  MOE_LAUNCH((dense_gate_up_mfma_kernel<E8, GR>), g1, dim3(kThreads), st1 > red ? st1 : red, s,
+             evb, eve, x, w13, s13, d.H, d.Is, d.T, P, ws, d.limit);
+  const int S = dense_down_splits(d);
+  const int n_dn = d.H / kDenseDnRows * S;
+  const dim3 g2(static_cast<unsigned>((n_dn + kXcds - 1) / kXcds * kXcds * P));
+  const size_t st2 = static_cast<size_t>(kWaves) * kDenseUDn * 2 * kSubtileBlock;
+  hipLaunchKernelGGL((dense_down_mfma_kernel<E8, GR>), g2, dim3(kThreads), st2 > red ? st2 : red,
+                     s, w2, s2, d.H, d.Is, d.T, P, S, ws);
+}
+
+hipError_t launch_dense_mfma(const LayerDims& d, const void* hidden, const void* sw13,
+                             const void* sw13_scale, const void* sw2, const void* sw2_scale,
+                             const Workspace& ws, hipStream_t s, hipEvent_t evb, hipEvent_t eve) {
+  if (d.E != 0 || d.Is <= 0 || d.T <= 0) return hipErrorInvalidValue;
+  const int groups = (d.T + 15) / 16;
+  const int GR = groups >= kDenseMaxGroups ? kDenseMaxGroups : (groups >= 2 ? 2 : 1);
+  const int P = (groups + GR - 1) / GR;  // grid passes of 16 GR tokens
+  const auto* x = static_cast<const uint16_t*>(hidden);
+  const auto* w13 = static_cast<const uint8_t*>(sw13);
+  const auto* w2 = static_cast<const uint8_t*>(sw2);
+#define MOE_DENSE(E8, GR_) \
+  launch_dense<E8, GR_>(d, P, x, w13, sw13_scale, w2, sw2_scale, ws, s, evb, eve)
+  if (GR == 1) {
+    if (d.e8m0) MOE_DENSE(true, 1); else MOE_DENSE(false, 1);
+  } else if (GR == 2) {
+    if (d.e8m0) MOE_DENSE(true, 2); else MOE_DENSE(false, 2);
+  } else {
+    if (d.e8m0) MOE_DENSE(true, kDenseMaxGroups); else MOE_DENSE(false, kDenseMaxGroups);
+  }
+#undef MOE_DENSE
   return hipGetLastError();
 }
 
@@ -632,9 +979,6 @@ hipError_t launch_down_mfma(const LayerDims& d, int rows, const void* w2, const 
   launch_dn<NS, E8, ROWS, GR>(R, s, w, w2_scale, sw, sw2_scale, d, SP, ws)
   if (rows == kAllRows) {
     if (d.e8m0) MOE_DN(kNsDn, true, kAllRows, kGR); else MOE_DN(kNsDn, false, kAllRows, kGR);
-  } else if (rows == kSharedRows && d.E == 0) {
-    if (d.e8m0) MOE_DN(kNsDnDense, true, kSharedRows, kGR);
-    else MOE_DN(kNsDnDense, false, kSharedRows, kGR);
   } else if (rows == kSharedRows) {
     if (d.e8m0) MOE_DN(kNsDn, true, kSharedRows, kGR);
     else MOE_DN(kNsDn, false, kSharedRows, kGR);

@@ -33,7 +33,8 @@ struct Workspace {
   float* act;          // [maxT * k, I]   routed SwiGLU output, permuted order
   float* act_s;        // [maxT, Is]      shared SwiGLU output
   float* rows;         // [maxT * k, H]   routed down output, at route index t*k+j
-  float* y_s;          // [maxT, H]       shared expert output
+  float* y_s;          // [maxT, H] shared expert output; a dense layer's down
+                       // partial planes [kDenseDnMaxSplits][maxT, H]
   uint32_t* counter;   // router arrival counters, router_cnt_words() (self-resetting)
   uint32_t* sync;      // [sync_words(E)] counters of the expert chain and grouped merged
                        // launches (zeroed by the router launch before them); the error word
@@ -110,13 +111,11 @@ constexpr int kGroupedMinTokens = 4;
 // from L2 (1.1 us), and the routing delay (about 5 us) is more than the
 // shared expert's weights can fill.  So AUTO keeps the two launches.
 constexpr int kStepAutoMaxTokens = 0;
-// The same for a dense layer (no routed experts).  Its MFMA launches have
-// few tiles per 16-token pass (I_s / 64 gate_up and H / 64 down tiles with
-// the dense tile sizes), so they win only where the GEMV tiles' per-token
-// work has grown (MI355X, H = 4096, I_s = 8192, µs per step GEMV / MFMA:
-// 8 tokens 94.8 / 93.6, 10: 110.9 / 95.3, 12: 128.5 / 98.1, 14: 143.7 /
-// 100.3, 16: 160.0 / 106.7).
-constexpr int kDenseGroupedMinTokens = 8;
+// The same for a dense layer (no routed experts).  Its MFMA kernels split
+// the contraction over waves and workgroups and win from one token on
+// (MI355X, H = 4096, I_s = 8192, us per step GEMV / MFMA: 1 token 35.7 /
+// 30.4, 4: 71.4 / 32.0, 8: 119.5 / 33.4, 16: 213.9 / 38.7).
+constexpr int kDenseGroupedMinTokens = 1;
 
 // Arguments of the expert chain launch of the few-token GEMV path (see
 // experts_chain.hip): item offsets and counts, the grid (items + 1).
@@ -285,10 +284,24 @@ size_t step_smem_bytes(const LayerDims& d);
 hipError_t launch_decode_step(const StepArgs& a, const Workspace& ws, hipStream_t s,
                               hipEvent_t evb = nullptr, hipEvent_t eve = nullptr);
 
+// A dense layer's MLP (d.E == 0) on the matrix cores: gate_up + SwiGLU with
+// each workgroup's contraction split over its waves, then down with the
+// contraction also split over dense_down_splits(d) workgroups, whose fp32
+// partial planes ([S][T][H] in ws.y_s, at most kDenseDnMaxSplits) the
+// boundary adds up.
+constexpr int kDenseDnMaxSplits = 8;
+int dense_down_splits(const LayerDims& d);
+hipError_t launch_dense_mfma(const LayerDims& d, const void* hidden, const void* sw13,
+                             const void* sw13_scale, const void* sw2, const void* sw2_scale,
+                             const Workspace& ws, hipStream_t s, hipEvent_t evb = nullptr,
+                             hipEvent_t eve = nullptr);
+
 // Weighted combine + shared + residual, RMSNorm * gamma, bf16 outputs.
 // moe_out (nullable): also the finalized MoE output (before the residual).
+// ys_planes: partial planes of the shared (or dense) output in ws.y_s,
+// added in plane order.
 hipError_t launch_epilogue(const LayerDims& d, const void* residual, const void* gamma,
                            const Workspace& ws, void* out, void* residual_out, void* moe_out,
-                           hipStream_t s);
+                           hipStream_t s, int ys_planes = 1);
 
 }  // namespace moe

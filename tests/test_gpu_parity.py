@@ -202,9 +202,9 @@ def test_same_expert_for_every_token(T, H, I, path, c_oracle):
 @pytest.mark.parametrize("fmt", ["fp32", "e8m0"])
 def test_dense_layer(T, fmt, c_oracle):
     """No routed experts: the layer's fp8 clamped-SwiGLU MLP (in the shared-
-    expert slot) and the boundary, on the GEMV kernels (few tokens) and the
-    MFMA kernels (AUTO from 8 tokens), against the dense oracle; each path
-    forced at T = 3 and 16 as well."""
+    expert slot) and the boundary, on the MFMA kernels (AUTO at every token
+    count) and the GEMV kernels, against the dense oracle; each path forced
+    at T = 3 and 16 as well."""
     sh = LayerShape(T=T, H=2048, E=0, k=0, I=0, Is=3072, scale_fmt=fmt, tag=320 + T)
     inp = make_layer(sh)
     dev = to_device(inp)
@@ -212,12 +212,33 @@ def test_dense_layer(T, fmt, c_oracle):
     for path in paths:
         _log("dense", sh, "path", path)
         plan = make_plan(sh, path=path)
-        want = (md.PATH_GROUPED if T >= 8 else md.PATH_GEMV_SPLIT) if path == md.PATH_AUTO else path
+        want = md.PATH_GROUPED if path == md.PATH_AUTO else path
         assert plan.path_for(T) == want
         got = run_layer(plan, dev, T)
         err = check_layer(inp, got)
         _log("  errors", err)
         plan.close()
+
+
+@pytest.mark.parametrize("T,H,Is,fmt", [(16, 4096, 8192, "fp32"), (64, 4096, 8192, "e8m0"),
+                                         (20, 1024, 6144, "fp32"), (33, 384, 512, "e8m0"),
+                                         (5, 4096, 4096, "fp32")])
+def test_dense_layer_mfma_splits(T, H, Is, fmt):
+    """The dense MFMA kernels at the shapes that set their contraction
+    splits: 8, 6, 4 and 1 down planes (I_s = 8192, 6144, 4096, 512), a
+    hidden size whose 128-column blocks do not divide over the four waves
+    (H = 384: one wave has none), one, two and four 16-token groups per
+    workgroup and a second pass with one group (33 tokens); every output row
+    against the dense oracle."""
+    sh = LayerShape(T=T, H=H, E=0, k=0, I=0, Is=Is, scale_fmt=fmt, tag=340 + T)
+    inp = make_layer(sh)
+    dev = to_device(inp)
+    _log("dense mfma", sh)
+    plan = make_plan(sh, path=md.PATH_GROUPED)
+    got = run_layer(plan, dev, T)
+    err = check_layer(inp, got)
+    _log("  errors", err)
+    plan.close()
 
 
 @pytest.mark.parametrize("T", [1, 5, 16])
