@@ -94,6 +94,8 @@ size_t layout(const moe_decode_desc& d, char* base, moe::Workspace* ws,
   w.msync = reinterpret_cast<uint32_t*>(take(moe::step_sync_lines(dmax_s) * moe::kSyncStride * 4));
   w.mlogits = reinterpret_cast<float*>(take(moe::kFlagRep * Ts * E * 4));
   w.mepi = reinterpret_cast<float*>(take(Ts * moe::kMaxBndSlices * 4));
+  // the router launch's encoded logits
+  w.rlogits = reinterpret_cast<float*>(take(T * E * 4));
   // the matrix-core router's counters (many tokens only)
   const bool rmfma = T >= moe::kRouterMfmaMinTokens && E > 0;
   w.rcnt = reinterpret_cast<uint32_t*>(

@@ -48,6 +48,9 @@ struct Workspace {
   uint32_t* msync;     // [step_sync_lines(dmax)] lines: route flag, counts, exit lines
   float* mlogits;      // [min(maxT, kChainMaxTokens), E] logits, inverted bits (0 = not yet)
   float* mepi;         // [min(maxT, kChainMaxTokens)][kMaxBndSlices] like epi_part
+  // The router launch's logits [maxT, E] with inverted bits (0 = not yet
+  // written), zeroed again by the workgroup that reads them.
+  float* rlogits;
   // The matrix-core router (many tokens): partial logits [slices][E][Tp]
   // and its arrival counters (one line each, self-resetting).
   float* rpart;

@@ -11,13 +11,15 @@
 // Grid: x = blocks of 4 experts (one expert row per wave), then, when asked,
 // the shared expert's gate_up tiles (8 SwiGLU rows each, grid row 0 only: it
 // depends on no routing, so its weights stream while the router waits on
-// its memory round trips); y = blocks of TB tokens (router_block_tokens).  Phase 1: every wave loads its whole bf16 router row at once
-// (one memory round trip), then dots it with the block's token rows.
-// Phase 2: the last workgroup of each token block (an arrival counter per
-// block) ranks that block's tokens, one wave per token.  Phase 3: the last
-// token block to finish (a second counter) builds the route tables from
-// per-expert token bitmasks in LDS.  Data handed between workgroups goes
-// through coherent stores and loads; the counters reset themselves, so the
+// its memory round trips); y = blocks of TB tokens (router_block_tokens).
+// Phase 1: every wave loads its whole bf16 router row at once (one memory
+// round trip), dots it with the block's token rows and stores the logits
+// with inverted bits.  Phase 2: the last router workgroup of each token
+// block polls the block's logits until all are written, ranks its tokens
+// (one wave per token) and zeroes the logits again.  Phase 3: the last token
+// block to finish (a counter) builds the route tables from per-expert token
+// bitmasks in LDS.  Data handed between workgroups goes through coherent
+// stores and loads; the counter and the logits reset themselves, so the
 // launch replays from a HIP graph.
 #include "device_common.h"
 #include "gemv_tiles.h"
@@ -58,25 +60,30 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
     return;
   }
 
-  // ---- phase 1: logits of this wave's expert for the block's tokens
+  // ---- phase 1: logits of this wave's expert for the block's tokens, stored
+  // with inverted bits (ws.rlogits reads 0 until a logit is written)
   const int e = blockIdx.x * 4 + wave;
   if (e < E)
-    router_wave<NJ2, true>(hidden + static_cast<size_t>(t0) * H,
-                           router_w + static_cast<size_t>(e) * H, H, nt, E, e,
-                           ws.logits + static_cast<size_t>(t0) * E);
-  wait_memory();
-  __syncthreads();
-  uint32_t* cnt = ws.counter + router_cnt_line(blockIdx.y);
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             static_cast<uint32_t>(n_router) - 1;
-  __syncthreads();
-  if (!s_last) return;
+    router_wave<NJ2, true, true>(hidden + static_cast<size_t>(t0) * H,
+                                 router_w + static_cast<size_t>(e) * H, H, nt, E, e,
+                                 ws.rlogits + static_cast<size_t>(t0) * E);
+  // The block's last router workgroup ranks its tokens: it polls their
+  // logits until every one is written (workgroups of lower index, which the
+  // dispatcher starts first; a bounded wait sets the error word), where a
+  // counter would cost each producer a store acknowledgement and an atomic
+  // before the reader's first load.
+  if (static_cast<int>(blockIdx.x) != n_router - 1) return;
+  uint32_t* err = ws.sync + static_cast<size_t>(kSyncError) * kSyncStride;
 
-  // ---- phase 2: top-k of the block's tokens
+  // ---- phase 2: top-k of the block's tokens (one wave per token), then,
+  // once every wave's selection has read them, their logits back to zero
+  // for the next launch
   const RouteSmem sm(smem, T, E, k);
-  select_tokens<true>(t0, t0 + nt, E, k, rsf, ws.logits, bias, ws, ids_out, w_out, sm);
-  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  select_tokens<true, true, true>(t0, t0 + nt, E, k, rsf, ws.rlogits, bias, ws, ids_out, w_out,
+                                  sm, err);
+  __syncthreads();
+  for (int i = threadIdx.x; i < nt * E; i += kThreads)
+    st_f32<true>(ws.rlogits + static_cast<size_t>(t0) * E + i, 0.f);
   if (gridDim.y > 1) {
     wait_memory();
     __syncthreads();
