@@ -48,6 +48,7 @@ MFMA_GATE_UP_TILE = "4, 1, 1"
 MFMA_ROUTED_TILE = "4, 1"  # NS, U of the routed-only gate_up launch
 DENSE_MAX_GROUPS = 4  # 16-token groups per dense gate_up workgroup (kDenseMaxGroups)
 GR2_MIN_MEAN = 10  # the library's kGr2MinMean
+SHARED_ACT_MIN_MEAN = 16  # the library's kSharedActMinMean
 METRIC = "µs per MoE layer and effective HBM TB/s (fraction of peak) at 1/16/64/128 tok"
 
 
@@ -349,8 +350,9 @@ def dominant_kernel(md, sh, path_taken, D, routed_b, shared_b, act_b):
         # and the shared expert runs beside it (two 16-token groups per pass
         # once the routes average 10 or more tokens per expert)
         gr = 2 if T * sh.k >= GR2_MIN_MEAN * sh.E else 1
+        sa = "true" if T * sh.k >= SHARED_ACT_MIN_MEAN * sh.E else "false"
         return ("gate_up_mfma_kernel<NS, U, GR, E8, ROWS> (routed experts)",
-                "gate_up_mfma_kernel<%s, %d, %s, 2>" % (MFMA_ROUTED_TILE, gr, e8), kb, fl)
+                "gate_up_mfma_kernel<%s, %d, %s, 2, %s>" % (MFMA_ROUTED_TILE, gr, e8, sa), kb, fl)
     if T <= CHAIN_MAX_TOKENS:
         # one launch streams the touched experts' gate_up and down weights and
         # the shared expert's down weights, and ends with the boundary (the

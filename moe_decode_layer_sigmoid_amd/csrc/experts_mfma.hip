@@ -139,6 +139,18 @@ __device__ __forceinline__ int block_at(int i, int KB, int rot) {
   return b >= KB ? b - KB : b;
 }
 
+// A shared activation tile (launches of one row kind): the 16 token rows
+// of one 128-column block, 256 bytes each, loaded once per workgroup
+// instead of once per wave.  Lane l of wave w loads tile row
+// r = 4 w + l / 16 and lands at piece l % 16 of it; it fetches piece
+// (l % 16) ^ r of the row, so piece p of row r sits at slot p ^ r and the
+// fragment reads (16 rows, one piece each) spread over the banks.
+constexpr int kActTile = 16 * 256;
+
+__device__ __forceinline__ uint4 act_piece(const unsigned char* tile, int r, int p) {
+  return *reinterpret_cast<const uint4*>(tile + 256 * r + 16 * (p ^ r));
+}
+
 // What one grid row works on (uniform).  Rows [0, SP) are the shared
 // expert, one 16 * GR-token pass each (they run in parallel); the rows after
 // them are the touched-expert slots, each taking all of its expert's tokens
@@ -178,7 +190,7 @@ __device__ __forceinline__ bool slot_of(int T, int SP, const Workspace& ws, int 
 // neighbouring lanes per 32-bit store), for readers in the same launch: a
 // plain store leaves the line in the writer's L2, possibly filled with stale
 // bytes of the part other workgroups write.
-template <int NS, int U, int GR, bool E8, int ROWS, bool C = false>
+template <int NS, int U, int GR, bool E8, int ROWS, bool C = false, bool SA = false>
 __device__ __forceinline__ bool gate_up_tile(
     int bx, int by, unsigned char* smem, const uint16_t* __restrict__ hidden,
     const uint8_t* __restrict__ w13, const void* __restrict__ scale13,
@@ -187,17 +199,22 @@ __device__ __forceinline__ bool gate_up_tile(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   constexpr int NH = NS / 2;  // gate (and up) subtiles
+  // SA: activation tiles shared through LDS (launches of one row kind)
+  static_assert(!SA || (U == 1 && ROWS != kAllRows), "a shared tile holds one block");
   const int i0 = (bx * kWaves + wave) * 16 * NH;
   Slot sl;
   if (!slot_of<GR>(T, SP, ws, by, &sl)) return false;
   const bool shared = ROWS == kAllRows ? sl.shared : ROWS == kSharedRows;
   const int I = shared ? Is : I_r;
+  // a workgroup covers 32 NS outputs, a divisor of 128: uniform over it
   if (i0 >= I) return false;
   const void* scale = shared ? sscale13 : scale13;
   constexpr int SB = NS * kSubtileBlock;  // stage bytes of one block
   unsigned char* stage = smem + wave * U * SB;
+  unsigned char* atile = smem + kWaves * U * SB;  // SA: GR tiles of kActTile bytes
   const int KB = H / kBlock;
-  const int rot = first_block(T, H, wave, KB, bx, by);
+  // with shared tiles every wave of the workgroup walks the same blocks
+  const int rot = first_block(T, H, SA ? 0 : wave, KB, bx, by);
   const uint8_t* W = shared ? sw13 : w13 + static_cast<size_t>(sl.e) * 2 * I * H;
   // load rows: instructions [0, NS) = gate rows i0 .. i0 + 8 NS - 1, then up
   const uint8_t* lrow[2 * NS];
@@ -213,12 +230,15 @@ __device__ __forceinline__ bool gate_up_tile(
 
   for (int p0 = sl.p_begin; p0 < sl.p_end; p0 += 16 * GR) {
     const int G = min(GR, (sl.p_end - p0 + 15) / 16);
+    // xrow: the lane's own fragment row; SA: the tile row this lane loads
+    // (tile row 4 wave + lane / 16, 16-byte piece (lane % 16) ^ row)
     const uint16_t* xrow[GR];
 #pragma unroll
     for (int gr = 0; gr < GR; ++gr) {
-      const int q = min(p0 + gr * 16 + c, sl.p_end - 1);
+      const int r = SA ? 4 * wave + (lane >> 4) : c;
+      const int q = min(p0 + gr * 16 + r, sl.p_end - 1);
       const int t = shared ? q : ws.perm[sl.base + q] / k;
-      xrow[gr] = hidden + static_cast<size_t>(t) * H + 32 * g;
+      xrow[gr] = hidden + static_cast<size_t>(t) * H + (SA ? 8 * ((lane & 15) ^ r) : 32 * g);
     }
     f32x4_t fg[GR][NH], fu[GR][NH];
 #pragma unroll
@@ -239,18 +259,33 @@ __device__ __forceinline__ bool gate_up_tile(
         sg[j] = kb0 + j < KB ? a : 0.f;
         su[j] = kb0 + j < KB ? b : 0.f;
       }
+      if (SA) {
+        // the block's activation tiles, one load per lane and group, once
+        // every wave is done reading the previous block's
+        __syncthreads();
+        const int kb = block_at(kb0, KB, rot);
+#pragma unroll
+        for (int gr = 0; gr < GR; ++gr) {
+          if (gr >= G) break;
+          __builtin_amdgcn_global_load_lds(xrow[gr] + kb * kBlock,
+                                           (lds_void_t*)(atile + gr * kActTile + 1024 * wave), 16,
+                                           0, 0);
+        }
+      }
       // every load of the round is issued before the first wait
       asm volatile("" ::: "memory");
       uint4 xa[GR][U][4];
+      if (!SA) {
 #pragma unroll
-      for (int gr = 0; gr < GR; ++gr) {
-        if (gr >= G) break;
+        for (int gr = 0; gr < GR; ++gr) {
+          if (gr >= G) break;
 #pragma unroll
-        for (int j = 0; j < U; ++j) {
-          const int kb = block_at(kb0 + j, KB, rot);
+          for (int j = 0; j < U; ++j) {
+            const int kb = block_at(kb0 + j, KB, rot);
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
-            xa[gr][j][m] = *reinterpret_cast<const uint4*>(xrow[gr] + kb * kBlock + 8 * m);
+            for (int m = 0; m < 4; ++m)
+              xa[gr][j][m] = *reinterpret_cast<const uint4*>(xrow[gr] + kb * kBlock + 8 * m);
+          }
         }
       }
       // The staged weights land in LDS through the loads' own path: the
@@ -258,6 +293,15 @@ __device__ __forceinline__ bool gate_up_tile(
       // for every load of the wave here (the activation loads above are
       // issued by then).
       wait_memory();
+      if (SA) {
+        __syncthreads();  // every wave's part of the tiles is in LDS
+#pragma unroll
+        for (int gr = 0; gr < GR; ++gr) {
+          if (gr >= G) break;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) xa[gr][0][m] = act_piece(atile + gr * kActTile, c, 4 * g + m);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         const unsigned char* st = stage + j * SB;
@@ -333,15 +377,16 @@ __device__ __forceinline__ bool gate_up_tile(
   return true;
 }
 
-template <int NS, int U, int GR, bool E8, int ROWS>
+template <int NS, int U, int GR, bool E8, int ROWS, bool SA>
 __global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
     const uint16_t* __restrict__ hidden, const uint8_t* __restrict__ w13,
     const void* __restrict__ scale13, const uint8_t* __restrict__ sw13,
     const void* __restrict__ sscale13, int H, int I_r, int Is, int k, int T, int SP,
     Workspace ws, float limit) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  gate_up_tile<NS, U, GR, E8, ROWS>(blockIdx.x, blockIdx.y, smem, hidden, w13, scale13, sw13,
-                                    sscale13, H, I_r, Is, k, T, SP, ws, limit);
+  gate_up_tile<NS, U, GR, E8, ROWS, false, SA>(blockIdx.x, blockIdx.y, smem, hidden, w13,
+                                               scale13, sw13, sscale13, H, I_r, Is, k, T, SP, ws,
+                                               limit);
 }
 
 // down projection.  Wave: output rows [h0, h0 + 16 NS) of one expert for all
@@ -352,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
 // first round of weight loads is issued and before the first activation is
 // read (every wave of the workgroup calls it); the kernel of its own passes
 // NoWait.
-template <int NS, int U, int GR, bool E8, int ROWS, typename Wait>
+template <int NS, int U, int GR, bool E8, int ROWS, typename Wait, bool SA = false>
 __device__ __forceinline__ void down_tile(
     int bx, int by, unsigned char* smem, const uint8_t* __restrict__ w2,
     const void* __restrict__ scale2, const uint8_t* __restrict__ sw2,
@@ -360,16 +405,23 @@ __device__ __forceinline__ void down_tile(
     const Workspace& ws, Wait wait) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  // SA: activation tiles shared through LDS (launches of one row kind)
+  static_assert(!SA || (U == 1 && ROWS != kAllRows), "a shared tile holds one block");
   const int h0 = (bx * kWaves + wave) * 16 * NS;
   Slot sl;
-  if (!slot_of<GR>(T, SP, ws, by, &sl) || h0 >= H) return;
+  if (!slot_of<GR>(T, SP, ws, by, &sl)) return;
+  // past the last row: with shared tiles the wave still loads its part of
+  // them and meets the workgroup's barriers, but streams no weights
+  const bool live = h0 < H;
+  if (!SA && !live) return;
   const bool shared = ROWS == kAllRows ? sl.shared : ROWS == kSharedRows;
   const int I = shared ? Is : I_r;
   const void* scale = shared ? sscale2 : scale2;
   constexpr int SB = NS * kSubtileBlock;
   unsigned char* stage = smem + wave * U * SB;
+  unsigned char* atile = smem + kWaves * U * SB;  // SA: GR x (hi, lo) tiles
   const int KB = I / kBlock;
-  const int rot = first_block(T, H, wave, KB, bx, by);
+  const int rot = first_block(T, H, SA ? 0 : wave, KB, bx, by);
   const uint8_t* W = shared ? sw2 : w2 + static_cast<size_t>(sl.e) * H * I;
   const uint8_t* lrow[2 * NS];
 #pragma unroll
@@ -385,11 +437,13 @@ __device__ __forceinline__ void down_tile(
 
   for (int p0 = sl.p_begin; p0 < sl.p_end; p0 += 16 * GR) {
     const int G = min(GR, (sl.p_end - p0 + 15) / 16);
+    // arow: the lane's own fragment row; SA: the tile row this lane loads
     size_t arow[GR];
 #pragma unroll
     for (int gr = 0; gr < GR; ++gr) {
-      const int q = min(p0 + gr * 16 + c, sl.p_end - 1);
-      arow[gr] = static_cast<size_t>(sl.base + q) * I + 32 * g;
+      const int r = SA ? 4 * wave + (lane >> 4) : c;
+      const int q = min(p0 + gr * 16 + r, sl.p_end - 1);
+      arow[gr] = static_cast<size_t>(sl.base + q) * I + (SA ? 8 * ((lane & 15) ^ r) : 32 * g);
     }
     f32x4_t f[GR][NS];
 #pragma unroll
@@ -401,8 +455,8 @@ __device__ __forceinline__ void down_tile(
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         const int kb = block_at(kb0 + j, KB, rot);
-        stage_block<2 * NS>(lrow, kb * kBlock, stage + j * SB);
-        const float s = load_scale<E8>(scale, s0 + kb);
+        if (live) stage_block<2 * NS>(lrow, kb * kBlock, stage + j * SB);
+        const float s = live ? load_scale<E8>(scale, s0 + kb) : 0.f;
         sc[j] = kb0 + j < KB ? s : 0.f;
       }
       asm volatile("" ::: "memory");
@@ -410,23 +464,55 @@ __device__ __forceinline__ void down_tile(
         wait();
         waited = true;
       }
+      if (SA) {
+        // the block's hi and lo activation tiles, once every wave is done
+        // reading the previous block's
+        __syncthreads();
+        const int kb = block_at(kb0, KB, rot);
+#pragma unroll
+        for (int gr = 0; gr < GR; ++gr) {
+          if (gr >= G) break;
+          unsigned char* t = atile + 2 * gr * kActTile + 1024 * wave;
+          __builtin_amdgcn_global_load_lds(act_hi + arow[gr] + kb * kBlock, (lds_void_t*)t, 16, 0,
+                                           0);
+          __builtin_amdgcn_global_load_lds(act_lo + arow[gr] + kb * kBlock,
+                                           (lds_void_t*)(t + kActTile), 16, 0, 0);
+        }
+      }
       uint4 ah[GR][U][4], al[GR][U][4];
+      if (!SA) {
 #pragma unroll
-      for (int gr = 0; gr < GR; ++gr) {
-        if (gr >= G) break;
+        for (int gr = 0; gr < GR; ++gr) {
+          if (gr >= G) break;
 #pragma unroll
-        for (int j = 0; j < U; ++j) {
-          const int kb = block_at(kb0 + j, KB, rot);
+          for (int j = 0; j < U; ++j) {
+            const int kb = block_at(kb0 + j, KB, rot);
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            ah[gr][j][m] = *reinterpret_cast<const uint4*>(act_hi + arow[gr] + kb * kBlock + 8 * m);
-            al[gr][j][m] = *reinterpret_cast<const uint4*>(act_lo + arow[gr] + kb * kBlock + 8 * m);
+            for (int m = 0; m < 4; ++m) {
+              ah[gr][j][m] =
+                  *reinterpret_cast<const uint4*>(act_hi + arow[gr] + kb * kBlock + 8 * m);
+              al[gr][j][m] =
+                  *reinterpret_cast<const uint4*>(act_lo + arow[gr] + kb * kBlock + 8 * m);
+            }
           }
         }
       }
       wait_memory();  // the staged weights are in LDS (see gate_up_tile)
+      if (SA) {
+        __syncthreads();  // every wave's part of the tiles is in LDS
+#pragma unroll
+        for (int gr = 0; gr < GR; ++gr) {
+          if (gr >= G) break;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            ah[gr][0][m] = act_piece(atile + 2 * gr * kActTile, c, 4 * g + m);
+            al[gr][0][m] = act_piece(atile + (2 * gr + 1) * kActTile, c, 4 * g + m);
+          }
+        }
+      }
 #pragma unroll
       for (int j = 0; j < U; ++j) {
+        if (!live) break;
         const unsigned char* st = stage + j * SB;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -461,7 +547,7 @@ __device__ __forceinline__ void down_tile(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int q = p0 + gr * 16 + 4 * g + i;
-        if (q < sl.p_end) {
+        if (live && q < sl.p_end) {
           const int o = shared ? q : ws.perm[sl.base + q];
           float* row = out + static_cast<size_t>(o) * H + h0 + c;
 #pragma unroll
@@ -476,14 +562,15 @@ struct NoWaitMfma {
   __device__ void operator()() const {}
 };
 
-template <int NS, int U, int GR, bool E8, int ROWS>
+template <int NS, int U, int GR, bool E8, int ROWS, bool SA>
 __global__ __launch_bounds__(kThreads) void down_mfma_kernel(
     const uint8_t* __restrict__ w2, const void* __restrict__ scale2,
     const uint8_t* __restrict__ sw2, const void* __restrict__ sscale2, int H, int I_r, int Is,
     int k, int T, int SP, Workspace ws) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  down_tile<NS, U, GR, E8, ROWS>(blockIdx.x, blockIdx.y, smem, w2, scale2, sw2, sscale2, H, I_r,
-                                 Is, k, T, SP, ws, NoWaitMfma());
+  down_tile<NS, U, GR, E8, ROWS, NoWaitMfma, SA>(blockIdx.x, blockIdx.y, smem, w2, scale2, sw2,
+                                                 sscale2, H, I_r, Is, k, T, SP, ws,
+                                                 NoWaitMfma());
 }
 
 // Per wave: NS 16-row weight subtiles, U scale blocks per round of loads,
@@ -508,25 +595,41 @@ constexpr int kNsDn = 4, kNsDnRouted = 8, kUDn = 1;
 constexpr int kGR = 1;  // 16-token groups per pass
 constexpr int kGr2MinMean = 10;
 bool routed_gr2(const LayerDims& d) { return d.T * d.k >= kGr2MinMean * d.E; }
+// From a mean of kSharedActMinMean tokens per expert the routed-only
+// launches load each 16-token activation tile once per workgroup into LDS
+// (SA), not once per wave.  Counters of the routed gate_up launch showed
+// every CU issuing about 0.1 L2 read request per clock whatever the kernel,
+// activation hits included: at H = 4096, E = 128 the hits were 18% of the
+// requests at 128 tokens and 33% at 256 (9% at H = 6144, E = 256, 128
+// tokens), a share the weight misses lose.  Measured at H = 4096 (step us,
+// two GPU sessions): 256 tokens 592 -> 568 and 589 -> 572; 128 tokens
+// 476 -> 472 and 474 -> 477, 192 tokens 536 -> 529 and 534 -> 540 (the
+// workgroup barriers cost about what the requests save); 96 tokens and
+// H = 6144 at 128 tokens slower by 1-2%.
+constexpr int kSharedActMinMean = 16;
+static_assert(kSharedActMinMean >= kGr2MinMean, "shared tiles come with two groups per pass");
+bool routed_sa(const LayerDims& d) { return d.T * d.k >= kSharedActMinMean * d.E; }
 constexpr size_t kLdsGu = static_cast<size_t>(kWaves) * kUGu * kNsGu * kSubtileBlock;
 
-template <bool E8, int ROWS, int GR = kGR, int NS = kNsGu>
+template <bool E8, int ROWS, int GR = kGR, int NS = kNsGu, bool SA = false>
 void launch_gu(dim3 grid, hipStream_t s, const uint16_t* x, const uint8_t* w, const void* scale,
                const uint8_t* sw, const void* sscale, const LayerDims& d, int SP,
                const Workspace& ws, hipEvent_t evb, hipEvent_t eve) {
-  MOE_LAUNCH((gate_up_mfma_kernel<NS, kUGu, GR, E8, ROWS>), grid, dim3(kThreads),
-             static_cast<size_t>(kWaves) * kUGu * NS * kSubtileBlock, s,
+  const size_t lds = static_cast<size_t>(kWaves) * kUGu * NS * kSubtileBlock +
+                     (SA ? static_cast<size_t>(GR) * kActTile : 0);
+  MOE_LAUNCH((gate_up_mfma_kernel<NS, kUGu, GR, E8, ROWS, SA>), grid, dim3(kThreads), lds, s,
              evb, eve, x, w, scale, sw, sscale, d.H, d.I, d.Is, d.k, d.T, SP, ws, d.limit);
 }
 
-template <int NS, bool E8, int ROWS, int GR = kGR>
+template <int NS, bool E8, int ROWS, int GR = kGR, bool SA = false>
 void launch_dn(int R, hipStream_t s, const uint8_t* w, const void* scale, const uint8_t* sw,
                const void* sscale, const LayerDims& d, int SP, const Workspace& ws) {
   const int per_wg = kWaves * 16 * NS;  // output rows per workgroup
   const dim3 grid((d.H + per_wg - 1) / per_wg, SP + R);
-  const size_t lds = static_cast<size_t>(kWaves) * kUDn * NS * kSubtileBlock;
-  hipLaunchKernelGGL((down_mfma_kernel<NS, kUDn, GR, E8, ROWS>), grid, dim3(kThreads), lds, s,
-                     w, scale, sw, sscale, d.H, d.I, d.Is, d.k, d.T, SP, ws);
+  const size_t lds = static_cast<size_t>(kWaves) * kUDn * NS * kSubtileBlock +
+                     (SA ? static_cast<size_t>(2 * GR) * kActTile : 0);
+  hipLaunchKernelGGL((down_mfma_kernel<NS, kUDn, GR, E8, ROWS, SA>), grid, dim3(kThreads), lds,
+                     s, w, scale, sw, sscale, d.H, d.I, d.Is, d.k, d.T, SP, ws);
 }
 
 // The gate_up and down tiles of the merged launch (shared passes and touched
@@ -904,16 +1007,22 @@ hipError_t launch_gate_up_mfma(const LayerDims& d, int rows, const void* hidden,
   const auto* x = static_cast<const uint16_t*>(hidden);
   const auto* w = static_cast<const uint8_t*>(w13);
   const auto* sw = static_cast<const uint8_t*>(sw13);
-#define MOE_GU(E8, ROWS, GR) \
-  launch_gu<E8, ROWS, GR>(grid, s, x, w, w13_scale, sw, sw13_scale, d, SP, ws, evb, eve)
+#define MOE_GU(E8, ROWS, GR, SA) \
+  launch_gu<E8, ROWS, GR, kNsGu, SA>(grid, s, x, w, w13_scale, sw, sw13_scale, d, SP, ws, evb, eve)
   if (rows == kAllRows) {
-    if (d.e8m0) MOE_GU(true, kAllRows, kGR); else MOE_GU(false, kAllRows, kGR);
+    if (d.e8m0) MOE_GU(true, kAllRows, kGR, false); else MOE_GU(false, kAllRows, kGR, false);
   } else if (rows == kSharedRows) {
-    if (d.e8m0) MOE_GU(true, kSharedRows, kGR); else MOE_GU(false, kSharedRows, kGR);
+    if (d.e8m0) MOE_GU(true, kSharedRows, kGR, false); else MOE_GU(false, kSharedRows, kGR, false);
   } else if (routed_gr2(d)) {
-    if (d.e8m0) MOE_GU(true, kRoutedRows, 2); else MOE_GU(false, kRoutedRows, 2);
+    // the shared tiles need the larger mean (kSharedActMinMean >= kGr2MinMean)
+    if (routed_sa(d)) {
+      if (d.e8m0) MOE_GU(true, kRoutedRows, 2, true); else MOE_GU(false, kRoutedRows, 2, true);
+    } else {
+      if (d.e8m0) MOE_GU(true, kRoutedRows, 2, false); else MOE_GU(false, kRoutedRows, 2, false);
+    }
   } else {
-    if (d.e8m0) MOE_GU(true, kRoutedRows, kGR); else MOE_GU(false, kRoutedRows, kGR);
+    if (d.e8m0) MOE_GU(true, kRoutedRows, kGR, false);
+    else MOE_GU(false, kRoutedRows, kGR, false);
   }
 #undef MOE_GU
   return hipGetLastError();
@@ -975,19 +1084,23 @@ hipError_t launch_down_mfma(const LayerDims& d, int rows, const void* w2, const 
   if (SP + R == 0) return hipSuccess;
   const auto* w = static_cast<const uint8_t*>(w2);
   const auto* sw = static_cast<const uint8_t*>(sw2);
-#define MOE_DN(NS, E8, ROWS, GR) \
-  launch_dn<NS, E8, ROWS, GR>(R, s, w, w2_scale, sw, sw2_scale, d, SP, ws)
+#define MOE_DN(NS, E8, ROWS, GR, SA) \
+  launch_dn<NS, E8, ROWS, GR, SA>(R, s, w, w2_scale, sw, sw2_scale, d, SP, ws)
   if (rows == kAllRows) {
-    if (d.e8m0) MOE_DN(kNsDn, true, kAllRows, kGR); else MOE_DN(kNsDn, false, kAllRows, kGR);
+    if (d.e8m0) MOE_DN(kNsDn, true, kAllRows, kGR, false);
+    else MOE_DN(kNsDn, false, kAllRows, kGR, false);
   } else if (rows == kSharedRows) {
-    if (d.e8m0) MOE_DN(kNsDn, true, kSharedRows, kGR);
-    else MOE_DN(kNsDn, false, kSharedRows, kGR);
+    if (d.e8m0) MOE_DN(kNsDn, true, kSharedRows, kGR, false);
+    else MOE_DN(kNsDn, false, kSharedRows, kGR, false);
+  } else if (routed_gr2(d) && routed_sa(d)) {
+    if (d.e8m0) MOE_DN(kNsDnRouted, true, kRoutedRows, 2, true);
+    else MOE_DN(kNsDnRouted, false, kRoutedRows, 2, true);
   } else if (routed_gr2(d)) {
-    if (d.e8m0) MOE_DN(kNsDnRouted, true, kRoutedRows, 2);
-    else MOE_DN(kNsDnRouted, false, kRoutedRows, 2);
+    if (d.e8m0) MOE_DN(kNsDnRouted, true, kRoutedRows, 2, false);
+    else MOE_DN(kNsDnRouted, false, kRoutedRows, 2, false);
   } else {
-    if (d.e8m0) MOE_DN(kNsDnRouted, true, kRoutedRows, kGR);
-    else MOE_DN(kNsDnRouted, false, kRoutedRows, kGR);
+    if (d.e8m0) MOE_DN(kNsDnRouted, true, kRoutedRows, kGR, false);
+    else MOE_DN(kNsDnRouted, false, kRoutedRows, kGR, false);
   }
 #undef MOE_DN
   return hipGetLastError();

@@ -38,6 +38,8 @@ def test_mfma_tile_matches_library():
     ns_r, u_r = (int(x) for x in bench.MFMA_ROUTED_TILE.split(","))
     assert (ns_r, u_r) == (ns, u)
     assert bench.GR2_MIN_MEAN == _const(mfma, "kGr2MinMean")
+    assert bench.SHARED_ACT_MIN_MEAN == _const(mfma, "kSharedActMinMean")
+    assert re.search(r"d\.T \* d\.k >= kSharedActMinMean \* d\.E", mfma)
     # a dense layer's gate_up kernel takes up to kDenseMaxGroups 16-token groups
     assert bench.DENSE_MAX_GROUPS == _const(mfma, "kDenseMaxGroups")
     assert "dense_gate_up_mfma_kernel" in mfma
