@@ -223,6 +223,7 @@ def cpu_model():
 
 MFMA_TAG = "mfma-record:"
 PEAK_BF16_MFMA_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+XCDS = 8  # MI355X accelerator complex dies
 
 
 def recorded_mfma(workload, kernel):
@@ -272,7 +273,8 @@ def mfma_summary(args):
             counters[name] = round(mean, 1)
             n = max(n, cnt)
     rec = {"workload": args.workload, "kernel": args.kernel, "counters": counters,
-           "dispatches": n, "cu_count": args.cu_count, "sources_sha256": sources_digest()}
+           "dispatches": n, "cu_count": args.cu_count, "xcds": XCDS,
+           "sources_sha256": sources_digest()}
     print(MFMA_TAG + json.dumps(rec))
 
 
@@ -597,7 +599,10 @@ def measure_point(name, args, ceiling):
             busy, gui, cus = (c.get("SQ_VALU_MFMA_BUSY_CYCLES"), c.get("GRBM_GUI_ACTIVE"),
                               mrec.get("cu_count"))
             if busy is not None and gui and cus:
-                mfma["mfma_busy_frac"] = round(busy / (gui * cus * 4), 5)
+                # GRBM_GUI_ACTIVE reads the busy cycles of each XCD's GRBM,
+                # summed over the XCDs; MFMA busy cycles are per SIMD (4 per CU)
+                cycles = gui / mrec.get("xcds", XCDS)
+                mfma["mfma_busy_frac"] = round(busy / (cycles * cus * 4), 5)
             mfma["counters"] = c
         else:
             mfma["counters"] = None
@@ -638,6 +643,8 @@ def measure_point(name, args, ceiling):
 
 HEADLINE = "decode_t1"
 POINTS = ["decode_t1", "decode_t16", "wide_t64_e8m0", "verify_t128"]
+# measured beside the metric's points, not part of it: the dense layer
+EXTRA_POINTS = ["dense_t16"]
 
 
 def main():
@@ -654,6 +661,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip the read-ceiling probe")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the points measured beside the metric (the dense layer)")
     ap.add_argument("--path", default="auto", choices=["auto", "step", "grouped", "split"])
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -707,6 +716,7 @@ def main():
         sys.exit(2)
     md.lib()  # fails loudly when the HIP library is missing
     names = [args.workload] if args.workload else POINTS
+    extra = [] if args.workload or args.no_extra else EXTRA_POINTS
     ceiling = None
     if not args.no_probe:
         ceiling = read_ceiling(torch, md)
@@ -714,9 +724,16 @@ def main():
                                                          100 * ceiling["frac_of_peak"],
                                                          PEAK_HBM_GBPS))
     points = [measure_point(n, args, ceiling) for n in names]
+    extra_points = []
+    for n in extra:
+        # no CPU baseline for these (it is reported for the headline point)
+        saved = args.no_cpu_baseline
+        args.no_cpu_baseline = True
+        extra_points.append(measure_point(n, args, ceiling))
+        args.no_cpu_baseline = saved
     head = points[0]
     cpu = head.get("cpu_baseline")
-    valid = all(p["waits_clean"] and p["check"]["pass"] for p in points)
+    valid = all(p["waits_clean"] and p["check"]["pass"] for p in points + extra_points)
     rec = {
         "metric": METRIC,
         "value": head["tbps"],
@@ -741,10 +758,11 @@ def main():
         "percentiles_us": {"p10": head["p10_us"], "p50": head["p50_us"], "p90": head["p90_us"]},
         "read_ceiling": ceiling,
         "frac_of_read_ceiling": head["frac_of_read_ceiling"],
-        "waits_clean": all(p["waits_clean"] for p in points),
+        "waits_clean": all(p["waits_clean"] for p in points + extra_points),
         "check": head["check"],
         "valid": valid,
         "points": points,
+        "extra_points": extra_points,
     }
     rec["config"]["parallelism"] = "none (1 GPU)"
     if cpu is not None:

@@ -72,6 +72,7 @@ WORKLOADS = {
     # slot) at the decode hidden size, intermediate 2 x hidden (the library's
     # largest): a synthetic choice, the pages give no dense-layer sizes
     "dense_t1": LayerShape(T=1, H=4096, E=0, k=0, I=0, Is=8192, scale_fmt="fp32", tag=5),
+    "dense_t16": LayerShape(T=16, H=4096, E=0, k=0, I=0, Is=8192, scale_fmt="fp32", tag=6),
 }
 WORKLOAD_ORDER = ["tiny_t1", "decode_t1", "decode_t16", "wide_t64_e8m0", "verify_t128"]
 
