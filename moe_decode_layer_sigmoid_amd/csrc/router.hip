@@ -114,10 +114,13 @@ __global__ __launch_bounds__(kThreads) void router_kernel(
 
 // Tokens per block: every wave of a block's workgroups loads all of the
 // block's token rows, so small blocks shorten the logits phase; larger ones
-// read the router weight fewer times (once per block).  One token per block
-// up to 16 tokens (2 us shorter at 16 tokens than blocks of 4), then
+// read the router weight fewer times (once per block).  With the logits
+// polled by each block's selecting workgroup (one wave per token), measured
+// on MI355X at E = 128, H = 4096 (us per launch, blocks of 1 / 2 / 4): 16
+// tokens 18.3 / 12.3 / 13.8, 8 tokens 10.8 / 11.1 / 12.5, 4 tokens 10.7 /
+// 11.6 / 11.8.  So one token per block up to 8 tokens, two up to 16, then
 // kRouterTokBlk (blocks of 2 measured slower at 64 and 128 tokens).
-int router_block_tokens(int T) { return T <= 16 ? 1 : kRouterTokBlk; }
+int router_block_tokens(int T) { return T <= 8 ? 1 : (T <= 16 ? 2 : kRouterTokBlk); }
 
 // ---------------------------------------------------------------------------
 // The router for many tokens on the matrix cores.  The logits are a small
