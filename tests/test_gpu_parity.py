@@ -111,6 +111,8 @@ SMALL = [
     # two tokens
     (1, 512, 256, 8, 256, 256, "e8m0"),
     (2, 384, 150, 6, 128, 0, "fp32"),
+    # the router's two-token blocks with a last block of one token
+    (13, 512, 48, 6, 256, 128, "fp32"),
 ]
 
 
@@ -368,6 +370,18 @@ def test_graph_replay_matches_eager(path, T, H, I, c_oracle):
     blocks (so at 24 tokens the rotated block walks wrap at odd points) and a
     shared expert narrower than the routed ones."""
     _graph_vs_eager(WORKLOADS["decode_t16"].replace(T=T, H=H, I=I, Is=256, tag=305), path)
+
+
+@pytest.mark.parametrize("path,T,H,Is", [(md.PATH_AUTO, 16, 2048, 3072),
+                                         (md.PATH_AUTO, 70, 1024, 2048),
+                                         (md.PATH_GEMV_SPLIT, 3, 1024, 2048)],
+                         ids=["dense-mfma-16", "dense-mfma-70", "dense-gemv-3"])
+def test_dense_graph_replay_matches_eager(path, T, H, Is):
+    """A dense layer's launches (the matrix-core kernels with their partial
+    planes and the boundary that adds them, or the GEMV kernels) captured
+    and replayed: every replay equals the eager run."""
+    _graph_vs_eager(LayerShape(T=T, H=H, E=0, k=0, I=0, Is=Is, scale_fmt="fp32", tag=350 + T),
+                    path)
 
 
 @pytest.mark.parametrize("name", ["decode_t1", "decode_t16"])

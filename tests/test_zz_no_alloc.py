@@ -74,6 +74,27 @@ def test_static_matches_plan_run(path, c_oracle):
         check_layer(inp, got, c_oracle=c_oracle)
 
 
+def test_static_dense_matches_plan_run():
+    """A dense layer (no routed experts) through the static entry point:
+    calls of 40, 16 and 1 tokens in a row (the matrix-core kernels' partial
+    planes and the GEMV kernels), each equal to moe_decode_run's output and
+    within the oracle's tolerance."""
+    base = LayerShape(T=40, H=1024, E=0, k=0, I=0, Is=2048, scale_fmt="fp32", tag=332)
+    for i, (T, path) in enumerate([(40, md.PATH_AUTO), (16, md.PATH_AUTO),
+                                   (1, md.PATH_GEMV_SPLIT)]):
+        sh = base.replace(T=T, tag=332 + T)
+        inp = make_layer(sh)
+        dev = to_device(inp)
+        plan = make_plan(sh, path=path)
+        ref = run_layer(plan, dev, T)
+        plan.close()
+        got = _run_static(sh, dev, path)
+        print("static dense call", i, "T", T, "path", path, flush=True)
+        for key in ("out", "residual_out", "moe"):
+            assert np.array_equal(got[key], ref[key]), (T, key)
+        check_layer(inp, got)
+
+
 def test_static_rejects_oversized_workspace():
     # 256 tokens x k = 16 x H = 8192 f32 down rows alone need 128 MiB
     sh = LayerShape(T=256, H=8192, E=64, k=16, I=128, Is=0, tag=331)
