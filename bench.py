@@ -49,6 +49,7 @@ MFMA_ROUTED_TILE = "4, 1"  # NS, U of the routed-only gate_up launch
 DENSE_MAX_GROUPS = 4  # 16-token groups per dense gate_up workgroup (kDenseMaxGroups)
 GR2_MIN_MEAN = 10  # the library's kGr2MinMean
 SHARED_ACT_MIN_MEAN = 16  # the library's kSharedActMinMean
+FUSED_BOUNDARY_MAX_TOKENS = 16  # the library's kFusedBoundaryMaxTokens
 METRIC = "µs per MoE layer and effective HBM TB/s (fraction of peak) at 1/16/64/128 tok"
 
 
@@ -344,6 +345,11 @@ def dominant_kernel(md, sh, path_taken, D, routed_b, shared_b, act_b):
     if path_taken == md.PATH_GROUPED and T <= MERGE_SHARED_MAX_TOKENS and H % 256 == 0:
         # one launch: the gate_up and down tiles of the touched experts and of
         # the shared expert's token passes (the boundary follows apart)
+        if T <= FUSED_BOUNDARY_MAX_TOKENS:
+            # with few tokens the boundary is in the same launch
+            return ("grouped_chain_kernel<E8> (routed + shared experts, gate_up and down, "
+                    "boundary)", "grouped_chain_kernel<%s>" % e8, routed_b + shared_b + act_b,
+                    6 * T * H * (k * sh.I + sh.Is))
         return ("grouped_chain_kernel<E8> (routed + shared experts, gate_up and down)",
                 "grouped_chain_kernel<%s>" % e8, routed_b + shared_b + T * H * 2,
                 6 * T * H * (k * sh.I + sh.Is))

@@ -438,11 +438,15 @@ static int run_on_device(moe_decode_plan_t p, const moe_decode_args* a, int32_t 
                                  p->ws, ss));
   }
   if (!side && moe::grouped_chain_supported(d)) {
-    // gate_up and down in one launch (the down tiles start in the gate_up drain)
+    // gate_up and down in one launch (the down tiles start in the gate_up
+    // drain), with few tokens the boundary too (right after the last down tile)
     if (err == hipSuccess)
       step(moe::launch_grouped_chain(d, a->hidden, a->w13, a->w13_scale, sw13, a->sw13_scale,
-                                     a->w2, a->w2_scale, sw2, a->sw2_scale, p->ws, s,
+                                     a->w2, a->w2_scale, sw2, a->sw2_scale, a->residual,
+                                     a->gamma, a->out, a->residual_out, a->moe_out, p->ws, s,
                                      p->user_begin, p->user_end));
+    if (moe::grouped_boundary_fused(d))
+      return err == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;
   } else {
     if (err == hipSuccess)
       step(moe::launch_gate_up_mfma(d, rows, a->hidden, a->w13, a->w13_scale, sw13,

@@ -35,6 +35,7 @@
 // i < 4.  A lane's 32 bytes of a 128-wide block feed the four MFMAs of the
 // block 8 bytes at a time (MFMA m takes contraction indices 32g + 8m + i),
 // and its activation loads follow the same order, so A and B agree.
+#include "boundary_device.h"
 #include "device_common.h"
 #include "launch.h"
 #include "sync_device.h"
@@ -397,7 +398,8 @@ __global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
 // first round of weight loads is issued and before the first activation is
 // read (every wave of the workgroup calls it); the kernel of its own passes
 // NoWait.
-template <int NS, int U, int GR, bool E8, int ROWS, typename Wait, bool SA = false>
+template <int NS, int U, int GR, bool E8, int ROWS, typename Wait, bool SA = false,
+          bool CST = false>
 __device__ __forceinline__ void down_tile(
     int bx, int by, unsigned char* smem, const uint8_t* __restrict__ w2,
     const void* __restrict__ scale2, const uint8_t* __restrict__ sw2,
@@ -551,7 +553,13 @@ __device__ __forceinline__ void down_tile(
           const int o = shared ? q : ws.perm[sl.base + q];
           float* row = out + static_cast<size_t>(o) * H + h0 + c;
 #pragma unroll
-          for (int s = 0; s < NS; ++s) row[16 * s] = f[gr][s][i];
+          for (int s = 0; s < NS; ++s) {
+            // CST: read in this launch (the merged launch's boundary)
+            if (CST)
+              st_f32<true>(row + 16 * s, f[gr][s][i]);
+            else
+              row[16 * s] = f[gr][s][i];
+          }
         }
       }
     }
@@ -633,9 +641,12 @@ void launch_dn(int R, hipStream_t s, const uint8_t* w, const void* scale, const 
 }
 
 // The gate_up and down tiles of the merged launch (shared passes and touched
-// slots, up to kMergeSharedMaxTokens tokens) as one launch: workgroups
-// [0, n_gu) are the gate_up tiles (row-major over grid rows), the rest the
-// down tiles.  A down tile issues its first round of weight loads, then waits
+// slots, up to kMergeSharedMaxTokens tokens) and the boundary as one launch:
+// workgroups [0, n_gu) are the gate_up tiles (row-major over grid rows), then
+// the n_dn down tiles, then T * bnd_ns boundary slices (boundary_device.h),
+// which wait until every down tile has written its rows (write-through
+// stores) and counted itself.  A down tile issues its first round of weight
+// loads, then waits
 // until every gate_up tile of its row has published its SwiGLU planes, so
 // the down weights stream while the gate_up tiles drain (their waves end over
 // a wide window: 130 to 187 us at 16 tokens).  A gate_up tile writes its
@@ -667,12 +678,31 @@ __global__ __launch_bounds__(kThreads, 4) void grouped_chain_kernel(GChainArgs a
     return;
   }
   const int v = it - a.n_gu;
-  const int by = v / a.dx, bx = v - by * a.dx;
-  // the row's gate_up tiles (a tile covers kWaves * 8 * kNsGu SwiGLU outputs)
-  const uint32_t target = static_cast<uint32_t>((by < a.SP ? a.Is : a.I) / (kWaves * 8 * kNsGu));
-  auto wait = [&]() { wait_count(sy, gchain_line(by, a.SP), 1, target, kGChainSpin); };
-  down_tile<kNsDn, kUDn, kGR, E8, kAllRows>(bx, by, smem, a.w2, a.w2_scale, a.sw2, a.sw2_scale,
-                                            a.H, a.I, a.Is, a.k, a.T, a.SP, ws, wait);
+  if (v < a.n_dn) {
+    const int by = v / a.dx, bx = v - by * a.dx;
+    // the row's gate_up tiles (a tile covers kWaves * 8 * kNsGu SwiGLU outputs)
+    const uint32_t target = static_cast<uint32_t>((by < a.SP ? a.Is : a.I) / (kWaves * 8 * kNsGu));
+    auto wait = [&]() { wait_count(sy, gchain_line(by, a.SP), 1, target, kGChainSpin); };
+    if (a.bnd_ns > 0) {
+      // the boundary is in this launch: rows written through, and counted
+      down_tile<kNsDn, kUDn, kGR, E8, kAllRows, decltype(wait), false, true>(
+          bx, by, smem, a.w2, a.w2_scale, a.sw2, a.sw2_scale, a.H, a.I, a.Is, a.k, a.T, a.SP,
+          ws, wait);
+      bump(sy, kSyncExit0 + v % kSyncExitLines);
+    } else {
+      down_tile<kNsDn, kUDn, kGR, E8, kAllRows, decltype(wait), false, false>(
+          bx, by, smem, a.w2, a.w2_scale, a.sw2, a.sw2_scale, a.H, a.I, a.Is, a.k, a.T, a.SP,
+          ws, wait);
+    }
+    return;
+  }
+  // ---- the boundary (the last T * bnd_ns workgroups), after every down tile
+  const int b = v - a.n_dn;
+  const BndArgs bn{a.residual, a.gamma, a.out, a.residual_out, a.moe_out, a.H, a.k, a.Is,
+                   a.bnd_ns, a.eps, ws.epi_part, sy.line(kSyncError)};
+  boundary_slice<false>(bn, ws, b / a.bnd_ns, b % a.bnd_ns, [&]() {
+    wait_count(sy, kSyncExit0, kSyncExitLines, static_cast<uint32_t>(a.n_dn), kGChainSpin);
+  }, StepTail{});
 }
 
 // Dense layers (no routed experts).  The MLP is one expert of I_s rows that
@@ -1110,10 +1140,14 @@ hipError_t launch_down_mfma(const LayerDims& d, int rows, const void* w2, const 
 
 namespace moe {
 
+bool grouped_boundary_fused(const LayerDims& d) { return d.T <= kFusedBoundaryMaxTokens; }
+
 bool grouped_chain_supported(const LayerDims& d) {
   // whole down tiles (every wave of a tile reaches the wait) and whole
   // gate_up tiles; the shared passes fit the flag lines
+  static_assert(kThreads == kBndThreads, "the boundary slices are workgroups of this launch");
   return d.T <= kMergeSharedMaxTokens && d.H % (kWaves * 16 * kNsDn) == 0 &&
+         (d.H + kBndCols - 1) / kBndCols <= kMaxBndSlices &&
          d.I % (kWaves * 8 * kNsGu) == 0 && d.Is % (kWaves * 8 * kNsGu) == 0 &&
          kNsDn * kWaves * 16 == 256 && shared_rows(d) <= kSyncSlot0 - kSyncFlags &&
          kLdsGu == static_cast<size_t>(kWaves) * kUDn * kNsDn * kSubtileBlock;
@@ -1122,8 +1156,10 @@ bool grouped_chain_supported(const LayerDims& d) {
 hipError_t launch_grouped_chain(const LayerDims& d, const void* hidden, const void* w13,
                                 const void* w13_scale, const void* sw13, const void* sw13_scale,
                                 const void* w2, const void* w2_scale, const void* sw2,
-                                const void* sw2_scale, const Workspace& ws, hipStream_t s,
-                                hipEvent_t evb, hipEvent_t eve) {
+                                const void* sw2_scale, const void* residual, const void* gamma,
+                                void* out, void* residual_out, void* moe_out,
+                                const Workspace& ws, hipStream_t s, hipEvent_t evb,
+                                hipEvent_t eve) {
   if (!grouped_chain_supported(d)) return hipErrorInvalidValue;
   GChainArgs a{};
   a.hidden = static_cast<const uint16_t*>(hidden);
@@ -1135,6 +1171,11 @@ hipError_t launch_grouped_chain(const LayerDims& d, const void* hidden, const vo
   a.w2_scale = w2_scale;
   a.sw2 = static_cast<const uint8_t*>(sw2);
   a.sw2_scale = sw2_scale;
+  a.residual = static_cast<const uint16_t*>(residual);
+  a.gamma = static_cast<const uint16_t*>(gamma);
+  a.out = static_cast<uint16_t*>(out);
+  a.residual_out = static_cast<uint16_t*>(residual_out);
+  a.moe_out = static_cast<uint16_t*>(moe_out);
   a.H = d.H;
   a.I = d.I;
   a.Is = d.Is;
@@ -1142,12 +1183,16 @@ hipError_t launch_grouped_chain(const LayerDims& d, const void* hidden, const vo
   a.T = d.T;
   a.SP = shared_rows(d);
   a.limit = d.limit;
+  a.eps = d.eps;
   const int rows = a.SP + slot_rows(d);
   const int Imax = d.I > d.Is ? d.I : d.Is;
   a.gx = Imax / (kWaves * 8 * kNsGu);
   a.dx = d.H / (kWaves * 16 * kNsDn);
   a.n_gu = a.gx * rows;
-  const int n = a.n_gu + a.dx * rows;
+  a.n_dn = a.dx * rows;
+  const bool bnd = grouped_boundary_fused(d);
+  a.bnd_ns = bnd ? (d.H + kBndCols - 1) / kBndCols : 0;
+  const int n = a.n_gu + a.n_dn + d.T * a.bnd_ns;
   if (d.e8m0)
     MOE_LAUNCH((grouped_chain_kernel<true>), dim3(n), dim3(kThreads), kLdsGu, s, evb, eve, a, ws);
   else

@@ -204,9 +204,15 @@ struct GChainArgs {
   const void* w2_scale;
   const uint8_t* sw2;
   const void* sw2_scale;
+  const uint16_t* residual;
+  const uint16_t* gamma;
+  uint16_t* out;
+  uint16_t* residual_out;
+  uint16_t* moe_out;  // nullable
   int H, I, Is, k, T, SP;
-  float limit;
+  float limit, eps;
   int gx, dx, n_gu;  // tiles per grid row (gate_up, down); gate_up workgroups
+  int n_dn, bnd_ns;  // down workgroups; boundary workgroups per token
 };
 
 struct LayerDims {
@@ -265,13 +271,25 @@ hipError_t launch_down_mfma(const LayerDims& d, int rows, const void* w2, const 
 
 // The same gate_up and down projections (shared passes and touched slots,
 // T <= kMergeSharedMaxTokens) as one launch whose down tiles wait for their
-// row's gate_up tiles; grouped_chain_supported tells whether the shape fits.
+// row's gate_up tiles; up to kFusedBoundaryMaxTokens tokens the boundary
+// joins it (grouped_boundary_fused), its slices waiting for every down tile,
+// which then writes its rows through to the coherence point.  Measured on
+// MI355X (us per step, boundary launched apart / in the launch): 16 tokens
+// 279.3 / 278.0, 8 tokens 180.9 / 180.0, 32 tokens 372.5 / 372.1, 64 tokens
+// at H = 6144 1296 / 1310 (the coherent stores of the down rows cost more
+// than the boundary launch they save).  grouped_chain_supported tells
+// whether the shape fits.  The router launch before it leaves the counters
+// and boundary slots at zero.
+constexpr int kFusedBoundaryMaxTokens = 16;
 bool grouped_chain_supported(const LayerDims& d);
+bool grouped_boundary_fused(const LayerDims& d);
 hipError_t launch_grouped_chain(const LayerDims& d, const void* hidden, const void* w13,
                                 const void* w13_scale, const void* sw13, const void* sw13_scale,
                                 const void* w2, const void* w2_scale, const void* sw2,
-                                const void* sw2_scale, const Workspace& ws, hipStream_t s,
-                                hipEvent_t evb = nullptr, hipEvent_t eve = nullptr);
+                                const void* sw2_scale, const void* residual, const void* gamma,
+                                void* out, void* residual_out, void* moe_out,
+                                const Workspace& ws, hipStream_t s, hipEvent_t evb = nullptr,
+                                hipEvent_t eve = nullptr);
 
 // Shared down, routed gate_up, routed down and the boundary in one launch
 // (T <= kChainMaxTokens; H <= 8192; I and I_s <= 4096).

@@ -277,11 +277,15 @@ __global__ __launch_bounds__(kThreads) void router_mfma_kernel(
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (int r = threadIdx.x; r < T * k; r += kThreads) sm.ids[r] = ld_i32<true>(ws.ids + r);
   build_routes<false>(T, E, k, ws, sm);
-  // the counters of the grouped merged launch that follows (zero_lines of
-  // them; none when separate launches follow)
+  // the counters and boundary slots of the grouped merged launch that
+  // follows (zero_lines of them; none when separate launches follow)
   for (int i = threadIdx.x; i < zero_lines; i += kThreads)
     if (i != kSyncError)
       __hip_atomic_store(ws.sync + static_cast<size_t>(i) * kSyncStride, 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  if (zero_lines > 0)
+    for (int i = threadIdx.x; i < T * kMaxBndSlices; i += kThreads)
+      __hip_atomic_store(reinterpret_cast<uint32_t*>(ws.epi_part) + i, 0u, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
 }
 

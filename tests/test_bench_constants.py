@@ -29,6 +29,7 @@ def test_token_limits_match_library():
     launch = _src("launch.h")
     assert bench.MERGE_SHARED_MAX_TOKENS == _const(launch, "kMergeSharedMaxTokens")
     assert bench.CHAIN_MAX_TOKENS == _const(launch, "kChainMaxTokens")
+    assert bench.FUSED_BOUNDARY_MAX_TOKENS == _const(launch, "kFusedBoundaryMaxTokens")
 
 
 def test_mfma_tile_matches_library():
