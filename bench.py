@@ -326,8 +326,9 @@ def dominant_kernel(md, sh, path_taken, D, routed_b, shared_b, act_b):
         if path_taken == md.PATH_GROUPED:
             groups = (T + 15) // 16
             gr = DENSE_MAX_GROUPS if groups >= DENSE_MAX_GROUPS else (2 if groups >= 2 else 1)
-            return ("dense_gate_up_mfma_kernel<E8, GR> (dense MLP)",
-                    "dense_gate_up_mfma_kernel<%s, %d>" % (e8, gr), kb, fl)
+            nb = 1 if gr == DENSE_MAX_GROUPS else 2  # blocks per round of loads
+            return ("dense_gate_up_mfma_kernel<E8, GR, NB> (dense MLP)",
+                    "dense_gate_up_mfma_kernel<%s, %d, %d>" % (e8, gr, nb), kb, fl)
         return ("router_kernel<NJ2, E8> (dense MLP gate_up tiles)",
                 "router_kernel<%d, %s>" % ((H + 511) // 512, e8), kb, fl)
     if path_taken == md.PATH_GEMV:

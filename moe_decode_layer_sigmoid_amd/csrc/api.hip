@@ -98,10 +98,13 @@ size_t layout(const moe_decode_desc& d, char* base, moe::Workspace* ws,
   w.rlogits = reinterpret_cast<float*>(take(T * E * 4));
   // the matrix-core router's counters (many tokens only)
   const bool rmfma = T >= moe::kRouterMfmaMinTokens && E > 0;
-  w.rcnt = reinterpret_cast<uint32_t*>(
-      take(rmfma ? moe::router_mfma_count_lines(static_cast<int>(T), static_cast<int>(E)) *
-                       moe::kSyncStride * 4
-                 : 0));
+  // (a dense layer: the arrival counters of its matrix-core launches)
+  const size_t rcnt_lines =
+      rmfma ? moe::router_mfma_count_lines(static_cast<int>(T), static_cast<int>(E))
+            : (E == 0 ? moe::dense_count_lines(static_cast<int>(T), static_cast<int>(H),
+                                               static_cast<int>(Is))
+                      : 0);
+  w.rcnt = reinterpret_cast<uint32_t*>(take(rcnt_lines * moe::kSyncStride * 4));
   if (state_bytes) *state_bytes = off;
   w.logits = reinterpret_cast<float*>(take(T * E * 4));
   w.ids = reinterpret_cast<int32_t*>(take(T * k * 4));
@@ -112,10 +115,14 @@ size_t layout(const moe_decode_desc& d, char* base, moe::Workspace* ws,
   w.n_touched = reinterpret_cast<int32_t*>(take(4));
   w.perm = reinterpret_cast<int32_t*>(take(T * k * 4));
   w.inv = reinterpret_cast<int32_t*>(take(T * k * 4));
-  w.act = reinterpret_cast<float*>(take(T * k * I * 4));
+  // (a dense layer: the partial sums of its matrix-core launches)
+  w.act = reinterpret_cast<float*>(
+      take(E == 0 ? moe::dense_part_floats(static_cast<int>(T), static_cast<int>(H),
+                                           static_cast<int>(Is)) * 4
+                  : T * k * I * 4));
   w.act_s = reinterpret_cast<float*>(take(T * (Is ? Is : 1) * 4));
   w.rows = reinterpret_cast<float*>(take(T * k * H * 4));
-  w.y_s = reinterpret_cast<float*>(take((E == 0 ? moe::kDenseDnMaxSplits : 1) * T * H * 4));
+  w.y_s = reinterpret_cast<float*>(take(T * H * 4));
   w.slot_tab = reinterpret_cast<int32_t*>(take(E * moe::kSlotInts * 4));
   w.rpart = reinterpret_cast<float*>(
       take(rmfma ? static_cast<size_t>(moe::router_mfma_slices(static_cast<int>(T),
@@ -328,18 +335,17 @@ static int run_step(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, hi
 // scales and swiglu_limit, and LayerStages.mlp sends dense(x) to the same
 // boundary as the MoE output.  GEMV path: the router kernel with no router
 // rows (only the gate_up tiles), the down kernel's shared row, the boundary;
-// MFMA path: the shared-row gate_up and down launches, the boundary.
+// MFMA path: the dense gate_up and down launches (launch_dense_mfma), the
+// boundary.
 static int run_dense(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, hipStream_t s) {
   const moe::LayerDims d = dims(p->desc, T);
   hipError_t err = hipSuccess;
   auto step = [&](hipError_t e) {
     if (err == hipSuccess && e != hipSuccess) err = e;
   };
-  int planes = 1;
   if (path_for(*p, T) == MOE_DECODE_PATH_GROUPED) {
     step(moe::launch_dense_mfma(d, a->hidden, a->sw13, a->sw13_scale, a->sw2, a->sw2_scale,
                                 p->ws, s, p->user_begin, p->user_end));
-    planes = moe::dense_down_splits(d);
   } else {
     step(moe::launch_router(d, a->hidden, nullptr, p->ws.zero_bias, p->ws, nullptr, nullptr,
                             a->sw13, a->sw13_scale, s, p->user_begin, p->user_end));
@@ -348,7 +354,7 @@ static int run_dense(moe_decode_plan_t p, const moe_decode_args* a, int32_t T, h
   }
   if (err == hipSuccess)
     step(moe::launch_epilogue(d, a->residual, a->gamma, p->ws, a->out, a->residual_out,
-                              a->moe_out, s, planes));
+                              a->moe_out, s));
   return err == hipSuccess ? MOE_DECODE_OK : MOE_DECODE_ERR_HIP;
 }
 

@@ -36,7 +36,7 @@ constexpr int kGroup = 8;        // routes whose rows one round of loads fetches
 // waves in order for the sum of squares.
 __global__ __launch_bounds__(kMaxThreads) void epilogue_kernel(
     const uint16_t* residual, const uint16_t* __restrict__ gamma, int H, int k, int has_shared,
-    int ys_planes, float eps, Workspace ws, uint16_t* out, uint16_t* residual_out,
+    float eps, Workspace ws, uint16_t* out, uint16_t* residual_out,
     uint16_t* moe_out) {
   __shared__ float s_part[kMaxThreads / kWave];
   const int t = blockIdx.x;
@@ -52,16 +52,8 @@ __global__ __launch_bounds__(kMaxThreads) void epilogue_kernel(
   // rows may then be incomplete, and out is written as NaN
   const uint32_t gave_up = ld_i32<true>(reinterpret_cast<const int*>(ws.sync) +
                                         kSyncError * kSyncStride);
-  float4 ya = *reinterpret_cast<const float4*>(ys);
-  float4 yb = *reinterpret_cast<const float4*>(ys + 4);
-  // a dense layer's down partial planes, added in plane order
-  const size_t plane = static_cast<size_t>(gridDim.x) * H;
-  for (int q = 1; q < ys_planes; ++q) {
-    const float4 pa = *reinterpret_cast<const float4*>(ys + q * plane);
-    const float4 pb = *reinterpret_cast<const float4*>(ys + q * plane + 4);
-    ya.x += pa.x; ya.y += pa.y; ya.z += pa.z; ya.w += pa.w;
-    yb.x += pb.x; yb.y += pb.y; yb.z += pb.z; yb.w += pb.w;
-  }
+  const float4 ya = *reinterpret_cast<const float4*>(ys);
+  const float4 yb = *reinterpret_cast<const float4*>(ys + 4);
   float acc[kCols];
 #pragma unroll
   for (int m = 0; m < kCols; ++m) acc[m] = 0.f;
@@ -131,11 +123,11 @@ __global__ __launch_bounds__(kMaxThreads) void epilogue_kernel(
 
 hipError_t launch_epilogue(const LayerDims& d, const void* residual, const void* gamma,
                            const Workspace& ws, void* out, void* residual_out, void* moe_out,
-                           hipStream_t s, int ys_planes) {
+                           hipStream_t s) {
   const int threads = ((d.H / kCols + kWave - 1) / kWave) * kWave;
   hipLaunchKernelGGL(epilogue_kernel, dim3(d.T), dim3(threads), 0, s,
                      static_cast<const uint16_t*>(residual), static_cast<const uint16_t*>(gamma),
-                     d.H, d.k, static_cast<int>(d.Is > 0), ys_planes, d.eps, ws,
+                     d.H, d.k, static_cast<int>(d.Is > 0), d.eps, ws,
                      static_cast<uint16_t*>(out),
                      static_cast<uint16_t*>(residual_out), static_cast<uint16_t*>(moe_out));
   return hipGetLastError();

@@ -35,6 +35,8 @@
 // i < 4.  A lane's 32 bytes of a 128-wide block feed the four MFMAs of the
 // block 8 bytes at a time (MFMA m takes contraction indices 32g + 8m + i),
 // and its activation loads follow the same order, so A and B agree.
+#include <algorithm>
+
 #include "boundary_device.h"
 #include "device_common.h"
 #include "launch.h"
@@ -708,22 +710,32 @@ __global__ __launch_bounds__(kThreads, 4) void grouped_chain_kernel(GChainArgs a
 // Dense layers (no routed experts).  The MLP is one expert of I_s rows that
 // every token takes, so a 16-token pass of the tiles above has only I_s / 64
 // gate_up and H / 64 down workgroups (128 and 64 at I_s = 8192, H = 4096):
-// too few loads in flight for HBM.  The kernels below give a workgroup a
-// narrow row tile and let its four waves split the contraction into four
-// contiguous ranges instead.  gate_up: 16 gate + 16 up rows per workgroup,
-// I_s / 16 workgroups per pass.  down: 32 output rows per workgroup, with
-// the contraction also split over S workgroups (dense_down_splits), each
-// writing an fp32 partial plane of the output that the boundary adds up in
-// plane order.  The waves' sums meet in LDS and are added in wave order, so
-// results stay deterministic.  Every 16-token pass streams the weights
-// again; workgroup b runs on XCD b % 8 (the dispatcher's round robin), so the
-// grid puts all passes of a tile on one XCD and next to each other in
-// dispatch order, where the later passes find the weight lines in that
-// XCD's L2.
-constexpr int kDenseUGu = 2, kDenseUDn = 1;  // scale blocks per round of loads
-constexpr int kDenseMaxGroups = 4;           // 16-token groups per workgroup
-constexpr int kDenseDnRows = 32;             // down rows per workgroup (8 per 16-row subtile pair)
+// too few loads in flight for HBM.  The kernels below split the contraction
+// over workgroups instead.  Each workgroup owns a row tile (gate_up: 64
+// SwiGLU outputs, wave w the 16 gate rows and the matching 16 up rows of
+// outputs 16 w ..; down: 128 output rows, wave w rows 32 w ..) over one of S
+// contiguous ranges of the contraction, and its four waves walk the same
+// 128-column blocks: the weights go to each wave's own LDS area, the
+// activations of a block are staged into LDS once per workgroup and read by
+// all four waves.  A CU serves L1 misses (L2 hits included) at about one
+// request per ten clocks, so activations read once per wave would cost as
+// many requests as the weights from 16 tokens on; staged once per workgroup
+// they cost a quarter of that.  The S workgroups of a tile write their fp32
+// partial sums; the last of them to arrive adds the ranges in range order
+// (results stay deterministic) and finishes the tile: the clamped SwiGLU into
+// the hi / lo planes, or the down output rows.  Every 16 GR-token pass
+// streams the weights again; workgroup b runs on XCD b % 8 (the dispatcher's
+// round robin), so the grid puts all passes of a unit on one XCD and next to
+// each other in dispatch order, where the later passes find the weight lines
+// in that XCD's L2.
+constexpr int kDenseGuOuts = 64;     // SwiGLU outputs per gate_up workgroup (16 per wave)
+constexpr int kDenseDnRows = 128;    // down output rows per workgroup (32 per wave)
+constexpr int kDenseMaxGroups = 4;   // 16-token groups per workgroup
+constexpr int kDenseGuMaxSplits = 4;
+constexpr int kDenseDnMaxSplits = 8;
+constexpr int kDenseMinGrid = 512;   // workgroups a launch aims for: two per CU
 constexpr int kXcds = 8;
+constexpr int kActBlock = 16 * kBlock * 2;  // LDS bytes of 16 tokens x 128 bf16 columns
 
 // blocks [*b0, *b0 + *nb) of range u of n equal contiguous ranges over KB blocks
 __device__ __forceinline__ void k_range(int u, int n, int KB, int* b0, int* nb) {
@@ -732,15 +744,15 @@ __device__ __forceinline__ void k_range(int u, int n, int KB, int* b0, int* nb) 
   *nb = b - a;
 }
 
-// Workgroup b -> (tile, pass), with every pass of a tile on one XCD and
-// adjacent in dispatch order (the grid holds ceil(tiles / 8) * 8 * P).
-__device__ __forceinline__ void xcd_tile_pass(int b, int P, int* tile, int* pass) {
+// Workgroup b -> (unit, pass), with every pass of a unit on one XCD and
+// adjacent in dispatch order (the grid holds ceil(units / 8) * 8 * P).
+__device__ __forceinline__ void xcd_tile_pass(int b, int P, int* unit, int* pass) {
   const int x = b % kXcds, r = b / kXcds;
   *pass = r % P;
-  *tile = (r / P) * kXcds + x;
+  *unit = (r / P) * kXcds + x;
 }
 
-// Block i of a wave's range (i past the end: the last, whose scale the
+// Block i of a workgroup's range (i past the end: the last, whose scale the
 // caller zeroes), rotated by rot so that the workgroups' first loads spread
 // over the row's columns.
 __device__ __forceinline__ int range_block(int i, int b0, int nb, int rot) {
@@ -748,14 +760,9 @@ __device__ __forceinline__ int range_block(int i, int b0, int nb, int rot) {
   return b0 + (j >= nb ? j - nb : j);
 }
 
-// The dense kernels read their activations line by line: load m of lane
-// (g, c) takes the 16 bytes at 64 m + 16 g of token c's 256-byte block row,
-// so the four lanes of a token read 64 contiguous bytes per load (the tiles
-// above, whose lanes read 64 bytes each over four loads, touch twice the
-// cache lines per load).  MFMA m then covers the block's columns
-// [32 m, 32 m + 32), lane group g its columns 32 m + 8 g .. + 7, and the
-// weight side follows: lane (g, c) reads the 8 bytes at 32 m + 8 g of row c,
-// half (g & 1) of staged piece 2 m + (g >> 1).
+// The weight side of MFMA m for lane (g, c): the 8 bytes at columns
+// 32 m + 8 g of row c of the staged block, half (g & 1) of staged piece
+// 2 m + (g >> 1) (pieces sit at slot p ^ (row % 8), see stage_block).
 __device__ __forceinline__ uint2 staged_half(const unsigned char* stage, int s, int c, int m,
                                              int g) {
   const int r8 = c & 7, p = 2 * m + (g >> 1);
@@ -763,26 +770,126 @@ __device__ __forceinline__ uint2 staged_half(const unsigned char* stage, int s, 
                                          16 * (p ^ r8) + 8 * (g & 1));
 }
 
-// gate_up + clamped SwiGLU of a dense layer: SwiGLU outputs [i0, i0 + 16),
-// tokens [16 GR pass, 16 GR (pass + 1)) as GR 16-token groups that share
-// each staged block of weights, into the hi / lo planes of ws.act_s.
-template <bool E8, int GR>
+// Activations of one 128-column block for one 16-token group, staged in LDS
+// (kActBlock bytes): token row r at 256 r, its 16-byte piece p at slot
+// p ^ r.  Wave w stages rows 4 w .. 4 w + 3 with one load instruction: lane
+// l takes row r = 4 w + l / 16 and lands at slot l % 16, so it fetches piece
+// (l % 16) ^ r; the 16 lanes of a row fetch its two whole 128-byte lines.
+// act_src gives lane l's source (row start + 8 ((l % 16) ^ r) elements).
+__device__ __forceinline__ const uint16_t* act_src(const uint16_t* row_start) {
+  const int lane = threadIdx.x & 63;
+  const int r = 4 * static_cast<int>(threadIdx.x >> 6) + (lane >> 4);
+  return row_start + 8 * ((lane & 15) ^ r);
+}
+__device__ __forceinline__ int act_row() {
+  return 4 * static_cast<int>(threadIdx.x >> 6) + ((threadIdx.x & 63) >> 4);
+}
+__device__ __forceinline__ void stage_act(const uint16_t* src, unsigned char* blk) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(blk + 1024 * (threadIdx.x >> 6)), 16, 0,
+                                   0);
+}
+// The activation side of MFMA m for lane (g, c): token c, columns
+// 32 m + 8 g .. + 7 (piece 4 m + g); the 16 lanes of one g read 16
+// different slots, so the read spreads over the banks.
+__device__ __forceinline__ bf16x8_t act_frag(const unsigned char* blk, int c, int m, int g) {
+  return as_bf16x8(*reinterpret_cast<const uint4*>(blk + 256 * c + 16 * ((4 * m + g) ^ c)));
+}
+
+// Contraction ranges of a dense launch: enough workgroups for two per CU,
+// at most max_s, two blocks per range at least.
+__host__ __device__ inline int dense_splits(int tiles, int P, int KB, int max_s) {
+  int S = (kDenseMinGrid + tiles * P - 1) / (tiles * P);
+  S = S < max_s ? S : max_s;
+  S = S < KB / 2 ? S : KB / 2;
+  return S > 1 ? S : 1;
+}
+
+// The S workgroups of (unit, pass) hand their sums to the last of them:
+// each stores its NV float4 per thread (write-through; nv of them hold
+// tokens) into its range's slot of `part`, then counts itself on `cnt`; the
+// last one resets the count and returns true with v[] replaced by the sums
+// over the ranges in range order (its own from registers).  The others
+// return false.  The loads of the sums are issued before their adds, up to
+// 16 per thread at a time: slots past S or nv are read too (they are in the
+// buffer) and not used.
+template <int NV, int MAXS>
+__device__ __forceinline__ bool dense_hand_in(f32x4_t (&v)[NV], int nv, float* part, int S,
+                                              int s, uint32_t* cnt, int* s_last) {
+  const int tid = threadIdx.x;
+  float* mine = part + static_cast<size_t>(s) * NV * kThreads * 4;
+#pragma unroll
+  for (int q = 0; q < NV; ++q)
+    if (q < nv)
+      st_f32x4<true>(mine + (static_cast<size_t>(q) * kThreads + tid) * 4,
+                     make_float4(v[q][0], v[q][1], v[q][2], v[q][3]));
+  wait_memory();
+  __syncthreads();
+  if (tid == 0)
+    *s_last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              static_cast<uint32_t>(S) - 1;
+  __syncthreads();
+  if (!*s_last) return false;
+  if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // QC slots at a time: at most 16 float4 loads (and their addresses) held
+  constexpr int QC = 16 / MAXS < NV ? (16 / MAXS > 0 ? 16 / MAXS : 1) : NV;
+  static_assert(NV % QC == 0, "whole chunks of slots");
+#pragma unroll
+  for (int q0 = 0; q0 < NV; q0 += QC) {
+    float4 y[QC][MAXS];
+#pragma unroll
+    for (int q = 0; q < QC; ++q)
+#pragma unroll
+      for (int r = 0; r < MAXS; ++r)
+      {
+        // uniform slot base (scalar registers) + the thread's 16 bytes
+        const float* slot = part + (static_cast<size_t>(r < S ? r : s) * NV + q0 + q) * kThreads * 4;
+        y[q][r] = *reinterpret_cast<const float4*>(slot + tid * 4);
+      }
+#pragma unroll
+    for (int q = 0; q < QC; ++q) {
+      const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+      f32x4_t t = zero;
+#pragma unroll
+      for (int r = 0; r < MAXS; ++r) {  // selects, no branches: ranges past S add zero
+        const f32x4_t x =
+            r == s ? v[q0 + q] : f32x4_t{y[q][r].x, y[q][r].y, y[q][r].z, y[q][r].w};
+        t += r < S ? x : zero;
+      }
+      v[q0 + q] = t;
+      asm volatile("" : "+v"(v[q0 + q]));  // the sums are done here, before the next
+    }                                       // slots' loads (which stay below)
+    asm volatile("" ::: "memory");
+  }
+  return true;
+}
+
+// gate_up + clamped SwiGLU of a dense layer: SwiGLU outputs of row tile
+// `tile` (64), tokens [16 GR pass, 16 GR (pass + 1)) as GR 16-token groups,
+// contraction range s of S; NB blocks per round of loads.  The activation
+// blocks are double-buffered, so one barrier per round orders both the
+// staging (its loads are in LDS) and the reuse of a buffer (every wave read
+// it two rounds before).
+template <bool E8, int GR, int NB>
 __global__ __launch_bounds__(kThreads, 2) void dense_gate_up_mfma_kernel(
     const uint16_t* __restrict__ hidden, const uint8_t* __restrict__ sw13,
-    const void* __restrict__ sscale13, int H, int Is, int T, int P, Workspace ws, float limit) {
+    const void* __restrict__ sscale13, int H, int Is, int T, int P, int S, Workspace ws,
+    float limit) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  int tile, pass;
-  xcd_tile_pass(blockIdx.x, P, &tile, &pass);
-  const int i0 = tile * 16;
-  if (i0 >= Is) return;  // uniform over the workgroup
+  __shared__ int s_last;
+  int unit, pass;
+  xcd_tile_pass(blockIdx.x, P, &unit, &pass);
+  if (unit >= (Is / kDenseGuOuts) * S) return;  // uniform over the workgroup
+  const int tile = unit / S, s = unit - tile * S;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-  constexpr int SB = 2 * kSubtileBlock;  // 16 gate + 16 up rows of one block
-  unsigned char* stage = smem + wave * kDenseUGu * SB;
+  const int i0 = tile * kDenseGuOuts + 16 * wave;  // this wave's SwiGLU outputs
+  constexpr int SB = 2 * kSubtileBlock;            // 16 gate + 16 up rows of one block
+  unsigned char* wst = smem + wave * NB * SB;
+  unsigned char* ast = smem + kWaves * NB * SB;    // [2][NB][GR] activation blocks
   const int KB = H / kBlock;
   int b0, nb;
-  k_range(wave, kWaves, KB, &b0, &nb);
-  const int rot = nb > 0 ? tile % nb : 0;
+  k_range(s, S, KB, &b0, &nb);
+  const int rot = tile % nb;
   // load rows: instructions 0, 1 = gate rows i0 .. i0 + 15, 2, 3 = up rows
   const uint8_t* lrow[4];
 #pragma unroll
@@ -792,44 +899,37 @@ __global__ __launch_bounds__(kThreads, 2) void dense_gate_up_mfma_kernel(
   const size_t su0 = static_cast<size_t>((Is + i0) / kBlock) * KB;
   const int p0 = pass * 16 * GR;
   const int G = min(GR, (T - p0 + 15) / 16);  // groups holding tokens (uniform)
-  const uint16_t* xrow[GR];
+  const uint16_t* xsrc[GR];
 #pragma unroll
   for (int gr = 0; gr < GR; ++gr)
-    xrow[gr] = hidden + static_cast<size_t>(min(p0 + 16 * gr + c, T - 1)) * H + 8 * g;
+    xsrc[gr] = act_src(hidden + static_cast<size_t>(min(p0 + 16 * gr + act_row(), T - 1)) * H);
   f32x4_t fg[GR], fu[GR];
 #pragma unroll
   for (int gr = 0; gr < GR; ++gr) {
     fg[gr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     fu[gr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  for (int i = 0; i < nb; i += kDenseUGu) {
-    float sg[kDenseUGu], su[kDenseUGu];
-    int kbs[kDenseUGu];
+  for (int i = 0, rd = 0; i < nb; i += NB, ++rd) {
+    unsigned char* ab = ast + (rd & 1) * NB * GR * kActBlock;
+    float sg[NB], su[NB];
 #pragma unroll
-    for (int j = 0; j < kDenseUGu; ++j) {
+    for (int j = 0; j < NB; ++j) {
       const int kb = range_block(i + j, b0, nb, rot);
-      kbs[j] = kb;
-      stage_block<4>(lrow, kb * kBlock, stage + j * SB);
+      stage_block<4>(lrow, kb * kBlock, wst + j * SB);
+      // every group, also past G (clamped rows): no branch around the staging
+#pragma unroll
+      for (int gr = 0; gr < GR; ++gr)
+        stage_act(xsrc[gr] + kb * kBlock, ab + (j * GR + gr) * kActBlock);
       const float a = load_scale<E8>(sscale13, sg0 + kb);
       const float b = load_scale<E8>(sscale13, su0 + kb);
       sg[j] = i + j < nb ? a : 0.f;
       su[j] = i + j < nb ? b : 0.f;
     }
-    asm volatile("" ::: "memory");
-    uint4 xa[GR][kDenseUGu][4];
+    wait_memory();    // this thread's staged pieces are in LDS
+    __syncthreads();  // and every other thread's
 #pragma unroll
-    for (int gr = 0; gr < GR; ++gr) {
-      if (gr >= G) break;
-#pragma unroll
-      for (int j = 0; j < kDenseUGu; ++j)
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          xa[gr][j][m] = *reinterpret_cast<const uint4*>(xrow[gr] + kbs[j] * kBlock + 32 * m);
-    }
-    wait_memory();  // the staged weights are in LDS (see gate_up_tile)
-#pragma unroll
-    for (int j = 0; j < kDenseUGu; ++j) {
-      const unsigned char* st = stage + j * SB;
+    for (int j = 0; j < NB; ++j) {
+      const unsigned char* st = wst + j * SB;
       f32x4_t pg[GR], pu[GR];
 #pragma unroll
       for (int gr = 0; gr < GR; ++gr) {
@@ -843,7 +943,7 @@ __global__ __launch_bounds__(kThreads, 2) void dense_gate_up_mfma_kernel(
 #pragma unroll
         for (int gr = 0; gr < GR; ++gr) {
           if (gr >= G) break;
-          const bf16x8_t a = as_bf16x8(xa[gr][j][m]);
+          const bf16x8_t a = act_frag(ab + (j * GR + gr) * kActBlock, c, m, g);
           pg[gr] = mfma(a, wg, pg[gr]);
           pu[gr] = mfma(a, wu, pu[gr]);
         }
@@ -858,63 +958,71 @@ __global__ __launch_bounds__(kThreads, 2) void dense_gate_up_mfma_kernel(
         }
       }
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): stage reads done
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS reads are done
   }
-  // The four ranges meet in LDS (the stage is free once every wave is past
-  // its last round): lane (g, c) of each wave holds tokens p0 + 16 gr + 4 g + e
-  // of SwiGLU output i0 + c; wave w then finishes e = w in wave order.
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);
+  // lane (g, c) holds tokens p0 + 16 gr + 4 g + e of SwiGLU output i0 + c
+  if (S > 1) {
+    f32x4_t v[2 * GR];
 #pragma unroll
-  for (int gr = 0; gr < GR; ++gr)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      red[((wave * GR + gr) * 8 + e) * kWave + lane] = fg[gr][e];
-      red[((wave * GR + gr) * 8 + 4 + e) * kWave + lane] = fu[gr][e];
+    for (int gr = 0; gr < GR; ++gr) {
+      v[2 * gr] = fg[gr];
+      v[2 * gr + 1] = fu[gr];
     }
-  __syncthreads();
+    const size_t u = static_cast<size_t>(tile) * P + pass;
+    float* part = ws.act + u * S * (2 * GR) * kThreads * 4;
+    if (!dense_hand_in<2 * GR, kDenseGuMaxSplits>(v, 2 * G, part, S, s, ws.rcnt + u * kSyncStride,
+                                                  &s_last))
+      return;
+#pragma unroll
+    for (int gr = 0; gr < GR; ++gr) {
+      fg[gr] = v[2 * gr];
+      fu[gr] = v[2 * gr + 1];
+    }
+  }
   uint16_t* act_hi = reinterpret_cast<uint16_t*>(ws.act_s);
 #pragma unroll
   for (int gr = 0; gr < GR; ++gr) {
-    const int q = p0 + 16 * gr + 4 * g + wave;
-    if (q < T) {
-      float ga = 0.f, ua = 0.f;
+    if (gr >= G) break;
 #pragma unroll
-      for (int v = 0; v < kWaves; ++v) {
-        ga += red[((v * GR + gr) * 8 + wave) * kWave + lane];
-        ua += red[((v * GR + gr) * 8 + 4 + wave) * kWave + lane];
+    for (int e = 0; e < 4; ++e) {
+      const int q = p0 + 16 * gr + 4 * g + e;
+      if (q < T) {
+        const float a = clamped_swiglu(fg[gr][e], fu[gr][e], limit);
+        const uint16_t hi = bf16_bits(a);
+        const uint16_t lo = bf16_bits(a - bf16_to_f32(hi));
+        const size_t o = static_cast<size_t>(q) * Is + i0 + c;
+        act_hi[o] = hi;
+        act_hi[static_cast<size_t>(T) * Is + o] = lo;
       }
-      const float a = clamped_swiglu(ga, ua, limit);
-      const uint16_t hi = bf16_bits(a);
-      const uint16_t lo = bf16_bits(a - bf16_to_f32(hi));
-      const size_t o = static_cast<size_t>(q) * Is + i0 + c;
-      act_hi[o] = hi;
-      act_hi[static_cast<size_t>(T) * Is + o] = lo;
     }
   }
 }
 
-// down projection of a dense layer: output rows [h0, h0 + 32), tokens
-// [16 GR pass, 16 GR (pass + 1)) as GR groups, contraction range s of S, into
-// the fp32 partial plane s of ws.y_s ([S][T][H]).
-template <bool E8, int GR>
+// down projection of a dense layer: output rows of row tile `rt` (128; wave
+// w rows 32 w .. 32 w + 31), tokens [16 GR pass, 16 GR (pass + 1)) as GR
+// groups, contraction range s of S, NB blocks per round; the last
+// workgroup of the tile writes the rows' sums to ws.y_s [T][H].  The
+// activations (the hi and lo planes) are staged as in the gate_up kernel.
+template <bool E8, int GR, int NB>
 __global__ __launch_bounds__(kThreads, 2) void dense_down_mfma_kernel(
     const uint8_t* __restrict__ sw2, const void* __restrict__ sscale2, int H, int Is, int T,
     int P, int S, Workspace ws) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int s_last;
   int unit, pass;
   xcd_tile_pass(blockIdx.x, P, &unit, &pass);
   if (unit >= (H / kDenseDnRows) * S) return;  // uniform over the workgroup
   const int rt = unit / S, s = unit - rt * S;
-  const int h0 = rt * kDenseDnRows;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-  constexpr int SB = 2 * kSubtileBlock;  // 32 rows of one block
-  unsigned char* stage = smem + wave * kDenseUDn * SB;
+  const int h0 = rt * kDenseDnRows + 32 * wave;  // this wave's rows
+  constexpr int SB = 2 * kSubtileBlock;          // 32 rows of one block
+  unsigned char* wst = smem + wave * NB * SB;
+  unsigned char* ast = smem + kWaves * NB * SB;  // [2][NB][GR][hi, lo] activation blocks
   const int KB = Is / kBlock;
   int b0, nb;
-  k_range(s * kWaves + wave, S * kWaves, KB, &b0, &nb);
-  const int rot = nb > 0 ? rt % nb : 0;
+  k_range(s, S, KB, &b0, &nb);
+  const int rot = rt % nb;
   const uint8_t* lrow[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -923,96 +1031,99 @@ __global__ __launch_bounds__(kThreads, 2) void dense_down_mfma_kernel(
   const int p0 = pass * 16 * GR;
   const int G = min(GR, (T - p0 + 15) / 16);
   const uint16_t* act_hi = reinterpret_cast<const uint16_t*>(ws.act_s);
-  const uint16_t* act_lo = act_hi + static_cast<size_t>(T) * Is;
-  size_t arow[GR];
+  const size_t lo_ofs = static_cast<size_t>(T) * Is;
+  const uint16_t* asrc[GR];
 #pragma unroll
   for (int gr = 0; gr < GR; ++gr)
-    arow[gr] = static_cast<size_t>(min(p0 + 16 * gr + c, T - 1)) * Is + 8 * g;
+    asrc[gr] = act_src(act_hi + static_cast<size_t>(min(p0 + 16 * gr + act_row(), T - 1)) * Is);
   f32x4_t f[GR][2];
 #pragma unroll
   for (int gr = 0; gr < GR; ++gr) {
     f[gr][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     f[gr][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  for (int i = 0; i < nb; i += kDenseUDn) {
-    float sc[kDenseUDn];
-    int kbs[kDenseUDn];
+  for (int i = 0, rd = 0; i < nb; i += NB, ++rd) {
+    unsigned char* ab = ast + (rd & 1) * NB * GR * 2 * kActBlock;
+    float sc[NB];
 #pragma unroll
-    for (int j = 0; j < kDenseUDn; ++j) {
+    for (int j = 0; j < NB; ++j) {
       const int kb = range_block(i + j, b0, nb, rot);
-      kbs[j] = kb;
-      stage_block<4>(lrow, kb * kBlock, stage + j * SB);
+      stage_block<4>(lrow, kb * kBlock, wst + j * SB);
+#pragma unroll
+      for (int gr = 0; gr < GR; ++gr) {  // every group (clamped rows), as in gate_up
+        unsigned char* blk = ab + (j * GR + gr) * 2 * kActBlock;
+        stage_act(asrc[gr] + kb * kBlock, blk);
+        stage_act(asrc[gr] + lo_ofs + kb * kBlock, blk + kActBlock);
+      }
       const float a = load_scale<E8>(sscale2, s0 + kb);
       sc[j] = i + j < nb ? a : 0.f;
     }
-    asm volatile("" ::: "memory");
-    uint4 ah[GR][kDenseUDn][4], al[GR][kDenseUDn][4];
+    wait_memory();    // this thread's staged pieces are in LDS
+    __syncthreads();  // and every other thread's
 #pragma unroll
-    for (int gr = 0; gr < GR; ++gr) {
-      if (gr >= G) break;
+    for (int j = 0; j < NB; ++j) {
+      // the block's weight fragments (both 16-row subtiles) once, then each
+      // group's activation fragments, each feeding both subtiles
+      bf16x8_t wa[2][4];
 #pragma unroll
-      for (int j = 0; j < kDenseUDn; ++j)
+      for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const size_t o = arow[gr] + kbs[j] * kBlock + 32 * m;
-          ah[gr][j][m] = *reinterpret_cast<const uint4*>(act_hi + o);
-          al[gr][j][m] = *reinterpret_cast<const uint4*>(act_lo + o);
+          const uint2 hw = staged_half(wst + j * SB, sub, c, m, g);
+          wa[sub][m] = fp8x8_to_bf16x8(hw.x, hw.y);
         }
-    }
-    wait_memory();  // the staged weights are in LDS (see gate_up_tile)
 #pragma unroll
-    for (int j = 0; j < kDenseUDn; ++j) {
-      const unsigned char* st = stage + j * SB;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        f32x4_t p[GR];
-#pragma unroll
-        for (int gr = 0; gr < GR; ++gr) p[gr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int gr = 0; gr < GR; ++gr) {
+        if (gr >= G) break;
+        const unsigned char* blk = ab + (j * GR + gr) * 2 * kActBlock;
+        f32x4_t p[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const uint2 hw = staged_half(st, sub, c, m, g);
-          const bf16x8_t wa = fp8x8_to_bf16x8(hw.x, hw.y);
+          const bf16x8_t ah = act_frag(blk, c, m, g);
+          const bf16x8_t al = act_frag(blk + kActBlock, c, m, g);
 #pragma unroll
-          for (int gr = 0; gr < GR; ++gr) {
-            if (gr >= G) break;
-            p[gr] = mfma(as_bf16x8(ah[gr][j][m]), wa, p[gr]);
-            p[gr] = mfma(as_bf16x8(al[gr][j][m]), wa, p[gr]);
+          for (int sub = 0; sub < 2; ++sub) {
+            p[sub] = mfma(ah, wa[sub][m], p[sub]);
+            p[sub] = mfma(al, wa[sub][m], p[sub]);
           }
         }
 #pragma unroll
-        for (int gr = 0; gr < GR; ++gr) {
-          if (gr >= G) break;
+        for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) f[gr][sub][e] = fmaf(sc[j], p[gr][e], f[gr][sub][e]);
-        }
+          for (int e = 0; e < 4; ++e) f[gr][sub][e] = fmaf(sc[j], p[sub][e], f[gr][sub][e]);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): stage reads done
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS reads are done
   }
-  // as in the gate_up kernel: lane (g, c) holds tokens p0 + 16 gr + 4 g + e
-  // of rows h0 + 16 sub + c; wave w adds up e = w over the waves, in wave order
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);
+  // lane (g, c) holds tokens p0 + 16 gr + 4 g + e of rows h0 + 16 sub + c
+  if (S > 1) {
+    f32x4_t v[2 * GR];
 #pragma unroll
-  for (int gr = 0; gr < GR; ++gr)
+    for (int gr = 0; gr < GR; ++gr) {
+      v[2 * gr] = f[gr][0];
+      v[2 * gr + 1] = f[gr][1];
+    }
+    const size_t u = static_cast<size_t>(rt) * P + pass;
+    float* part = ws.act + u * S * (2 * GR) * kThreads * 4;
+    if (!dense_hand_in<2 * GR, kDenseDnMaxSplits>(v, 2 * G, part, S, s, ws.rcnt + u * kSyncStride,
+                                                  &s_last))
+      return;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        red[((wave * GR + gr) * 8 + 4 * sub + e) * kWave + lane] = f[gr][sub][e];
-  __syncthreads();
+    for (int gr = 0; gr < GR; ++gr) {
+      f[gr][0] = v[2 * gr];
+      f[gr][1] = v[2 * gr + 1];
+    }
+  }
 #pragma unroll
   for (int gr = 0; gr < GR; ++gr) {
-    const int q = p0 + 16 * gr + 4 * g + wave;
-    if (q < T) {
-      float* out = ws.y_s + (static_cast<size_t>(s) * T + q) * H + h0 + c;
+    if (gr >= G) break;
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        float y = 0.f;
-#pragma unroll
-        for (int v = 0; v < kWaves; ++v)
-          y += red[((v * GR + gr) * 8 + 4 * sub + wave) * kWave + lane];
-        out[16 * sub] = y;
+    for (int e = 0; e < 4; ++e) {
+      const int q = p0 + 16 * gr + 4 * g + e;
+      if (q < T) {
+        float* out = ws.y_s + static_cast<size_t>(q) * H + h0 + c;
+        out[0] = f[gr][0][e];
+        out[16] = f[gr][1][e];
       }
     }
   }
@@ -1058,51 +1169,105 @@ hipError_t launch_gate_up_mfma(const LayerDims& d, int rows, const void* hidden,
   return hipGetLastError();
 }
 
-int dense_down_splits(const LayerDims& d) {
-  // two rounds of loads per wave at least
-  const int S = d.Is / kBlock / (kWaves * 2 * kDenseUDn);
-  return S < 1 ? 1 : (S > kDenseDnMaxSplits ? kDenseDnMaxSplits : S);
+// Token groups, passes and contraction ranges of a dense layer's launches.
+// The down kernel takes at most kDenseDnMaxGroups groups per workgroup: with
+// four, its activation blocks (two rounds, hi and lo planes) would not leave
+// room for two workgroups per CU.
+constexpr int kDenseDnMaxGroups = 2;
+struct DenseGrid {
+  int gr_gu, p_gu, n_gu, s_gu;  // gate_up: groups per workgroup, passes, row tiles, ranges
+  int gr_dn, p_dn, n_dn, s_dn;  // down
+};
+static int dense_gr(int groups, int max_gr) {
+  const int gr = groups >= 4 ? 4 : (groups >= 2 ? 2 : 1);
+  return gr < max_gr ? gr : max_gr;
+}
+static DenseGrid dense_grid(int T, int H, int Is) {
+  DenseGrid g;
+  const int groups = (T + 15) / 16;
+  g.gr_gu = dense_gr(groups, kDenseMaxGroups);
+  g.p_gu = (groups + g.gr_gu - 1) / g.gr_gu;
+  g.n_gu = Is / kDenseGuOuts;
+  g.s_gu = dense_splits(g.n_gu, g.p_gu, H / kBlock, kDenseGuMaxSplits);
+  g.gr_dn = dense_gr(groups, kDenseDnMaxGroups);
+  g.p_dn = (groups + g.gr_dn - 1) / g.gr_dn;
+  g.n_dn = H / kDenseDnRows;
+  g.s_dn = dense_splits(g.n_dn, g.p_dn, Is / kBlock, kDenseDnMaxSplits);
+  return g;
+}
+
+// (the grid depends on the token count only through its 16-token groups)
+size_t dense_part_floats(int maxT, int H, int Is) {
+  if (maxT < 1 || H < kDenseDnRows || Is < kDenseGuOuts) return 0;
+  size_t most = 0;
+  for (int groups = 1; groups <= (maxT + 15) / 16; ++groups) {
+    const DenseGrid g = dense_grid(16 * groups, H, Is);
+    const size_t gu = g.s_gu > 1 ? static_cast<size_t>(2 * g.gr_gu) * kThreads * 4 * g.p_gu *
+                                       g.n_gu * g.s_gu
+                                 : 0;
+    const size_t dn = g.s_dn > 1 ? static_cast<size_t>(2 * g.gr_dn) * kThreads * 4 * g.p_dn *
+                                       g.n_dn * g.s_dn
+                                 : 0;
+    most = std::max(most, std::max(gu, dn));
+  }
+  return most;
+}
+
+int dense_count_lines(int maxT, int H, int Is) {
+  if (maxT < 1 || H < kDenseDnRows || Is < kDenseGuOuts) return 0;
+  return std::max(Is / kDenseGuOuts, H / kDenseDnRows) * ((maxT + 15) / 16);
 }
 
 template <bool E8, int GR>
-static void launch_dense(const LayerDims& d, int P, const uint16_t* x, const uint8_t* w13,
-                         const void* s13, const uint8_t* w2, const void* s2, const Workspace& ws,
-                         hipStream_t s, hipEvent_t evb, hipEvent_t eve) {
-  const int n_gu = d.Is / 16;
-  const dim3 g1(static_cast<unsigned>((n_gu + kXcds - 1) / kXcds * kXcds * P));
-  // the stage, or the waves' sums after it (4 waves x GR groups x 8 x 64 floats)
-  const size_t red = static_cast<size_t>(kWaves) * GR * 8 * kWave * 4;
-  const size_t st1 = static_cast<size_t>(kWaves) * kDenseUGu * 2 * kSubtileBlock;
-  MOE_LAUNCH((dense_gate_up_mfma_kernel<E8, GR>), g1, dim3(kThreads), st1 > red ? st1 : red, s,
-             evb, eve, x, w13, s13, d.H, d.Is, d.T, P, ws, d.limit);
-  const int S = dense_down_splits(d);
-  const int n_dn = d.H / kDenseDnRows * S;
-  const dim3 g2(static_cast<unsigned>((n_dn + kXcds - 1) / kXcds * kXcds * P));
-  const size_t st2 = static_cast<size_t>(kWaves) * kDenseUDn * 2 * kSubtileBlock;
-  hipLaunchKernelGGL((dense_down_mfma_kernel<E8, GR>), g2, dim3(kThreads), st2 > red ? st2 : red,
-                     s, w2, s2, d.H, d.Is, d.T, P, S, ws);
+static void launch_dense_gate_up(const LayerDims& d, const DenseGrid& g, const uint16_t* x,
+                                 const uint8_t* w13, const void* s13, const Workspace& ws,
+                                 hipStream_t s, hipEvent_t evb, hipEvent_t eve) {
+  constexpr int NB = GR == kDenseMaxGroups ? 1 : 2;  // blocks per round
+  const size_t lds = kWaves * NB * 2 * kSubtileBlock + 2 * NB * GR * static_cast<size_t>(kActBlock);
+  const int units = g.n_gu * g.s_gu;
+  const dim3 grid(static_cast<unsigned>((units + kXcds - 1) / kXcds * kXcds * g.p_gu));
+  MOE_LAUNCH((dense_gate_up_mfma_kernel<E8, GR, NB>), grid, dim3(kThreads), lds, s, evb, eve, x,
+             w13, s13, d.H, d.Is, d.T, g.p_gu, g.s_gu, ws, d.limit);
+}
+
+template <bool E8, int GR>
+static void launch_dense_down(const LayerDims& d, const DenseGrid& g, const uint8_t* w2,
+                              const void* s2, const Workspace& ws, hipStream_t s) {
+  // blocks per round: two for one group, one for two (LDS for two workgroups per CU)
+  constexpr int NB = GR == 1 ? 2 : 1;
+  const size_t lds = kWaves * NB * 2 * kSubtileBlock +
+                     2 * NB * 2 * GR * static_cast<size_t>(kActBlock);
+  const int units = g.n_dn * g.s_dn;
+  const dim3 grid(static_cast<unsigned>((units + kXcds - 1) / kXcds * kXcds * g.p_dn));
+  hipLaunchKernelGGL((dense_down_mfma_kernel<E8, GR, NB>), grid, dim3(kThreads), lds, s, w2, s2,
+                     d.H, d.Is, d.T, g.p_dn, g.s_dn, ws);
 }
 
 hipError_t launch_dense_mfma(const LayerDims& d, const void* hidden, const void* sw13,
                              const void* sw13_scale, const void* sw2, const void* sw2_scale,
                              const Workspace& ws, hipStream_t s, hipEvent_t evb, hipEvent_t eve) {
-  if (d.E != 0 || d.Is <= 0 || d.T <= 0) return hipErrorInvalidValue;
-  const int groups = (d.T + 15) / 16;
-  const int GR = groups >= kDenseMaxGroups ? kDenseMaxGroups : (groups >= 2 ? 2 : 1);
-  const int P = (groups + GR - 1) / GR;  // grid passes of 16 GR tokens
+  if (d.E != 0 || d.Is <= 0 || d.T <= 0 || d.H % kDenseDnRows || d.Is % kDenseGuOuts)
+    return hipErrorInvalidValue;
+  const DenseGrid g = dense_grid(d.T, d.H, d.Is);
   const auto* x = static_cast<const uint16_t*>(hidden);
   const auto* w13 = static_cast<const uint8_t*>(sw13);
   const auto* w2 = static_cast<const uint8_t*>(sw2);
-#define MOE_DENSE(E8, GR_) \
-  launch_dense<E8, GR_>(d, P, x, w13, sw13_scale, w2, sw2_scale, ws, s, evb, eve)
-  if (GR == 1) {
-    if (d.e8m0) MOE_DENSE(true, 1); else MOE_DENSE(false, 1);
-  } else if (GR == 2) {
-    if (d.e8m0) MOE_DENSE(true, 2); else MOE_DENSE(false, 2);
+#define MOE_GU(E8, GR_) launch_dense_gate_up<E8, GR_>(d, g, x, w13, sw13_scale, ws, s, evb, eve)
+  if (g.gr_gu == 1) {
+    if (d.e8m0) MOE_GU(true, 1); else MOE_GU(false, 1);
+  } else if (g.gr_gu == 2) {
+    if (d.e8m0) MOE_GU(true, 2); else MOE_GU(false, 2);
   } else {
-    if (d.e8m0) MOE_DENSE(true, kDenseMaxGroups); else MOE_DENSE(false, kDenseMaxGroups);
+    if (d.e8m0) MOE_GU(true, kDenseMaxGroups); else MOE_GU(false, kDenseMaxGroups);
   }
-#undef MOE_DENSE
+#undef MOE_GU
+#define MOE_DN(E8, GR_) launch_dense_down<E8, GR_>(d, g, w2, sw2_scale, ws, s)
+  if (g.gr_dn == 1) {
+    if (d.e8m0) MOE_DN(true, 1); else MOE_DN(false, 1);
+  } else {
+    if (d.e8m0) MOE_DN(true, kDenseDnMaxGroups); else MOE_DN(false, kDenseDnMaxGroups);
+  }
+#undef MOE_DN
   return hipGetLastError();
 }
 

@@ -30,11 +30,11 @@ struct Workspace {
   int32_t* n_touched;  // [1]
   int32_t* perm;       // [maxT * k]  permuted position -> route t*k+j
   int32_t* inv;        // [maxT * k]  route -> permuted position
-  float* act;          // [maxT * k, I]   routed SwiGLU output, permuted order
+  float* act;          // [maxT * k, I]   routed SwiGLU output, permuted order; a dense
+                       // layer's partial sums (dense_part_floats)
   float* act_s;        // [maxT, Is]      shared SwiGLU output
   float* rows;         // [maxT * k, H]   routed down output, at route index t*k+j
-  float* y_s;          // [maxT, H] shared expert output; a dense layer's down
-                       // partial planes [kDenseDnMaxSplits][maxT, H]
+  float* y_s;          // [maxT, H] shared expert (or dense MLP) output
   uint32_t* counter;   // router arrival counters, router_cnt_words() (self-resetting)
   uint32_t* sync;      // [sync_words(E)] counters of the expert chain and grouped merged
                        // launches (zeroed by the router launch before them); the error word
@@ -52,7 +52,8 @@ struct Workspace {
   // written), zeroed again by the workgroup that reads them.
   float* rlogits;
   // The matrix-core router (many tokens): partial logits [slices][E][Tp]
-  // and its arrival counters (one line each, self-resetting).
+  // and its arrival counters (one line each, self-resetting); a dense
+  // layer's arrival counters (dense_count_lines).
   float* rpart;
   uint32_t* rcnt;
 };
@@ -305,13 +306,15 @@ size_t step_smem_bytes(const LayerDims& d);
 hipError_t launch_decode_step(const StepArgs& a, const Workspace& ws, hipStream_t s,
                               hipEvent_t evb = nullptr, hipEvent_t eve = nullptr);
 
-// A dense layer's MLP (d.E == 0) on the matrix cores: gate_up + SwiGLU with
-// each workgroup's contraction split over its waves, then down with the
-// contraction also split over dense_down_splits(d) workgroups, whose fp32
-// partial planes ([S][T][H] in ws.y_s, at most kDenseDnMaxSplits) the
-// boundary adds up.
-constexpr int kDenseDnMaxSplits = 8;
-int dense_down_splits(const LayerDims& d);
+// A dense layer's MLP (d.E == 0) on the matrix cores: gate_up + SwiGLU, then
+// down, each with the contraction split over workgroups whose fp32 partial
+// sums the last of a tile's workgroups adds up; the down output goes to
+// ws.y_s.  The partial sums use ws.act (a dense layer has no routed rows),
+// dense_part_floats(maxT, H, Is) floats; the arrival counters use ws.rcnt,
+// dense_count_lines(maxT, H, Is) lines (zero before the first run, reset by
+// the workgroups that use them).
+size_t dense_part_floats(int maxT, int H, int Is);
+int dense_count_lines(int maxT, int H, int Is);
 hipError_t launch_dense_mfma(const LayerDims& d, const void* hidden, const void* sw13,
                              const void* sw13_scale, const void* sw2, const void* sw2_scale,
                              const Workspace& ws, hipStream_t s, hipEvent_t evb = nullptr,
@@ -319,10 +322,8 @@ hipError_t launch_dense_mfma(const LayerDims& d, const void* hidden, const void*
 
 // Weighted combine + shared + residual, RMSNorm * gamma, bf16 outputs.
 // moe_out (nullable): also the finalized MoE output (before the residual).
-// ys_planes: partial planes of the shared (or dense) output in ws.y_s,
-// added in plane order.
 hipError_t launch_epilogue(const LayerDims& d, const void* residual, const void* gamma,
                            const Workspace& ws, void* out, void* residual_out, void* moe_out,
-                           hipStream_t s, int ys_planes = 1);
+                           hipStream_t s);
 
 }  // namespace moe
