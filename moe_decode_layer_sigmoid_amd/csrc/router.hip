@@ -21,6 +21,8 @@
 // bitmasks in LDS.  Data handed between workgroups goes through coherent
 // stores and loads; the counter and the logits reset themselves, so the
 // launch replays from a HIP graph.
+#include <algorithm>
+
 #include "device_common.h"
 #include "gemv_tiles.h"
 #include "launch.h"
@@ -131,7 +133,9 @@ int router_block_tokens(int T) { return T <= 8 ? 1 : (T <= 16 ? 2 : kRouterTokBl
 // 32 columns: bf16 products are exact, sums fp32) over one slice of the
 // contraction, so each operand row is read once per tile.  Phases:
 //   1 partials   workgroup (expert tile, token tile, slice): the tile's
-//                partial logits to ws.rpart[slice][expert][token]
+//                partial logits to ws.rpart[slice][expert][token]; each
+//                round's token rows are staged into LDS once for the four
+//                waves, which load their own expert rows
 //   2 logits     the last slice of a (token tile, expert tile) to finish
 //                sums the slices in slice order (deterministic) into
 //                ws.logits
@@ -142,6 +146,13 @@ int router_block_tokens(int T) { return T <= 8 ? 1 : (T <= 16 ? 2 : kRouterTokBl
 //                allows
 //   4 routes     the last of those to finish builds the route tables and
 //                empties the counters of the launch that follows
+// Measured on MI355X (rocprofv3, 128 tokens, E = 256, H = 6144): 24.8 us
+// with 384 workgroups whose waves each loaded the token rows, 22.9 us with
+// the rows staged once per workgroup and one workgroup per CU.  Ranking
+// workgroups that sum their token's slices themselves (no logits round
+// trip, no wait per expert tile) measured no faster (25.0 us): the launch
+// is a chain of dependent memory round trips (partials, counts, logits,
+// ids, route tables), not bound by its loads.
 // The MFMA takes any one-to-one assignment of contraction columns to lanes
 // as long as both operands use it: lane (g, c) holds, for steps 2j and
 // 2j + 1, columns 64 j + 16 g + [0, 8) and [8, 16) of its row, so that it
@@ -153,11 +164,13 @@ int router_block_tokens(int T) { return T <= 8 ? 1 : (T <= 16 ? 2 : kRouterTokBl
 constexpr int kRtTok = 16;     // tokens per tile (MFMA rows)
 constexpr int kRtExp = 64;     // experts per workgroup (16 per wave)
 constexpr int kRtSteps = 16;   // MFMA steps (32 columns each) per round of loads
-constexpr int kRtMaxGrid = 384;  // workgroups: all resident at once (2 or more per CU)
+constexpr int kRtMaxGrid = 256;  // workgroups: one per CU, all resident at once
+constexpr int kRtStageBytes = kRtTok * kRtSteps * 32 * 2;  // a round's token rows (16 KB)
 constexpr uint32_t kRtSpin = 1u << 17;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 __global__ __launch_bounds__(kThreads) void router_mfma_kernel(
     const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ router_w,
@@ -174,33 +187,64 @@ __global__ __launch_bounds__(kThreads) void router_mfma_kernel(
   const int e0 = et * kRtExp + wave * 16;
   uint32_t* err = ws.sync + kSyncError * kSyncStride;
 
-  // ---- phase 1: partial logits of tokens t0.., experts e0.. over the slice
-  if (e0 < E) {  // uniform per wave
+  // ---- phase 1: partial logits of tokens t0.., experts e0.. over the slice.
+  // The token rows of a round (16 x 512 columns) are staged into LDS once for
+  // the four waves (double-buffered: one barrier per round); each wave loads
+  // its own expert rows into registers.
+  {
+    const bool live = e0 < E;  // uniform per wave; the others only stage
     const int kb = sl * Ks;
-    const int nst = (min(H, kb + Ks) - kb) / 32;  // even: H and Ks are multiples of 64
+    const int kend = min(H, kb + Ks);
+    const int nst = (kend - kb) / 32;  // even: H and Ks are multiples of 64
     // rows past T or E repeat the last one (loads stay in bounds; never stored)
-    const uint16_t* xa = hidden + static_cast<size_t>(min(t0 + c, T - 1)) * H + kb + 16 * g;
     const uint16_t* wb = router_w + static_cast<size_t>(min(e0 + c, E - 1)) * H + kb + 16 * g;
+    // staging: piece L = 256 q + tid of the round's tile is token L / 64, LDS
+    // slot L % 64, and fetches 16-byte piece (L % 64) ^ token of that token's
+    // 512 columns, so that piece p of token c sits at slot p ^ c
+    const uint16_t* xs[4];
+    int xcol[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int L = 256 * q + static_cast<int>(threadIdx.x);
+      const int tok = L >> 6;
+      xs[q] = hidden + static_cast<size_t>(min(t0 + tok, T - 1)) * H;
+      xcol[q] = kb + 8 * ((L & 63) ^ tok);
+    }
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int r0 = 0; r0 < nst; r0 += kRtSteps) {
-      uint4 av[kRtSteps], bv[kRtSteps];
+    for (int r0 = 0, rd = 0; r0 < nst; r0 += kRtSteps, ++rd) {
+      unsigned char* stage = smem + (rd & 1) * kRtStageBytes;
 #pragma unroll
-      for (int i = 0; i < kRtSteps; ++i) {
-        // step i of the round: columns 64 (i / 2) + 16 g + 8 (i % 2), clamped
-        const int st = min(r0 + i, nst - 1);
-        const int col = 64 * (st >> 1) + 8 * (st & 1);
-        av[i] = *reinterpret_cast<const uint4*>(xa + col);
-        bv[i] = *reinterpret_cast<const uint4*>(wb + col);
+      for (int q = 0; q < 4; ++q)  // columns past the slice are staged but not used
+        __builtin_amdgcn_global_load_lds(xs[q] + min(xcol[q] + 32 * r0, H - 8),
+                                         (lds_void_t*)(stage + 4096 * q + 1024 * wave), 16, 0,
+                                         0);
+      uint4 bv[kRtSteps];
+      if (live) {
+#pragma unroll
+        for (int i = 0; i < kRtSteps; ++i) {
+          // step i of the round: columns 64 (i / 2) + 16 g + 8 (i % 2), clamped
+          const int st = min(r0 + i, nst - 1);
+          bv[i] = *reinterpret_cast<const uint4*>(wb + 64 * (st >> 1) + 8 * (st & 1));
+        }
       }
+      wait_memory();    // this thread's staged pieces are in LDS
+      __syncthreads();  // and every other thread's
+      if (live) {
 #pragma unroll
-      for (int i = 0; i < kRtSteps; ++i)
-        if (r0 + i < nst)  // uniform
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[i]),
-                                                        __builtin_bit_cast(bf16x8_t, bv[i]),
-                                                        acc, 0, 0, 0);
+        for (int i = 0; i < kRtSteps; ++i)
+          if (r0 + i < nst) {  // uniform
+            // token c's piece 8 (i / 2) + 2 g + i % 2: the same columns as bv[i]
+            const int pc = (8 * (i >> 1) + 2 * g + (i & 1)) ^ c;
+            const uint4 av = *reinterpret_cast<const uint4*>(stage + 1024 * c + 16 * pc);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                          __builtin_bit_cast(bf16x8_t, bv[i]),
+                                                          acc, 0, 0, 0);
+          }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS reads are done
     }
     // lane holds tokens t0 + 4g .. +3 of expert e0 + c
-    if (e0 + c < E)
+    if (live && e0 + c < E)
       st_f32x4<true>(ws.rpart + (static_cast<size_t>(sl) * E + e0 + c) * Tp + t0 + 4 * g,
                      make_float4(acc[0], acc[1], acc[2], acc[3]));
   }
@@ -318,7 +362,9 @@ hipError_t launch_router_mfma(const LayerDims& d, const void* hidden, const void
       router_mfma_tokens_padded(d.T) > Tp_alloc)
     return hipErrorInvalidValue;
   dim3 grid(n_et, n_tt, (d.H + Ks - 1) / Ks);
-  const size_t smem = route_smem_bytes(d.T, d.E, d.k);
+  // the staged token rows (two rounds), or the routing step's scratch after them
+  const size_t smem =
+      std::max(route_smem_bytes(d.T, d.E, d.k), 2 * static_cast<size_t>(kRtStageBytes));
   hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(kThreads), smem, s,
                      static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(router_w),
                      bias, d.T, d.H, d.E, d.k, d.rsf, static_cast<int>(grid.z), Ks, Tp_alloc,
