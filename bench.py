@@ -325,7 +325,10 @@ def dominant_kernel(md, sh, path_taken, D, routed_b, shared_b, act_b):
         fl = 2 * T * 2 * sh.Is * H
         if path_taken == md.PATH_GROUPED:
             groups = (T + 15) // 16
-            gr = DENSE_MAX_GROUPS if groups >= DENSE_MAX_GROUPS else (2 if groups >= 2 else 1)
+            if groups == 1:  # one token group: the waves split the contraction
+                return ("dense_gate_up_waves_mfma_kernel<E8> (dense MLP)",
+                        "dense_gate_up_waves_mfma_kernel<%s>" % e8, kb, fl)
+            gr = DENSE_MAX_GROUPS if groups >= DENSE_MAX_GROUPS else 2
             nb = 1 if gr == DENSE_MAX_GROUPS else 2  # blocks per round of loads
             return ("dense_gate_up_mfma_kernel<E8, GR, NB> (dense MLP)",
                     "dense_gate_up_mfma_kernel<%s, %d, %d>" % (e8, gr, nb), kb, fl)

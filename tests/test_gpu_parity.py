@@ -230,7 +230,8 @@ def test_dense_layer_mfma_splits(T, H, Is, fmt):
     """The dense MFMA kernels at the shapes that set their contraction
     ranges and token groups: 4 and 1 gate_up ranges, 8 and 2 down ranges,
     ranges of unequal length (H = 1408 and I_s = 640: 11 and 5 blocks), one
-    range per launch (H = 384, I_s = 512: no hand-over of sums), one, two and
+    range per launch (H = 384, I_s = 512: no hand-over of sums), the
+    one-group gate_up kernel (whose waves split the contraction), two and
     four 16-token groups per gate_up workgroup, two passes of the down
     launch, a second pass with one group (33 tokens) and a second pass whose
     one group is partial (75 tokens); every output row against the dense
