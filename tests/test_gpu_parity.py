@@ -381,9 +381,10 @@ def test_graph_replay_matches_eager(path, T, H, I, c_oracle):
                                          (md.PATH_GEMV_SPLIT, 3, 1024, 2048)],
                          ids=["dense-mfma-16", "dense-mfma-70", "dense-gemv-3"])
 def test_dense_graph_replay_matches_eager(path, T, H, Is):
-    """A dense layer's launches (the matrix-core kernels with their partial
-    planes and the boundary that adds them, or the GEMV kernels) captured
-    and replayed: every replay equals the eager run."""
+    """A dense layer's launches (the matrix-core kernels, whose workgroups
+    hand partial sums to the last of each tile through counters that they
+    reset, or the GEMV kernels) captured and replayed: every replay equals
+    the eager run."""
     _graph_vs_eager(LayerShape(T=T, H=H, E=0, k=0, I=0, Is=Is, scale_fmt="fp32", tag=350 + T),
                     path)
 
