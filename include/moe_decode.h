@@ -112,9 +112,12 @@ typedef enum {
  * (sw13, sw2 and their scales), the router and routed-expert pointers may be
  * NULL, and a run computes out, residual_out and moe_out (= the MLP output)
  * through the same boundary.  AUTO takes the MFMA kernels at every token
- * count: gate_up with each workgroup's contraction split over its four
- * waves, then down with the contraction also split over up to eight
- * workgroups, whose partial outputs the boundary adds in a fixed order.
+ * count: gate_up (up to 16 tokens with each workgroup's contraction split
+ * over its four waves; above, with the contraction split over up to four
+ * workgroups), then down with the contraction split over up to eight
+ * workgroups; the last workgroup of a tile adds the partial sums in a fixed
+ * order.  Such a plan's workspace also holds those partial sums and their
+ * arrival counters.
  */
 typedef struct {
   int32_t hidden;              /* H */
