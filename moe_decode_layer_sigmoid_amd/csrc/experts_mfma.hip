@@ -214,7 +214,9 @@ __device__ __forceinline__ bool gate_up_tile(
   const void* scale = shared ? sscale13 : scale13;
   constexpr int SB = NS * kSubtileBlock;  // stage bytes of one block
   unsigned char* stage = smem + wave * U * SB;
-  unsigned char* atile = smem + kWaves * U * SB;  // SA: GR tiles of kActTile bytes
+  // SA: two rounds of GR tiles of kActTile bytes (double-buffered)
+  unsigned char* atile = smem + kWaves * U * SB;
+  int rd = 0;  // rounds so far, over all passes: the tiles' buffer
   const int KB = H / kBlock;
   // with shared tiles every wave of the workgroup walks the same blocks
   const int rot = first_block(T, H, SA ? 0 : wave, KB, bx, by);
@@ -262,17 +264,18 @@ __device__ __forceinline__ bool gate_up_tile(
         sg[j] = kb0 + j < KB ? a : 0.f;
         su[j] = kb0 + j < KB ? b : 0.f;
       }
+      unsigned char* at = atile + (rd & 1) * GR * kActTile;
       if (SA) {
-        // the block's activation tiles, one load per lane and group, once
-        // every wave is done reading the previous block's
-        __syncthreads();
+        // the block's activation tiles, one load per lane and group, into
+        // the buffer every wave last read two rounds ago (before its barrier
+        // of the previous round)
         const int kb = block_at(kb0, KB, rot);
 #pragma unroll
         for (int gr = 0; gr < GR; ++gr) {
           if (gr >= G) break;
           __builtin_amdgcn_global_load_lds(xrow[gr] + kb * kBlock,
-                                           (lds_void_t*)(atile + gr * kActTile + 1024 * wave), 16,
-                                           0, 0);
+                                           (lds_void_t*)(at + gr * kActTile + 1024 * wave), 16, 0,
+                                           0);
         }
       }
       // every load of the round is issued before the first wait
@@ -302,7 +305,7 @@ __device__ __forceinline__ bool gate_up_tile(
         for (int gr = 0; gr < GR; ++gr) {
           if (gr >= G) break;
 #pragma unroll
-          for (int m = 0; m < 4; ++m) xa[gr][0][m] = act_piece(atile + gr * kActTile, c, 4 * g + m);
+          for (int m = 0; m < 4; ++m) xa[gr][0][m] = act_piece(at + gr * kActTile, c, 4 * g + m);
         }
       }
 #pragma unroll
@@ -344,6 +347,7 @@ __device__ __forceinline__ bool gate_up_tile(
       }
       // the next round's loads overwrite the stage: its reads must be done
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      ++rd;
     }
     // lane holds tokens p0 + 16 gr + 4 g + i of SwiGLU outputs i0 + 16 h + c
 #pragma unroll
@@ -400,6 +404,16 @@ __global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(
 // first round of weight loads is issued and before the first activation is
 // read (every wave of the workgroup calls it); the kernel of its own passes
 // NoWait.
+// Activation tile buffers of a shared-tile (SA) down launch: two (one
+// barrier per block) where the workgroup's LDS stays within half a CU's
+// 160 KB, so that two workgroups fit; else one, refilled after a second
+// barrier.  Measured on MI355X at H = 4096, E = 128, 256 tokens (two groups,
+// 128 rows per wave): double-buffered tiles took 96 KB and one workgroup per
+// CU, 574 -> 611 us per layer.
+__host__ __device__ constexpr int dn_sa_buffers(int NS, int U, int GR) {
+  return kWaves * U * NS * kSubtileBlock + 4 * GR * kActTile <= 80 * 1024 ? 2 : 1;
+}
+
 template <int NS, int U, int GR, bool E8, int ROWS, typename Wait, bool SA = false,
           bool CST = false>
 __device__ __forceinline__ void down_tile(
@@ -423,7 +437,11 @@ __device__ __forceinline__ void down_tile(
   const void* scale = shared ? sscale2 : scale2;
   constexpr int SB = NS * kSubtileBlock;
   unsigned char* stage = smem + wave * U * SB;
-  unsigned char* atile = smem + kWaves * U * SB;  // SA: GR x (hi, lo) tiles
+  // SA: GR x (hi, lo) tiles, double-buffered where two workgroups per CU
+  // still fit (dn_sa_buffers)
+  constexpr int NBUF = dn_sa_buffers(NS, U, GR);
+  unsigned char* atile = smem + kWaves * U * SB;
+  int rd = 0;  // rounds so far, over all passes: the tiles' buffer
   const int KB = I / kBlock;
   const int rot = first_block(T, H, SA ? 0 : wave, KB, bx, by);
   const uint8_t* W = shared ? sw2 : w2 + static_cast<size_t>(sl.e) * H * I;
@@ -468,15 +486,17 @@ __device__ __forceinline__ void down_tile(
         wait();
         waited = true;
       }
+      unsigned char* at = atile + (NBUF == 2 ? (rd & 1) * 2 * GR * kActTile : 0);
       if (SA) {
-        // the block's hi and lo activation tiles, once every wave is done
-        // reading the previous block's
-        __syncthreads();
+        // the block's hi and lo activation tiles: into the buffer every wave
+        // last read two rounds ago (as in gate_up_tile), or into the one
+        // buffer once every wave is done reading the previous block's
+        if (NBUF == 1) __syncthreads();
         const int kb = block_at(kb0, KB, rot);
 #pragma unroll
         for (int gr = 0; gr < GR; ++gr) {
           if (gr >= G) break;
-          unsigned char* t = atile + 2 * gr * kActTile + 1024 * wave;
+          unsigned char* t = at + 2 * gr * kActTile + 1024 * wave;
           __builtin_amdgcn_global_load_lds(act_hi + arow[gr] + kb * kBlock, (lds_void_t*)t, 16, 0,
                                            0);
           __builtin_amdgcn_global_load_lds(act_lo + arow[gr] + kb * kBlock,
@@ -509,8 +529,8 @@ __device__ __forceinline__ void down_tile(
           if (gr >= G) break;
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            ah[gr][0][m] = act_piece(atile + 2 * gr * kActTile, c, 4 * g + m);
-            al[gr][0][m] = act_piece(atile + (2 * gr + 1) * kActTile, c, 4 * g + m);
+            ah[gr][0][m] = act_piece(at + 2 * gr * kActTile, c, 4 * g + m);
+            al[gr][0][m] = act_piece(at + (2 * gr + 1) * kActTile, c, 4 * g + m);
           }
         }
       }
@@ -544,6 +564,7 @@ __device__ __forceinline__ void down_tile(
         }
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): stage reads done
+      ++rd;
     }
 #pragma unroll
     for (int gr = 0; gr < GR; ++gr) {
@@ -619,6 +640,13 @@ bool routed_gr2(const LayerDims& d) { return d.T * d.k >= kGr2MinMean * d.E; }
 constexpr int kSharedActMinMean = 16;
 static_assert(kSharedActMinMean >= kGr2MinMean, "shared tiles come with two groups per pass");
 bool routed_sa(const LayerDims& d) { return d.T * d.k >= kSharedActMinMean * d.E; }
+// One group per pass: shared tiles from this mean on.  With the tiles
+// double-buffered (one barrier per block; the down launch's where LDS
+// allows), measured on MI355X (us per layer): H = 4096, E = 128, 128 tokens
+// 474.5 -> 463.4; H = 6144, E = 256, 256 tokens 1703.5 -> 1665.9; and with
+// two groups at H = 4096, 256 tokens 574.5 -> 562.0.
+constexpr int kSharedActMinMean1 = 8;
+bool routed_sa1(const LayerDims& d) { return d.T * d.k >= kSharedActMinMean1 * d.E; }
 constexpr size_t kLdsGu = static_cast<size_t>(kWaves) * kUGu * kNsGu * kSubtileBlock;
 
 template <bool E8, int ROWS, int GR = kGR, int NS = kNsGu, bool SA = false>
@@ -626,7 +654,7 @@ void launch_gu(dim3 grid, hipStream_t s, const uint16_t* x, const uint8_t* w, co
                const uint8_t* sw, const void* sscale, const LayerDims& d, int SP,
                const Workspace& ws, hipEvent_t evb, hipEvent_t eve) {
   const size_t lds = static_cast<size_t>(kWaves) * kUGu * NS * kSubtileBlock +
-                     (SA ? static_cast<size_t>(GR) * kActTile : 0);
+                     (SA ? static_cast<size_t>(2 * GR) * kActTile : 0);
   MOE_LAUNCH((gate_up_mfma_kernel<NS, kUGu, GR, E8, ROWS, SA>), grid, dim3(kThreads), lds, s,
              evb, eve, x, w, scale, sw, sscale, d.H, d.I, d.Is, d.k, d.T, SP, ws, d.limit);
 }
@@ -637,7 +665,8 @@ void launch_dn(int R, hipStream_t s, const uint8_t* w, const void* scale, const 
   const int per_wg = kWaves * 16 * NS;  // output rows per workgroup
   const dim3 grid((d.H + per_wg - 1) / per_wg, SP + R);
   const size_t lds = static_cast<size_t>(kWaves) * kUDn * NS * kSubtileBlock +
-                     (SA ? static_cast<size_t>(2 * GR) * kActTile : 0);
+                     (SA ? static_cast<size_t>(2 * dn_sa_buffers(NS, kUDn, GR) * GR) * kActTile
+                         : 0);
   hipLaunchKernelGGL((down_mfma_kernel<NS, kUDn, GR, E8, ROWS, SA>), grid, dim3(kThreads), lds,
                      s, w, scale, sw, sscale, d.H, d.I, d.Is, d.k, d.T, SP, ws);
 }
@@ -1269,6 +1298,8 @@ hipError_t launch_gate_up_mfma(const LayerDims& d, int rows, const void* hidden,
     } else {
       if (d.e8m0) MOE_GU(true, kRoutedRows, 2, false); else MOE_GU(false, kRoutedRows, 2, false);
     }
+  } else if (routed_sa1(d)) {
+    if (d.e8m0) MOE_GU(true, kRoutedRows, kGR, true); else MOE_GU(false, kRoutedRows, kGR, true);
   } else {
     if (d.e8m0) MOE_GU(true, kRoutedRows, kGR, false);
     else MOE_GU(false, kRoutedRows, kGR, false);
@@ -1417,6 +1448,9 @@ hipError_t launch_down_mfma(const LayerDims& d, int rows, const void* w2, const 
   } else if (routed_gr2(d)) {
     if (d.e8m0) MOE_DN(kNsDnRouted, true, kRoutedRows, 2, false);
     else MOE_DN(kNsDnRouted, false, kRoutedRows, 2, false);
+  } else if (!routed_gr2(d) && routed_sa1(d)) {
+    if (d.e8m0) MOE_DN(kNsDnRouted, true, kRoutedRows, kGR, true);
+    else MOE_DN(kNsDnRouted, false, kRoutedRows, kGR, true);
   } else {
     if (d.e8m0) MOE_DN(kNsDnRouted, true, kRoutedRows, kGR, false);
     else MOE_DN(kNsDnRouted, false, kRoutedRows, kGR, false);

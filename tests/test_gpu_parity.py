@@ -66,13 +66,14 @@ def test_wide_layers_full(name, path, c_oracle):
     _case(WORKLOADS[name], c_oracle, path=path)
 
 
-@pytest.mark.parametrize("T", [48, 192, 256])
+@pytest.mark.parametrize("T", [48, 128, 192, 256])
 def test_decode_shape_many_tokens_full(T, c_oracle):
     """The decode shape (H = 4096, E = 128) with more tokens, at full size:
     the rotated block walk past 32 tokens (H is a power of two), the shared
-    expert on its own stream past 64 tokens, and from 160 tokens (10 or more
-    tokens per expert on average) the routed launches' two 16-token groups
-    per pass over the weights."""
+    expert on its own stream past 64 tokens, from 128 tokens (8 or more
+    tokens per expert on average) the routed launches' activation tiles
+    shared per workgroup, and from 160 tokens (10 or more) their two 16-token
+    groups per pass over the weights."""
     sh = WORKLOADS["decode_t16"].replace(T=T)
     _, got, _ = _case(sh, c_oracle)
     counts = np.bincount(got["ids"].ravel(), minlength=sh.E)
@@ -85,7 +86,7 @@ def test_wide_shape_max_tokens_full(c_oracle):
     """H = 6144, E = 256, e8m0 scales at the plan's 256-token maximum, full
     size: sixteen shared-expert passes on the side stream beside the routed
     launches, and one 16-token group per pass (8 tokens per expert on
-    average)."""
+    average) with the activation tiles shared per workgroup."""
     sh = WORKLOADS["wide_t64_e8m0"].replace(T=256)
     _case(sh, c_oracle)
 
