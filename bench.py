@@ -48,7 +48,8 @@ MFMA_GATE_UP_TILE = "4, 1, 1"
 MFMA_ROUTED_TILE = "4, 1"  # NS, U of the routed-only gate_up launch
 DENSE_MAX_GROUPS = 4  # 16-token groups per dense gate_up workgroup (kDenseMaxGroups)
 GR2_MIN_MEAN = 10  # the library's kGr2MinMean
-SHARED_ACT_MIN_MEAN = 16  # the library's kSharedActMinMean
+SHARED_ACT_MIN_MEAN = 10  # the library's kSharedActMinMean (two groups per pass)
+SHARED_ACT_MIN_MEAN1 = 4  # the library's kSharedActMinMean1 (one group per pass)
 FUSED_BOUNDARY_MAX_TOKENS = 16  # the library's kFusedBoundaryMaxTokens
 METRIC = "µs per MoE layer and effective HBM TB/s (fraction of peak) at 1/16/64/128 tok"
 
@@ -362,7 +363,9 @@ def dominant_kernel(md, sh, path_taken, D, routed_b, shared_b, act_b):
         # and the shared expert runs beside it (two 16-token groups per pass
         # once the routes average 10 or more tokens per expert)
         gr = 2 if T * sh.k >= GR2_MIN_MEAN * sh.E else 1
-        sa = "true" if T * sh.k >= SHARED_ACT_MIN_MEAN * sh.E else "false"
+        # activation tiles shared per workgroup from a mean that depends on gr
+        sa_min = SHARED_ACT_MIN_MEAN if gr == 2 else SHARED_ACT_MIN_MEAN1
+        sa = "true" if T * sh.k >= sa_min * sh.E else "false"
         return ("gate_up_mfma_kernel<NS, U, GR, E8, ROWS> (routed experts)",
                 "gate_up_mfma_kernel<%s, %d, %s, 2, %s>" % (MFMA_ROUTED_TILE, gr, e8, sa), kb, fl)
     if T <= CHAIN_MAX_TOKENS:

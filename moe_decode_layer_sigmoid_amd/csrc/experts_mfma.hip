@@ -626,26 +626,26 @@ constexpr int kNsDn = 4, kNsDnRouted = 8, kUDn = 1;
 constexpr int kGR = 1;  // 16-token groups per pass
 constexpr int kGr2MinMean = 10;
 bool routed_gr2(const LayerDims& d) { return d.T * d.k >= kGr2MinMean * d.E; }
-// From a mean of kSharedActMinMean tokens per expert the routed-only
-// launches load each 16-token activation tile once per workgroup into LDS
-// (SA), not once per wave.  Counters of the routed gate_up launch showed
+// The routed-only launches load each 16-token activation tile once per
+// workgroup into LDS (SA), not once per wave: from a mean of
+// kSharedActMinMean tokens per expert with two groups per pass, and of
+// kSharedActMinMean1 with one.  Counters of the routed gate_up launch showed
 // every CU issuing about 0.1 L2 read request per clock whatever the kernel,
 // activation hits included: at H = 4096, E = 128 the hits were 18% of the
 // requests at 128 tokens and 33% at 256 (9% at H = 6144, E = 256, 128
-// tokens), a share the weight misses lose.  Measured at H = 4096 (step us,
-// two GPU sessions): 256 tokens 592 -> 568 and 589 -> 572; 128 tokens
-// 476 -> 472 and 474 -> 477, 192 tokens 536 -> 529 and 534 -> 540 (the
-// workgroup barriers cost about what the requests save); 96 tokens and
-// H = 6144 at 128 tokens slower by 1-2%.
-constexpr int kSharedActMinMean = 16;
-static_assert(kSharedActMinMean >= kGr2MinMean, "shared tiles come with two groups per pass");
+// tokens), a share the weight misses lose.  The tiles alternate between two
+// buffers, so a block needs one workgroup barrier (the down launch keeps one
+// buffer, and a second barrier, where two would leave room for only one
+// workgroup per CU: dn_sa_buffers).  Measured on MI355X (us per layer,
+// against the per-wave loads): H = 4096, E = 128: 96 tokens 454.4 -> 452.9,
+// 128 tokens 474.5 -> 463.4, 160 tokens 514.1 -> 505.6, 192 tokens
+// 536.0 -> 525.7, 256 tokens 574.5 -> 562.0; H = 6144, E = 256: 128 tokens
+// 1548.7 -> 1540.1, 256 tokens 1703.5 -> 1665.9.  With two barriers per
+// block the tiles had paid only from 16 tokens per expert.
+constexpr int kSharedActMinMean = 10;
+static_assert(kSharedActMinMean >= kGr2MinMean, "this threshold is for two groups per pass");
 bool routed_sa(const LayerDims& d) { return d.T * d.k >= kSharedActMinMean * d.E; }
-// One group per pass: shared tiles from this mean on.  With the tiles
-// double-buffered (one barrier per block; the down launch's where LDS
-// allows), measured on MI355X (us per layer): H = 4096, E = 128, 128 tokens
-// 474.5 -> 463.4; H = 6144, E = 256, 256 tokens 1703.5 -> 1665.9; and with
-// two groups at H = 4096, 256 tokens 574.5 -> 562.0.
-constexpr int kSharedActMinMean1 = 8;
+constexpr int kSharedActMinMean1 = 4;
 bool routed_sa1(const LayerDims& d) { return d.T * d.k >= kSharedActMinMean1 * d.E; }
 constexpr size_t kLdsGu = static_cast<size_t>(kWaves) * kUGu * kNsGu * kSubtileBlock;
 

@@ -41,6 +41,8 @@ def test_mfma_tile_matches_library():
     assert bench.GR2_MIN_MEAN == _const(mfma, "kGr2MinMean")
     assert bench.SHARED_ACT_MIN_MEAN == _const(mfma, "kSharedActMinMean")
     assert re.search(r"d\.T \* d\.k >= kSharedActMinMean \* d\.E", mfma)
+    assert bench.SHARED_ACT_MIN_MEAN1 == _const(mfma, "kSharedActMinMean1")
+    assert re.search(r"d\.T \* d\.k >= kSharedActMinMean1 \* d\.E", mfma)
     # a dense layer's gate_up kernel takes up to kDenseMaxGroups 16-token groups
     assert bench.DENSE_MAX_GROUPS == _const(mfma, "kDenseMaxGroups")
     assert "dense_gate_up_mfma_kernel" in mfma
