@@ -646,6 +646,17 @@ constexpr int kSharedActMinMean = 10;
 static_assert(kSharedActMinMean >= kGr2MinMean, "this threshold is for two groups per pass");
 bool routed_sa(const LayerDims& d) { return d.T * d.k >= kSharedActMinMean * d.E; }
 constexpr int kSharedActMinMean1 = 4;
+// The shared expert's own launches (beside the routed-only ones, above
+// kMergeSharedMaxTokens tokens) take two 16-token groups per pass, with
+// shared activation tiles, from kSharedGr2MinTokens tokens on: each pass
+// streams the shared weights again, 16 passes at 256 tokens with one group.
+// Measured on MI355X (us per layer): H = 4096, E = 128: 160 tokens
+// 505.0 -> 495.2, 192 tokens 523.9 -> 502.3, 256 tokens 560.1 -> 532.2;
+// H = 6144, E = 256, 192 tokens 1622.6 -> 1613.0.  From 65 tokens on, the
+// shared passes' fewer and longer workgroups delayed the join: 96 tokens
+// 453.8 -> 456.8, 128 tokens 462.1 -> 464.7, and 1539 -> 1553 at H = 6144.
+constexpr int kSharedGr2MinTokens = 160;
+int shared_gr(const LayerDims& d) { return d.T >= kSharedGr2MinTokens ? 2 : kGR; }
 bool routed_sa1(const LayerDims& d) { return d.T * d.k >= kSharedActMinMean1 * d.E; }
 constexpr size_t kLdsGu = static_cast<size_t>(kWaves) * kUGu * kNsGu * kSubtileBlock;
 
@@ -1267,7 +1278,9 @@ __global__ __launch_bounds__(kThreads, 2) void dense_down_mfma_kernel(
 }
 
 // grid rows: the shared expert's passes, then the touched-expert slots
-int shared_rows(const LayerDims& d) { return d.Is > 0 ? (d.T + 16 * kGR - 1) / (16 * kGR) : 0; }
+int shared_rows(const LayerDims& d, int gr = kGR) {
+  return d.Is > 0 ? (d.T + 16 * gr - 1) / (16 * gr) : 0;
+}
 int slot_rows(const LayerDims& d) { return d.T * d.k < d.E ? d.T * d.k : d.E; }
 
 }  // namespace
@@ -1276,7 +1289,7 @@ hipError_t launch_gate_up_mfma(const LayerDims& d, int rows, const void* hidden,
                                const void* w13_scale, const void* sw13, const void* sw13_scale,
                                const Workspace& ws, hipStream_t s, hipEvent_t evb,
                                hipEvent_t eve) {
-  const int SP = rows == kRoutedRows ? 0 : shared_rows(d);
+  const int SP = rows == kRoutedRows ? 0 : shared_rows(d, rows == kSharedRows ? shared_gr(d) : kGR);
   const int R = rows == kSharedRows ? 0 : slot_rows(d);
   if (SP + R == 0) return hipSuccess;
   const int Imax = d.I > d.Is ? d.I : d.Is;
@@ -1289,6 +1302,8 @@ hipError_t launch_gate_up_mfma(const LayerDims& d, int rows, const void* hidden,
   launch_gu<E8, ROWS, GR, kNsGu, SA>(grid, s, x, w, w13_scale, sw, sw13_scale, d, SP, ws, evb, eve)
   if (rows == kAllRows) {
     if (d.e8m0) MOE_GU(true, kAllRows, kGR, false); else MOE_GU(false, kAllRows, kGR, false);
+  } else if (rows == kSharedRows && shared_gr(d) == 2) {
+    if (d.e8m0) MOE_GU(true, kSharedRows, 2, true); else MOE_GU(false, kSharedRows, 2, true);
   } else if (rows == kSharedRows) {
     if (d.e8m0) MOE_GU(true, kSharedRows, kGR, false); else MOE_GU(false, kSharedRows, kGR, false);
   } else if (routed_gr2(d)) {
@@ -1429,7 +1444,7 @@ hipError_t launch_dense_mfma(const LayerDims& d, const void* hidden, const void*
 hipError_t launch_down_mfma(const LayerDims& d, int rows, const void* w2, const void* w2_scale,
                             const void* sw2, const void* sw2_scale, const Workspace& ws,
                             hipStream_t s) {
-  const int SP = rows == kRoutedRows ? 0 : shared_rows(d);
+  const int SP = rows == kRoutedRows ? 0 : shared_rows(d, rows == kSharedRows ? shared_gr(d) : kGR);
   const int R = rows == kSharedRows ? 0 : slot_rows(d);
   if (SP + R == 0) return hipSuccess;
   const auto* w = static_cast<const uint8_t*>(w2);
@@ -1439,6 +1454,9 @@ hipError_t launch_down_mfma(const LayerDims& d, int rows, const void* w2, const 
   if (rows == kAllRows) {
     if (d.e8m0) MOE_DN(kNsDn, true, kAllRows, kGR, false);
     else MOE_DN(kNsDn, false, kAllRows, kGR, false);
+  } else if (rows == kSharedRows && shared_gr(d) == 2) {
+    if (d.e8m0) MOE_DN(kNsDn, true, kSharedRows, 2, true);
+    else MOE_DN(kNsDn, false, kSharedRows, 2, true);
   } else if (rows == kSharedRows) {
     if (d.e8m0) MOE_DN(kNsDn, true, kSharedRows, kGR, false);
     else MOE_DN(kNsDn, false, kSharedRows, kGR, false);
