@@ -50,6 +50,7 @@ DENSE_MAX_GROUPS = 4  # 16-token groups per dense gate_up workgroup (kDenseMaxGr
 GR2_MIN_MEAN = 10  # the library's kGr2MinMean
 SHARED_ACT_MIN_MEAN = 10  # the library's kSharedActMinMean (two groups per pass)
 SHARED_ACT_MIN_MEAN1 = 4  # the library's kSharedActMinMean1 (one group per pass)
+MFMA_GATE_UP_WIDE_NS = 8  # the library's kNsGuWide (two groups, shared tiles)
 FUSED_BOUNDARY_MAX_TOKENS = 16  # the library's kFusedBoundaryMaxTokens
 METRIC = "µs per MoE layer and effective HBM TB/s (fraction of peak) at 1/16/64/128 tok"
 
@@ -366,8 +367,11 @@ def dominant_kernel(md, sh, path_taken, D, routed_b, shared_b, act_b):
         # activation tiles shared per workgroup from a mean that depends on gr
         sa_min = SHARED_ACT_MIN_MEAN if gr == 2 else SHARED_ACT_MIN_MEAN1
         sa = "true" if T * sh.k >= sa_min * sh.E else "false"
+        tile = MFMA_ROUTED_TILE
+        if gr == 2 and sa == "true" and sh.I % (4 * 8 * MFMA_GATE_UP_WIDE_NS) == 0:
+            tile = "%d, 1" % MFMA_GATE_UP_WIDE_NS  # wider waves (kNsGuWide)
         return ("gate_up_mfma_kernel<NS, U, GR, E8, ROWS> (routed experts)",
-                "gate_up_mfma_kernel<%s, %d, %s, 2, %s>" % (MFMA_ROUTED_TILE, gr, e8, sa), kb, fl)
+                "gate_up_mfma_kernel<%s, %d, %s, 2, %s>" % (tile, gr, e8, sa), kb, fl)
     if T <= CHAIN_MAX_TOKENS:
         # one launch streams the touched experts' gate_up and down weights and
         # the shared expert's down weights, and ends with the boundary (the

@@ -42,6 +42,7 @@ def test_mfma_tile_matches_library():
     assert bench.SHARED_ACT_MIN_MEAN == _const(mfma, "kSharedActMinMean")
     assert re.search(r"d\.T \* d\.k >= kSharedActMinMean \* d\.E", mfma)
     assert bench.SHARED_ACT_MIN_MEAN1 == _const(mfma, "kSharedActMinMean1")
+    assert bench.MFMA_GATE_UP_WIDE_NS == _const(mfma, "kNsGuWide")
     assert re.search(r"d\.T \* d\.k >= kSharedActMinMean1 \* d\.E", mfma)
     # a dense layer's gate_up kernel takes up to kDenseMaxGroups 16-token groups
     assert bench.DENSE_MAX_GROUPS == _const(mfma, "kDenseMaxGroups")
