@@ -226,7 +226,8 @@ def test_dense_layer(T, fmt, c_oracle):
 @pytest.mark.parametrize("T,H,Is,fmt", [(16, 4096, 8192, "fp32"), (64, 4096, 8192, "e8m0"),
                                          (20, 1024, 6144, "fp32"), (33, 384, 512, "e8m0"),
                                          (5, 4096, 4096, "fp32"), (40, 1408, 640, "fp32"),
-                                         (75, 2048, 1024, "e8m0")])
+                                         (75, 2048, 1024, "e8m0"), (128, 4096, 8192, "fp32"),
+                                         (256, 2048, 3072, "e8m0")])
 def test_dense_layer_mfma_splits(T, H, Is, fmt):
     """The dense MFMA kernels at the shapes that set their contraction
     ranges and token groups: 4 and 1 gate_up ranges, 8 and 2 down ranges,
@@ -234,8 +235,9 @@ def test_dense_layer_mfma_splits(T, H, Is, fmt):
     range per launch (H = 384, I_s = 512: no hand-over of sums), the
     one-group gate_up kernel (whose waves split the contraction), two and
     four 16-token groups per gate_up workgroup, two passes of the down
-    launch, a second pass with one group (33 tokens) and a second pass whose
-    one group is partial (75 tokens); every output row against the dense
+    launch, a second pass with one group (33 tokens), a second pass whose
+    one group is partial (75 tokens), and many passes at the full size and
+    at the plan's 256-token limit; every output row against the dense
     oracle."""
     sh = LayerShape(T=T, H=H, E=0, k=0, I=0, Is=Is, scale_fmt=fmt, tag=340 + T)
     inp = make_layer(sh)
