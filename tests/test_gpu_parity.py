@@ -227,7 +227,8 @@ def test_dense_layer(T, fmt, c_oracle):
                                          (20, 1024, 6144, "fp32"), (33, 384, 512, "e8m0"),
                                          (5, 4096, 4096, "fp32"), (40, 1408, 640, "fp32"),
                                          (75, 2048, 1024, "e8m0"), (128, 4096, 8192, "fp32"),
-                                         (256, 2048, 3072, "e8m0")])
+                                         (256, 2048, 3072, "e8m0"), (1, 128, 128, "fp32"),
+                                         (40, 128, 128, "e8m0")])
 def test_dense_layer_mfma_splits(T, H, Is, fmt):
     """The dense MFMA kernels at the shapes that set their contraction
     ranges and token groups: 4 and 1 gate_up ranges, 8 and 2 down ranges,
@@ -237,7 +238,9 @@ def test_dense_layer_mfma_splits(T, H, Is, fmt):
     four 16-token groups per gate_up workgroup, two passes of the down
     launch, a second pass with one group (33 tokens), a second pass whose
     one group is partial (75 tokens), and many passes at the full size and
-    at the plan's 256-token limit; every output row against the dense
+    at the plan's 256-token limit, and the smallest layer (H = I_s = 128:
+    one contraction block, so three of the one-group kernel's waves have
+    no range, and one down tile); every output row against the dense
     oracle."""
     sh = LayerShape(T=T, H=H, E=0, k=0, I=0, Is=Is, scale_fmt=fmt, tag=340 + T)
     inp = make_layer(sh)
@@ -247,6 +250,31 @@ def test_dense_layer_mfma_splits(T, H, Is, fmt):
     got = run_layer(plan, dev, T)
     err = check_layer(inp, got)
     _log("  errors", err)
+    plan.close()
+
+
+def test_dense_token_counts_in_turn():
+    """The dense MFMA launches leave their arrival counters at zero and
+    nothing else behind: dense layers in turn on one plan (another layer's
+    weights and tokens each run), at token counts that change the grid
+    between runs (64: four gate_up ranges of four groups; 20 and 33: two
+    groups; 16 and 1: the one-group kernel; 80: two passes), each match
+    their own oracle; the first layer run again at the end is bitwise equal
+    to its first run (the last workgroup adds the ranges in range order)."""
+    base = LayerShape(T=80, H=1024, E=0, k=0, I=0, Is=2048, tag=360)
+    plan = make_plan(base, path=md.PATH_GROUPED)
+    first = None
+    for i, T in enumerate([64, 20, 16, 80, 1, 33, 64]):
+        sh = base.replace(T=T, tag=360 if i in (0, 6) else 361 + i)
+        inp = make_layer(sh)
+        _log("dense in turn", sh)
+        got = run_layer(plan, to_device(inp), T)
+        check_layer(inp, got)
+        if i == 0:
+            first = got
+        if i == 6:
+            for key in ("out", "residual_out", "moe"):
+                assert np.array_equal(first[key], got[key]), key
     plan.close()
 
 
