@@ -1054,6 +1054,11 @@ __global__ __launch_bounds__(kThreads, 2) void dense_gate_up_mfma_kernel(
 // weights, and no workgroup hands sums to another: measured on MI355X
 // (H = 4096, I_s = 8192) 16.1 us at one token against 18.6 for the
 // shared-activation kernel above, 17.6 against 17.8 at 16 tokens.
+// kDenseWavesNb blocks per round of loads.  Measured per layer at 16 tokens
+// (one token): one block (eight rounds per wave at H = 4096) 32.3 us (29.8),
+// two 33.8 (30.7), four 36.3 (32.6); eight waves per workgroup 34.3 (31.5);
+// two 16-output tiles per wave (256 workgroups) 33.3 (32.7).
+constexpr int kDenseWavesNb = 1;
 template <bool E8>
 __global__ __launch_bounds__(kThreads, 2) void dense_gate_up_waves_mfma_kernel(
     const uint16_t* __restrict__ hidden, const uint8_t* __restrict__ sw13,
@@ -1065,7 +1070,7 @@ __global__ __launch_bounds__(kThreads, 2) void dense_gate_up_waves_mfma_kernel(
   if (i0 >= Is) return;  // uniform over the workgroup
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
-  constexpr int NB = 2;                  // blocks per round of loads
+  constexpr int NB = kDenseWavesNb;      // blocks per round of loads
   constexpr int SB = 2 * kSubtileBlock;  // 16 gate + 16 up rows of one block
   unsigned char* stage = smem + wave * NB * SB;
   const int KB = H / kBlock;
@@ -1408,7 +1413,8 @@ static void launch_dense_gate_up_waves(const LayerDims& d, const uint16_t* x, co
                                        const void* s13, const Workspace& ws, hipStream_t s,
                                        hipEvent_t evb, hipEvent_t eve) {
   // the stage, or the waves' sums after it (4 waves x 8 x 64 floats)
-  const size_t lds = std::max<size_t>(kWaves * 2 * 2 * kSubtileBlock, kWaves * 8 * kWave * 4);
+  const size_t lds =
+      std::max<size_t>(kWaves * kDenseWavesNb * 2 * kSubtileBlock, kWaves * 8 * kWave * 4);
   const int units = d.Is / 16;
   const dim3 grid(static_cast<unsigned>((units + kXcds - 1) / kXcds * kXcds));
   MOE_LAUNCH((dense_gate_up_waves_mfma_kernel<E8>), grid, dim3(kThreads), lds, s, evb, eve, x,
