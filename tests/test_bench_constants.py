@@ -47,5 +47,18 @@ def test_mfma_tile_matches_library():
     # a dense layer's gate_up kernel takes up to kDenseMaxGroups 16-token groups
     assert bench.DENSE_MAX_GROUPS == _const(mfma, "kDenseMaxGroups")
     assert "dense_gate_up_mfma_kernel" in mfma
+    # bench.py names that kernel's blocks per round by the same rule
+    assert re.search(r"constexpr int NB = GR == kDenseMaxGroups \? 1 : 2;", mfma)
     # the rule bench.py applies is the library's: T * k >= kGr2MinMean * E
     assert re.search(r"d\.T \* d\.k >= kGr2MinMean \* d\.E", mfma)
+
+
+def test_bench_refuses_several_gpus():
+    """The layer runs on one GPU: asked for more, bench.py says so and exits
+    with an error before it touches a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
