@@ -349,6 +349,25 @@ def test_smaller_T_than_plan_and_zero(c_oracle):
     plan.close()
 
 
+def test_dense_smaller_T_than_plan_and_zero():
+    """A dense plan runs fewer tokens than it was made for, T = 0 launches
+    nothing and succeeds, and more tokens than the plan holds is refused."""
+    sh = LayerShape(T=5, H=1024, E=0, k=0, I=0, Is=1024, tag=370)
+    inp = make_layer(sh)
+    dev = to_device(inp)
+    plan = make_plan(sh, max_tokens=40, path=md.PATH_GROUPED)
+    check_layer(inp, run_layer(plan, dev, sh.T))
+    # (no router or routed weights: the layer has no routed experts)
+    plan.run(0, hidden=dev["hidden"], residual=dev["residual"], router_w=None, w13=None,
+             w13_scale=None, w2=None, w2_scale=None, sw13=dev["sw13"],
+             sw13_scale=dev["sw13_scale"], sw2=dev["sw2"], sw2_scale=dev["sw2_scale"],
+             gamma=dev["gamma"], out=torch.empty(1, 1024, dtype=torch.int16, device="cuda"),
+             residual_out=torch.empty(1, 1024, dtype=torch.int16, device="cuda"))
+    with pytest.raises(md.MoeDecodeError):
+        run_layer(plan, dev, 41)
+    plan.close()
+
+
 def _graph_vs_eager(sh, path):
     """One run captured into a HIP graph, replayed four times with eager runs
     in between; every replay equals the eager result bit for bit."""
