@@ -20,7 +20,25 @@ constexpr int kBndWaves = kBndThreads / kWave;
 // Polls before the slices' exchange gives up (a poll is a memory round trip
 // plus a short sleep; a legitimate wait lasts microseconds).
 constexpr uint32_t kBndSpin = 1u << 17;
-static_assert(kBndCols == 8 * kBndThreads, "a slice is 8 columns per thread");
+
+// N bf16 (N = 4 or 8, 8- or 16-byte aligned) as N / 2 packed pairs, and back.
+template <int N>
+__device__ __forceinline__ void load_bf16_pairs(const uint16_t* p, uint32_t* u) {
+  if constexpr (N == 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    u[0] = v.x; u[1] = v.y; u[2] = v.z; u[3] = v.w;
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    u[0] = v.x; u[1] = v.y;
+  }
+}
+template <int N>
+__device__ __forceinline__ void store_bf16_pairs(uint16_t* p, const uint32_t* u) {
+  if constexpr (N == 8)
+    *reinterpret_cast<uint4*>(p) = make_uint4(u[0], u[1], u[2], u[3]);
+  else
+    *reinterpret_cast<uint2*>(p) = make_uint2(u[0], u[1]);
+}
 
 // What a boundary slice reads and writes besides the workspace rows.
 struct BndArgs {
@@ -46,8 +64,8 @@ struct StepTail {
   int n_part;         // words of the boundary slots
 };
 
-// The boundary of token t, columns [kBndCols * s, +kBndCols) (8 per thread),
-// by one of the token's ns workgroups: h = sum_j w[t, j] * rows[t*k + j]
+// The boundary of token t, columns [CPT kBndThreads s, + CPT kBndThreads)
+// (CPT = 4 or 8 per thread), by one of the token's ns workgroups: h = sum_j w[t, j] * rows[t*k + j]
 // + y_s[t] + residual[t] (fixed order; with moe_out, the sum before the
 // residual goes there too); the slice's sum of squares (waves in order) goes
 // to part[t][s] as inverted bits; once every slice of the token is in, their
@@ -59,7 +77,7 @@ struct StepTail {
 // after the wait, coherently); the rest of the slice's loads all before
 // their first use.  STEP: the step launch's slice, which afterwards counts
 // itself done, and the last one clears the launch's state (`tail`).
-template <bool STEP, typename Wait>
+template <bool STEP, int CPT, typename Wait>
 __device__ __forceinline__ void boundary_slice(const BndArgs& b, const Workspace& ws, int t,
                                                int s, Wait wait, const StepTail& tail) {
   __shared__ float s_part[kBndWaves];
@@ -68,11 +86,15 @@ __device__ __forceinline__ void boundary_slice(const BndArgs& b, const Workspace
   __shared__ int s_last;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int H = b.H, k = b.k, ns = b.ns;
-  const int c = kBndCols * s + 8 * static_cast<int>(threadIdx.x);
+  static_assert(CPT == 4 || CPT == 8, "4 or 8 columns per thread");
+  constexpr int NQ = CPT / 4;  // float4 per routed row piece
+  const int c = CPT * (kBndThreads * s + static_cast<int>(threadIdx.x));
   const bool live = c < H;
-  const int c0 = live ? c : H - 8;  // clamped: loads stay in the row
-  const uint4 rv = *reinterpret_cast<const uint4*>(b.residual + static_cast<size_t>(t) * H + c0);
-  const uint4 gv = *reinterpret_cast<const uint4*>(b.gamma + c0);
+  const int c0 = live ? c : H - CPT;  // clamped: loads stay in the row
+  // residual and gamma, CPT / 2 pairs of bf16
+  uint32_t rv[CPT / 2], gv[CPT / 2];
+  load_bf16_pairs<CPT>(b.residual + static_cast<size_t>(t) * H + c0, rv);
+  load_bf16_pairs<CPT>(b.gamma + c0, gv);
   float wts[kMaxTopK];
   if (!STEP) {
 #pragma unroll
@@ -85,48 +107,59 @@ __device__ __forceinline__ void boundary_slice(const BndArgs& b, const Workspace
   }
   const float* rows_t = ws.rows + static_cast<size_t>(t) * k * H + c0;
   const float* ys = ws.y_s + static_cast<size_t>(t) * H + c0;
-  const float4 ya = *reinterpret_cast<const float4*>(ys);
-  const float4 yb = *reinterpret_cast<const float4*>(ys + 4);
-  float acc[8];
+  float4 yv[NQ];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) acc[m] = 0.f;
+  for (int h = 0; h < NQ; ++h) yv[h] = *reinterpret_cast<const float4*>(ys + 4 * h);
+  float acc[CPT];
+#pragma unroll
+  for (int m = 0; m < CPT; ++m) acc[m] = 0.f;
 #pragma unroll
   for (int j0 = 0; j0 < kMaxTopK; j0 += 8) {
     if (j0 >= k) break;  // uniform
-    float4 ra[8], rb[8];
+    float4 r[8][NQ];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int j = j0 + q < k ? j0 + q : k - 1;  // clamped: no branch around the loads
-      ra[q] = *reinterpret_cast<const float4*>(rows_t + static_cast<size_t>(j) * H);
-      rb[q] = *reinterpret_cast<const float4*>(rows_t + static_cast<size_t>(j) * H + 4);
+#pragma unroll
+      for (int h = 0; h < NQ; ++h)
+        r[q][h] = *reinterpret_cast<const float4*>(rows_t + static_cast<size_t>(j) * H + 4 * h);
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const float w = j0 + q < k ? wts[j0 + q] : 0.f;
-      acc[0] = fmaf(w, ra[q].x, acc[0]);
-      acc[1] = fmaf(w, ra[q].y, acc[1]);
-      acc[2] = fmaf(w, ra[q].z, acc[2]);
-      acc[3] = fmaf(w, ra[q].w, acc[3]);
-      acc[4] = fmaf(w, rb[q].x, acc[4]);
-      acc[5] = fmaf(w, rb[q].y, acc[5]);
-      acc[6] = fmaf(w, rb[q].z, acc[6]);
-      acc[7] = fmaf(w, rb[q].w, acc[7]);
+#pragma unroll
+      for (int h = 0; h < NQ; ++h) {
+        acc[4 * h + 0] = fmaf(w, r[q][h].x, acc[4 * h + 0]);
+        acc[4 * h + 1] = fmaf(w, r[q][h].y, acc[4 * h + 1]);
+        acc[4 * h + 2] = fmaf(w, r[q][h].z, acc[4 * h + 2]);
+        acc[4 * h + 3] = fmaf(w, r[q][h].w, acc[4 * h + 3]);
+      }
     }
   }
   if (b.Is > 0) {
-    acc[0] += ya.x; acc[1] += ya.y; acc[2] += ya.z; acc[3] += ya.w;
-    acc[4] += yb.x; acc[5] += yb.y; acc[6] += yb.z; acc[7] += yb.w;
-  }
-  if (b.moe_out && live) store_bf16x8(b.moe_out + static_cast<size_t>(t) * H + c, acc);
-  const uint32_t u[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    acc[2 * m] += bf16_lo(u[m]);
-    acc[2 * m + 1] += bf16_hi(u[m]);
+    for (int h = 0; h < NQ; ++h) {
+      acc[4 * h + 0] += yv[h].x;
+      acc[4 * h + 1] += yv[h].y;
+      acc[4 * h + 2] += yv[h].z;
+      acc[4 * h + 3] += yv[h].w;
+    }
+  }
+  if (b.moe_out && live) {
+    uint32_t w[CPT / 2];
+#pragma unroll
+    for (int m = 0; m < CPT / 2; ++m)
+      w[m] = f32_to_bf16(acc[2 * m]) | (f32_to_bf16(acc[2 * m + 1]) << 16);
+    store_bf16_pairs<CPT>(b.moe_out + static_cast<size_t>(t) * H + c, w);
+  }
+#pragma unroll
+  for (int m = 0; m < CPT / 2; ++m) {
+    acc[2 * m] += bf16_lo(rv[m]);
+    acc[2 * m + 1] += bf16_hi(rv[m]);
   }
   float ss = 0.f;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) ss = fmaf(acc[m], acc[m], ss);
+  for (int m = 0; m < CPT; ++m) ss = fmaf(acc[m], acc[m], ss);
   ss = wave_sum(live ? ss : 0.f);
   if (lane == 0) s_part[wave] = ss;
   __syncthreads();
@@ -167,20 +200,17 @@ __device__ __forceinline__ void boundary_slice(const BndArgs& b, const Workspace
   for (int i = 0; i < ns; ++i) tot += s_tot[i];
   const float inv_rms = 1.0f / sqrtf(tot / static_cast<float>(H) + b.eps);
   if (live) {
-    const uint32_t g[4] = {gv.x, gv.y, gv.z, gv.w};
-    uint32_t o[4], r[4];
+    uint32_t o[CPT / 2], r[CPT / 2];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < CPT / 2; ++m) {
       const float h0 = acc[2 * m], h1 = acc[2 * m + 1];
-      o[m] = f32_to_bf16(h0 * inv_rms * bf16_lo(g[m])) |
-             (f32_to_bf16(h1 * inv_rms * bf16_hi(g[m])) << 16);
+      o[m] = f32_to_bf16(h0 * inv_rms * bf16_lo(gv[m])) |
+             (f32_to_bf16(h1 * inv_rms * bf16_hi(gv[m])) << 16);
       r[m] = f32_to_bf16(h0) | (f32_to_bf16(h1) << 16);
       if (gave_up) o[m] = kBf16NanPair;
     }
-    *reinterpret_cast<uint4*>(b.out + static_cast<size_t>(t) * H + c) =
-        make_uint4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<uint4*>(b.residual_out + static_cast<size_t>(t) * H + c) =
-        make_uint4(r[0], r[1], r[2], r[3]);
+    store_bf16_pairs<CPT>(b.out + static_cast<size_t>(t) * H + c, o);
+    store_bf16_pairs<CPT>(b.residual_out + static_cast<size_t>(t) * H + c, r);
   }
   if (STEP) {
     if (threadIdx.x == 0) s_last = prev + 1 == tail.total;

@@ -23,8 +23,8 @@
 //   routed down      32 (or 16) output rows of one touched slot; it issues its
 //                    weight loads first and then waits for the slot's gate_up
 //                    count, so the down weights stream while gate_up ends
-//   boundary         the last T * ceil(H / 2048) workgroups: after every
-//                    down item, combine + shared + residual of a 2048-column
+//   boundary         the last T * ceil(H / 1024) workgroups: after every
+//                    down item, combine + shared + residual of a 1024-column
 //                    slice of one token, the slices' sums of squares
 //                    exchanged, then RMSNorm * gamma of the slice
 // decode_step_kernel (the whole step):
@@ -36,7 +36,8 @@
 //   shared gate_up   8 SwiGLU rows of the shared expert (no routing needed:
 //                    its weights stream while the router runs)
 //   shared down      as above, after every shared gate_up item
-//   routed gate_up, routed down, boundary: as above.  At one token each
+//   routed gate_up, routed down, boundary: as above (2048-column boundary
+//                    slices).  At one token each
 //                    routed item finds its slot's expert itself, from the
 //                    logits (it polls them until every router item has
 //                    stored its logits, then runs the same selection as the
@@ -59,9 +60,10 @@
 // counters, the boundary slots) is written and read coherently.
 // A workgroup waits only for workgroups of lower index, which the dispatcher
 // has started before it (workgroups are dispatched in index order), except
-// that a token's boundary slices wait for each other: all T * ceil(H / 2048)
-// (at most 64) boundary workgroups must be resident together, which they are
-// once every other item has ended.  Every wait is bounded anyway: an
+// that a token's boundary slices wait for each other: all of a launch's
+// boundary workgroups (T * ceil(H / 1024) in the chain, T * ceil(H / 2048)
+// in the step launch, at most 128) must be resident together, which they
+// are once every other item has ended.  Every wait is bounded anyway: an
 // exhausted wait sets the sticky error word (moe_decode_check_waits) and
 // goes on, and the boundary then writes NaN to out.  Completion counts are
 // bumped with atomics whose result is not used.
@@ -158,7 +160,8 @@ __global__ __launch_bounds__(kThreads) void expert_chain_kernel(ChainArgs a, Wor
   const int b = it - a.n_items;
   const BndArgs bn{a.residual, a.gamma, a.out, a.residual_out, a.moe_out, H, k, a.Is, a.bnd_ns,
                    a.eps, ws.epi_part, sy.line(kSyncError)};
-  boundary_slice<false>(bn, ws, b / a.bnd_ns, b % a.bnd_ns, [&]() {
+  constexpr int kCpt = kBndColsChain / kBndThreads;
+  boundary_slice<false, kCpt>(bn, ws, b / a.bnd_ns, b % a.bnd_ns, [&]() {
     wait_count(sy, kSyncExit0, kSyncExitLines, static_cast<uint32_t>(a.n_items - a.gu_items),
                kChainSpin);
   }, StepTail{});
@@ -348,7 +351,8 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(StepArgs a, Works
   const StepTail tail{sy.line(kStepBnd), static_cast<uint32_t>(T * a.bnd_ns), ws.msync,
                       step_sync_lines(a.dmax), ws.mlogits, kFlagRep * T * E,
                       T * kMaxBndSlices};
-  boundary_slice<true>(bn, ws, b / a.bnd_ns, b % a.bnd_ns, [&]() {
+  constexpr int kCpt = kBndCols / kBndThreads;
+  boundary_slice<true, kCpt>(bn, ws, b / a.bnd_ns, b % a.bnd_ns, [&]() {
     wait_count(sy, kStepExit0, kSyncExitLines, static_cast<uint32_t>(a.n_items), kChainSpin, err);
   }, tail);
 }
@@ -425,7 +429,7 @@ void chain_items(const LayerDims& d, ChainArgs* a) {
   a->o_rdn = a->o_rgu + a->dmax * a->gu_per;
   a->n_items = a->o_rdn + a->dmax * a->dn_per;
   a->gu_items = a->dmax * a->gu_per;
-  a->bnd_ns = (d.H + kBndCols - 1) / kBndCols;
+  a->bnd_ns = (d.H + kBndColsChain - 1) / kBndColsChain;
   a->grid = static_cast<uint32_t>(a->n_items + d.T * a->bnd_ns);
 }
 

@@ -749,7 +749,8 @@ __global__ __launch_bounds__(kThreads, 4) void grouped_chain_kernel(GChainArgs a
   const int b = v - a.n_dn;
   const BndArgs bn{a.residual, a.gamma, a.out, a.residual_out, a.moe_out, a.H, a.k, a.Is,
                    a.bnd_ns, a.eps, ws.epi_part, sy.line(kSyncError)};
-  boundary_slice<false>(bn, ws, b / a.bnd_ns, b % a.bnd_ns, [&]() {
+  constexpr int kCpt = kBndCols / kBndThreads;
+  boundary_slice<false, kCpt>(bn, ws, b / a.bnd_ns, b % a.bnd_ns, [&]() {
     wait_count(sy, kSyncExit0, kSyncExitLines, static_cast<uint32_t>(a.n_dn), kGChainSpin);
   }, StepTail{});
 }

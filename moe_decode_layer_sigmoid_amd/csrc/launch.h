@@ -124,8 +124,15 @@ constexpr int kDenseGroupedMinTokens = 1;
 // Arguments of the expert chain launch of the few-token GEMV path (see
 // experts_chain.hip): item offsets and counts, the grid (items + 1).
 constexpr int kChainMaxTokens = 16;
-constexpr int kBndCols = 2048;     // columns of one boundary workgroup (8 per thread)
-constexpr int kMaxBndSlices = 4;   // H <= 8192
+// Columns of one boundary workgroup: 2048 (8 per thread) in the grouped
+// merged launch and the single-launch step, 1024 (4 per thread) in the
+// expert chain.  Measured on MI355X (us per layer, H = 4096): 1024-column
+// slices took one token 48.0 -> 47.4 and two 76.9 -> 76.5 in the chain, and
+// 16 tokens 276.1 -> 279.5 in the grouped launch (twice the workgroups
+// exchanging their sums).
+constexpr int kBndCols = 2048;
+constexpr int kBndColsChain = 1024;
+constexpr int kMaxBndSlices = 8;   // H <= 8192 at 1024 columns
 struct ChainArgs {
   const uint16_t* hidden;
   const uint16_t* residual;
