@@ -127,9 +127,9 @@ constexpr int kChainMaxTokens = 16;
 // Columns of one boundary workgroup: 2048 (8 per thread) in the grouped
 // merged launch and the single-launch step, 1024 (4 per thread) in the
 // expert chain.  Measured on MI355X (us per layer, H = 4096): 1024-column
-// slices took one token 48.0 -> 47.4 and two 76.9 -> 76.5 in the chain, and
-// 16 tokens 276.1 -> 279.5 in the grouped launch (twice the workgroups
-// exchanging their sums).
+// slices took one token 48.0 -> 47.4 and two 76.9 -> 76.5 in the chain
+// (512-column slices: no further gain), and 16 tokens 276.1 -> 279.5 in the
+// grouped launch (twice the workgroups exchanging their sums).
 constexpr int kBndCols = 2048;
 constexpr int kBndColsChain = 1024;
 constexpr int kMaxBndSlices = 8;   // H <= 8192 at 1024 columns
