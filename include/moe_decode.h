@@ -106,8 +106,8 @@ typedef enum {
  * constructors).  Limits: H, I and Is multiples of 128 with H <= 8192,
  * I <= 8192 and Is <= 8192; 1 <= top_k <= 16; top_k <= E <= 1024;
  * 1 <= max_tokens <= 256.  shared_intermediate = 0 means no shared expert.
- * num_experts = 0 (with top_k = 0, intermediate ignored, shared_intermediate
- * > 0) is a dense layer: its fp8 clamped-SwiGLU MLP (the decode page's
+ * num_experts = 0 (with top_k = 0, shared_intermediate > 0, and intermediate
+ * unused: 0, or any size within the limits) is a dense layer: its fp8 clamped-SwiGLU MLP (the decode page's
  * DenseMlp, LayerStages._build_dense) goes in the shared-expert slot
  * (sw13, sw2 and their scales), the router and routed-expert pointers may be
  * NULL, and a run computes out, residual_out and moe_out (= the MLP output)

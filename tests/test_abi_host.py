@@ -8,6 +8,7 @@ import os
 import re
 
 import pytest
+from hypothesis import given, settings, strategies as st
 
 import moe_decode_layer_sigmoid_amd as md
 
@@ -144,3 +145,40 @@ def test_strerror_and_null_plan():
     out = ctypes.c_void_p(1)
     assert lib.moe_decode_plan(None, 0, ctypes.byref(out)) == md.ERR_INVALID_ARG
     assert not out.value
+
+
+def _expected_desc_code(H, E, k, I, Is, T, fmt, path, limit, eps):
+    """The descriptor rules as include/moe_decode.h states them: INVALID_ARG
+    for a non-positive or negative size, a bad enum or constant, or a layer
+    that is neither a MoE layer (k >= 1, I > 0) nor a dense one (E = k = 0
+    with a shared-expert slot); UNSUPPORTED outside the size limits."""
+    if H <= 0 or E < 0 or k < 0 or I < 0 or Is < 0 or T <= 0:
+        return md.ERR_INVALID_ARG
+    if (E == 0 and (k != 0 or Is == 0)) or (E > 0 and (k == 0 or I == 0)):
+        return md.ERR_INVALID_ARG
+    if fmt not in (md.SCALE_FP32, md.SCALE_E8M0) or path not in (0, 1, 2, 3):
+        return md.ERR_INVALID_ARG
+    if not limit > 0 or not eps >= 0:
+        return md.ERR_INVALID_ARG
+    if H % 128 or I % 128 or Is % 128 or max(H, I, Is) > 8192:
+        return md.ERR_UNSUPPORTED
+    if k > 16 or k > E or E > 1024 or T > 256:
+        return md.ERR_UNSUPPORTED
+    return md.OK
+
+
+SIZES = [-128, 0, 64, 100, 128, 1536, 4096, 8192, 8320]
+
+
+@settings(max_examples=400, deadline=None)
+@given(H=st.sampled_from(SIZES), E=st.sampled_from([-1, 0, 1, 8, 128, 1024, 1025]),
+       k=st.sampled_from([-1, 0, 1, 2, 8, 16, 17]), I=st.sampled_from(SIZES),
+       Is=st.sampled_from(SIZES), T=st.sampled_from([-1, 0, 1, 16, 256, 257]),
+       fmt=st.sampled_from([0, 1, 2, -1]), path=st.sampled_from([0, 1, 2, 3, 4, -1]),
+       limit=st.sampled_from([7.0, 0.0, -1.0, float("nan")]),
+       eps=st.sampled_from([1e-5, 0.0, -1e-6, float("nan")]))
+def test_desc_check_matches_documented_rules(H, E, k, I, Is, T, fmt, path, limit, eps):
+    """moe_decode_desc_check on descriptors drawn around every limit agrees
+    with the rules the header documents."""
+    d = md.make_desc(H, E, k, I, Is, T, scale_fmt=fmt, path=path, limit=limit, eps=eps)
+    assert md.desc_check(d) == _expected_desc_code(H, E, k, I, Is, T, fmt, path, limit, eps)
