@@ -15,7 +15,7 @@
 
 namespace moe {
 
-constexpr int kBndThreads = 256;  // threads of a boundary workgroup (8 columns each)
+constexpr int kBndThreads = 256;  // threads of a boundary workgroup (4 or 8 columns each)
 constexpr int kBndWaves = kBndThreads / kWave;
 // Polls before the slices' exchange gives up (a poll is a memory round trip
 // plus a short sleep; a legitimate wait lasts microseconds).
